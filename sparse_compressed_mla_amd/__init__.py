@@ -1,0 +1,12 @@
+"""Quantized sparse shared-KV MLA attention for AMD MI355X (gfx950).
+
+The compute path is the HIP library libcsmla.so (C ABI: include/csmla.h);
+this package is its thin ctypes binding.  There is no CPU fallback: the
+binding raises if the library is missing.
+"""
+from .binding import (  # noqa: F401
+    CsmlaProblem, CsmlaHostLengths, CsmlaTensors, CsmlaError, Plan,
+    csmla_abi_version, csmla_status_string, csmla_last_error, csmla_metadata_words,
+    csmla_validate, csmla_plan, csmla_forward, csmla_debug_resolve,
+    problem_from, host_lengths_from, tensors_from, forward, debug_resolve, load, LIB_PATH,
+)

@@ -1,0 +1,286 @@
+"""ctypes binding of the C ABI in include/csmla.h (argument marshalling only).
+
+Every step of the attention runs inside libcsmla.so on the GPU.  This module
+only converts Python / torch objects into the ABI's plain structs and
+pointers; it has no compute path of its own and raises if the library is
+missing.  torch provides device memory and the HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsmla.so")
+
+CSMLA_METADATA_WORDS = 1024
+LAYOUTS = {"BSND": 0, "TND": 1, "PA_BBND": 2}
+
+STATUS = {0: "CSMLA_OK", 1: "CSMLA_ERR_INVALID_ARG", 2: "CSMLA_ERR_UNSUPPORTED", 3: "CSMLA_ERR_WORKSPACE",
+          4: "CSMLA_ERR_METADATA_MISMATCH", 5: "CSMLA_ERR_HIP"}
+
+_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+
+
+class CsmlaProblem(ctypes.Structure):
+    _fields_ = [(n, _i32) for n in (
+        "batch", "n1", "n2", "d", "layout_q", "layout_kv", "q_s", "t1", "ori_s", "cmp_s",
+        "ori_block_size", "cmp_block_size", "ori_num_blocks", "cmp_num_blocks",
+        "ori_table_cols", "cmp_table_cols", "has_cmp", "topk")] + [("softmax_scale", ctypes.c_float)] + [
+        (n, _i32) for n in ("cmp_ratio", "ori_mask_mode", "cmp_mask_mode", "ori_win_left", "ori_win_right",
+                            "kv_scale_mode", "q_descale_per_head", "topk_value_mode", "return_softmax_lse")]
+
+
+class CsmlaHostLengths(ctypes.Structure):
+    _fields_ = [(n, _p) for n in (
+        "cu_seqlens_q", "seqused_q", "seqused_ori_kv", "cu_seqlens_ori_kv", "seqused_cmp_kv",
+        "cu_seqlens_cmp_kv", "cmp_residual_kv", "cmp_topk_length")]
+
+
+TENSOR_FIELDS = ("q", "q_descale", "ori_kv", "ori_kv_descale", "cmp_kv", "cmp_kv_descale", "cmp_sparse_indices",
+                 "ori_block_table", "cmp_block_table", "cu_seqlens_q", "cu_seqlens_ori_kv", "cu_seqlens_cmp_kv",
+                 "seqused_q", "seqused_ori_kv", "seqused_cmp_kv", "cmp_residual_kv", "cmp_topk_length", "sinks",
+                 "attn_out", "softmax_lse", "workspace")
+
+
+class CsmlaTensors(ctypes.Structure):
+    _fields_ = [(n, _p) for n in TENSOR_FIELDS] + [("workspace_bytes", ctypes.c_size_t)]
+
+
+class CsmlaError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libcsmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    lib.csmla_abi_version.restype = ctypes.c_int
+    lib.csmla_status_string.restype = ctypes.c_char_p
+    lib.csmla_status_string.argtypes = [ctypes.c_int]
+    lib.csmla_last_error.restype = ctypes.c_char_p
+    lib.csmla_metadata_words.restype = ctypes.c_size_t
+    lib.csmla_validate.restype = ctypes.c_int
+    lib.csmla_validate.argtypes = [ctypes.POINTER(CsmlaProblem)]
+    lib.csmla_plan.restype = ctypes.c_int
+    lib.csmla_plan.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaHostLengths),
+                               ctypes.POINTER(_i32), ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
+    lib.csmla_forward.restype = ctypes.c_int
+    lib.csmla_forward.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaTensors),
+                                  ctypes.POINTER(_i32), _p]
+    lib.csmla_debug_resolve.restype = ctypes.c_int
+    lib.csmla_debug_resolve.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaTensors),
+                                        _p, _p, _i32, _p]
+    _lib = lib
+    return lib
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise CsmlaError(st, where, load().csmla_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# the C entry points, same names
+# ---------------------------------------------------------------------------
+
+def csmla_abi_version() -> int:
+    return load().csmla_abi_version()
+
+
+def csmla_status_string(status: int) -> str:
+    return load().csmla_status_string(status).decode()
+
+
+def csmla_last_error() -> str:
+    return load().csmla_last_error().decode()
+
+
+def csmla_metadata_words() -> int:
+    return int(load().csmla_metadata_words())
+
+
+def csmla_validate(problem: CsmlaProblem) -> int:
+    return load().csmla_validate(ctypes.byref(problem))
+
+
+def csmla_plan(problem: CsmlaProblem, lengths: Optional[CsmlaHostLengths] = None,
+               raise_on_error: bool = True) -> Tuple[int, np.ndarray, int]:
+    """Returns (status, int32[1024] metadata, workspace bytes)."""
+    md = np.zeros(CSMLA_METADATA_WORDS, dtype=np.int32)
+    ws = ctypes.c_size_t(0)
+    st = load().csmla_plan(ctypes.byref(problem), ctypes.byref(lengths) if lengths is not None else None,
+                           md.ctypes.data_as(ctypes.POINTER(_i32)), md.size, ctypes.byref(ws))
+    if raise_on_error:
+        _check(st, "csmla_plan")
+    return st, md, int(ws.value)
+
+
+def csmla_forward(problem: CsmlaProblem, tensors: CsmlaTensors, metadata: np.ndarray, stream: int = 0,
+                  raise_on_error: bool = True) -> int:
+    md = np.ascontiguousarray(metadata, dtype=np.int32)
+    st = load().csmla_forward(ctypes.byref(problem), ctypes.byref(tensors),
+                              md.ctypes.data_as(ctypes.POINTER(_i32)), _p(stream))
+    if raise_on_error:
+        _check(st, "csmla_forward")
+    return st
+
+
+def csmla_debug_resolve(problem: CsmlaProblem, tensors: CsmlaTensors, keys_ptr: int, counts_ptr: int,
+                        max_keys: int, stream: int = 0) -> int:
+    st = load().csmla_debug_resolve(ctypes.byref(problem), ctypes.byref(tensors), _p(keys_ptr), _p(counts_ptr),
+                                    max_keys, _p(stream))
+    _check(st, "csmla_debug_resolve")
+    return st
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers for torch tensors
+# ---------------------------------------------------------------------------
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    return int(x.data_ptr())
+
+
+def problem_from(inp) -> CsmlaProblem:
+    """Fill the problem struct from an object with the pages' tensor names
+    (q, ori_kv, ... as torch tensors) and attributes."""
+    p = CsmlaProblem()
+    p.batch = int(inp.batch)
+    p.n1 = int(inp.q.shape[1])
+    p.n2 = 1
+    p.d = int(inp.q.shape[2])
+    p.layout_q = LAYOUTS[inp.layout_q]
+    p.layout_kv = LAYOUTS[inp.layout_kv]
+    p.q_s = int(inp.q_s)
+    p.t1 = int(inp.q.shape[0])
+    if inp.layout_kv == "PA_BBND":
+        p.ori_block_size = int(inp.ori_kv.shape[1])
+        p.ori_num_blocks = int(inp.ori_kv.shape[0])
+        p.ori_table_cols = int(inp.ori_block_table.shape[1])
+    elif inp.layout_kv == "BSND":
+        p.ori_s = int(inp.ori_kv.shape[1])
+    else:
+        p.ori_s = int(inp.ori_kv.shape[0])
+    if inp.cmp_kv is not None:
+        p.has_cmp = 1
+        if inp.layout_kv == "PA_BBND":
+            p.cmp_block_size = int(inp.cmp_kv.shape[1])
+            p.cmp_num_blocks = int(inp.cmp_kv.shape[0])
+            p.cmp_table_cols = int(inp.cmp_block_table.shape[1])
+        elif inp.layout_kv == "BSND":
+            p.cmp_s = int(inp.cmp_kv.shape[1])
+        else:
+            p.cmp_s = int(inp.cmp_kv.shape[0])
+    p.topk = 0 if inp.cmp_sparse_indices is None else int(inp.cmp_sparse_indices.shape[-1])
+    p.softmax_scale = float(inp.softmax_scale)
+    p.cmp_ratio = int(inp.cmp_ratio)
+    p.ori_mask_mode = int(inp.ori_mask_mode)
+    p.cmp_mask_mode = int(inp.cmp_mask_mode)
+    p.ori_win_left = int(inp.ori_win_left) if inp.ori_mask_mode == 4 else -1
+    p.ori_win_right = int(inp.ori_win_right) if inp.ori_mask_mode == 4 else -1
+    p.kv_scale_mode = int(inp.kv_scale_mode)
+    p.q_descale_per_head = 1 if inp.q_descale.dim() == 2 else 0
+    p.topk_value_mode = 0
+    p.return_softmax_lse = 1 if inp.return_lse else 0
+    return p
+
+
+_LEN_NAMES = ("cu_seqlens_q", "seqused_q", "seqused_ori_kv", "cu_seqlens_ori_kv", "seqused_cmp_kv",
+              "cu_seqlens_cmp_kv", "cmp_residual_kv", "cmp_topk_length")
+
+
+def host_lengths_from(inp):
+    """Host copies of the length tensors (kept alive by the returned list)."""
+    keep = []
+    hl = CsmlaHostLengths()
+    for n in _LEN_NAMES:
+        x = getattr(inp, n, None)
+        if x is None:
+            continue
+        arr = np.ascontiguousarray(x.detach().cpu().numpy().astype(np.int32))
+        keep.append(arr)
+        setattr(hl, n, arr.ctypes.data)
+    return hl, keep
+
+
+def tensors_from(inp, out, lse, workspace=None) -> CsmlaTensors:
+    """Device pointers of the inputs (attributes of `inp`) and the outputs."""
+    t = CsmlaTensors()
+    for n in TENSOR_FIELDS:
+        if n in ("attn_out", "softmax_lse", "workspace"):
+            continue
+        v = getattr(inp, n, None)
+        if v is not None:
+            setattr(t, n, _ptr(v))
+    t.attn_out = _ptr(out)
+    t.softmax_lse = _ptr(lse)
+    if workspace is not None:
+        t.workspace = _ptr(workspace)
+        t.workspace_bytes = int(workspace.numel() * workspace.element_size())
+    return t
+
+
+class Plan:
+    """A planned call: problem struct, metadata and workspace size."""
+
+    def __init__(self, inp, lengths: bool = True):
+        self.problem = problem_from(inp)
+        hl, keep = host_lengths_from(inp) if lengths else (None, [])
+        _, self.metadata, self.workspace_bytes = csmla_plan(self.problem, hl)
+        self._keep = keep
+
+    @property
+    def splits(self) -> int:
+        return int(self.metadata[5])
+
+    @property
+    def grid(self) -> int:
+        return int(self.metadata[7])
+
+
+def forward(inp, out=None, lse=None, workspace=None, plan: Optional[Plan] = None, stream=None):
+    """Run the attention on inputs already on the GPU.  Allocates the outputs
+    (and the workspace) with torch when they are not given.  Returns (out, lse)."""
+    import torch
+    plan = plan or Plan(inp)
+    dev = inp.q.device
+    if out is None:
+        out = torch.empty(inp.q.shape, dtype=torch.bfloat16, device=dev)
+    if lse is None and inp.return_lse:
+        lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device=dev)
+    if workspace is None and plan.workspace_bytes > 0:
+        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    t = tensors_from(inp, out, lse, workspace)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
+    csmla_forward(plan.problem, t, plan.metadata, s)
+    return out, lse
+
+
+def debug_resolve(inp, max_keys: int, stream=None):
+    """Resolved physical rows per query token (the kernels' resolution code).
+    Returns (keys int32 [t1, max_keys], counts int32 [t1, 2]) on the GPU."""
+    import torch
+    dev = inp.q.device
+    keys = torch.full((inp.q.shape[0], max_keys), -1, dtype=torch.int32, device=dev)
+    counts = torch.zeros((inp.q.shape[0], 2), dtype=torch.int32, device=dev)
+    p = problem_from(inp)
+    t = tensors_from(inp, None, None)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
+    csmla_debug_resolve(p, t, _ptr(keys), _ptr(counts), max_keys, s)
+    return keys, counts

@@ -1,0 +1,399 @@
+// Host side of the C ABI: validation against the pages' constraints, the
+// split planner (the counterpart of QuantSparseFlashMlaMetadata), and the
+// marshalling of csmla_forward / csmla_debug_resolve into kernel launches.
+// No device memory is allocated here and nothing synchronises.
+#include "../../include/csmla.h"
+#include "csmla_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace csmla;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+csmla_status fail(csmla_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+uint32_t fnv1a(const void* data, size_t n, uint32_t h = 2166136261u) {
+  const uint8_t* p = static_cast<const uint8_t*>(data);
+  for (size_t i = 0; i < n; ++i) { h ^= p[i]; h *= 16777619u; }
+  return h;
+}
+
+uint32_t problem_hash(const csmla_problem* p) {
+  return fnv1a(p, sizeof(csmla_problem)) & 0x7fffffffu;
+}
+
+int64_t floordiv64(int64_t a, int64_t b) {
+  int64_t q = a / b;
+  if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+  return q;
+}
+
+// Per-token key counts from host lengths: exact band size and an upper bound
+// of the compressed part (indices may be -1).  Mirrors the device resolution.
+struct TokCost { int64_t n_o, n_c_up; };
+
+std::vector<TokCost> token_costs(const csmla_problem* p, const csmla_host_lengths* hl) {
+  std::vector<TokCost> out;
+  out.reserve(p->t1);
+  const csmla_host_lengths empty{};
+  const csmla_host_lengths& h = hl ? *hl : empty;
+  const int B = p->batch;
+  for (int b = 0; b < B; ++b) {
+    int64_t q0, span;
+    if (p->layout_q == CSMLA_LAYOUT_TND) {
+      if (h.cu_seqlens_q) { q0 = h.cu_seqlens_q[b]; span = h.cu_seqlens_q[b + 1] - q0; }
+      else { // unknown split of t1 over batches: spread evenly (estimate only)
+        q0 = (int64_t)p->t1 * b / B; span = (int64_t)p->t1 * (b + 1) / B - q0;
+      }
+    } else { q0 = (int64_t)b * p->q_s; span = p->q_s; }
+    int64_t s1 = span;
+    if (h.seqused_q) s1 = std::min<int64_t>(span, h.seqused_q[b]);
+    int64_t s2;
+    if (h.seqused_ori_kv) s2 = h.seqused_ori_kv[b];
+    else if (h.cu_seqlens_ori_kv) s2 = h.cu_seqlens_ori_kv[b + 1] - h.cu_seqlens_ori_kv[b];
+    else if (p->layout_kv == CSMLA_LAYOUT_PA_BBND) s2 = (int64_t)p->ori_table_cols * p->ori_block_size;
+    else s2 = p->ori_s;
+    int64_t c = 0;
+    const int r = p->cmp_ratio;
+    if (p->has_cmp) {
+      if (h.seqused_cmp_kv) c = h.seqused_cmp_kv[b];
+      else if (h.cu_seqlens_cmp_kv) c = h.cu_seqlens_cmp_kv[b + 1] - h.cu_seqlens_cmp_kv[b];
+      else if (p->layout_kv == CSMLA_LAYOUT_BSND) c = p->cmp_s;
+      else if (p->layout_kv == CSMLA_LAYOUT_PA_BBND) c = s2 / r;
+      else c = p->cmp_s;
+    }
+    const int64_t res = h.cmp_residual_kv ? h.cmp_residual_kv[b] : 0;
+    const int64_t L = c * r + res;
+    for (int64_t i = 0; i < span; ++i) {
+      TokCost tc{0, 0};
+      if (i < s1) {
+        const int64_t pos = s2 - s1 + i;
+        int64_t lo = 0, hi = s2;
+        if (p->ori_mask_mode == CSMLA_MASK_RIGHT_DOWN_CAUSAL) hi = std::max<int64_t>(0, std::min<int64_t>(s2, pos + 1));
+        if (p->ori_mask_mode == CSMLA_MASK_BAND) {
+          lo = p->ori_win_left < 0 ? 0 : std::max<int64_t>(0, pos - p->ori_win_left);
+          hi = p->ori_win_right < 0 ? s2 : std::max<int64_t>(0, std::min<int64_t>(s2, pos + p->ori_win_right + 1));
+          hi = std::max(hi, lo);
+        }
+        tc.n_o = hi - lo;
+        if (p->has_cmp) {
+          int64_t vis = c;
+          if (p->cmp_mask_mode == CSMLA_MASK_RIGHT_DOWN_CAUSAL)
+            vis = std::max<int64_t>(0, std::min<int64_t>(c, floordiv64(L - s1 + i + 1, r)));
+          if (p->topk > 0) {
+            int64_t k = p->topk;
+            const int64_t t = q0 + i;
+            if (h.cmp_topk_length && t < p->t1) k = std::max<int64_t>(0, std::min<int64_t>(k, h.cmp_topk_length[t]));
+            tc.n_c_up = std::min(k, vis);
+          } else {
+            tc.n_c_up = vis;
+          }
+        }
+      }
+      out.push_back(tc);
+    }
+  }
+  if ((int)out.size() != p->t1) out.resize(p->t1, TokCost{0, 0});
+  return out;
+}
+
+uint32_t lengths_hash(const csmla_problem* p, const csmla_host_lengths* hl) {
+  if (!hl) return 0;
+  uint32_t h = 2166136261u;
+  const int B = p->batch;
+  auto mix = [&](const int32_t* a, size_t n, uint32_t tag) {
+    h = fnv1a(&tag, 4, h);
+    if (a) h = fnv1a(a, n * 4, h);
+  };
+  mix(hl->cu_seqlens_q, B + 1, 1);
+  mix(hl->seqused_q, B, 2);
+  mix(hl->seqused_ori_kv, B, 3);
+  mix(hl->cu_seqlens_ori_kv, B + 1, 4);
+  mix(hl->seqused_cmp_kv, B, 5);
+  mix(hl->cu_seqlens_cmp_kv, B + 1, 6);
+  mix(hl->cmp_residual_kv, B, 7);
+  mix(hl->cmp_topk_length, p->t1, 8);
+  return h & 0x7fffffffu;
+}
+
+bool is_win(int w) { return w == -1 || w >= 0; }
+
+}  // namespace
+
+size_t csmla::workspace_bytes_for(int n_units, int splits) {
+  if (splits <= 1) return 0;
+  const size_t o = (size_t)n_units * kN1 * kD * 2;          // bf16 partial outputs
+  const size_t ml = (size_t)n_units * kN1 * 2 * sizeof(float);  // (max, sum) per head
+  return ((o + 255) & ~size_t(255)) + ml;
+}
+
+extern "C" {
+
+int csmla_abi_version(void) { return CSMLA_ABI_VERSION; }
+
+const char* csmla_status_string(int status) {
+  switch (status) {
+    case CSMLA_OK: return "ok";
+    case CSMLA_ERR_INVALID_ARG: return "invalid argument";
+    case CSMLA_ERR_UNSUPPORTED: return "unsupported";
+    case CSMLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSMLA_ERR_METADATA_MISMATCH: return "metadata planned for another problem";
+    case CSMLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* csmla_last_error(void) { return g_last_error.c_str(); }
+
+size_t csmla_metadata_words(void) { return CSMLA_METADATA_WORDS; }
+
+csmla_status csmla_validate(const csmla_problem* p) {
+  if (!p) return fail(CSMLA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 1) return fail(CSMLA_ERR_INVALID_ARG, "batch must be >= 1 (empty tensors are rejected)");
+  if (p->t1 < 1) return fail(CSMLA_ERR_INVALID_ARG, "t1 must be >= 1 (empty tensors are rejected)");
+  if (p->n2 != 1) return fail(CSMLA_ERR_INVALID_ARG, "n2 must be 1, got %d", p->n2);
+  if (p->d != 512) return fail(CSMLA_ERR_INVALID_ARG, "d must be 512, got %d", p->d);
+  if (p->n1 < 1) return fail(CSMLA_ERR_INVALID_ARG, "n1 must be >= 1");
+  if (p->n1 != kN1) return fail(CSMLA_ERR_UNSUPPORTED, "only n1 = 64 query heads are built, got %d", p->n1);
+  if (p->layout_q != CSMLA_LAYOUT_BSND && p->layout_q != CSMLA_LAYOUT_TND)
+    return fail(CSMLA_ERR_INVALID_ARG, "layout_q must be BSND or TND");
+  if (p->layout_kv != CSMLA_LAYOUT_BSND && p->layout_kv != CSMLA_LAYOUT_TND && p->layout_kv != CSMLA_LAYOUT_PA_BBND)
+    return fail(CSMLA_ERR_INVALID_ARG, "layout_kv must be BSND, TND or PA_BBND");
+  if (p->layout_kv != CSMLA_LAYOUT_PA_BBND && p->layout_kv != p->layout_q)
+    return fail(CSMLA_ERR_INVALID_ARG, "without PA_BBND, layout_q and layout_kv must match");
+  if (p->layout_q == CSMLA_LAYOUT_BSND) {
+    if (p->q_s < 1) return fail(CSMLA_ERR_INVALID_ARG, "BSND q needs q_s >= 1");
+    if ((int64_t)p->batch * p->q_s != p->t1) return fail(CSMLA_ERR_INVALID_ARG, "BSND q: t1 must equal batch * q_s");
+  }
+  if (p->layout_kv == CSMLA_LAYOUT_PA_BBND) {
+    if (p->ori_block_size < 1 || p->ori_block_size > 1024)
+      return fail(CSMLA_ERR_INVALID_ARG, "ori_block_size must be in 1..1024");
+    if (p->ori_num_blocks < 1 || p->ori_table_cols < 1)
+      return fail(CSMLA_ERR_INVALID_ARG, "ori cache / block table must not be empty");
+    if (p->has_cmp) {
+      if (p->cmp_block_size < 1 || p->cmp_block_size > 1024)
+        return fail(CSMLA_ERR_INVALID_ARG, "cmp_block_size must be in 1..1024");
+      if (p->cmp_num_blocks < 1 || p->cmp_table_cols < 1)
+        return fail(CSMLA_ERR_INVALID_ARG, "cmp cache / block table must not be empty");
+    }
+  } else {
+    if (p->ori_s < 1) return fail(CSMLA_ERR_INVALID_ARG, "ori_kv must not be empty");
+    if (p->has_cmp && p->cmp_s < 1) return fail(CSMLA_ERR_INVALID_ARG, "cmp_kv must not be empty");
+  }
+  if (p->cmp_ratio < 1 || p->cmp_ratio > 128) return fail(CSMLA_ERR_INVALID_ARG, "cmp_ratio must be in 1..128");
+  if (!p->has_cmp && p->cmp_ratio != 1) return fail(CSMLA_ERR_INVALID_ARG, "cmp_ratio must be 1 without cmp_kv");
+  if (!p->has_cmp && p->topk != 0) return fail(CSMLA_ERR_INVALID_ARG, "cmp_sparse_indices need cmp_kv");
+  if (p->topk < 0) return fail(CSMLA_ERR_INVALID_ARG, "topk must be >= 0");
+  if (p->ori_mask_mode != 0 && p->ori_mask_mode != 3 && p->ori_mask_mode != 4)
+    return fail(CSMLA_ERR_INVALID_ARG, "ori_mask_mode must be 0, 3 or 4");
+  if (p->cmp_mask_mode != 0 && p->cmp_mask_mode != 3) return fail(CSMLA_ERR_INVALID_ARG, "cmp_mask_mode must be 0 or 3");
+  if (!is_win(p->ori_win_left) || !is_win(p->ori_win_right))
+    return fail(CSMLA_ERR_INVALID_ARG, "ori_win_left/right must be -1 or >= 0");
+  if (p->ori_mask_mode != CSMLA_MASK_BAND && (p->ori_win_left >= 0 || p->ori_win_right >= 0))
+    return fail(CSMLA_ERR_INVALID_ARG, "ori_win_left/right may be >= 0 only with ori_mask_mode 4");
+  if (p->kv_scale_mode != CSMLA_KV_SCALE_PER_TOKEN && p->kv_scale_mode != CSMLA_KV_SCALE_PER_TILE64)
+    return fail(CSMLA_ERR_INVALID_ARG, "kv_scale_mode must be 0 or 1");
+  if (p->topk_value_mode != 0) return fail(CSMLA_ERR_UNSUPPORTED, "only topk_value_mode 0 is built");
+  if (!(std::isfinite(p->softmax_scale))) return fail(CSMLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  g_last_error.clear();
+  return CSMLA_OK;
+}
+
+csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, int32_t* md, size_t md_words,
+                        size_t* ws_bytes) {
+  csmla_status st = csmla_validate(p);
+  if (st != CSMLA_OK) return st;
+  if (!md) return fail(CSMLA_ERR_INVALID_ARG, "metadata buffer is NULL (it is mandatory)");
+  if (md_words < CSMLA_METADATA_WORDS) return fail(CSMLA_ERR_INVALID_ARG, "metadata needs %d words", CSMLA_METADATA_WORDS);
+  if (p->layout_q == CSMLA_LAYOUT_TND && hl && hl->cu_seqlens_q) {
+    if (hl->cu_seqlens_q[0] != 0) return fail(CSMLA_ERR_INVALID_ARG, "cu_seqlens_q[0] must be 0");
+    for (int b = 0; b < p->batch; ++b)
+      if (hl->cu_seqlens_q[b + 1] < hl->cu_seqlens_q[b]) return fail(CSMLA_ERR_INVALID_ARG, "cu_seqlens_q must be non-decreasing");
+    if (hl->cu_seqlens_q[p->batch] != p->t1) return fail(CSMLA_ERR_INVALID_ARG, "cu_seqlens_q[B] must equal t1");
+  }
+  for (const int32_t* cu : {hl ? hl->cu_seqlens_ori_kv : nullptr, hl ? hl->cu_seqlens_cmp_kv : nullptr}) {
+    if (!cu) continue;
+    if (cu[0] != 0) return fail(CSMLA_ERR_INVALID_ARG, "cu_seqlens_*_kv[0] must be 0");
+    for (int b = 0; b < p->batch; ++b)
+      if (cu[b + 1] < cu[b]) return fail(CSMLA_ERR_INVALID_ARG, "cu_seqlens_*_kv must be non-decreasing");
+  }
+
+  const std::vector<TokCost> cost = token_costs(p, hl);
+  const int T1 = p->t1;
+  int64_t max_n = 0, max_c = 0, total = 0;
+  for (const auto& c : cost) {
+    max_n = std::max(max_n, c.n_o + c.n_c_up);
+    max_c = std::max(max_c, c.n_c_up);
+    total += c.n_o + c.n_c_up;
+  }
+  // splits per token: enough units to occupy every CU, units of >= 64 keys,
+  // and at most kListMax compressed indices per unit
+  int64_t s_list = 1;
+  if (p->topk > 0 && max_c > kListMax) s_list = (max_n + kListMax - 1) / kListMax;
+  const int64_t avg = T1 ? total / T1 : 0;
+  int64_t s_par = 1;
+  if (T1 < kMaxGrid) s_par = std::min<int64_t>((kMaxGrid + T1 - 1) / T1, std::max<int64_t>(1, avg / 64));
+  int64_t S = std::max(s_list, s_par);
+  if (const char* env = std::getenv("CSMLA_SPLITS")) {
+    const int64_t f = std::atoll(env);
+    if (f >= 1) S = std::max(s_list, f);
+  }
+  S = std::min<int64_t>(S, 4096);
+  const int64_t n_units64 = (int64_t)T1 * S;
+  if (n_units64 > (int64_t)1 << 30) return fail(CSMLA_ERR_UNSUPPORTED, "too many work units");
+  const int n_units = (int)n_units64;
+  const int G = (int)std::min<int64_t>(n_units64, kMaxGrid);
+
+  // contiguous unit ranges per work-group, balanced by estimated keys
+  std::vector<double> pre(n_units + 1, 0.0);
+  for (int u = 0; u < n_units; ++u) {
+    const auto& c = cost[u / S];
+    pre[u + 1] = pre[u] + (double)(c.n_o + c.n_c_up) / (double)S + 48.0;
+  }
+  std::vector<int32_t> starts(G + 1);
+  starts[0] = 0;
+  int u = 0;
+  for (int g = 1; g < G; ++g) {
+    const double target = pre[n_units] * g / G;
+    while (u < n_units && pre[u] < target) ++u;
+    int lo = starts[g - 1] + 1, hi = n_units - (G - g);
+    starts[g] = std::min(std::max(u, lo), hi);
+    u = starts[g];
+  }
+  starts[G] = n_units;
+
+  std::memset(md, 0, sizeof(int32_t) * CSMLA_METADATA_WORDS);
+  md[MD_MAGIC] = kMagic;
+  md[MD_VERSION] = CSMLA_ABI_VERSION;
+  md[MD_PROBLEM_HASH] = (int32_t)problem_hash(p);
+  md[MD_LENGTHS_HASH] = (int32_t)lengths_hash(p, hl);
+  md[MD_T1] = T1;
+  md[MD_SPLITS] = (int32_t)S;
+  md[MD_UNITS] = n_units;
+  md[MD_GRID] = G;
+  md[MD_LIST_MAX] = kListMax;
+  const size_t ws = workspace_bytes_for(n_units, (int)S);
+  md[MD_WS_LO] = (int32_t)(ws & 0x7fffffff);
+  md[MD_WS_HI] = (int32_t)(ws >> 31);
+  md[MD_FLAGS] = S > 1 ? 1 : 0;
+  for (int g = 0; g <= G; ++g) md[MD_STARTS + g] = starts[g];
+  if (ws_bytes) *ws_bytes = ws;
+  g_last_error.clear();
+  return CSMLA_OK;
+}
+
+static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, const int32_t* md, KArgs& a,
+                               bool need_plan) {
+  csmla_status st = csmla_validate(p);
+  if (st != CSMLA_OK) return st;
+  if (!t) return fail(CSMLA_ERR_INVALID_ARG, "tensors is NULL");
+  if (!t->q || !t->q_descale) return fail(CSMLA_ERR_INVALID_ARG, "q and q_descale are required");
+  if (!t->ori_kv || !t->ori_kv_descale) return fail(CSMLA_ERR_INVALID_ARG, "ori_kv and ori_kv_descale are required");
+  if (p->has_cmp && (!t->cmp_kv || !t->cmp_kv_descale))
+    return fail(CSMLA_ERR_INVALID_ARG, "has_cmp needs cmp_kv and cmp_kv_descale");
+  if (p->topk > 0 && !t->cmp_sparse_indices) return fail(CSMLA_ERR_INVALID_ARG, "topk > 0 needs cmp_sparse_indices");
+  if (p->layout_q == CSMLA_LAYOUT_TND && !t->cu_seqlens_q) return fail(CSMLA_ERR_INVALID_ARG, "TND q needs cu_seqlens_q");
+  if (p->layout_kv == CSMLA_LAYOUT_PA_BBND) {
+    if (!t->seqused_ori_kv || !t->ori_block_table)
+      return fail(CSMLA_ERR_INVALID_ARG, "PA_BBND needs seqused_ori_kv and ori_block_table");
+    if (p->has_cmp && !t->cmp_block_table) return fail(CSMLA_ERR_INVALID_ARG, "PA_BBND cmp_kv needs cmp_block_table");
+  }
+  if (p->layout_kv == CSMLA_LAYOUT_TND) {
+    if (!t->cu_seqlens_ori_kv) return fail(CSMLA_ERR_INVALID_ARG, "TND kv needs cu_seqlens_ori_kv");
+    if (p->has_cmp && !t->cu_seqlens_cmp_kv) return fail(CSMLA_ERR_INVALID_ARG, "TND kv with cmp_kv needs cu_seqlens_cmp_kv");
+  }
+  if (need_plan && !t->attn_out) return fail(CSMLA_ERR_INVALID_ARG, "attn_out is required");
+  if (need_plan && p->return_softmax_lse && !t->softmax_lse)
+    return fail(CSMLA_ERR_INVALID_ARG, "return_softmax_lse needs softmax_lse");
+
+  std::memset(&a, 0, sizeof(a));
+  a.batch = p->batch; a.t1 = p->t1; a.q_s = p->q_s; a.layout_q = p->layout_q; a.layout_kv = p->layout_kv;
+  a.ori_s = p->ori_s; a.cmp_s = p->cmp_s; a.ori_bs = p->ori_block_size; a.cmp_bs = p->cmp_block_size;
+  a.ori_cols = p->ori_table_cols; a.cmp_cols = p->cmp_table_cols;
+  a.has_cmp = p->has_cmp; a.topk = p->topk; a.cmp_ratio = p->cmp_ratio;
+  a.ori_mask = p->ori_mask_mode; a.cmp_mask = p->cmp_mask_mode;
+  a.win_left = p->ori_mask_mode == CSMLA_MASK_BAND ? p->ori_win_left : -1;
+  a.win_right = p->ori_mask_mode == CSMLA_MASK_BAND ? p->ori_win_right : -1;
+  a.scale_mode = p->kv_scale_mode; a.q_ds_per_head = p->q_descale_per_head; a.ret_lse = p->return_softmax_lse;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.q = (const uint8_t*)t->q; a.q_ds = t->q_descale;
+  a.ori_kv = (const uint8_t*)t->ori_kv; a.ori_ds = t->ori_kv_descale;
+  a.cmp_kv = p->has_cmp ? (const uint8_t*)t->cmp_kv : nullptr; a.cmp_ds = p->has_cmp ? t->cmp_kv_descale : nullptr;
+  a.idx = p->topk > 0 ? t->cmp_sparse_indices : nullptr;
+  a.ori_tab = t->ori_block_table; a.cmp_tab = t->cmp_block_table;
+  a.cu_q = t->cu_seqlens_q; a.cu_ori = t->cu_seqlens_ori_kv; a.cu_cmp = t->cu_seqlens_cmp_kv;
+  a.su_q = t->seqused_q; a.su_ori = t->seqused_ori_kv; a.su_cmp = t->seqused_cmp_kv;
+  a.res = t->cmp_residual_kv; a.topk_len = t->cmp_topk_length; a.sinks = t->sinks;
+  a.out = (uint16_t*)t->attn_out; a.lse = p->return_softmax_lse ? t->softmax_lse : nullptr;
+
+  if (need_plan) {
+    if (!md) return fail(CSMLA_ERR_INVALID_ARG, "metadata is NULL (it is mandatory)");
+    if (md[MD_MAGIC] != kMagic || md[MD_VERSION] != CSMLA_ABI_VERSION)
+      return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was not written by csmla_plan of this version");
+    if ((uint32_t)md[MD_PROBLEM_HASH] != problem_hash(p) || md[MD_T1] != p->t1)
+      return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was planned for a different problem");
+    const int S = md[MD_SPLITS], U = md[MD_UNITS], G = md[MD_GRID];
+    if (S < 1 || U != p->t1 * S || G < 1 || G > kMaxGrid || G > U)
+      return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata header is inconsistent");
+    for (int g = 0; g <= G; ++g) {
+      const int s0 = md[MD_STARTS + g];
+      if (s0 < 0 || s0 > U || (g > 0 && s0 < md[MD_STARTS + g - 1]) || (g == 0 && s0 != 0) || (g == G && s0 != U))
+        return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata work ranges are inconsistent");
+      a.starts[g] = s0;
+    }
+    a.splits = S; a.n_units = U; a.grid = G;
+    const size_t ws = workspace_bytes_for(U, S);
+    if (ws > 0) {
+      if (!t->workspace || t->workspace_bytes < ws)
+        return fail(CSMLA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", ws, t->workspace ? t->workspace_bytes : (size_t)0);
+      if ((reinterpret_cast<uintptr_t>(t->workspace) & 255) != 0)
+        return fail(CSMLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+      a.ws_o = (uint16_t*)t->workspace;
+      const size_t o = (size_t)U * kN1 * kD * 2;
+      a.ws_ml = (float*)((char*)t->workspace + ((o + 255) & ~size_t(255)));
+    }
+  }
+  return CSMLA_OK;
+}
+
+csmla_status csmla_forward(const csmla_problem* p, const csmla_tensors* t, const int32_t* md, void* stream) {
+  KArgs a;
+  csmla_status st = build_args(p, t, md, a, true);
+  if (st != CSMLA_OK) return st;
+  const int e = launch_forward(a, stream);
+  if (e != 0) return fail(CSMLA_ERR_HIP, "kernel launch failed (hipError %d)", e);
+  g_last_error.clear();
+  return CSMLA_OK;
+}
+
+csmla_status csmla_debug_resolve(const csmla_problem* p, const csmla_tensors* t, int32_t* keys, int32_t* counts,
+                                 int32_t max_keys, void* stream) {
+  KArgs a;
+  csmla_status st = build_args(p, t, nullptr, a, false);
+  if (st != CSMLA_OK) return st;
+  if (!keys || !counts || max_keys < 0) return fail(CSMLA_ERR_INVALID_ARG, "keys/counts buffers are required");
+  const int e = launch_debug_resolve(a, keys, counts, max_keys, stream);
+  if (e != 0) return fail(CSMLA_ERR_HIP, "kernel launch failed (hipError %d)", e);
+  g_last_error.clear();
+  return CSMLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal definitions shared by the host planner (csmla_host.cpp) and the
+// HIP kernels (csmla_kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <stdint.h>
+#include <stddef.h>
+
+namespace csmla {
+
+constexpr int kN1 = 64;            // query heads handled by one work unit
+constexpr int kD = 512;            // head dim (QuantSparseFlashMla, 约束说明: D = 512)
+constexpr int kTileKeys = 64;      // keys per LDS tile
+constexpr int kListMax = 1024;     // compacted cmp indices a unit keeps in LDS
+constexpr int kMaxGrid = 256;      // persistent work-groups (one per CU on MI355X)
+constexpr int kHeaderWords = 16;
+constexpr int32_t kMagic = 0x4C4D5343;   // "CSML"
+
+// metadata word offsets (int32[1024])
+enum {
+  MD_MAGIC = 0, MD_VERSION = 1, MD_PROBLEM_HASH = 2, MD_LENGTHS_HASH = 3, MD_T1 = 4,
+  MD_SPLITS = 5, MD_UNITS = 6, MD_GRID = 7, MD_LIST_MAX = 8, MD_WS_LO = 9, MD_WS_HI = 10,
+  MD_FLAGS = 11, MD_STARTS = kHeaderWords
+};
+
+// Everything one kernel launch needs, passed by value in the kernarg segment.
+struct KArgs {
+  // problem attributes
+  int32_t batch, t1, q_s, layout_q, layout_kv;
+  int32_t ori_s, cmp_s, ori_bs, cmp_bs, ori_cols, cmp_cols;
+  int32_t has_cmp, topk, cmp_ratio, ori_mask, cmp_mask, win_left, win_right;
+  int32_t scale_mode, q_ds_per_head, ret_lse;
+  float scale_log2;                 // softmax_scale * log2(e)
+  // tensors
+  const uint8_t* q; const float* q_ds;
+  const uint8_t* ori_kv; const float* ori_ds;
+  const uint8_t* cmp_kv; const float* cmp_ds;
+  const int32_t* idx; const int32_t* ori_tab; const int32_t* cmp_tab;
+  const int32_t* cu_q; const int32_t* cu_ori; const int32_t* cu_cmp;
+  const int32_t* su_q; const int32_t* su_ori; const int32_t* su_cmp;
+  const int32_t* res; const int32_t* topk_len; const float* sinks;
+  uint16_t* out; float* lse;
+  uint16_t* ws_o; float* ws_ml;
+  // plan
+  int32_t splits, n_units, grid;
+  int32_t starts[kMaxGrid + 1];
+};
+
+size_t workspace_bytes_for(int n_units, int splits);
+
+// launchers (csmla_kernels.hip); return a hipError_t as int
+int launch_forward(const KArgs& a, void* stream);
+int launch_debug_resolve(const KArgs& a, int32_t* keys, int32_t* counts, int32_t max_keys, void* stream);
+
+}  // namespace csmla

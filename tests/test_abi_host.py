@@ -1,0 +1,208 @@
+"""Host-side tests of the C ABI (no GPU): exported symbols, the validation
+matrix of the QuantSparseFlashMla page's constraints, the planner's
+invariants, and the errors csmla_forward reports before any launch."""
+import copy
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sparse_compressed_mla_amd as m
+from sparse_compressed_mla_amd.binding import CsmlaProblem, CsmlaHostLengths, CsmlaTensors
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, MISMATCH = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "csmla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csmla_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = m.load()
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings():
+    assert m.csmla_abi_version() == 1
+    assert m.csmla_metadata_words() == 1024
+    for s in range(6):
+        assert m.csmla_status_string(s)
+    assert m.csmla_status_string(99) == "unknown status"
+
+
+def base_problem(**kw):
+    p = CsmlaProblem()
+    vals = dict(batch=32, n1=64, n2=1, d=512, layout_q=0, layout_kv=2, q_s=1, t1=32,
+                ori_block_size=128, cmp_block_size=128, ori_num_blocks=2056, cmp_num_blocks=520,
+                ori_table_cols=64, cmp_table_cols=16, has_cmp=1, topk=512, softmax_scale=512 ** -0.5,
+                cmp_ratio=4, ori_mask_mode=4, cmp_mask_mode=3, ori_win_left=127, ori_win_right=0,
+                kv_scale_mode=0, q_descale_per_head=1, topk_value_mode=0, return_softmax_lse=0)
+    vals.update(kw)
+    for k, v in vals.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), OK),
+    (dict(n2=2), INVALID),                      # N2 only 1
+    (dict(d=576), INVALID),                     # D only 512
+    (dict(n1=128), UNSUPPORTED),                # N1 = 128 allowed by KvQuantSparseAttnSharedkv, not built
+    (dict(batch=0, t1=0), INVALID),             # empty tensors
+    (dict(cmp_ratio=0), INVALID),
+    (dict(cmp_ratio=129), INVALID),             # 1..128
+    (dict(has_cmp=0, topk=0, cmp_ratio=4), INVALID),   # SWA keeps cmp_ratio 1
+    (dict(has_cmp=0, topk=0, cmp_ratio=1), OK),
+    (dict(has_cmp=0, topk=16, cmp_ratio=1), INVALID),  # indices need cmp_kv
+    (dict(ori_mask_mode=1), INVALID),           # 0/3/4
+    (dict(cmp_mask_mode=4), INVALID),           # 0/3
+    (dict(ori_mask_mode=3, ori_win_left=127, ori_win_right=0), INVALID),   # windows >= 0 only with band
+    (dict(ori_mask_mode=3, ori_win_left=-1, ori_win_right=-1), OK),
+    (dict(ori_win_left=-2), INVALID),
+    (dict(ori_win_right=-1), OK),
+    (dict(layout_q=1, layout_kv=0), INVALID),   # layout pairs
+    (dict(layout_q=0, layout_kv=1), INVALID),
+    (dict(layout_q=1, layout_kv=1, ori_s=100, cmp_s=25, t1=32), OK),
+    (dict(ori_block_size=0), INVALID),          # block size 1..1024
+    (dict(ori_block_size=1025), INVALID),
+    (dict(cmp_block_size=2048), INVALID),
+    (dict(ori_block_size=1024), OK),
+    (dict(q_s=2, t1=32), INVALID),              # BSND: t1 = B * Q_S
+    (dict(kv_scale_mode=2), INVALID),
+    (dict(topk_value_mode=1), UNSUPPORTED),
+    (dict(softmax_scale=float("inf")), INVALID),
+])
+def test_validation_matrix(kw, status):
+    assert m.csmla_validate(base_problem(**kw)) == status, m.csmla_last_error()
+
+
+def test_plan_invariants_and_determinism():
+    p = base_problem()
+    _, md, ws = m.csmla_plan(p)
+    assert md[0] == 0x4C4D5343 and md[1] == 1
+    S, U, G = md[5], md[6], md[7]
+    assert U == 32 * S and 1 <= G <= 256 and G <= U
+    starts = md[16:16 + G + 1]
+    assert starts[0] == 0 and starts[-1] == U and np.all(np.diff(starts) >= 1)
+    assert ws == (0 if S == 1 else ((U * 64 * 512 * 2 + 255) // 256 * 256 + U * 64 * 8))
+    _, md2, ws2 = m.csmla_plan(p)
+    assert np.array_equal(md, md2) and ws == ws2
+    # a decode batch of 32 tokens is split so that the grid fills the chip
+    assert S > 1 and G == 256
+
+
+def test_plan_balances_prefill_ramp():
+    """Prefill rows have fewer visible keys early on; the contiguous unit
+    ranges are cut by estimated keys, not by count."""
+    B, S1 = 4, 4096
+    p = base_problem(batch=B, layout_q=1, q_s=0, t1=B * S1, ori_table_cols=32, cmp_table_cols=8,
+                     kv_scale_mode=1, return_softmax_lse=1)
+    cu = np.arange(0, B * S1 + 1, S1, dtype=np.int32)
+    su = np.full(B, S1, dtype=np.int32)
+    sc = np.full(B, S1 // 4, dtype=np.int32)
+    res = np.zeros(B, dtype=np.int32)
+    hl = CsmlaHostLengths()
+    hl.cu_seqlens_q, hl.seqused_ori_kv, hl.seqused_cmp_kv, hl.cmp_residual_kv = (
+        cu.ctypes.data, su.ctypes.data, sc.ctypes.data, res.ctypes.data)
+    _, md, ws = m.csmla_plan(p, hl)
+    assert md[5] == 1 and ws == 0
+    G = md[7]
+    starts = md[16:16 + G + 1]
+    sizes = np.diff(starts)
+    # the first range (cheap early tokens) holds more tokens than a late one
+    assert sizes[0] > sizes[G // 8 - 1]
+    assert md[3] != 0  # lengths hash recorded
+
+
+def test_plan_rejects_bad_lengths_and_buffers():
+    p = base_problem(layout_q=1, q_s=0)
+    cu = np.array([0] + [1] * 31 + [31], dtype=np.int32)  # last element != t1
+    hl = CsmlaHostLengths()
+    hl.cu_seqlens_q = cu.ctypes.data
+    st, _, _ = m.csmla_plan(p, hl, raise_on_error=False)
+    assert st == INVALID
+    cu2 = np.arange(33, dtype=np.int32)
+    cu2[5] = 2  # decreasing
+    hl.cu_seqlens_q = cu2.ctypes.data
+    assert m.csmla_plan(p, hl, raise_on_error=False)[0] == INVALID
+    lib = m.load()
+    md = np.zeros(10, dtype=np.int32)
+    ws = ctypes.c_size_t()
+    assert lib.csmla_plan(ctypes.byref(base_problem()), None, md.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                          10, ctypes.byref(ws)) == INVALID
+    assert lib.csmla_plan(ctypes.byref(base_problem()), None, None, 1024, ctypes.byref(ws)) == INVALID
+
+
+def test_split_override_from_environment(monkeypatch):
+    monkeypatch.setenv("CSMLA_SPLITS", "3")
+    _, md, ws = m.csmla_plan(base_problem())
+    assert md[5] == 3 and md[6] == 96 and ws > 0
+
+
+def fake_tensors(ws_bytes=0):
+    t = CsmlaTensors()
+    for i, (name, _) in enumerate(CsmlaTensors._fields_[:-1]):
+        setattr(t, name, 0x10000 * (i + 1))       # never dereferenced: every call below fails validation
+    t.workspace_bytes = ws_bytes
+    return t
+
+
+def test_forward_rejects_before_launch():
+    p = base_problem()
+    _, md, ws = m.csmla_plan(p)
+    t = fake_tensors(ws)
+    # metadata for another problem
+    _, md_other, _ = m.csmla_plan(base_problem(topk=256))
+    assert m.csmla_forward(p, t, md_other, raise_on_error=False) == MISMATCH
+    # corrupted header / ranges
+    bad = md.copy(); bad[0] = 0
+    assert m.csmla_forward(p, t, bad, raise_on_error=False) == MISMATCH
+    bad = md.copy(); bad[16 + 3] = bad[16 + 2] - 1
+    assert m.csmla_forward(p, t, bad, raise_on_error=False) == MISMATCH
+    # workspace
+    t2 = fake_tensors(ws - 1)
+    assert m.csmla_forward(p, t2, md, raise_on_error=False) == WORKSPACE
+    t3 = fake_tensors(ws); t3.workspace = None
+    assert m.csmla_forward(p, t3, md, raise_on_error=False) == WORKSPACE
+    t4 = fake_tensors(ws); t4.workspace = 0x10008
+    assert m.csmla_forward(p, t4, md, raise_on_error=False) == WORKSPACE   # alignment
+    # required pointers (QuantSparseFlashMla 约束说明: PA needs seqused_ori_kv + block table)
+    for name in ("q", "q_descale", "ori_kv", "ori_kv_descale", "cmp_kv", "cmp_sparse_indices",
+                 "seqused_ori_kv", "ori_block_table", "cmp_block_table", "attn_out"):
+        tt = fake_tensors(ws); setattr(tt, name, None)
+        assert m.csmla_forward(p, tt, md, raise_on_error=False) == INVALID, name
+    p_lse = base_problem(return_softmax_lse=1)
+    _, md_lse, _ = m.csmla_plan(p_lse)
+    tt = fake_tensors(ws); tt.softmax_lse = None
+    assert m.csmla_forward(p_lse, tt, md_lse, raise_on_error=False) == INVALID
+    # TND q needs cu_seqlens_q; TND kv needs cu_seqlens_ori_kv / cu_seqlens_cmp_kv
+    pt = base_problem(layout_q=1, layout_kv=1, q_s=0, ori_s=1000, cmp_s=250)
+    _, mdt, wst = m.csmla_plan(pt)
+    for name in ("cu_seqlens_q", "cu_seqlens_ori_kv", "cu_seqlens_cmp_kv"):
+        tt = fake_tensors(wst); setattr(tt, name, None)
+        assert m.csmla_forward(pt, tt, mdt, raise_on_error=False) == INVALID, name
+    # a NULL metadata pointer
+    lib = m.load()
+    assert lib.csmla_forward(ctypes.byref(p), ctypes.byref(t), None, None) == INVALID
+    assert "metadata" in m.csmla_last_error()
+
+
+def test_problem_struct_layout_matches_header():
+    """Field order of the ctypes mirror equals the C struct's."""
+    src = open(os.path.join(ROOT, "include", "csmla.h")).read()
+    body = src[src.index("typedef struct {", src.index("Shapes and attributes")):src.index("} csmla_problem;")]
+    names = re.findall(r"^\s*(?:int32_t|float)\s+([\w,\s]+);", body, flags=re.M)
+    flat = [n.strip() for grp in names for n in grp.split(",")]
+    assert flat == [f[0] for f in CsmlaProblem._fields_]
+    body_t = src[src.index("typedef struct {", src.index("Device pointers")):src.index("} csmla_tensors;")]
+    tnames = re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+);", body_t, flags=re.M)
+    assert tnames == [f[0] for f in CsmlaTensors._fields_]

@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: bf16 outputs within |g - r| <= 1e-2 + 1e-2|r|, lse within 1e-3, and the
+resolved gather rows bit-exact (csmla_debug_resolve vs the oracle's lists).
+Inputs are seeded and synthetic; unused cache slots hold NaN so that any
+stray read poisons the result.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_compressed_mla_amd as m
+from oracle import oracle_forward
+from oracle.attention import token_rows, token_table
+from workloads import make_config, make_custom
+from tests.parity_util import compare
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def run_gpu(inp_gpu, plan=None):
+    out, lse = m.forward(inp_gpu, plan=plan)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy() if lse is not None else None
+    return o, l
+
+
+def check(inp_cpu, tokens=None, name="", inp_gpu=None, splits=None, monkeypatch=None):
+    say(f"case {name}: t1={inp_cpu.t1} topk={inp_cpu.topk} scale_mode={inp_cpu.kv_scale_mode}")
+    toks = list(range(inp_cpu.t1)) if tokens is None else list(tokens)
+    ref = oracle_forward(inp_cpu, toks)
+    g = inp_gpu if inp_gpu is not None else inp_cpu.to(DEV)
+    if splits is not None:
+        os.environ["CSMLA_SPLITS"] = str(splits)
+    try:
+        plan = m.Plan(g)
+    finally:
+        os.environ.pop("CSMLA_SPLITS", None)
+    say(f"  plan splits={plan.splits} grid={plan.grid}; launching")
+    o, l = run_gpu(g, plan)
+    stats = compare(o, ref.out, toks, l if inp_cpu.return_lse else None,
+                    ref.lse if inp_cpu.return_lse else None, name=name)
+    return stats, o, l, ref
+
+
+def check_rows(inp_cpu, tokens=None, name=""):
+    """csmla_debug_resolve row lists == the oracle's, bit for bit and in order."""
+    toks = list(range(inp_cpu.t1)) if tokens is None else list(tokens)
+    tt = token_table(inp_cpu)
+    want = {t: token_rows(inp_cpu, t, tt) for t in toks}
+    max_keys = max([len(v) for v in want.values()] + [1])
+    say(f"rows {name}: max_keys={max_keys}")
+    keys, counts = m.debug_resolve(inp_cpu.to(DEV), max_keys)
+    torch.cuda.synchronize()
+    keys, counts = keys.cpu().numpy(), counts.cpu().numpy()
+    for t in toks:
+        w = want[t]
+        n_o = sum(1 for k, _ in w if k == 0)
+        n_c = len(w) - n_o
+        assert counts[t, 0] == n_o and counts[t, 1] == n_c, (name, t, counts[t], n_o, n_c)
+        assert np.array_equal(keys[t, :len(w)], np.array([r for _, r in w], dtype=np.int32)), (name, t)
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def test_cfg1_swa_tiny():
+    inp = make_config(1)
+    check(inp, name="cfg1 swa tiny (lse)")
+    inp.return_lse = False
+    check(inp, name="cfg1 swa tiny (no lse)")
+    check_rows(inp, name="cfg1")
+
+
+def test_cfg2_csa_decode():
+    inp = make_config(2)
+    check(inp, name="cfg2 csa decode")
+    check_rows(inp, name="cfg2")
+
+
+def test_cfg2_tnd_layout_and_forced_splits():
+    inp = make_config(2, batch=8, layout_q="TND")
+    check(inp, name="cfg2 TND q", splits=1)
+    check(inp, name="cfg2 TND q, 5 splits", splits=5)
+    check(inp, name="cfg2 TND q, 16 splits", splits=16)
+
+
+def test_cfg3_hca_decode():
+    inp_g = make_config(3, device=DEV)
+    inp = inp_g.to("cpu")
+    check(inp, name="cfg3 hca decode", inp_gpu=inp_g)
+    check_rows(inp, name="cfg3")
+
+
+def test_cfg4_csa_mtp_long():
+    inp_g = make_config(4, device=DEV)
+    inp = inp_g.to("cpu")
+    check(inp, name="cfg4 csa mtp", inp_gpu=inp_g)
+    check_rows(inp, tokens=range(0, 128, 3), name="cfg4")
+
+
+def test_cfg5_csa_prefill_sampled():
+    inp_g = make_config(5, device=DEV)
+    inp = inp_g.to("cpu")
+    T1 = inp.t1
+    toks = sorted(set(list(range(0, 160)) + list(range(160, T1, 211)) + list(range(T1 - 40, T1))
+                      + [4095, 4096, 8191, 8192, 12287, 12288]))
+    check(inp, tokens=toks, name="cfg5 csa prefill (sampled rows)", inp_gpu=inp_g)
+    check_rows(inp, tokens=toks[::4], name="cfg5")
+
+
+# ---------------------------------------------------------------- edge cases
+
+def _rand_idx(rng, t1, k2, hi, p_invalid=0.2):
+    idx = rng.integers(-3, hi + 4, size=(t1, k2))
+    idx[rng.random(idx.shape) < p_invalid] = -1
+    return idx
+
+
+@pytest.mark.parametrize("kv_scale_mode", [0, 1])
+def test_edge_invalid_duplicate_and_topk_length(kv_scale_mode):
+    rng = np.random.default_rng(11)
+    q_lens, ori = [3, 5, 1], [700, 260, 90]
+    cmp = [o // 4 for o in ori]
+    idx = _rand_idx(rng, sum(q_lens), 300, max(cmp))
+    idx[0, 10:20] = idx[0, 0]          # duplicates count as separate keys
+    inp = make_custom(seed=12, q_lens=q_lens, ori_lens=ori, cmp_lens=cmp, cmp_ratio=4,
+                      residual=[o % 4 for o in ori], indices=idx, kv_scale_mode=kv_scale_mode,
+                      topk_length=rng.integers(0, 300, size=sum(q_lens)), return_lse=True)
+    check(inp, name=f"invalid/dup/topk_length mode{kv_scale_mode}")
+    check(inp, name=f"invalid/dup/topk_length mode{kv_scale_mode} 3 splits", splits=3)
+    check_rows(inp, name="invalid/dup")
+
+
+@pytest.mark.parametrize("case", [
+    dict(ori_mask_mode=0, win_left=-1, win_right=-1, cmp_mask_mode=0, ori=[1500, 3000]),  # > 1024-key chunks
+    dict(ori_mask_mode=3, win_left=-1, win_right=-1, ori=[2100, 40]),
+    dict(ori_mask_mode=4, win_left=-1, win_right=0, ori=[1300, 77]),
+    dict(ori_mask_mode=4, win_left=5, win_right=9, ori=[300, 31]),
+    dict(ori_mask_mode=4, win_left=0, win_right=-1, ori=[129, 64]),
+])
+def test_edge_mask_modes(case):
+    ori = case.pop("ori")
+    r = 7
+    cmp = [o // r for o in ori]
+    inp = make_custom(seed=21, q_lens=[6, 6], ori_lens=ori, cmp_lens=cmp, cmp_ratio=r,
+                      residual=[o % r for o in ori], indices=None, layout_q="BSND", return_lse=True, **case)
+    check(inp, name=f"mask {case}")
+    check_rows(inp, name=f"mask {case}")
+
+
+def test_edge_empty_rows_padding_and_no_sink():
+    # more query rows than kv tokens: early rows see nothing (O = 0, lse = sink or -inf)
+    for sinks in (True, False):
+        inp = make_custom(seed=31, q_lens=[9, 4], ori_lens=[5, 300], cmp_lens=[1, 75], cmp_ratio=4,
+                          residual=[1, 0], indices=None, with_sinks=sinks, seqused_q=[7, 2], return_lse=True)
+        check(inp, name=f"empty rows + padding, sinks={sinks}")
+        check(inp, name=f"empty rows + padding, sinks={sinks}, 2 splits", splits=2)
+
+
+@pytest.mark.parametrize("layout_kv", ["TND", "BSND"])
+def test_edge_contiguous_kv_layouts(layout_kv):
+    rng = np.random.default_rng(41)
+    ori = [333, 150, 700]
+    cmp = [o // 4 for o in ori]
+    lq = "TND" if layout_kv == "TND" else "BSND"
+    q_lens = [3, 2, 4] if lq == "TND" else [3, 3, 3]
+    idx = _rand_idx(rng, sum(q_lens), 128, max(cmp), 0.1)
+    inp = make_custom(seed=42, q_lens=q_lens, ori_lens=ori, cmp_lens=cmp, cmp_ratio=4, residual=[0, 0, 0],
+                      indices=idx, layout_q=lq, layout_kv=layout_kv, return_lse=True)
+    check(inp, name=f"kv layout {layout_kv}")
+    check_rows(inp, name=f"kv layout {layout_kv}")
+
+
+@pytest.mark.parametrize("bs,r", [(16, 1), (64, 128), (1, 2), (1024, 3)])
+def test_edge_block_sizes_and_ratios(bs, r):
+    rng = np.random.default_rng(51)
+    ori = [1100, 517]
+    cmp = [o // r for o in ori]
+    idx = _rand_idx(rng, 4, 64, max(cmp), 0.3)
+    inp = make_custom(seed=52, q_lens=[2, 2], ori_lens=ori, cmp_lens=cmp, cmp_ratio=r,
+                      residual=[o % r for o in ori], indices=idx, block_size=bs, return_lse=True)
+    check(inp, name=f"block {bs} ratio {r}")
+    check_rows(inp, name=f"block {bs} ratio {r}")
+
+
+def test_edge_topk_beyond_list_window():
+    """2500 index slots: the unit's compressed entries span several
+    1024-entry list windows."""
+    rng = np.random.default_rng(61)
+    ori = [12000]
+    cmp = [3000]
+    idx = rng.permutation(3000)[:2500][None, :].repeat(2, axis=0)
+    idx[1, ::7] = -1
+    inp = make_custom(seed=62, q_lens=[2], ori_lens=ori, cmp_lens=cmp, cmp_ratio=4, residual=[0],
+                      indices=idx, return_lse=True)
+    check(inp, name="topk 2500")
+    check(inp, name="topk 2500, 2 splits", splits=2)
+    check_rows(inp, name="topk 2500")
+
+
+def test_edge_per_token_q_descale_and_zero_descale_row():
+    inp = make_custom(seed=71, q_lens=[3], ori_lens=[200], cmp_lens=[50], cmp_ratio=4, residual=[0],
+                      indices=np.tile(np.arange(50), (3, 1)), q_descale_per_head=False, return_lse=True)
+    # zero one visible ori row and its descale: score 0, value 0
+    tab = inp.ori_block_table[0]
+    blk = int(tab[1])
+    inp.ori_kv[blk, 60] = 0
+    inp.ori_kv_descale[blk, 60] = 0.0
+    check(inp, name="per-token q descale, zero descale row")
+
+
+def test_determinism_and_nan_canaries():
+    inp_g = make_config(2, device=DEV, batch=8)
+    o1, _ = run_gpu(inp_g)
+    o2, _ = run_gpu(inp_g)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.all(np.isfinite(o1))
+
+
+# ---------------------------------------------------------------- sensitivity
+
+def _dominant_key_case(pos_offset, which="ori"):
+    """One key whose score is ~40 above the rest: query row 0 must return that
+    key's value row iff the key is visible.  Row 0 of a 2-row batch sits at
+    p = S2 - 2; its band is [p - 127, p] and its compressed prefix [0, (p+1)//r)."""
+    s2, s1, r = 400, 2, 4
+    c = s2 // r
+    inp = make_custom(seed=81, q_lens=[s1], ori_lens=[s2], cmp_lens=[c], cmp_ratio=r, residual=[0],
+                      indices=None, return_lse=True)
+    q = inp.q[0].clone()
+    q[:] = q[0]                        # every head uses the same query vector
+    inp.q[0] = q
+    inp.q_descale[0] = inp.q_descale[0, 0]
+    p = s2 - s1
+    qq = float((q[0].view(torch.float8_e4m3fn).float() ** 2).sum())
+    kds = 40.0 / (float(inp.q_descale[0, 0]) * 512 ** -0.5 * qq)
+    if which == "ori":
+        j = p + pos_offset
+        kv, ds, tab = inp.ori_kv, inp.ori_kv_descale, inp.ori_block_table
+    else:
+        j = (p + 1) // r + pos_offset
+        kv, ds, tab = inp.cmp_kv, inp.cmp_kv_descale, inp.cmp_block_table
+    bs = kv.shape[1]
+    blk = int(tab[0, j // bs])
+    kv[blk, j % bs, 0] = q[0]
+    ds[blk, j % bs] = kds
+    value = q[0].view(torch.float8_e4m3fn).double().numpy() * kds
+    return inp, value
+
+
+@pytest.mark.parametrize("which,off", [("ori", -128), ("ori", -127), ("ori", 0), ("ori", 1), ("ori", -64),
+                                       ("cmp", -1), ("cmp", 0), ("cmp", -40)])
+def test_sensitivity_dominant_key(which, off):
+    inp, value = _dominant_key_case(off, which)
+    _, o, l, ref = check(inp, tokens=[0], name=f"dominant {which} {off}")
+    visible = (which == "ori" and -127 <= off <= 0) or (which == "cmp" and off < 0)
+    # the key decides the result: O equals its value row exactly when visible
+    near = np.abs(ref.out[0] - value[None, :]).max() < 1e-3
+    assert near == visible, (which, off)
+    assert (np.abs(o[0] - value[None, :]).max() < 0.05) == visible, (which, off)
+
+
+def test_sensitivity_sink_dominance():
+    inp = make_config(1)
+    inp.sinks = torch.full((64,), 30.0)
+    _, o, l, ref = check(inp, name="sink dominates")
+    assert np.abs(ref.out).max() < 1e-6 and np.abs(o).max() < 1e-6
