@@ -189,71 +189,133 @@ __device__ int compact_indices(const KArgs& a, const Tok& k, int t, int* list, i
   return base;
 }
 
-// Physical cache row of key `key` (0-based in the token's list): ori band
-// positions first, then cmp entries.  The same code backs the debug export.
-__device__ __forceinline__ int64_t resolve_row(const KArgs& a, const Tok& k, int n_o, int key, const int* list,
-                                               int w_lo, bool& is_cmp) {
-  int j;
-  is_cmp = key >= n_o;
-  if (!is_cmp) j = k.lo + key;
-  else j = (a.topk > 0) ? list[key - n_o - w_lo] : key - n_o;
-  if (a.layout_kv == 2) {  // PA_BBND: block table
-    const int bs = is_cmp ? a.cmp_bs : a.ori_bs;
-    const int* tab = is_cmp ? a.cmp_tab : a.ori_tab;
-    const int cols = is_cmp ? a.cmp_cols : a.ori_cols;
-    const int blk = tab[(size_t)k.b * cols + j / bs];
-    return (int64_t)blk * bs + (j % bs);
+// Resolving one tile of 64 keys takes three stages, spread over pipeline
+// steps so that no wave waits on a dependent load: (1) the block-table
+// lookup, (2) the row address and the descale loads, (3) the descales into
+// meta.  One wave, one key per lane.
+struct KeyLoc {
+  int j;       // logical token position in its cache
+  int cmp;     // 1: the key lives in cmp_kv
+  int blk;     // PA block id (loaded in stage 1)
+  int valid;   // key < end of the chunk
+};
+
+template <int PER_TILE>
+struct KeyScale {
+  float v[PER_TILE ? 8 : 1];
+};
+
+__device__ __forceinline__ KeyLoc resolve_issue(const KArgs& a, const Tok& k, int n_o, const int* list, int w_lo,
+                                                int key0, int key_end) {
+  const int key = key0 + (int)(threadIdx.x & 63);
+  KeyLoc kl;
+  kl.valid = key < key_end;
+  kl.cmp = key >= n_o;
+  kl.j = 0;
+  kl.blk = 0;
+  if (kl.valid) {
+    kl.j = !kl.cmp ? k.lo + key : ((a.topk > 0) ? list[key - n_o - w_lo] : key - n_o);
+    if (a.layout_kv == 2) {
+      const int bs = kl.cmp ? a.cmp_bs : a.ori_bs;
+      const int* tab = kl.cmp ? a.cmp_tab : a.ori_tab;
+      const int cols = kl.cmp ? a.cmp_cols : a.ori_cols;
+      kl.blk = tab[(size_t)k.b * cols + kl.j / bs];
+    }
   }
-  if (a.layout_kv == 1) return (int64_t)(is_cmp ? k.cmp0 : k.kv0) + j;   // TND
-  return (int64_t)k.b * (is_cmp ? a.cmp_s : a.ori_s) + j;                  // BSND
+  return kl;
 }
 
-// Resolve the 64 keys [key0, key0+64) (valid below key_end) of one tile into
-// meta.  One wave, one key per lane.
+__device__ __forceinline__ int64_t key_row(const KArgs& a, const Tok& k, const KeyLoc& kl) {
+  if (a.layout_kv == 2) {
+    const int bs = kl.cmp ? a.cmp_bs : a.ori_bs;
+    return (int64_t)kl.blk * bs + (kl.j % bs);
+  }
+  if (a.layout_kv == 1) return (int64_t)(kl.cmp ? k.cmp0 : k.kv0) + kl.j;
+  return (int64_t)k.b * (kl.cmp ? a.cmp_s : a.ori_s) + kl.j;
+}
+
 template <int PER_TILE>
-__device__ __forceinline__ void resolve_tile(const KArgs& a, const Tok& k, int n_o, const int* list, int w_lo,
-                                             int key0, int key_end, Meta* m) {
+__device__ __forceinline__ void resolve_rows(const KArgs& a, const Tok& k, const KeyLoc& kl, Meta* m,
+                                             KeyScale<PER_TILE>& sc) {
   const int lane = threadIdx.x & 63;
-  const int key = key0 + lane;
   uint64_t addr = 0;
-  float lam = kNegInf, inv = 0.f;
-  float ks[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (key < key_end) {
-    bool is_cmp;
-    const int64_t row = resolve_row(a, k, n_o, key, list, w_lo, is_cmp);
-    const uint8_t* base = is_cmp ? a.cmp_kv : a.ori_kv;
-    const float* ds = is_cmp ? a.cmp_ds : a.ori_ds;
-    addr = (uint64_t)(base + row * kD);
-    float mx;
+#pragma unroll
+  for (int c = 0; c < (PER_TILE ? 8 : 1); ++c) sc.v[c] = 0.f;
+  if (kl.valid) {
+    const int64_t row = key_row(a, k, kl);
+    addr = (uint64_t)((kl.cmp ? a.cmp_kv : a.ori_kv) + row * kD);
+    const float* ds = kl.cmp ? a.cmp_ds : a.ori_ds;
     if (PER_TILE) {
       const v4f* p = (const v4f*)(ds + row * 8);
       const v4f x0 = p[0], x1 = p[1];
-      ks[0] = x0[0]; ks[1] = x0[1]; ks[2] = x0[2]; ks[3] = x0[3];
-      ks[4] = x1[0]; ks[5] = x1[1]; ks[6] = x1[2]; ks[7] = x1[3];
-      mx = ks[0];
-#pragma unroll
-      for (int c = 1; c < 8; ++c) mx = fmaxf(mx, ks[c]);
-      // NaN in any tile scale must poison the row
-#pragma unroll
-      for (int c = 0; c < 8; ++c) if (ks[c] != ks[c]) mx = ks[c];
+      sc.v[0] = x0[0]; sc.v[1] = x0[1]; sc.v[2] = x0[2]; sc.v[3] = x0[3];
+      sc.v[4] = x1[0]; sc.v[5] = x1[1]; sc.v[6] = x1[2]; sc.v[7] = x1[3];
     } else {
-      ks[0] = ds[row];
-      mx = ks[0];
+      sc.v[0] = ds[row];
     }
+  }
+  m->addr[lane] = addr;
+}
+
+template <int PER_TILE>
+__device__ __forceinline__ void resolve_scales(const KeyScale<PER_TILE>& sc, int valid, Meta* m) {
+  const int lane = threadIdx.x & 63;
+  float lam = kNegInf, inv = 0.f;
+  if (valid) {
+    float mx = sc.v[0];
+#pragma unroll
+    for (int c = 1; c < (PER_TILE ? 8 : 1); ++c) mx = fmaxf(mx, sc.v[c]);
+#pragma unroll
+    for (int c = 0; c < (PER_TILE ? 8 : 1); ++c)
+      if (sc.v[c] != sc.v[c]) mx = sc.v[c];   // a NaN scale poisons the row
     mx = (mx == 0.f) ? kMinDescale : mx;
     lam = __log2f(mx);
     inv = 1.0f / mx;
     if (mx != mx) { lam = mx; inv = mx; }
   }
-  m->addr[lane] = addr;
   m->lam[lane] = lam;
   m->inv[lane] = inv;
 #pragma unroll
-  for (int c = 0; c < (PER_TILE ? 8 : 1); ++c) m->ks[c][lane] = ks[c];
+  for (int c = 0; c < (PER_TILE ? 8 : 1); ++c) m->ks[c][lane] = valid ? sc.v[c] : 0.f;
+}
+
+// Whole-tile resolve in one go (used by the pipeline prologue).
+template <int PER_TILE>
+__device__ __forceinline__ void resolve_tile(const KArgs& a, const Tok& k, int n_o, const int* list, int w_lo,
+                                             int key0, int key_end, Meta* m) {
+  const KeyLoc kl = resolve_issue(a, k, n_o, list, w_lo, key0, key_end);
+  KeyScale<PER_TILE> sc;
+  resolve_rows<PER_TILE>(a, k, kl, m, sc);
+  resolve_scales<PER_TILE>(sc, kl.valid, m);
+}
+
+// Row of key `key` for the debug export (same resolution code).
+__device__ __forceinline__ int64_t resolve_row(const KArgs& a, const Tok& k, int n_o, int key, const int* list,
+                                               int w_lo) {
+  KeyLoc kl;
+  kl.valid = 1;
+  kl.cmp = key >= n_o;
+  kl.j = !kl.cmp ? k.lo + key : ((a.topk > 0) ? list[key - n_o - w_lo] : key - n_o);
+  kl.blk = 0;
+  if (a.layout_kv == 2) {
+    const int bs = kl.cmp ? a.cmp_bs : a.ori_bs;
+    const int* tab = kl.cmp ? a.cmp_tab : a.ori_tab;
+    const int cols = kl.cmp ? a.cmp_cols : a.ori_cols;
+    kl.blk = tab[(size_t)k.b * cols + kl.j / bs];
+  }
+  return key_row(a, k, kl);
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // Gather the 64 rows of a tile into LDS: 4 waves x 8 instructions, each
-// instruction 2 rows (lanes 0-31 and 32-63, 16 bytes per lane).
+// instruction 2 rows (lanes 0-31 and 32-63, 16 bytes per lane), issued as
+// global_load_lds_dwordx4 (M0 = LDS destination, lane l writes base + 16 l).
+// The loads are ordered only by the explicit waits of the pipeline barriers,
+// so the compiler does not hold the other tile's LDS reads behind them.
 __device__ __forceinline__ void gather_tile(const Meta* m, uint8_t* tb, int w) {
   const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31;
 #pragma unroll
@@ -262,8 +324,9 @@ __device__ __forceinline__ void gather_tile(const Meta* m, uint8_t* tb, int w) {
     const int r = r0 + g;
     const uint64_t p = m->addr[r];
     if (p) {
-      __builtin_amdgcn_global_load_lds((const void*)(p + 16u * (uint32_t)(li ^ swz(r))),
-                                       (lds_void*)(tb + r0 * kD), 16, 0, 0);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + r0 * kD));
+      const uint64_t src = p + 16u * (uint32_t)(li ^ swz(r));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "m0");
     } else {
       *(v4i*)(tb + r * kD + li * 16) = v4i{0, 0, 0, 0};
     }
@@ -273,6 +336,21 @@ __device__ __forceinline__ void gather_tile(const Meta* m, uint8_t* tb, int w) {
 __device__ __forceinline__ void wait_all_and_sync() {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+}
+
+// Work-group barrier that orders LDS only: outstanding global loads (the
+// next tile's gather, descale prefetches) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Barrier at the end of a pipeline step: the gather into LDS must have landed;
+// the wave's last NDS global loads (descale prefetches) may still be in flight.
+template <int NDS>
+__device__ __forceinline__ void step_barrier() {
+  if (NDS == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if (NDS == 1) asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -335,10 +413,14 @@ __device__ __forceinline__ v8i read_vt(const uint8_t* smem, const LaneOffsets& o
 }
 
 // One 64-key tile of one wave (32 heads, 256 output columns of half DH).
-template <int PER_TILE, int BUF, int DH>
+// The first tile with visible keys fixes each head's reference Mrun (unless
+// it was preset); a later tile that would push P' past 2^8 only raises
+// *flag, and the unit is then recomputed with Mrun preset from its true
+// maximum (MAXONLY = 1 computes that maximum: S^T and the max, no P V).
+template <int PER_TILE, int BUF, int DH, int MAXONLY>
 __device__ __forceinline__ void compute_tile(uint8_t* smem, const LaneOffsets& o, const Meta* m,
                                              const v8i (&qreg)[4], float qs, int nvalid, int w, int lane,
-                                             v16f (&oacc)[8], float& Mrun, float& lsum) {
+                                             v16f (&oacc)[8], float& Mrun, float& lsum, int* flag) {
   const int g = lane >> 5;
   // ---- partial S^T over this wave's half of D ----
   v16f sacc[2];
@@ -371,7 +453,7 @@ __device__ __forceinline__ void compute_tile(uint8_t* smem, const LaneOffsets& o
     for (int r4 = 0; r4 < 4; ++r4)
       *(v4f*)&xw[((tt * 4 + r4) * 64 + lane) * 4] =
           v4f{sacc[tt][4 * r4], sacc[tt][4 * r4 + 1], sacc[tt][4 * r4 + 2], sacc[tt][4 * r4 + 3]};
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -400,16 +482,14 @@ __device__ __forceinline__ void compute_tile(uint8_t* smem, const LaneOffsets& o
     }
   }
   mt = fmaxf(mt, __shfl_xor(mt, 32));
-  // Mrun is the reference of P' = 2^(E - Mrun): set so that the max maps to
-  // 2^4 and kept (lazy rescale) until some P' would exceed 2^8.
-  if (__ballot(mt > Mrun + kTau)) {
-    const float Mn = fmaxf(Mrun, mt - kPShift);
-    const float alpha = (Mrun == kNegInf) ? 0.f : exp2f(Mrun - Mn);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) oacc[nt] *= alpha;
-    lsum *= alpha;
-    Mrun = Mn;
+  if (MAXONLY) {
+    Mrun = fmaxf(Mrun, mt);
+    return;
   }
+  // Mrun is the reference of P' = 2^(E - Mrun): the max maps to 2^4, and P'
+  // may grow to 2^8 before the reference would have to move.
+  if (Mrun == kNegInf) Mrun = mt - kPShift;          // first tile with keys: O is still zero
+  else if (__ballot(mt > Mrun + kTau)) *flag = 1;    // would overflow fp8: redo with a preset reference
   const float Ms = (Mrun == kNegInf) ? 0.f : Mrun;
   // ---- P' = 2^(E - M) in (0, 2^8]; l accumulates P' / vds_max ----
 #pragma unroll
@@ -420,7 +500,7 @@ __device__ __forceinline__ void compute_tile(uint8_t* smem, const LaneOffsets& o
       const v4f iv = *(const v4f*)&m->inv[kb4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pv = exp2f(sacc[tt][4 * q4 + r] - Ms);
+        const float pv = __builtin_amdgcn_exp2f(sacc[tt][4 * q4 + r] - Ms);
         const float lt = pv * iv[r];
         lsum += lt;
         sacc[tt][4 * q4 + r] = PER_TILE ? lt : pv;
@@ -475,18 +555,86 @@ struct Chunk {
   int st, en, tiles;
 };
 
-// One pipeline step: gather tile i+1, compute tile i, resolve tile i+2.
-template <int PER_TILE, int BUF, int DH>
-__device__ __forceinline__ void pipeline_step(const KArgs& a, const Tok& k, int n_o, const int* list, int w_lo,
-                                              uint8_t* smem, const LaneOffsets& o, Meta* mm, const Chunk& ck,
-                                              int i, int w, int lane, const v8i (&qreg)[4], float qs,
-                                              v16f (&oacc)[8], float& Mrun, float& lsum) {
+struct UnitState {
+  Tok k;
+  int t, n_o, w_lo, n_c, kb, ke;
+};
+
+// One pipeline step i: gather tile i+1 | issue table loads of tile i+2 |
+// compute tile i | descales of tile i+1 into meta, row addresses and
+// descale loads of tile i+2 | barrier (gather landed).
+template <int PER_TILE, int BUF, int DH, int MAXONLY>
+__device__ __forceinline__ void pipeline_step(const KArgs& a, const UnitState& us, const int* list, uint8_t* smem,
+                                              const LaneOffsets& o, Meta* mm, const Chunk& ck, int i, int w, int lane,
+                                              const v8i (&qreg)[4], float qs, v16f (&oacc)[8], float& Mrun,
+                                              float& lsum, KeyScale<PER_TILE>& sc_next, int& valid_next, int* flag) {
   if (i + 1 < ck.tiles) gather_tile(mm + (i + 1) % 3, smem + kOffTiles + (BUF ^ 1) * kTileBytes, w);
+  KeyLoc kl2;
+  const bool r2 = (w == 0) && (i + 2 < ck.tiles);
+  if (r2) kl2 = resolve_issue(a, us.k, us.n_o, list, us.w_lo, ck.st + (i + 2) * kTileKeys, ck.en);
   const int nvalid = min(kTileKeys, ck.en - ck.st - i * kTileKeys);
-  compute_tile<PER_TILE, BUF, DH>(smem, o, mm + i % 3, qreg, qs, nvalid, w, lane, oacc, Mrun, lsum);
-  if (w == 0 && i + 2 < ck.tiles)
-    resolve_tile<PER_TILE>(a, k, n_o, list, w_lo, ck.st + (i + 2) * kTileKeys, ck.en, mm + (i + 2) % 3);
-  wait_all_and_sync();
+  compute_tile<PER_TILE, BUF, DH, MAXONLY>(smem, o, mm + i % 3, qreg, qs, nvalid, w, lane, oacc, Mrun, lsum, flag);
+  if (w == 0) {
+    if (i + 1 < ck.tiles) resolve_scales<PER_TILE>(sc_next, valid_next, mm + (i + 1) % 3);
+    if (r2) {
+      resolve_rows<PER_TILE>(a, us.k, kl2, mm + (i + 2) % 3, sc_next);
+      valid_next = kl2.valid;
+      step_barrier<PER_TILE ? 2 : 1>();
+      return;
+    }
+  }
+  step_barrier<0>();
+}
+
+// Runs the unit's key range [kb, ke) into (oacc, Mrun, lsum); Mrun enters
+// as the preset reference (-inf: set by the first tile).  With MAXONLY it
+// only leaves the per-head maximum exponent in Mrun.
+template <int PER_TILE, int DH, int MAXONLY>
+__device__ __forceinline__ void run_unit(const KArgs& a, UnitState& us, int* list, int* misc, uint8_t* smem,
+                                         const LaneOffsets& lo, int w, int lane, const v8i (&qreg)[4], float qs,
+                                         v16f (&oacc)[8], float& Mrun, float& lsum) {
+  Meta* mm = reinterpret_cast<Meta*>(smem + kOffMeta);
+  int* flag = misc + 4;
+  if (!MAXONLY) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oacc[j] = v16f{};
+  }
+  lsum = 0.f;
+  // chunks of at most kListMax keys, so that a chunk's cmp entries fit the list
+  for (int c0 = us.kb; c0 < us.ke; c0 += kListMax) {
+    const int c1 = min(us.ke, c0 + kListMax);
+    if (a.topk > 0 && us.n_c > kListMax) {
+      const int need_lo = max(c0 - us.n_o, 0), need_hi = max(c1 - us.n_o, 0);
+      if (need_hi > need_lo && (need_lo < us.w_lo || need_hi > us.w_lo + kListMax)) {
+        us.w_lo = need_lo;
+        compact_indices(a, us.k, us.t, list, misc, us.w_lo);
+      }
+    }
+    Chunk ck;
+    ck.st = c0;
+    ck.en = c1;
+    ck.tiles = (c1 - c0 + kTileKeys - 1) / kTileKeys;
+    KeyScale<PER_TILE> sc_next;
+    int valid_next = 0;
+    if (w == 0) {
+      resolve_tile<PER_TILE>(a, us.k, us.n_o, list, us.w_lo, ck.st, ck.en, mm + 0);
+      if (ck.tiles > 1) {
+        const KeyLoc kl1 = resolve_issue(a, us.k, us.n_o, list, us.w_lo, ck.st + kTileKeys, ck.en);
+        resolve_rows<PER_TILE>(a, us.k, kl1, mm + 1, sc_next);
+        valid_next = kl1.valid;
+      }
+    }
+    wait_all_and_sync();
+    gather_tile(mm + 0, smem + kOffTiles, w);
+    wait_all_and_sync();
+    for (int i = 0; i < ck.tiles; i += 2) {
+      pipeline_step<PER_TILE, 0, DH, MAXONLY>(a, us, list, smem, lo, mm, ck, i, w, lane, qreg, qs, oacc, Mrun, lsum,
+                                              sc_next, valid_next, flag);
+      if (i + 1 < ck.tiles)
+        pipeline_step<PER_TILE, 1, DH, MAXONLY>(a, us, list, smem, lo, mm, ck, i + 1, w, lane, qreg, qs, oacc, Mrun,
+                                                lsum, sc_next, valid_next, flag);
+    }
+  }
 }
 
 template <int PER_TILE, int DH>
@@ -498,21 +646,26 @@ __device__ __forceinline__ void attn_body(const KArgs& a, uint8_t* smem, int w) 
   const int bid = blockIdx.x;
   const int lw = (G % 8 == 0) ? ((bid & 7) * (G >> 3) + (bid >> 3)) : bid;  // one XCD per contiguous range
   const int u_begin = a.starts[lw], u_end = a.starts[lw + 1];
-  Meta* mm = reinterpret_cast<Meta*>(smem + kOffMeta);
   int* list = reinterpret_cast<int*>(smem + kOffList);
   int* misc = reinterpret_cast<int*>(smem + kOffMisc);
   const LaneOffsets lo = lane_offsets(lane);
 
   for (int u = u_begin; u < u_end; ++u) {
-    const int t = u / a.splits, s = u - t * a.splits;
-    const Tok k = token_ctx(a, t);
-    if (!k.valid) {
-      if (a.splits == 1) {  // padded query row: O = 0, lse = -inf
+    UnitState us;
+    us.t = u / a.splits;
+    const int s = u - us.t * a.splits;
+    us.k = token_ctx(a, us.t);
+    const int t = us.t;
+    if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
+      if (a.splits == 1) {
         for (int x = lane; x < 32 * 64; x += 64) {
           const int hr = 32 * hh + x / 64, d = 256 * DH + 4 * (x % 64);
           *(uint2*)(a.out + ((size_t)t * kN1 + hr) * kD + d) = make_uint2(0, 0);
         }
         if (a.lse && DH == 0 && g == 0) a.lse[(size_t)t * kN1 + h] = kNegInf;
+      } else if (DH == 0 && g == 0) {
+        a.ws_ml[((size_t)u * kN1 + h) * 2] = kNegInf;
+        a.ws_ml[((size_t)u * kN1 + h) * 2 + 1] = -1.0f;   // marks a padded row for the combine
       }
       continue;
     }
@@ -531,46 +684,29 @@ __device__ __forceinline__ void attn_body(const KArgs& a, uint8_t* smem, int w) 
     const float qd = a.q_ds_per_head ? a.q_ds[(size_t)t * kN1 + h] : a.q_ds[t];
     const float qs = a.scale_log2 * qd;
 
-    const int n_o = k.hi - k.lo;
-    int n_c = 0;
-    int w_lo = 0;
-    if (a.topk > 0) n_c = compact_indices(a, k, t, list, misc, 0);
-    else if (a.has_cmp) n_c = k.vis;
-    const int64_t n = (int64_t)n_o + n_c;
-    const int kb = (int)(n * s / a.splits), ke = (int)(n * (s + 1) / a.splits);
+    us.n_o = us.k.hi - us.k.lo;
+    us.n_c = 0;
+    us.w_lo = 0;
+    if (a.topk > 0) us.n_c = compact_indices(a, us.k, t, list, misc, 0);
+    else if (a.has_cmp) us.n_c = us.k.vis;
+    const int64_t n = (int64_t)us.n_o + us.n_c;
+    us.kb = (int)(n * s / a.splits);
+    us.ke = (int)(n * (s + 1) / a.splits);
 
     v16f oacc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) oacc[j] = v16f{};
     float Mrun = kNegInf, lsum = 0.f;
-
-    // chunks of at most kListMax keys, so that a chunk's cmp entries fit the list
-    for (int c0 = kb; c0 < ke; c0 += kListMax) {
-      const int c1 = min(ke, c0 + kListMax);
-      if (a.topk > 0 && n_c > kListMax) {
-        const int need_lo = max(c0 - n_o, 0), need_hi = max(c1 - n_o, 0);
-        if (need_hi > need_lo && (need_lo < w_lo || need_hi > w_lo + kListMax)) {
-          w_lo = need_lo;
-          compact_indices(a, k, t, list, misc, w_lo);
-        }
-      }
-      Chunk ck;
-      ck.st = c0;
-      ck.en = c1;
-      ck.tiles = (c1 - c0 + kTileKeys - 1) / kTileKeys;
-      if (w == 0) {
-        resolve_tile<PER_TILE>(a, k, n_o, list, w_lo, ck.st, ck.en, mm + 0);
-        if (ck.tiles > 1) resolve_tile<PER_TILE>(a, k, n_o, list, w_lo, ck.st + kTileKeys, ck.en, mm + 1);
-      }
-      wait_all_and_sync();
-      gather_tile(mm + 0, smem + kOffTiles, w);
-      wait_all_and_sync();
-      for (int i = 0; i < ck.tiles; i += 2) {
-        pipeline_step<PER_TILE, 0, DH>(a, k, n_o, list, w_lo, smem, lo, mm, ck, i, w, lane, qreg, qs, oacc, Mrun, lsum);
-        if (i + 1 < ck.tiles)
-          pipeline_step<PER_TILE, 1, DH>(a, k, n_o, list, w_lo, smem, lo, mm, ck, i + 1, w, lane, qreg, qs, oacc, Mrun,
-                                         lsum);
-      }
+    for (int pass = 0;; ++pass) {
+      if (tid == 0) misc[4] = 0;
+      run_unit<PER_TILE, DH, 0>(a, us, list, misc, smem, lo, w, lane, qreg, qs, oacc, Mrun, lsum);
+      __syncthreads();
+      const int redo = misc[4];
+      __syncthreads();
+      if (!redo || pass > 0) break;
+      // a later tile outgrew the first tile's fp8 window: find each head's
+      // maximum exponent, then recompute with the reference preset from it
+      float mx = kNegInf;
+      run_unit<PER_TILE, DH, 1>(a, us, list, misc, smem, lo, w, lane, qreg, qs, oacc, mx, lsum);
+      Mrun = (mx == kNegInf) ? kNegInf : mx - kPShift;
     }
 
     // ---------------- write: final output (one split) or partial state ----------------
@@ -620,42 +756,67 @@ attn_kernel(const KArgs a) {
 // ---------------------------------------------------------------------------
 // split-KV combine: merge the sink-free partial states of every split with
 // the log-sum-exp rule and add the sink logit once.
-// grid (t1, 8): 8 heads per work-group; 256 threads = 8 heads x 32 x 16 cols
+// grid (t1, 8): 8 heads per work-group; 256 threads = 8 heads x 32 x 16 cols.
+// All loads of a batch of 8 splits are issued before any is used.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) combine_kernel(const KArgs a) {
   const int t = blockIdx.x;
   const int h = blockIdx.y * 8 + (threadIdx.x >> 5);
   const int col = (threadIdx.x & 31) * 16;
-  const Tok k = token_ctx(a, t);
+  const int S = a.splits;
   uint16_t* dst = a.out + ((size_t)t * kN1 + h) * kD + col;
-  if (!k.valid) {
-    *(uint4*)dst = make_uint4(0, 0, 0, 0);
-    *(uint4*)(dst + 8) = make_uint4(0, 0, 0, 0);
-    if (a.lse && (threadIdx.x & 31) == 0) a.lse[(size_t)t * kN1 + h] = kNegInf;
-    return;
-  }
+  const float* ml = a.ws_ml + ((size_t)t * S * kN1 + h) * 2;   // split s at + s * kN1 * 2
+  const size_t ostride = (size_t)kN1 * kD;
+  const uint16_t* op = a.ws_o + ((size_t)t * S * kN1 + h) * kD + col;
   const float sg = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
   float M = sg;
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.ws_ml[(((size_t)t * a.splits + s) * kN1 + h) * 2]);
+  bool padded = false;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float m8[8], l8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      m8[j] = (s0 + j < S) ? ml[(size_t)(s0 + j) * kN1 * 2] : kNegInf;
+      l8[j] = (s0 + j < S) ? ml[(size_t)(s0 + j) * kN1 * 2 + 1] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      M = fmaxf(M, m8[j]);
+      padded |= l8[j] < 0.f;
+    }
+  }
   float acc[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = 0.f;
   float L = 0.f;
-  if (M != kNegInf) {
+  if (!padded && M != kNegInf) {
     L = (sg == kNegInf) ? 0.f : exp2f(sg - M);
-    for (int s = 0; s < a.splits; ++s) {
-      const size_t uu = (size_t)t * a.splits + s;
-      const float Ms = a.ws_ml[(uu * kN1 + h) * 2], ls = a.ws_ml[(uu * kN1 + h) * 2 + 1];
-      if (Ms == kNegInf) continue;
-      const float wgt = ls * exp2f(Ms - M);
-      L += wgt;
-      const uint4* src = (const uint4*)(a.ws_o + (uu * kN1 + h) * kD + col);
-      const uint4 x0 = src[0], x1 = src[1];
-      const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float wgt[8];
+      uint4 x0[8], x1[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        acc[2 * j] += wgt * __uint_as_float(xs[j] << 16);
-        acc[2 * j + 1] += wgt * __uint_as_float(xs[j] & 0xffff0000u);
+        const bool in = s0 + j < S;
+        const float Ms = in ? ml[(size_t)(s0 + j) * kN1 * 2] : kNegInf;
+        const float ls = in ? ml[(size_t)(s0 + j) * kN1 * 2 + 1] : 0.f;
+        wgt[j] = (Ms == kNegInf) ? 0.f : ls * exp2f(Ms - M);
+        if (in) {
+          const uint4* src = (const uint4*)(op + (size_t)(s0 + j) * ostride);
+          x0[j] = src[0];
+          x1[j] = src[1];
+        } else {
+          x0[j] = make_uint4(0, 0, 0, 0);
+          x1[j] = x0[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        L += wgt[j];
+        const uint32_t xs[8] = {x0[j].x, x0[j].y, x0[j].z, x0[j].w, x1[j].x, x1[j].y, x1[j].z, x1[j].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc[2 * e] += wgt[j] * __uint_as_float(xs[e] << 16);
+          acc[2 * e + 1] += wgt[j] * __uint_as_float(xs[e] & 0xffff0000u);
+        }
       }
     }
   }
@@ -665,7 +826,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const KArgs a) {
   for (int j = 0; j < 8; ++j) o[j] = bf16_rne(acc[2 * j] * inv) | (bf16_rne(acc[2 * j + 1] * inv) << 16);
   *(uint4*)dst = make_uint4(o[0], o[1], o[2], o[3]);
   *(uint4*)(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
-  if (a.lse && (threadIdx.x & 31) == 0) a.lse[(size_t)t * kN1 + h] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
+  if (a.lse && (threadIdx.x & 31) == 0)
+    a.lse[(size_t)t * kN1 + h] = (!padded && L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
@@ -693,10 +855,8 @@ __global__ void __launch_bounds__(kThreads) debug_resolve_kernel(const KArgs a, 
         compact_indices(a, k, t, list, wtot, w_lo);
       }
     }
-    for (int key = c0 + threadIdx.x; key < c1; key += kThreads) {
-      bool is_cmp;
-      keys[(size_t)t * max_keys + key] = (int32_t)resolve_row(a, k, n_o, key, list, w_lo, is_cmp);
-    }
+    for (int key = c0 + threadIdx.x; key < c1; key += kThreads)
+      keys[(size_t)t * max_keys + key] = (int32_t)resolve_row(a, k, n_o, key, list, w_lo);
     __syncthreads();
   }
 }
@@ -725,3 +885,4 @@ int launch_debug_resolve(const KArgs& a, int32_t* keys, int32_t* counts, int32_t
 }
 
 }  // namespace csmla
+
