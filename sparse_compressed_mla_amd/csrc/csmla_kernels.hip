@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "csmla_internal.h"
 
 namespace csmla {
@@ -42,22 +44,56 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 constexpr int kThreads = 256;
 constexpr int kTileBytes = kTileKeys * kD;      // 32 KiB
+constexpr int kStageRow = 2 * 256 + 16;         // bytes per head row of the output staging
 
-struct Meta {                 // per-key data of one tile, in LDS
-  uint64_t addr[kTileKeys];   // byte address of the fp8 row; 0 = no row (tail)
-  float lam[kTileKeys];       // log2 of the largest V descale of the row
-  float inv[kTileKeys];       // 2^-lam
-  float ks[8][kTileKeys];     // descales: per-token in ks[0]; per-tile in ks[0..7]
+// LDS layout.  Tiles: 3 buffers of 64 rows x 512 fp8 bytes (XOR-swizzled
+// 16-byte chunks).  Per-key arrays of the current chunk of a unit's key list
+// (row address, log2 / inverse of the row's largest V descale, descales).
+template <int PER_TILE>
+struct Lds {
+  static constexpr int kChunk = PER_TILE ? 512 : 1024;     // keys resolved at once
+  static constexpr int kNks = PER_TILE ? 8 : 1;            // descales per key
+  static constexpr int kTiles = 0;                         // 3 x 32 KiB
+  static constexpr int kSx = 3 * kTileBytes;               // partial scores for the partner, 4 waves x 4 KiB
+  static constexpr int kPx = kSx + 4 * 4096;               // P halves for the partner, 4 waves x 4 KiB
+  static constexpr int kAddr = kPx + 4 * 4096;             // uint64 [kChunk]
+  static constexpr int kLam = kAddr + 8 * kChunk;          // float [kChunk]
+  static constexpr int kInv = kLam + 4 * kChunk;           // float [kChunk]
+  static constexpr int kKs = kInv + 4 * kChunk;            // float [kNks][kChunk]
+  static constexpr int kList = kKs + 4 * kNks * kChunk;    // int [kListMax]: compacted cmp indices
+  static constexpr int kMisc = kList + 4 * kListMax;       // [0..3] compaction, [4] redo flag, [64..319] pair values
+  static constexpr int kBytes = kMisc + 4 * 64 + 4 * 4 * 64;
 };
-constexpr int kMetaBytes = 3072;
-static_assert(sizeof(Meta) <= kMetaBytes, "meta");
+static_assert(Lds<0>::kBytes <= 160 * 1024 && Lds<1>::kBytes <= 160 * 1024, "LDS");
 
-constexpr int kOffTiles = 0;                               // 2 tile buffers
-constexpr int kOffXchg = 2 * kTileBytes;                   // partial scores, 4 waves x 8 KiB
-constexpr int kOffMeta = kOffXchg + 4 * 8192;              // 3 meta stages
-constexpr int kOffList = kOffMeta + 3 * kMetaBytes;        // compacted cmp indices
-constexpr int kOffMisc = kOffList + kListMax * 4;
-constexpr int kLdsBytes = kOffMisc + 256;
+// The kernel arguments live in the kernarg segment (constant address space).
+// args() re-derives a view of them through an opaque copy of the pointer, so
+// that fields are reloaded with scalar loads where they are used instead of
+// being held in scalar registers across the whole kernel.
+typedef const __attribute__((address_space(4))) KArgs* KArgPtr;
+
+__device__ __forceinline__ const KArgs& args(KArgPtr p) {
+  asm volatile("" : "+s"(p));
+  return *(const KArgs*)p;
+}
+
+// Source of the rows of key slots past the end of a chunk: the gather always
+// issues the same number of loads per wave, so that the pipeline can count them.
+__device__ __attribute__((aligned(4096))) uint8_t g_zero_row[kD];
+
+// Work-group barrier that orders LDS only: outstanding global loads (the
+// next tiles' gathers, stores of a finished unit) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A copy of x that the compiler cannot see through: values derived from it
+// are recomputed where they are used instead of being hoisted out of loops
+// and held in registers across the whole kernel.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ (((r >> 3) & 1) << 2); }
 
@@ -85,15 +121,17 @@ __device__ __forceinline__ int floordiv(int64_t a, int64_t b) {
   return (int)q;
 }
 
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 values as packed bf16 (round to nearest even; v_cvt_pk_bf16_f32),
+// the first in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
-  return make_uint2(bf16_rne(a) | (bf16_rne(b) << 16), bf16_rne(c) | (bf16_rne(d) << 16));
+  return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
 // ---------------------------------------------------------------------------
@@ -108,7 +146,7 @@ struct Tok {
   int k_eff;       // index slots read
 };
 
-__device__ Tok token_ctx(const KArgs& a, int t) {
+__device__ __forceinline__ Tok token_ctx(const KArgs& a, int t) {
   Tok k;
   int b, q0, span;
   if (a.layout_q == 1) {  // TND: largest b with cu_q[b] <= t
@@ -165,145 +203,155 @@ __device__ Tok token_ctx(const KArgs& a, int t) {
 
 // Compact the valid index slots of token t in slot order; entries whose
 // compacted position lies in [w_lo, w_lo + kListMax) go to list[pos - w_lo].
-// Returns the number of valid slots.  Whole-work-group call.
-__device__ int compact_indices(const KArgs& a, const Tok& k, int t, int* list, int* wtot, int w_lo) {
+// Returns the number of valid slots.  Whole-work-group call.  The loads of
+// four rounds are issued before the first ballot, and bounded by topk rather
+// than the token's effective length so that they do not wait for it.
+__device__ __forceinline__ int compact_indices(const KArgs& a, const Tok& k, int t, int* list, int* wtot, int w_lo) {
   const int* row = a.idx + (size_t)t * a.topk;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tid = opaque((int)threadIdx.x);
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int base = 0;
-  for (int s0 = 0; s0 < k.k_eff; s0 += kThreads) {
-    const int s = s0 + threadIdx.x;
-    const int v = (s < k.k_eff) ? row[s] : -1;
-    const bool ok = (v >= 0) && (v < k.vis);
-    const uint64_t bal = __ballot(ok);
-    const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wtot[w] = __popcll(bal);
-    __syncthreads();
-    int off = 0;
-    for (int j = 0; j < w; ++j) off += wtot[j];
-    const int tot = wtot[0] + wtot[1] + wtot[2] + wtot[3];
-    const int pos = base + off + pre;
-    if (ok && pos >= w_lo && pos < w_lo + kListMax) list[pos - w_lo] = v;
-    base += tot;
-    __syncthreads();
+  for (int s0 = 0; s0 < k.k_eff; s0 += 4 * kThreads) {
+    int v[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int s = s0 + m * kThreads + tid;
+      v[m] = (s < a.topk) ? row[s] : -1;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int s = s0 + m * kThreads + tid;
+      const bool ok = (s < k.k_eff) && (v[m] >= 0) && (v[m] < k.vis);
+      const uint64_t bal = __ballot(ok);
+      const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wtot[w] = __popcll(bal);
+      lds_barrier();
+      int off = 0;
+      for (int j = 0; j < w; ++j) off += wtot[j];
+      const int tot = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+      const int pos = base + off + pre;
+      if (ok && pos >= w_lo && pos < w_lo + kListMax) list[pos - w_lo] = v[m];
+      base += tot;
+      lds_barrier();
+    }
   }
   return base;
 }
 
-// Resolving one tile of 64 keys takes three stages, spread over pipeline
-// steps so that no wave waits on a dependent load: (1) the block-table
-// lookup, (2) the row address and the descale loads, (3) the descales into
-// meta.  One wave, one key per lane.
-struct KeyLoc {
-  int j;       // logical token position in its cache
-  int cmp;     // 1: the key lives in cmp_kv
-  int blk;     // PA block id (loaded in stage 1)
-  int valid;   // key < end of the chunk
-};
+// ---------------------------------------------------------------------------
+// key resolution: list position -> cache row (QuantSparseFlashMla, 参数说明:
+// the block tables, the band window, cmp_sparse_indices with -1 skipped)
+// ---------------------------------------------------------------------------
 
-template <int PER_TILE>
-struct KeyScale {
-  float v[PER_TILE ? 8 : 1];
-};
-
-__device__ __forceinline__ KeyLoc resolve_issue(const KArgs& a, const Tok& k, int n_o, const int* list, int w_lo,
-                                                int key0, int key_end) {
-  const int key = key0 + (int)(threadIdx.x & 63);
-  KeyLoc kl;
-  kl.valid = key < key_end;
-  kl.cmp = key >= n_o;
-  kl.j = 0;
-  kl.blk = 0;
-  if (kl.valid) {
-    kl.j = !kl.cmp ? k.lo + key : ((a.topk > 0) ? list[key - n_o - w_lo] : key - n_o);
-    if (a.layout_kv == 2) {
-      const int bs = kl.cmp ? a.cmp_bs : a.ori_bs;
-      const int* tab = kl.cmp ? a.cmp_tab : a.ori_tab;
-      const int cols = kl.cmp ? a.cmp_cols : a.ori_cols;
-      kl.blk = tab[(size_t)k.b * cols + kl.j / bs];
-    }
-  }
-  return kl;
+// Logical token position of key `key` of the token's list (ori band first,
+// then cmp entries) and whether it lives in cmp_kv.
+__device__ __forceinline__ int key_pos(const KArgs& a, const Tok& k, int n_o, int key, const int* list, int w_lo,
+                                       bool& is_cmp) {
+  is_cmp = key >= n_o;
+  if (!is_cmp) return k.lo + key;
+  return (a.topk > 0) ? list[key - n_o - w_lo] : key - n_o;
 }
 
-__device__ __forceinline__ int64_t key_row(const KArgs& a, const Tok& k, const KeyLoc& kl) {
+__device__ __forceinline__ int64_t row_of(const KArgs& a, const Tok& k, bool is_cmp, int j, int blk) {
   if (a.layout_kv == 2) {
-    const int bs = kl.cmp ? a.cmp_bs : a.ori_bs;
-    return (int64_t)kl.blk * bs + (kl.j % bs);
+    const int bs = is_cmp ? a.cmp_bs : a.ori_bs;
+    return (int64_t)blk * bs + (j % bs);
   }
-  if (a.layout_kv == 1) return (int64_t)(kl.cmp ? k.cmp0 : k.kv0) + kl.j;
-  return (int64_t)k.b * (kl.cmp ? a.cmp_s : a.ori_s) + kl.j;
+  if (a.layout_kv == 1) return (int64_t)(is_cmp ? k.cmp0 : k.kv0) + j;
+  return (int64_t)k.b * (is_cmp ? a.cmp_s : a.ori_s) + j;
 }
 
-template <int PER_TILE>
-__device__ __forceinline__ void resolve_rows(const KArgs& a, const Tok& k, const KeyLoc& kl, Meta* m,
-                                             KeyScale<PER_TILE>& sc) {
-  const int lane = threadIdx.x & 63;
-  uint64_t addr = 0;
-#pragma unroll
-  for (int c = 0; c < (PER_TILE ? 8 : 1); ++c) sc.v[c] = 0.f;
-  if (kl.valid) {
-    const int64_t row = key_row(a, k, kl);
-    addr = (uint64_t)((kl.cmp ? a.cmp_kv : a.ori_kv) + row * kD);
-    const float* ds = kl.cmp ? a.cmp_ds : a.ori_ds;
-    if (PER_TILE) {
-      const v4f* p = (const v4f*)(ds + row * 8);
-      const v4f x0 = p[0], x1 = p[1];
-      sc.v[0] = x0[0]; sc.v[1] = x0[1]; sc.v[2] = x0[2]; sc.v[3] = x0[3];
-      sc.v[4] = x1[0]; sc.v[5] = x1[1]; sc.v[6] = x1[2]; sc.v[7] = x1[3];
-    } else {
-      sc.v[0] = ds[row];
-    }
-  }
-  m->addr[lane] = addr;
-}
-
-template <int PER_TILE>
-__device__ __forceinline__ void resolve_scales(const KeyScale<PER_TILE>& sc, int valid, Meta* m) {
-  const int lane = threadIdx.x & 63;
-  float lam = kNegInf, inv = 0.f;
-  if (valid) {
-    float mx = sc.v[0];
-#pragma unroll
-    for (int c = 1; c < (PER_TILE ? 8 : 1); ++c) mx = fmaxf(mx, sc.v[c]);
-#pragma unroll
-    for (int c = 0; c < (PER_TILE ? 8 : 1); ++c)
-      if (sc.v[c] != sc.v[c]) mx = sc.v[c];   // a NaN scale poisons the row
-    mx = (mx == 0.f) ? kMinDescale : mx;
-    lam = __log2f(mx);
-    inv = 1.0f / mx;
-    if (mx != mx) { lam = mx; inv = mx; }
-  }
-  m->lam[lane] = lam;
-  m->inv[lane] = inv;
-#pragma unroll
-  for (int c = 0; c < (PER_TILE ? 8 : 1); ++c) m->ks[c][lane] = valid ? sc.v[c] : 0.f;
-}
-
-// Whole-tile resolve in one go (used by the pipeline prologue).
-template <int PER_TILE>
-__device__ __forceinline__ void resolve_tile(const KArgs& a, const Tok& k, int n_o, const int* list, int w_lo,
-                                             int key0, int key_end, Meta* m) {
-  const KeyLoc kl = resolve_issue(a, k, n_o, list, w_lo, key0, key_end);
-  KeyScale<PER_TILE> sc;
-  resolve_rows<PER_TILE>(a, k, kl, m, sc);
-  resolve_scales<PER_TILE>(sc, kl.valid, m);
+__device__ __forceinline__ int block_of(const KArgs& a, const Tok& k, bool is_cmp, int j) {
+  const int bs = is_cmp ? a.cmp_bs : a.ori_bs;
+  const int* tab = is_cmp ? a.cmp_tab : a.ori_tab;
+  const int cols = is_cmp ? a.cmp_cols : a.ori_cols;
+  return tab[(size_t)k.b * cols + j / bs];
 }
 
 // Row of key `key` for the debug export (same resolution code).
 __device__ __forceinline__ int64_t resolve_row(const KArgs& a, const Tok& k, int n_o, int key, const int* list,
                                                int w_lo) {
-  KeyLoc kl;
-  kl.valid = 1;
-  kl.cmp = key >= n_o;
-  kl.j = !kl.cmp ? k.lo + key : ((a.topk > 0) ? list[key - n_o - w_lo] : key - n_o);
-  kl.blk = 0;
-  if (a.layout_kv == 2) {
-    const int bs = kl.cmp ? a.cmp_bs : a.ori_bs;
-    const int* tab = kl.cmp ? a.cmp_tab : a.ori_tab;
-    const int cols = kl.cmp ? a.cmp_cols : a.ori_cols;
-    kl.blk = tab[(size_t)k.b * cols + kl.j / bs];
+  bool is_cmp;
+  const int j = key_pos(a, k, n_o, key, list, w_lo, is_cmp);
+  const int blk = (a.layout_kv == 2) ? block_of(a, k, is_cmp, j) : 0;
+  return row_of(a, k, is_cmp, j, blk);
+}
+
+// Resolve the keys [c0, c1) of a unit into the chunk arrays: row address,
+// descales, and lam = log2 / inv = 1 / the row's largest descale.  Slots past
+// c1 read the zero row with zero descales and lam = -inf.  All block-table
+// loads of the chunk are issued together, then all row / descale loads:
+// two dependent round trips per chunk.  Whole-work-group call; ends with a
+// barrier.
+template <int PER_TILE>
+__device__ __forceinline__ void resolve_chunk(const KArgs& a, const Tok& k, int n_o, const int* list, int w_lo,
+                                              int c0, int c1, uint8_t* smem) {
+  using L = Lds<PER_TILE>;
+  constexpr int M = L::kChunk / kThreads, NKS = L::kNks;
+  uint64_t* kaddr = reinterpret_cast<uint64_t*>(smem + L::kAddr);
+  float* klam = reinterpret_cast<float*>(smem + L::kLam);
+  float* kinv = reinterpret_cast<float*>(smem + L::kInv);
+  float* kks = reinterpret_cast<float*>(smem + L::kKs);
+  const int tid = opaque((int)threadIdx.x);
+  int j[M], blk[M];
+  bool cmp[M], ok[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int key = c0 + m * kThreads + tid;
+    ok[m] = key < c1;
+    j[m] = ok[m] ? key_pos(a, k, n_o, key, list, w_lo, cmp[m]) : 0;
+    if (!ok[m]) cmp[m] = false;
+    blk[m] = 0;
   }
-  return key_row(a, k, kl);
+  if (a.layout_kv == 2) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if (ok[m]) blk[m] = block_of(a, k, cmp[m], j[m]);
+  }
+  float ds[M][NKS];
+  uint64_t addr[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    addr[m] = (uint64_t)(uintptr_t)g_zero_row;
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) ds[m][c] = 0.f;
+    if (ok[m]) {
+      const int64_t row = row_of(a, k, cmp[m], j[m], blk[m]);
+      addr[m] = (uint64_t)(uintptr_t)((cmp[m] ? a.cmp_kv : a.ori_kv) + row * kD);
+      const float* dsp = cmp[m] ? a.cmp_ds : a.ori_ds;
+      if constexpr (PER_TILE) {
+        const v4f x0 = *(const v4f*)(dsp + row * 8);
+        const v4f x1 = *(const v4f*)(dsp + row * 8 + 4);
+        ds[m][0] = x0[0]; ds[m][1] = x0[1]; ds[m][2] = x0[2]; ds[m][3] = x0[3];
+        ds[m][4] = x1[0]; ds[m][5] = x1[1]; ds[m][6] = x1[2]; ds[m][7] = x1[3];
+      } else {
+        ds[m][0] = dsp[row];
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int slot = m * kThreads + tid;
+    float lam = kNegInf, inv = 0.f;
+    if (ok[m]) {
+      float mx = ds[m][0];
+#pragma unroll
+      for (int c = 1; c < NKS; ++c) mx = fmaxf(mx, ds[m][c]);
+#pragma unroll
+      for (int c = 0; c < NKS; ++c)
+        if (ds[m][c] != ds[m][c]) mx = ds[m][c];   // a NaN descale poisons the row
+      mx = (mx == 0.f) ? kMinDescale : mx;
+      lam = __log2f(mx);
+      inv = 1.0f / mx;
+      if (mx != mx) { lam = mx; inv = mx; }
+    }
+    kaddr[slot] = addr[m];
+    klam[slot] = lam;
+    kinv[slot] = inv;
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) kks[c * L::kChunk + slot] = ds[m][c];
+  }
+  lds_barrier();
 }
 
 // LDS byte address of a pointer into a __shared__ array.
@@ -311,25 +359,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Gather the 64 rows of a tile into LDS: 4 waves x 8 instructions, each
-// instruction 2 rows (lanes 0-31 and 32-63, 16 bytes per lane), issued as
-// global_load_lds_dwordx4 (M0 = LDS destination, lane l writes base + 16 l).
-// The loads are ordered only by the explicit waits of the pipeline barriers,
-// so the compiler does not hold the other tile's LDS reads behind them.
-__device__ __forceinline__ void gather_tile(const Meta* m, uint8_t* tb, int w) {
-  const int lane = threadIdx.x & 63, g = lane >> 5, li = lane & 31;
+// Gather the 64 rows of chunk tile `tile` into a tile buffer: wave w loads
+// rows [16 w, +16) with 8 global_load_lds_dwordx4 (2 rows each: lanes 0-31 and
+// 32-63, 16 bytes per lane; M0 = LDS destination, lane l writes base + 16 l).
+// Exactly 8 vector-memory instructions per wave, whatever the tile holds.
+// The loads are ordered only by the explicit waits of the pipeline, so the
+// compiler does not hold the other tiles' LDS reads behind them.
+__device__ __forceinline__ void gather_tile(const uint64_t* kaddr, int tile, uint8_t* tb, int w) {
+  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
+  uint64_t src[8];
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi) {   // all row addresses first: one LDS wait for the tile
+    const int r = 16 * w + 2 * mi + g;
+    src[mi] = kaddr[tile * kTileKeys + r] + 16u * (uint32_t)(li ^ swz(r));
+  }
 #pragma unroll
   for (int mi = 0; mi < 8; ++mi) {
-    const int r0 = 16 * w + 2 * mi;
-    const int r = r0 + g;
-    const uint64_t p = m->addr[r];
-    if (p) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + r0 * kD));
-      const uint64_t src = p + 16u * (uint32_t)(li ^ swz(r));
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "m0");
-    } else {
-      *(v4i*)(tb + r * kD + li * 16) = v4i{0, 0, 0, 0};
-    }
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + (16 * w + 2 * mi) * kD));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src[mi]) : "m0");
   }
 }
 
@@ -338,342 +385,510 @@ __device__ __forceinline__ void wait_all_and_sync() {
   __syncthreads();
 }
 
-// Work-group barrier that orders LDS only: outstanding global loads (the
-// next tile's gather, descale prefetches) stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Barrier at the end of a pipeline step: the gather into LDS must have landed;
-// the wave's last NDS global loads (descale prefetches) may still be in flight.
-template <int NDS>
-__device__ __forceinline__ void step_barrier() {
-  if (NDS == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if (NDS == 1) asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Work-group barrier after which the older of the wave's gathers has landed:
+// with `newer` set, the 8 loads of the most recent gather may still be in flight.
+__device__ __forceinline__ void gather_barrier(bool newer) {
+  if (newer) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
 // attention kernel
 // ---------------------------------------------------------------------------
+//
+// Wave w: heads [32 hh, +32) with hh = w & 1, output columns [256 dh, +256)
+// with dh = w >> 1.  The pair (w, w ^ 2) shares its heads.  For a 64-key
+// tile each wave of the pair computes S^T over its half of D for both
+// 32-key m-tiles, hands the partner the half it does not own through LDS,
+// and runs the softmax of its own 32 keys (m-tile dh); the fp8 P halves are
+// swapped back, so that both waves hold P for all 64 keys.
+//
+// Pipelined by one tile: step i runs P V of tile i in two halves around
+// S^T and the softmax of tile i+1, so that the softmax VALU work has MFMAs to
+// hide under.  The keys of a chunk are resolved before its first tile; the
+// gather of tile i+2 is issued at the start of step i (3 LDS tile buffers).
 
-// Per-lane LDS byte offsets, fixed for the whole kernel.  The parts that vary
-// with the K-step / d-block are multiples of 128 bytes and the buffer parity
-// is 32 KiB: both go into the ds_read immediate offset.
+// Per-lane LDS byte offsets into tile buffer 0, fixed for the whole kernel
+// (they include the wave's half of D).  Within a row the 16-byte chunk index
+// is XOR-swizzled, so the offsets of the other chunks a lane reads differ
+// from a base by an XOR: bit 4 (16-byte half of a K operand), bit 6 (K-step
+// parity), bits 5-6 (d-block of a V^T read).  Per step the buffer offset is
+// added and the XORs applied (qk_at / tr_at); what varies with the K-step
+// pair / d-block group is a multiple of 128 bytes and goes into the ds_read
+// immediate offset.
 struct LaneOffsets {
-  int qk[2][2][2];   // [m-tile tt][K-step parity][16-byte half]: K row reads for S^T = K Q^T
-  int tr[4][4];      // [rho][d-block mod 4]: source address of the V^T transpose reads
+  int qk[2];   // [own m-tile / other m-tile]: K row base for S^T = K Q^T
+  int tr[4];   // [rho]: V^T transpose-read base
+};
+struct QkOff {
+  int v[2][2][2];   // [own / other m-tile][K-step parity][16-byte half]
+};
+struct TrOff {
+  int v[4][4];      // [rho][d-block mod 4]
 };
 
-__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane, int dh) {
   LaneOffsets o;
   const int g = lane >> 5, li = lane & 31;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int which = 0; which < 2; ++which) {
+    const int tt = which ? 1 - dh : dh;
     const int key = 32 * tt + li, f = swz(key);
-#pragma unroll
-    for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-      for (int x = 0; x < 2; ++x) o.qk[tt][sp][x] = kOffTiles + key * kD + 16 * ((4 * sp + 2 * g + x) ^ f);
+    o.qk[which] = key * kD + 256 * dh + 16 * ((2 * g) ^ f);
   }
   const int trx = (lane >> 4) & 1;
 #pragma unroll
   for (int rho = 0; rho < 4; ++rho) {
     const int key = 16 * rho + 8 * ((lane >> 3) & 1) + 4 * (lane >> 5) + ((lane >> 1) & 3);
     const int f = swz(key);
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      o.tr[rho][b] = kOffTiles + key * kD + 8 * (lane & 1) + 16 * (((2 * b) ^ (f & 6)) + (trx ^ (f & 1)));
+    o.tr[rho] = key * kD + 256 * dh + 8 * (lane & 1) + 16 * ((f & 6) + (trx ^ (f & 1)));
   }
   return o;
 }
 
-// K operand (32 keys x 64 d, d in [64 s8, +64)) of m-tile tt.
-template <int BUF>
-__device__ __forceinline__ v8i read_k(const uint8_t* smem, const LaneOffsets& o, int tt, int s8) {
-  const int a = s8 >> 1, sp = s8 & 1;
-  const v4i lo = *(const v4i*)(smem + o.qk[tt][sp][0] + BUF * kTileBytes + 128 * a);
-  const v4i hi = *(const v4i*)(smem + o.qk[tt][sp][1] + BUF * kTileBytes + 128 * a);
+// chunk (4 sp + 2 g + x) ^ f  =  (2 g ^ f) ^ 4 sp ^ x;  the key and dh terms
+// lie above bit 7, so the XOR of the chunk bits commutes with them.
+__device__ __forceinline__ QkOff qk_at(const LaneOffsets& o, int boff) {
+  QkOff q;
+#pragma unroll
+  for (int which = 0; which < 2; ++which)
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) q.v[which][sp][x] = (o.qk[which] ^ (64 * sp + 16 * x)) + boff;
+  return q;
+}
+
+// chunk ((2 b) ^ (f & 6)) + (trx ^ (f & 1))  =  ((f & 6) + (trx ^ (f & 1))) ^ 2 b
+__device__ __forceinline__ TrOff tr_at(const LaneOffsets& o, int boff) {
+  TrOff t;
+#pragma unroll
+  for (int rho = 0; rho < 4; ++rho)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) t.v[rho][b] = (o.tr[rho] ^ (32 * b)) + boff;
+  return t;
+}
+
+// K operand (32 keys x 64 d): m-tile `which`, d in [256 dh + 64 s4, +64).
+__device__ __forceinline__ v8i read_k(const uint8_t* smem, const QkOff& q, int which, int s4) {
+  const int a = s4 >> 1, sp = s4 & 1;
+  const v4i lo = *(const v4i*)(smem + q.v[which][sp][0] + 128 * a);
+  const v4i hi = *(const v4i*)(smem + q.v[which][sp][1] + 128 * a);
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// V^T operand (32 d x 64 keys) of d-block nt, via LDS transpose reads.
-template <int BUF>
-__device__ __forceinline__ v8i read_vt(const uint8_t* smem, const LaneOffsets& o, int nt) {
-  const int a = nt >> 2, b = nt & 3;
+// V^T operand (32 d x 64 keys) of the wave's d-block j (0..7), via LDS transpose reads.
+__device__ __forceinline__ v8i read_vt(const uint8_t* smem, const TrOff& t, int j) {
+  const int a = j >> 2, b = j & 3;
   v8i av;
 #pragma unroll
   for (int rho = 0; rho < 4; ++rho) {
-    const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        (lds_v2i*)(smem + o.tr[rho][b] + BUF * kTileBytes + 128 * a));
+    const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(smem + t.v[rho][b] + 128 * a));
     av[2 * rho] = x[0];
     av[2 * rho + 1] = x[1];
   }
   return av;
 }
 
-// One 64-key tile of one wave (32 heads, 256 output columns of half DH).
-// The first tile with visible keys fixes each head's reference Mrun (unless
-// it was preset); a later tile that would push P' past 2^8 only raises
-// *flag, and the unit is then recomputed with Mrun preset from its true
-// maximum (MAXONLY = 1 computes that maximum: S^T and the max, no P V).
-template <int PER_TILE, int BUF, int DH, int MAXONLY>
-__device__ __forceinline__ void compute_tile(uint8_t* smem, const LaneOffsets& o, const Meta* m,
-                                             const v8i (&qreg)[4], float qs, int nvalid, int w, int lane,
-                                             v16f (&oacc)[8], float& Mrun, float& lsum, int* flag) {
-  const int g = lane >> 5;
-  // ---- partial S^T over this wave's half of D ----
-  v16f sacc[2];
+// P of one tile as the B operand of O^T += V^T P^T: byte r of register 4 tt + q
+// is key 32 tt + 8 q + 4 g + r.  Per-token descales: an fp8 hi/lo pair.  Per-tile
+// descales: P' / vds_max in fp32 (16 values per m-tile), scaled per 64-wide D tile
+// at use.
+template <int PER_TILE>
+struct PTile;
+template <>
+struct PTile<0> { v8i hi, lo; };
+template <>
+struct PTile<1> { v16f lt[2]; };
+
+// Per-key arrays of one tile of the current chunk.
+template <int PER_TILE>
+struct TileView {
+  const float* lam;   // [64]
+  const float* inv;   // [64]
+  const float* ks;    // descale c of key k at ks[c * kChunk + k]
+};
+
+template <int PER_TILE>
+__device__ __forceinline__ TileView<PER_TILE> tile_view(const uint8_t* smem, int tile) {
+  using L = Lds<PER_TILE>;
+  TileView<PER_TILE> v;
+  v.lam = reinterpret_cast<const float*>(smem + L::kLam) + tile * kTileKeys;
+  v.inv = reinterpret_cast<const float*>(smem + L::kInv) + tile * kTileKeys;
+  v.ks = reinterpret_cast<const float*>(smem + L::kKs) + tile * kTileKeys;
+  return v;
+}
+
+// Partial S^T of both m-tiles over this wave's half of D.  Per-tile
+// descales scale each 64-wide D tile's partial product before the sum.
+template <int PER_TILE>
+__device__ __forceinline__ void qk_partial(const uint8_t* smem, const QkOff& o, const TileView<PER_TILE>& tv,
+                                           int dh, const v8i (&qreg)[4], int g, v16f& s_own, v16f& s_oth) {
+  s_own = v16f{};
+  s_oth = v16f{};
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    sacc[tt] = v16f{};
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const v8i k_oth = read_k(smem, o, 1, s4);
+    const v8i k_own = read_k(smem, o, 0, s4);
+    if constexpr (PER_TILE) {
+      const v16f p_oth = mma(k_oth, qreg[s4], v16f{});
+      const v16f p_own = mma(k_own, qreg[s4], v16f{});
+      const float* ks = tv.ks + (4 * dh + s4) * Lds<PER_TILE>::kChunk;
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int s8 = 4 * DH + s4;
-      const v8i av = read_k<BUF>(smem, o, tt, s8);
-      if (PER_TILE) {
-        const v16f part = mma(av, qreg[s4], v16f{});
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const v4f ko = *(const v4f*)&ks[32 * (1 - dh) + 8 * q4 + 4 * g];
+        const v4f km = *(const v4f*)&ks[32 * dh + 8 * q4 + 4 * g];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const v4f kv = *(const v4f*)&m->ks[s8][32 * tt + 8 * q4 + 4 * g];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sacc[tt][4 * q4 + r] += kv[r] * part[4 * q4 + r];
+        for (int r = 0; r < 4; ++r) {
+          s_oth[4 * q4 + r] += ko[r] * p_oth[4 * q4 + r];
+          s_own[4 * q4 + r] += km[r] * p_own[4 * q4 + r];
         }
-      } else {
-        sacc[tt] = mma(av, qreg[s4], sacc[tt]);
       }
+    } else {
+      s_oth = mma(k_oth, qreg[s4], s_oth);
+      s_own = mma(k_own, qreg[s4], s_own);
     }
   }
-  // ---- add the partner's half (same heads, other half of D) ----
-  float* xw = reinterpret_cast<float*>(smem + kOffXchg) + w * 2048;
-  const float* xp = reinterpret_cast<const float*>(smem + kOffXchg) + (w ^ 2) * 2048;
+}
+
+// O^T += V^T P^T for d-blocks [J0, J0 + 4) of this wave's half of D.
+template <int PER_TILE, int J0>
+__device__ __forceinline__ void pv_half(const uint8_t* smem, const TrOff& o, const TileView<PER_TILE>& tv,
+                                        int dh, const PTile<PER_TILE>& P, int g, v16f (&oacc)[8]) {
+  if constexpr (PER_TILE) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      *(v4f*)&xw[((tt * 4 + r4) * 64 + lane) * 4] =
-          v4f{sacc[tt][4 * r4], sacc[tt][4 * r4 + 1], sacc[tt][4 * r4 + 2], sacc[tt][4 * r4 + 3]};
-  lds_barrier();
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const v4f pv = *(const v4f*)&xp[((tt * 4 + r4) * 64 + lane) * 4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sacc[tt][4 * r4 + r] += pv[r];
-    }
-  // ---- exponent E = s*log2(e) + log2(vds), masked past nvalid; in place ----
-  float mt = kNegInf;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int kb4 = 32 * tt + 8 * q4 + 4 * g;
-      const v4f lam = *(const v4f*)&m->lam[kb4];
-      v4f kd = {1.f, 1.f, 1.f, 1.f};
-      if (!PER_TILE) kd = *(const v4f*)&m->ks[0][kb4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sv = sacc[tt][4 * q4 + r] * (PER_TILE ? qs : qs * kd[r]) + lam[r];
-        const float ev = (kb4 + r < nvalid) ? sv : kNegInf;
-        sacc[tt][4 * q4 + r] = ev;
-        mt = fmaxf(mt, ev);
-      }
-    }
-  }
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
-  if (MAXONLY) {
-    Mrun = fmaxf(Mrun, mt);
-    return;
-  }
-  // Mrun is the reference of P' = 2^(E - Mrun): the max maps to 2^4, and P'
-  // may grow to 2^8 before the reference would have to move.
-  if (Mrun == kNegInf) Mrun = mt - kPShift;          // first tile with keys: O is still zero
-  else if (__ballot(mt > Mrun + kTau)) *flag = 1;    // would overflow fp8: redo with a preset reference
-  const float Ms = (Mrun == kNegInf) ? 0.f : Mrun;
-  // ---- P' = 2^(E - M) in (0, 2^8]; l accumulates P' / vds_max ----
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int kb4 = 32 * tt + 8 * q4 + 4 * g;
-      const v4f iv = *(const v4f*)&m->inv[kb4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(sacc[tt][4 * q4 + r] - Ms);
-        const float lt = pv * iv[r];
-        lsum += lt;
-        sacc[tt][4 * q4 + r] = PER_TILE ? lt : pv;
-      }
-    }
-  }
-  // ---- O^T += V^T P'^T over this wave's 8 d-blocks; P' = hi + lo, both fp8 ----
-  if (PER_TILE) {
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      const int c = 4 * DH + c4;   // 64-wide D tile
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int c4 = J0 / 2 + c2;             // 64-wide D tile within the half
+      const float* ks = tv.ks + (4 * dh + c4) * Lds<PER_TILE>::kChunk;
       v8i ph, pl;
 #pragma unroll
       for (int rg = 0; rg < 8; ++rg) {
-        // P byte b = 16*tt + r  <->  key 32*tt + 8*(r/4) + 4*g + r%4
         const int tt = rg >> 2, q4 = rg & 3;
-        const v4f kv = *(const v4f*)&m->ks[c][32 * tt + 8 * q4 + 4 * g];
+        const v4f kv = *(const v4f*)&ks[32 * tt + 8 * q4 + 4 * g];
+        const v16f& x = P.lt[tt];
         int hv, lv;
-        split_fp8(sacc[tt][4 * q4] * kv[0], sacc[tt][4 * q4 + 1] * kv[1], sacc[tt][4 * q4 + 2] * kv[2],
-                  sacc[tt][4 * q4 + 3] * kv[3], hv, lv);
+        split_fp8(x[4 * q4] * kv[0], x[4 * q4 + 1] * kv[1], x[4 * q4 + 2] * kv[2], x[4 * q4 + 3] * kv[3], hv, lv);
         ph[rg] = hv;
         pl[rg] = lv;
       }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int j = 2 * c4 + h2;
-        const v8i vt = read_vt<BUF>(smem, o, 8 * DH + j);
+        const v8i vt = read_vt(smem, o, j);
         oacc[j] = mma(vt, ph, oacc[j]);
         oacc[j] = mma(vt, pl, oacc[j]);
       }
     }
   } else {
-    v8i ph, pl;
+    v8i vt = read_vt(smem, o, J0);
 #pragma unroll
-    for (int rg = 0; rg < 8; ++rg) {
-      const int tt = rg >> 2, q4 = rg & 3;
-      int hv, lv;
-      split_fp8(sacc[tt][4 * q4], sacc[tt][4 * q4 + 1], sacc[tt][4 * q4 + 2], sacc[tt][4 * q4 + 3], hv, lv);
-      ph[rg] = hv;
-      pl[rg] = lv;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const v8i vt = read_vt<BUF>(smem, o, 8 * DH + j);
-      oacc[j] = mma(vt, ph, oacc[j]);
-      oacc[j] = mma(vt, pl, oacc[j]);
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = J0 + jj;
+      const v8i vn = (jj < 3) ? read_vt(smem, o, j + 1) : vt;   // next operand in flight during these MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+      oacc[j] = mma(vt, P.hi, oacc[j]);
+      oacc[j] = mma(vt, P.lo, oacc[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      vt = vn;
     }
   }
 }
 
-struct Chunk {
-  int st, en, tiles;
+template <int PER_TILE>
+__device__ __forceinline__ void put_v16(uint8_t* smem, int off, int w, int lane, const v16f& v) {
+  float* p = reinterpret_cast<float*>(smem + off) + (w * 64 + lane) * 16;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) *(v4f*)&p[4 * r4] = v4f{v[4 * r4], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]};
+}
+
+__device__ __forceinline__ v16f get_v16(const uint8_t* smem, int off, int w, int lane) {
+  const float* p = reinterpret_cast<const float*>(smem + off) + (w * 64 + lane) * 16;
+  v16f v;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const v4f x = *(const v4f*)&p[4 * r4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[4 * r4 + r] = x[r];
+  }
+  return v;
+}
+
+struct WaveCtx {
+  int w, lane, g, dh;
+  float qs;   // softmax_scale * log2(e) * q descale of the lane's head
 };
+
+// Hand the partner the partial scores of the m-tile it owns.
+template <int PER_TILE>
+__device__ __forceinline__ void scores_publish(uint8_t* smem, const WaveCtx& c, const v16f& s_oth) {
+  put_v16<PER_TILE>(smem, Lds<PER_TILE>::kSx, c.w, c.lane, s_oth);
+}
+
+// Per-key values of the wave's own 32 keys (m-tile dh) that the softmax of a
+// tile needs, loaded ahead of the score exchange.
+template <int PER_TILE>
+struct KeyVals {
+  v4f lam[4], inv[4], kd[PER_TILE ? 1 : 4];
+};
+
+template <int PER_TILE>
+__device__ __forceinline__ KeyVals<PER_TILE> key_vals(const TileView<PER_TILE>& tv, const WaveCtx& c) {
+  KeyVals<PER_TILE> kv;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int kb4 = 32 * c.dh + 8 * q4 + 4 * c.g;
+    kv.lam[q4] = *(const v4f*)&tv.lam[kb4];
+    kv.inv[q4] = *(const v4f*)&tv.inv[kb4];
+    if constexpr (!PER_TILE) kv.kd[q4] = *(const v4f*)&tv.ks[kb4];
+  }
+  return kv;
+}
+
+// Full scores of the own m-tile (own partial + the partner's), turned into
+// exponents E = s * log2(e) + log2(vds) in place.  Slots past the end of the
+// chunk need no mask: their row is zero and their lam is -inf.  Returns the
+// per-head maximum of the half.
+template <int PER_TILE>
+__device__ __forceinline__ float scores_finish(const uint8_t* smem, const KeyVals<PER_TILE>& kv, const WaveCtx& c,
+                                               v16f& s_own) {
+  const v16f x = get_v16(smem, Lds<PER_TILE>::kSx, c.w ^ 2, c.lane);
+  float mt = kNegInf;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float sv = s_own[4 * q4 + r] + x[4 * q4 + r];
+      float e;
+      if constexpr (PER_TILE) e = sv * c.qs + kv.lam[q4][r];
+      else e = sv * (c.qs * kv.kd[q4][r]) + kv.lam[q4][r];
+      s_own[4 * q4 + r] = e;
+      mt = fmaxf(mt, e);
+    }
+  }
+  return fmaxf(mt, __shfl_xor(mt, 32));
+}
+
+// P' = 2^(E - Mrun) of the own half; accumulates l += P' / vds_max and
+// publishes the half for the partner (fp8 hi/lo words, or fp32 P' / vds_max).
+template <int PER_TILE>
+__device__ __forceinline__ void probs_half(uint8_t* smem, const KeyVals<PER_TILE>& kv, const WaveCtx& c, float Mrun,
+                                           const v16f& ev, float& lsum) {
+  const float Ms = (Mrun == kNegInf) ? 0.f : Mrun;
+  v16f pv;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = __builtin_amdgcn_exp2f(ev[4 * q4 + r] - Ms);
+      const float lt = p * kv.inv[q4][r];
+      lsum += lt;
+      pv[4 * q4 + r] = PER_TILE ? lt : p;
+    }
+  }
+  if constexpr (PER_TILE) {
+    put_v16<PER_TILE>(smem, Lds<PER_TILE>::kPx, c.w, c.lane, pv);
+  } else {
+    int hv[4], lv[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) split_fp8(pv[4 * q4], pv[4 * q4 + 1], pv[4 * q4 + 2], pv[4 * q4 + 3], hv[q4], lv[q4]);
+    int* px = reinterpret_cast<int*>(smem + Lds<PER_TILE>::kPx) + (c.w * 64 + c.lane) * 8;
+    *(v4i*)&px[0] = v4i{hv[0], hv[1], hv[2], hv[3]};
+    *(v4i*)&px[4] = v4i{lv[0], lv[1], lv[2], lv[3]};
+  }
+}
+
+// P of the whole tile from both halves published by the pair (after a barrier).
+template <int PER_TILE>
+__device__ __forceinline__ void probs_gather(const uint8_t* smem, const WaveCtx& c, PTile<PER_TILE>& P) {
+  const int w0 = c.w & 1, w1 = w0 | 2;   // the pair's waves owning m-tiles 0 and 1
+  if constexpr (PER_TILE) {
+    P.lt[0] = get_v16(smem, Lds<PER_TILE>::kPx, w0, c.lane);
+    P.lt[1] = get_v16(smem, Lds<PER_TILE>::kPx, w1, c.lane);
+  } else {
+    const int* p0 = reinterpret_cast<const int*>(smem + Lds<PER_TILE>::kPx) + (w0 * 64 + c.lane) * 8;
+    const int* p1 = reinterpret_cast<const int*>(smem + Lds<PER_TILE>::kPx) + (w1 * 64 + c.lane) * 8;
+    const v4i h0 = *(const v4i*)&p0[0], l0 = *(const v4i*)&p0[4];
+    const v4i h1 = *(const v4i*)&p1[0], l1 = *(const v4i*)&p1[4];
+    P.hi = v8i{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+    P.lo = v8i{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+  }
+}
+
+// Per-head value shared by the pair (w, w ^ 2): the max or the sum of both.
+__device__ __forceinline__ float pair_reduce(int* misc, int w, int lane, float v, bool is_max) {
+  float* pm = reinterpret_cast<float*>(misc + 64);
+  pm[w * 64 + lane] = v;
+  lds_barrier();
+  const float o = pm[(w ^ 2) * 64 + lane];
+  lds_barrier();
+  return is_max ? fmaxf(v, o) : v + o;
+}
 
 struct UnitState {
   Tok k;
   int t, n_o, w_lo, n_c, kb, ke;
 };
 
-// One pipeline step i: gather tile i+1 | issue table loads of tile i+2 |
-// compute tile i | descales of tile i+1 into meta, row addresses and
-// descale loads of tile i+2 | barrier (gather landed).
-template <int PER_TILE, int BUF, int DH, int MAXONLY>
-__device__ __forceinline__ void pipeline_step(const KArgs& a, const UnitState& us, const int* list, uint8_t* smem,
-                                              const LaneOffsets& o, Meta* mm, const Chunk& ck, int i, int w, int lane,
-                                              const v8i (&qreg)[4], float qs, v16f (&oacc)[8], float& Mrun,
-                                              float& lsum, KeyScale<PER_TILE>& sc_next, int& valid_next, int* flag) {
-  if (i + 1 < ck.tiles) gather_tile(mm + (i + 1) % 3, smem + kOffTiles + (BUF ^ 1) * kTileBytes, w);
-  KeyLoc kl2;
-  const bool r2 = (w == 0) && (i + 2 < ck.tiles);
-  if (r2) kl2 = resolve_issue(a, us.k, us.n_o, list, us.w_lo, ck.st + (i + 2) * kTileKeys, ck.en);
-  const int nvalid = min(kTileKeys, ck.en - ck.st - i * kTileKeys);
-  compute_tile<PER_TILE, BUF, DH, MAXONLY>(smem, o, mm + i % 3, qreg, qs, nvalid, w, lane, oacc, Mrun, lsum, flag);
-  if (w == 0) {
-    if (i + 1 < ck.tiles) resolve_scales<PER_TILE>(sc_next, valid_next, mm + (i + 1) % 3);
-    if (r2) {
-      resolve_rows<PER_TILE>(a, us.k, kl2, mm + (i + 2) % 3, sc_next);
-      valid_next = kl2.valid;
-      step_barrier<PER_TILE ? 2 : 1>();
-      return;
+// Slide the compacted index window so that it covers the cmp entries of the
+// keys [c0, c1); only a token with more than kListMax valid indices moves it.
+__device__ __forceinline__ void cover_chunk(const KArgs& a, UnitState& us, int* list, int* misc, int c0, int c1) {
+  if (a.topk > 0 && us.n_c > kListMax) {
+    const int need_lo = max(c0 - us.n_o, 0), need_hi = max(c1 - us.n_o, 0);
+    if (need_hi > need_lo && (need_lo < us.w_lo || need_hi > us.w_lo + kListMax)) {
+      us.w_lo = need_lo;
+      compact_indices(a, us.k, us.t, list, misc, us.w_lo);
     }
   }
-  step_barrier<0>();
 }
 
-// Runs the unit's key range [kb, ke) into (oacc, Mrun, lsum); Mrun enters
-// as the preset reference (-inf: set by the first tile).  With MAXONLY it
-// only leaves the per-head maximum exponent in Mrun.
-template <int PER_TILE, int DH, int MAXONLY>
-__device__ __forceinline__ void run_unit(const KArgs& a, UnitState& us, int* list, int* misc, uint8_t* smem,
-                                         const LaneOffsets& lo, int w, int lane, const v8i (&qreg)[4], float qs,
-                                         v16f (&oacc)[8], float& Mrun, float& lsum) {
-  Meta* mm = reinterpret_cast<Meta*>(smem + kOffMeta);
-  int* flag = misc + 4;
-  if (!MAXONLY) {
+// One step i of a chunk (tile T in buffer T % 3; bv = i % 3):
+//   gather tile i+2 | P V(i), d-blocks 0-3 | barrier: tile i+1 landed
+//   | S^T of tile i+1, publish | barrier | softmax of tile i+1, publish P
+//   | P V(i), d-blocks 4-7 | barrier | P of tile i+1
+// One code path for all three buffers (the buffer offset is added to the
+// lane offsets), so that the accumulators keep their registers.
+template <int PER_TILE>
+__device__ __forceinline__ void pipeline_step(uint8_t* smem, const LaneOffsets& o_in, int tiles, int i, int bv,
+                                              const WaveCtx& c, const v8i (&qreg)[4], v16f (&oacc)[8], float Mrun,
+                                              float& lsum, PTile<PER_TILE>& P, int* flag) {
+  using L = Lds<PER_TILE>;
+  LaneOffsets o = o_in;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) oacc[j] = v16f{};
+  for (int k = 0; k < 2; ++k) o.qk[k] = opaque(o.qk[k]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o.tr[k] = opaque(o.tr[k]);
+  const int bq = (bv == 2) ? 0 : bv + 1, bg = (bq == 2) ? 0 : bq + 1;
+  const bool g2 = i + 2 < tiles;
+  if (g2) gather_tile(reinterpret_cast<const uint64_t*>(smem + L::kAddr), i + 2, smem + L::kTiles + bg * kTileBytes, c.w);
+  const TileView<PER_TILE> tv = tile_view<PER_TILE>(smem, i);
+  const TrOff tro = tr_at(o, L::kTiles + bv * kTileBytes);
+  pv_half<PER_TILE, 0>(smem, tro, tv, c.dh, P, c.g, oacc);
+  gather_barrier(g2);
+  const bool has_next = i + 1 < tiles;
+  const TileView<PER_TILE> tq = tile_view<PER_TILE>(smem, i + 1);
+  v16f s_own, s_oth;
+  KeyVals<PER_TILE> kv;
+  if (has_next) {
+    kv = key_vals<PER_TILE>(tq, c);
+    qk_partial<PER_TILE>(smem, qk_at(o, L::kTiles + bq * kTileBytes), tq, c.dh, qreg, c.g, s_own, s_oth);
+    scores_publish<PER_TILE>(smem, c, s_oth);
   }
+  lds_barrier();
+  if (has_next) {
+    const float mt = scores_finish<PER_TILE>(smem, kv, c, s_own);
+    if (__ballot(mt > Mrun + kTau)) *flag = 1;   // would overflow fp8: the unit is redone
+    probs_half<PER_TILE>(smem, kv, c, Mrun, s_own, lsum);
+  }
+  pv_half<PER_TILE, 4>(smem, tro, tv, c.dh, P, c.g, oacc);
+  lds_barrier();
+  if (has_next) probs_gather<PER_TILE>(smem, c, P);
+}
+
+// Runs the unit's keys [kb, ke) into (oacc, lsum).  Mrun enters as the preset
+// reference, or -inf: then the first tile sets it (the pair's max maps to 2^4).
+template <int PER_TILE>
+__device__ __forceinline__ void run_unit(KArgPtr ap, UnitState& us, int* list, int* misc, uint8_t* smem,
+                                         const LaneOffsets& o, const WaveCtx& c, const v8i (&qreg)[4],
+                                         v16f (&oacc)[8], float& Mrun, float& lsum) {
+  using L = Lds<PER_TILE>;
+  int* flag = misc + 4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) oacc[j] = v16f{};
   lsum = 0.f;
-  // chunks of at most kListMax keys, so that a chunk's cmp entries fit the list
-  for (int c0 = us.kb; c0 < us.ke; c0 += kListMax) {
-    const int c1 = min(us.ke, c0 + kListMax);
-    if (a.topk > 0 && us.n_c > kListMax) {
-      const int need_lo = max(c0 - us.n_o, 0), need_hi = max(c1 - us.n_o, 0);
-      if (need_hi > need_lo && (need_lo < us.w_lo || need_hi > us.w_lo + kListMax)) {
-        us.w_lo = need_lo;
-        compact_indices(a, us.k, us.t, list, misc, us.w_lo);
+  for (int c0 = us.kb; c0 < us.ke; c0 += L::kChunk) {
+    const int c1 = min(us.ke, c0 + L::kChunk);
+    const KArgs& a = args(ap);
+    cover_chunk(a, us, list, misc, c0, c1);
+    resolve_chunk<PER_TILE>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
+    const int nkeys = c1 - c0, tiles = (nkeys + kTileKeys - 1) / kTileKeys;
+    const uint64_t* kaddr = reinterpret_cast<const uint64_t*>(smem + L::kAddr);
+    gather_tile(kaddr, 0, smem + L::kTiles, c.w);
+    if (tiles > 1) gather_tile(kaddr, 1, smem + L::kTiles + kTileBytes, c.w);
+    gather_barrier(tiles > 1);
+    // ---- P of tile 0 ----
+    PTile<PER_TILE> P;
+    {
+      const TileView<PER_TILE> t0 = tile_view<PER_TILE>(smem, 0);
+      const KeyVals<PER_TILE> kv = key_vals<PER_TILE>(t0, c);
+      v16f s_own, s_oth;
+      qk_partial<PER_TILE>(smem, qk_at(o, L::kTiles), t0, c.dh, qreg, c.g, s_own, s_oth);
+      scores_publish<PER_TILE>(smem, c, s_oth);
+      lds_barrier();
+      const float mt = scores_finish<PER_TILE>(smem, kv, c, s_own);
+      if (Mrun == kNegInf) {
+        const float mx = pair_reduce(misc, c.w, c.lane, mt, true);
+        Mrun = (mx == kNegInf) ? kNegInf : mx - kPShift;
+      } else if (__ballot(mt > Mrun + kTau)) {
+        *flag = 1;
       }
+      probs_half<PER_TILE>(smem, kv, c, Mrun, s_own, lsum);
+      lds_barrier();
+      probs_gather<PER_TILE>(smem, c, P);
     }
-    Chunk ck;
-    ck.st = c0;
-    ck.en = c1;
-    ck.tiles = (c1 - c0 + kTileKeys - 1) / kTileKeys;
-    KeyScale<PER_TILE> sc_next;
-    int valid_next = 0;
-    if (w == 0) {
-      resolve_tile<PER_TILE>(a, us.k, us.n_o, list, us.w_lo, ck.st, ck.en, mm + 0);
-      if (ck.tiles > 1) {
-        const KeyLoc kl1 = resolve_issue(a, us.k, us.n_o, list, us.w_lo, ck.st + kTileKeys, ck.en);
-        resolve_rows<PER_TILE>(a, us.k, kl1, mm + 1, sc_next);
-        valid_next = kl1.valid;
-      }
-    }
-    wait_all_and_sync();
-    gather_tile(mm + 0, smem + kOffTiles, w);
-    wait_all_and_sync();
-    for (int i = 0; i < ck.tiles; i += 2) {
-      pipeline_step<PER_TILE, 0, DH, MAXONLY>(a, us, list, smem, lo, mm, ck, i, w, lane, qreg, qs, oacc, Mrun, lsum,
-                                              sc_next, valid_next, flag);
-      if (i + 1 < ck.tiles)
-        pipeline_step<PER_TILE, 1, DH, MAXONLY>(a, us, list, smem, lo, mm, ck, i + 1, w, lane, qreg, qs, oacc, Mrun,
-                                                lsum, sc_next, valid_next, flag);
-    }
+    // ---- steady state ----
+    for (int i = 0, bv = 0; i < tiles; ++i, bv = (bv == 2) ? 0 : bv + 1)
+      pipeline_step<PER_TILE>(smem, o, tiles, i, bv, c, qreg, oacc, Mrun, lsum, P, flag);
   }
 }
 
-template <int PER_TILE, int DH>
-__device__ __forceinline__ void attn_body(const KArgs& a, uint8_t* smem, int w) {
+// Per-head maximum exponent over the unit (S^T only, not pipelined), for the
+// rare unit where a later tile outgrows the first tile's fp8 window.
+template <int PER_TILE>
+__device__ __forceinline__ float unit_max(KArgPtr ap, UnitState& us, int* list, int* misc, uint8_t* smem,
+                                          const LaneOffsets& o, const WaveCtx& c, const v8i (&qreg)[4]) {
+  using L = Lds<PER_TILE>;
+  float mx = kNegInf;
+  for (int c0 = us.kb; c0 < us.ke; c0 += L::kChunk) {
+    const int c1 = min(us.ke, c0 + L::kChunk);
+    const KArgs& a = args(ap);
+    cover_chunk(a, us, list, misc, c0, c1);
+    resolve_chunk<PER_TILE>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
+    const int nkeys = c1 - c0, tiles = (nkeys + kTileKeys - 1) / kTileKeys;
+    for (int i = 0; i < tiles; ++i) {
+      gather_tile(reinterpret_cast<const uint64_t*>(smem + L::kAddr), i, smem + L::kTiles, c.w);
+      gather_barrier(false);
+      const TileView<PER_TILE> tv = tile_view<PER_TILE>(smem, i);
+      v16f s_own, s_oth;
+      qk_partial<PER_TILE>(smem, qk_at(o, L::kTiles), tv, c.dh, qreg, c.g, s_own, s_oth);
+      scores_publish<PER_TILE>(smem, c, s_oth);
+      lds_barrier();
+      mx = fmaxf(mx, scores_finish<PER_TILE>(smem, key_vals<PER_TILE>(tv, c), c, s_own));
+      lds_barrier();
+    }
+  }
+  return pair_reduce(misc, c.w, c.lane, mx, true);
+}
+
+template <int PER_TILE>
+__device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
+  using L = Lds<PER_TILE>;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int hh = w & 1, g = lane >> 5, li = lane & 31;
-  const int h = 32 * hh + li;
-  const int G = a.grid;
+  WaveCtx c;
+  c.w = w;
+  c.lane = lane;
+  c.g = lane >> 5;
+  c.dh = w >> 1;
+  const int hh = w & 1, g = c.g, dh = c.dh;
+  const int G = ap->grid;
   const int bid = blockIdx.x;
   const int lw = (G % 8 == 0) ? ((bid & 7) * (G >> 3) + (bid >> 3)) : bid;  // one XCD per contiguous range
-  const int u_begin = a.starts[lw], u_end = a.starts[lw + 1];
-  int* list = reinterpret_cast<int*>(smem + kOffList);
-  int* misc = reinterpret_cast<int*>(smem + kOffMisc);
-  const LaneOffsets lo = lane_offsets(lane);
+  const int u_begin = ap->starts[lw], u_end = ap->starts[lw + 1];
+  int* list = reinterpret_cast<int*>(smem + L::kList);
+  int* misc = reinterpret_cast<int*>(smem + L::kMisc);
+  const LaneOffsets o = lane_offsets(lane, dh);
 
   for (int u = u_begin; u < u_end; ++u) {
+    const KArgs& a = args(ap);
+    const int h = 32 * hh + (opaque(lane) & 31);   // the lane's head, recomputed per unit
     UnitState us;
     us.t = u / a.splits;
     const int s = u - us.t * a.splits;
-    us.k = token_ctx(a, us.t);
     const int t = us.t;
-    if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
-      if (a.splits == 1) {
-        for (int x = lane; x < 32 * 64; x += 64) {
-          const int hr = 32 * hh + x / 64, d = 256 * DH + 4 * (x % 64);
-          *(uint2*)(a.out + ((size_t)t * kN1 + hr) * kD + d) = make_uint2(0, 0);
-        }
-        if (a.lse && DH == 0 && g == 0) a.lse[(size_t)t * kN1 + h] = kNegInf;
-      } else if (DH == 0 && g == 0) {
-        a.ws_ml[((size_t)u * kN1 + h) * 2] = kNegInf;
-        a.ws_ml[((size_t)u * kN1 + h) * 2 + 1] = -1.0f;   // marks a padded row for the combine
-      }
-      continue;
-    }
-
-    // query fragment: B operand of S^T = K Q^T for d in [256 DH + 64 s4 + 32 g, +32)
+    // query fragment (B operand of S^T = K Q^T for d in [256 dh + 64 s4 + 32 g, +32))
+    // and descale: loaded before the lengths, nothing depends on them
     v8i qreg[4];
     {
-      const uint8_t* qrow = a.q + ((size_t)t * kN1 + h) * kD + 256 * DH + 32 * g;
+      const uint8_t* qrow = a.q + ((size_t)t * kN1 + h) * kD + 256 * dh + 32 * g;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const v4i x0 = *(const v4i*)(qrow + 64 * s4);
@@ -682,7 +897,21 @@ __device__ __forceinline__ void attn_body(const KArgs& a, uint8_t* smem, int w) 
       }
     }
     const float qd = a.q_ds_per_head ? a.q_ds[(size_t)t * kN1 + h] : a.q_ds[t];
-    const float qs = a.scale_log2 * qd;
+    c.qs = a.scale_log2 * qd;
+    us.k = token_ctx(a, t);
+    if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
+      if (a.splits == 1) {
+        for (int x = lane; x < 32 * 64; x += 64) {
+          const int hr = 32 * hh + x / 64, d = 256 * dh + 4 * (x % 64);
+          *(uint2*)(a.out + ((size_t)t * kN1 + hr) * kD + d) = make_uint2(0, 0);
+        }
+        if (a.lse && dh == 0 && g == 0) a.lse[(size_t)t * kN1 + h] = kNegInf;
+      } else if (dh == 0 && g == 0) {
+        a.ws_ml[((size_t)u * kN1 + h) * 2] = kNegInf;
+        a.ws_ml[((size_t)u * kN1 + h) * 2 + 1] = -1.0f;   // marks a padded row for the combine
+      }
+      continue;
+    }
 
     us.n_o = us.k.hi - us.k.lo;
     us.n_c = 0;
@@ -697,23 +926,23 @@ __device__ __forceinline__ void attn_body(const KArgs& a, uint8_t* smem, int w) 
     float Mrun = kNegInf, lsum = 0.f;
     for (int pass = 0;; ++pass) {
       if (tid == 0) misc[4] = 0;
-      run_unit<PER_TILE, DH, 0>(a, us, list, misc, smem, lo, w, lane, qreg, qs, oacc, Mrun, lsum);
-      __syncthreads();
+      run_unit<PER_TILE>(ap, us, list, misc, smem, o, c, qreg, oacc, Mrun, lsum);
+      lds_barrier();
       const int redo = misc[4];
-      __syncthreads();
+      lds_barrier();
       if (!redo || pass > 0) break;
-      // a later tile outgrew the first tile's fp8 window: find each head's
-      // maximum exponent, then recompute with the reference preset from it
-      float mx = kNegInf;
-      run_unit<PER_TILE, DH, 1>(a, us, list, misc, smem, lo, w, lane, qreg, qs, oacc, mx, lsum);
+      // recompute with the reference preset from the unit's true maximum
+      const float mx = unit_max<PER_TILE>(ap, us, list, misc, smem, o, c, qreg);
       Mrun = (mx == kNegInf) ? kNegInf : mx - kPShift;
     }
 
     // ---------------- write: final output (one split) or partial state ----------------
-    const float lh = lsum + __shfl_xor(lsum, 32);
+    const KArgs& ae = args(ap);
+    float lh = lsum + __shfl_xor(lsum, 32);
+    lh = pair_reduce(misc, w, lane, lh, false);   // both key halves
     float sc;
-    if (a.splits == 1) {
-      const float sg = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+    if (ae.splits == 1) {
+      const float sg = ae.sinks ? ae.sinks[h] * kLog2e : kNegInf;
       const float Mf = fmaxf(Mrun, sg);
       float lse_v = kNegInf;
       sc = 0.f;
@@ -723,23 +952,33 @@ __device__ __forceinline__ void attn_body(const KArgs& a, uint8_t* smem, int w) 
         sc = af / Lf;
         lse_v = (Mf + __log2f(Lf)) * kLn2;
       }
-      if (a.lse && DH == 0 && g == 0) a.lse[(size_t)t * kN1 + h] = lse_v;
+      if (ae.lse && dh == 0 && g == 0) ae.lse[(size_t)t * kN1 + h] = lse_v;
     } else {
       sc = (lh > 0.f) ? 1.0f / lh : 0.f;
-      if (DH == 0 && g == 0) {
-        a.ws_ml[((size_t)u * kN1 + h) * 2] = Mrun;
-        a.ws_ml[((size_t)u * kN1 + h) * 2 + 1] = lh;
+      if (dh == 0 && g == 0) {
+        ae.ws_ml[((size_t)u * kN1 + h) * 2] = Mrun;
+        ae.ws_ml[((size_t)u * kN1 + h) * 2 + 1] = lh;
       }
     }
-    uint16_t* dst = (a.splits == 1) ? a.out + ((size_t)t * kN1 + h) * kD : a.ws_o + ((size_t)u * kN1 + h) * kD;
+    // The wave's 32 heads x 256 columns go through LDS (rows padded to 528
+    // bytes), so that each half-wave stores one contiguous 512-byte row.
+    lds_barrier();   // every wave is done with the tile buffers
+    uint8_t* stage = smem + L::kTiles + w * (32 * kStageRow);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const v16f& ov = oacc[j];
-        const int d = 32 * (8 * DH + j) + 8 * r4 + 4 * g;
-        *(uint2*)(dst + d) = pack_bf16x4(sc * ov[4 * r4], sc * ov[4 * r4 + 1], sc * ov[4 * r4 + 2], sc * ov[4 * r4 + 3]);
+        *(uint2*)(stage + (lane & 31) * kStageRow + 2 * (32 * j + 8 * r4 + 4 * g)) =
+            pack_bf16x4(sc * ov[4 * r4], sc * ov[4 * r4 + 1], sc * ov[4 * r4 + 2], sc * ov[4 * r4 + 3]);
       }
+    }
+    uint16_t* dst = (ae.splits == 1) ? ae.out + (size_t)t * kN1 * kD : ae.ws_o + (size_t)u * kN1 * kD;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = 2 * it + g;   // head 32 hh + row
+      const v4i x = *(const v4i*)(stage + row * kStageRow + 16 * (lane & 31));
+      *(v4i*)(dst + (size_t)(32 * hh + row) * kD + 256 * dh + 8 * (lane & 31)) = x;
     }
   }
 }
@@ -747,21 +986,47 @@ __device__ __forceinline__ void attn_body(const KArgs& a, uint8_t* smem, int w) 
 template <int PER_TILE>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_kernel(const KArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds<PER_TILE>::kBytes];
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  if (w >> 1) attn_body<PER_TILE, 1>(a, smem, w);
-  else attn_body<PER_TILE, 0>(a, smem, w);
+  attn_body<PER_TILE>((KArgPtr)__builtin_amdgcn_kernarg_segment_ptr(), smem, w);
 }
 
 // ---------------------------------------------------------------------------
 // split-KV combine: merge the sink-free partial states of every split with
-// the log-sum-exp rule and add the sink logit once.
-// grid (t1, 8): 8 heads per work-group; 256 threads = 8 heads x 32 x 16 cols.
-// All loads of a batch of 8 splits are issued before any is used.
+// the log-sum-exp rule and add the sink logit once.  A block is (token, 8
+// heads); 256 threads = 8 heads x 32 x 16 columns.  All loads of a batch of 8
+// splits are issued before any is used.
+//
+// The partial states of a token are read on the XCD that wrote them: work-
+// groups are dispatched to the 8 XCDs round-robin by block id, and the
+// attention kernel gives XCD x the units of logical work-groups
+// [x G/8, (x+1) G/8).  Block b serves XCD b % 8; its tokens are those whose
+// first unit XCD x computed.  (Reading another XCD's fresh partials costs
+// several microseconds at the kernel boundary.)
 // ---------------------------------------------------------------------------
+
+// Tokens whose first split was computed by XCD x: [t0, t1).
+__host__ __device__ __forceinline__ void xcd_tokens(const KArgs& a, int x, int& t0, int& t1) {
+  const int per = a.grid / 8;
+  const int u0 = a.starts[x * per], u1 = a.starts[(x + 1) * per];
+  t0 = (u0 + a.splits - 1) / a.splits;
+  t1 = (u1 + a.splits - 1) / a.splits;
+}
+
 __global__ void __launch_bounds__(256) combine_kernel(const KArgs a) {
-  const int t = blockIdx.x;
-  const int h = blockIdx.y * 8 + (threadIdx.x >> 5);
+  int t, hg;
+  if (a.grid % 8 == 0) {
+    const int x = blockIdx.x % 8, k = blockIdx.x / 8;
+    int t0, t1;
+    xcd_tokens(a, x, t0, t1);
+    t = t0 + k / 8;
+    hg = k % 8;
+    if (t >= t1) return;
+  } else {
+    t = blockIdx.x / 8;
+    hg = blockIdx.x % 8;
+  }
+  const int h = hg * 8 + (threadIdx.x >> 5);
   const int col = (threadIdx.x & 31) * 16;
   const int S = a.splits;
   uint16_t* dst = a.out + ((size_t)t * kN1 + h) * kD + col;
@@ -823,7 +1088,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const KArgs a) {
   const float inv = (L > 0.f) ? 1.0f / L : 0.f;
   uint32_t o[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = bf16_rne(acc[2 * j] * inv) | (bf16_rne(acc[2 * j + 1] * inv) << 16);
+  for (int j = 0; j < 8; ++j) o[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
   *(uint4*)dst = make_uint4(o[0], o[1], o[2], o[3]);
   *(uint4*)(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
   if (a.lse && (threadIdx.x & 31) == 0)
@@ -872,7 +1137,17 @@ int launch_forward(const KArgs& a, void* stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   if (a.splits > 1) {
-    hipLaunchKernelGGL(combine_kernel, dim3(a.t1, kN1 / 8), dim3(256), 0, st, a);
+    int blocks = a.t1 * 8;
+    if (a.grid % 8 == 0) {
+      int most = 0;
+      for (int x = 0; x < 8; ++x) {
+        int t0, t1;
+        xcd_tokens(a, x, t0, t1);
+        most = std::max(most, t1 - t0);
+      }
+      blocks = 8 * 8 * most;
+    }
+    if (blocks > 0) hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, st, a);
     e = hipGetLastError();
   }
   return (int)e;
