@@ -67,7 +67,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "multi-GPU sharding is described in DESIGN.md, not built.", file=sys.stderr)
+              "the path would shard by batch across GPUs; that is not built.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

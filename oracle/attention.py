@@ -15,7 +15,7 @@ K~ is the concatenation of
     valid entries of cmp_sparse_indices (CSA)  (QuantSparseFlashMla,
     功能说明: the three computation modes).
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
   R1 sink: an extra logit sinks[h] with a zero value row; not multiplied by
      softmax_scale or any descale.  lse includes it.
   R2 ori band / causal masks are bottom-right aligned: query row i of a batch

@@ -104,8 +104,8 @@ class Inputs:
 
 
 # ---------------------------------------------------------------------------
-# quantisation of synthetic values (input construction, BASELINE recipe:
-# descale = amax / 448, cast to OCP e4m3fn with round-to-nearest-even)
+# quantisation of synthetic values (input construction: descale = amax / 448,
+# cast to OCP e4m3fn with round-to-nearest-even)
 # ---------------------------------------------------------------------------
 
 def quantize_rows_e4m3(x: torch.Tensor, tile: Optional[int] = None):
