@@ -128,7 +128,7 @@ def main():
 
     plan = m.Plan(inp)
     out = torch.empty(inp.q.shape, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
     tens = [m.tensors_from(x, out, None, ws if plan.workspace_bytes else None) for x in layers]
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream

@@ -265,7 +265,7 @@ def forward(inp, out=None, lse=None, workspace=None, plan: Optional[Plan] = None
     if lse is None and inp.return_lse:
         lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device=dev)
     if workspace is None and plan.workspace_bytes > 0:
-        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     t = tensors_from(inp, out, lse, workspace)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
     csmla_forward(plan.problem, t, plan.metadata, s)

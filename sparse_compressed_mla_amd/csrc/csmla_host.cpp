@@ -138,11 +138,15 @@ bool is_win(int w) { return w == -1 || w >= 0; }
 
 }  // namespace
 
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace of a split plan: bf16 partial outputs [units, 64, 512], then
+// (max, sum) [units, 64, 2] fp32.
 size_t csmla::workspace_bytes_for(int n_units, int splits) {
   if (splits <= 1) return 0;
-  const size_t o = (size_t)n_units * kN1 * kD * 2;          // bf16 partial outputs
-  const size_t ml = (size_t)n_units * kN1 * 2 * sizeof(float);  // (max, sum) per head
-  return ((o + 255) & ~size_t(255)) + ml;
+  const size_t o = (size_t)n_units * kN1 * kD * 2;
+  const size_t ml = (size_t)n_units * kN1 * 2 * sizeof(float);
+  return align256(o) + ml;
 }
 
 extern "C" {
@@ -256,7 +260,7 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
     const int64_t f = std::atoll(env);
     if (f >= 1) S = std::max(s_list, f);
   }
-  S = std::min<int64_t>(S, 4096);
+  if (S > kMaxSplits) return fail(CSMLA_ERR_UNSUPPORTED, "a token needs %lld splits; at most %d are built", (long long)S, kMaxSplits);
   const int64_t n_units64 = (int64_t)T1 * S;
   if (n_units64 > (int64_t)1 << 30) return fail(CSMLA_ERR_UNSUPPORTED, "too many work units");
   const int n_units = (int)n_units64;
@@ -367,8 +371,7 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
       if ((reinterpret_cast<uintptr_t>(t->workspace) & 255) != 0)
         return fail(CSMLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
       a.ws_o = (uint16_t*)t->workspace;
-      const size_t o = (size_t)U * kN1 * kD * 2;
-      a.ws_ml = (float*)((char*)t->workspace + ((o + 255) & ~size_t(255)));
+      a.ws_ml = (float*)((char*)t->workspace + align256((size_t)U * kN1 * kD * 2));
     }
   }
   return CSMLA_OK;

@@ -11,6 +11,7 @@ constexpr int kD = 512;            // head dim (QuantSparseFlashMla, Á∫¶ÊùüËØ¥Êò
 constexpr int kTileKeys = 64;      // keys per LDS tile
 constexpr int kListMax = 1024;     // compacted cmp indices a unit keeps in LDS
 constexpr int kMaxGrid = 256;      // persistent work-groups (one per CU on MI355X)
+constexpr int kMaxSplits = 4096;   // splits per token
 constexpr int kHeaderWords = 16;
 constexpr int32_t kMagic = 0x4C4D5343;   // "CSML"
 

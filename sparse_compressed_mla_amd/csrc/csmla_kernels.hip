@@ -201,27 +201,43 @@ __device__ __forceinline__ Tok token_ctx(const KArgs& a, int t) {
   return k;
 }
 
+// The first kIdxPre index slots of token t, one value per thread per round,
+// loaded before the token's lengths are known (bounded by topk, not by the
+// effective length), so that these loads share a round trip with them.
+constexpr int kIdxRounds = 4;
+constexpr int kIdxPre = kIdxRounds * kThreads;
+
+struct IdxPre {
+  int v[kIdxRounds];
+};
+
+__device__ __forceinline__ IdxPre load_indices(const KArgs& a, int t, int s0) {
+  IdxPre p;
+  const int* row = a.idx + (size_t)t * a.topk;
+  const int tid = opaque((int)threadIdx.x);
+#pragma unroll
+  for (int m = 0; m < kIdxRounds; ++m) {
+    const int slot = s0 + m * kThreads + tid;
+    p.v[m] = (slot < a.topk) ? row[slot] : -1;
+  }
+  return p;
+}
+
 // Compact the valid index slots of token t in slot order; entries whose
 // compacted position lies in [w_lo, w_lo + kListMax) go to list[pos - w_lo].
-// Returns the number of valid slots.  Whole-work-group call.  The loads of
-// four rounds are issued before the first ballot, and bounded by topk rather
-// than the token's effective length so that they do not wait for it.
-__device__ __forceinline__ int compact_indices(const KArgs& a, const Tok& k, int t, int* list, int* wtot, int w_lo) {
-  const int* row = a.idx + (size_t)t * a.topk;
+// Returns the number of valid slots.  Whole-work-group call; `first` holds
+// the slots [0, kIdxPre), later rounds are loaded here.
+__device__ __forceinline__ int compact_indices(const KArgs& a, const Tok& k, int t, int* list, int* wtot, int w_lo,
+                                               const IdxPre& first) {
   const int tid = opaque((int)threadIdx.x);
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int base = 0;
-  for (int s0 = 0; s0 < k.k_eff; s0 += 4 * kThreads) {
-    int v[4];
+  for (int s0 = 0; s0 < k.k_eff; s0 += kIdxPre) {
+    const IdxPre cur = (s0 == 0) ? first : load_indices(a, t, s0);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int s = s0 + m * kThreads + tid;
-      v[m] = (s < a.topk) ? row[s] : -1;
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int s = s0 + m * kThreads + tid;
-      const bool ok = (s < k.k_eff) && (v[m] >= 0) && (v[m] < k.vis);
+    for (int m = 0; m < kIdxRounds; ++m) {
+      const int slot = s0 + m * kThreads + tid;
+      const bool ok = (slot < k.k_eff) && (cur.v[m] >= 0) && (cur.v[m] < k.vis);
       const uint64_t bal = __ballot(ok);
       const int pre = __popcll(bal & ((1ull << lane) - 1ull));
       if (lane == 0) wtot[w] = __popcll(bal);
@@ -230,12 +246,16 @@ __device__ __forceinline__ int compact_indices(const KArgs& a, const Tok& k, int
       for (int j = 0; j < w; ++j) off += wtot[j];
       const int tot = wtot[0] + wtot[1] + wtot[2] + wtot[3];
       const int pos = base + off + pre;
-      if (ok && pos >= w_lo && pos < w_lo + kListMax) list[pos - w_lo] = v[m];
+      if (ok && pos >= w_lo && pos < w_lo + kListMax) list[pos - w_lo] = cur.v[m];
       base += tot;
       lds_barrier();
     }
   }
   return base;
+}
+
+__device__ __forceinline__ int compact_indices(const KArgs& a, const Tok& k, int t, int* list, int* wtot, int w_lo) {
+  return compact_indices(a, k, t, list, wtot, w_lo, load_indices(a, t, 0));
 }
 
 // ---------------------------------------------------------------------------
@@ -277,80 +297,103 @@ __device__ __forceinline__ int64_t resolve_row(const KArgs& a, const Tok& k, int
   return row_of(a, k, is_cmp, j, blk);
 }
 
-// Resolve the keys [c0, c1) of a unit into the chunk arrays: row address,
-// descales, and lam = log2 / inv = 1 / the row's largest descale.  Slots past
-// c1 read the zero row with zero descales and lam = -inf.  All block-table
-// loads of the chunk are issued together, then all row / descale loads:
-// two dependent round trips per chunk.  Whole-work-group call; ends with a
-// barrier.
+// Resolving the keys [c0, c1) of a unit into the chunk arrays takes two
+// phases.  resolve_rows: all block-table loads of the chunk at once, then
+// the row addresses into LDS (slots past c1 point at the zero row) and the
+// descale loads, left in flight.  resolve_scales: the descales and
+// lam = log2 / inv = 1 / the row's largest descale into LDS (slots past c1:
+// zero descales, lam = -inf).  In between, the caller publishes the
+// addresses with a barrier and issues the first gathers, so that the rows
+// and their descales travel in the same round trip.  Whole-work-group calls.
 template <int PER_TILE>
-__device__ __forceinline__ void resolve_chunk(const KArgs& a, const Tok& k, int n_o, const int* list, int w_lo,
-                                              int c0, int c1, uint8_t* smem) {
+struct ChunkScales {
+  float ds[Lds<PER_TILE>::kChunk / kThreads][Lds<PER_TILE>::kNks];
+  bool ok[Lds<PER_TILE>::kChunk / kThreads];
+};
+
+template <int PER_TILE>
+__device__ __forceinline__ ChunkScales<PER_TILE> resolve_rows(const KArgs& a, const Tok& k, int n_o, const int* list,
+                                                              int w_lo, int c0, int c1, uint8_t* smem) {
   using L = Lds<PER_TILE>;
   constexpr int M = L::kChunk / kThreads, NKS = L::kNks;
   uint64_t* kaddr = reinterpret_cast<uint64_t*>(smem + L::kAddr);
-  float* klam = reinterpret_cast<float*>(smem + L::kLam);
-  float* kinv = reinterpret_cast<float*>(smem + L::kInv);
-  float* kks = reinterpret_cast<float*>(smem + L::kKs);
   const int tid = opaque((int)threadIdx.x);
+  ChunkScales<PER_TILE> cs;
   int j[M], blk[M];
-  bool cmp[M], ok[M];
+  bool cmp[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int key = c0 + m * kThreads + tid;
-    ok[m] = key < c1;
-    j[m] = ok[m] ? key_pos(a, k, n_o, key, list, w_lo, cmp[m]) : 0;
-    if (!ok[m]) cmp[m] = false;
+    cs.ok[m] = key < c1;
+    j[m] = cs.ok[m] ? key_pos(a, k, n_o, key, list, w_lo, cmp[m]) : 0;
+    if (!cs.ok[m]) cmp[m] = false;
     blk[m] = 0;
   }
   if (a.layout_kv == 2) {
 #pragma unroll
     for (int m = 0; m < M; ++m)
-      if (ok[m]) blk[m] = block_of(a, k, cmp[m], j[m]);
+      if (cs.ok[m]) blk[m] = block_of(a, k, cmp[m], j[m]);
   }
-  float ds[M][NKS];
-  uint64_t addr[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    addr[m] = (uint64_t)(uintptr_t)g_zero_row;
+    uint64_t addr = (uint64_t)(uintptr_t)g_zero_row;
 #pragma unroll
-    for (int c = 0; c < NKS; ++c) ds[m][c] = 0.f;
-    if (ok[m]) {
+    for (int c = 0; c < NKS; ++c) cs.ds[m][c] = 0.f;
+    if (cs.ok[m]) {
       const int64_t row = row_of(a, k, cmp[m], j[m], blk[m]);
-      addr[m] = (uint64_t)(uintptr_t)((cmp[m] ? a.cmp_kv : a.ori_kv) + row * kD);
+      addr = (uint64_t)(uintptr_t)((cmp[m] ? a.cmp_kv : a.ori_kv) + row * kD);
       const float* dsp = cmp[m] ? a.cmp_ds : a.ori_ds;
       if constexpr (PER_TILE) {
         const v4f x0 = *(const v4f*)(dsp + row * 8);
         const v4f x1 = *(const v4f*)(dsp + row * 8 + 4);
-        ds[m][0] = x0[0]; ds[m][1] = x0[1]; ds[m][2] = x0[2]; ds[m][3] = x0[3];
-        ds[m][4] = x1[0]; ds[m][5] = x1[1]; ds[m][6] = x1[2]; ds[m][7] = x1[3];
+        cs.ds[m][0] = x0[0]; cs.ds[m][1] = x0[1]; cs.ds[m][2] = x0[2]; cs.ds[m][3] = x0[3];
+        cs.ds[m][4] = x1[0]; cs.ds[m][5] = x1[1]; cs.ds[m][6] = x1[2]; cs.ds[m][7] = x1[3];
       } else {
-        ds[m][0] = dsp[row];
+        cs.ds[m][0] = dsp[row];
       }
     }
+    kaddr[m * kThreads + tid] = addr;
   }
+  return cs;
+}
+
+template <int PER_TILE>
+__device__ __forceinline__ void resolve_scales(const ChunkScales<PER_TILE>& cs, uint8_t* smem) {
+  using L = Lds<PER_TILE>;
+  constexpr int M = L::kChunk / kThreads, NKS = L::kNks;
+  float* klam = reinterpret_cast<float*>(smem + L::kLam);
+  float* kinv = reinterpret_cast<float*>(smem + L::kInv);
+  float* kks = reinterpret_cast<float*>(smem + L::kKs);
+  const int tid = opaque((int)threadIdx.x);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int slot = m * kThreads + tid;
     float lam = kNegInf, inv = 0.f;
-    if (ok[m]) {
-      float mx = ds[m][0];
+    if (cs.ok[m]) {
+      float mx = cs.ds[m][0];
 #pragma unroll
-      for (int c = 1; c < NKS; ++c) mx = fmaxf(mx, ds[m][c]);
+      for (int c = 1; c < NKS; ++c) mx = fmaxf(mx, cs.ds[m][c]);
 #pragma unroll
       for (int c = 0; c < NKS; ++c)
-        if (ds[m][c] != ds[m][c]) mx = ds[m][c];   // a NaN descale poisons the row
+        if (cs.ds[m][c] != cs.ds[m][c]) mx = cs.ds[m][c];   // a NaN descale poisons the row
       mx = (mx == 0.f) ? kMinDescale : mx;
       lam = __log2f(mx);
       inv = 1.0f / mx;
       if (mx != mx) { lam = mx; inv = mx; }
     }
-    kaddr[slot] = addr[m];
     klam[slot] = lam;
     kinv[slot] = inv;
 #pragma unroll
-    for (int c = 0; c < NKS; ++c) kks[c * L::kChunk + slot] = ds[m][c];
+    for (int c = 0; c < NKS; ++c) kks[c * L::kChunk + slot] = cs.ds[m][c];
   }
+}
+
+// Both phases with nothing in between (ends with a barrier).
+template <int PER_TILE>
+__device__ __forceinline__ void resolve_chunk(const KArgs& a, const Tok& k, int n_o, const int* list, int w_lo,
+                                              int c0, int c1, uint8_t* smem) {
+  const ChunkScales<PER_TILE> cs = resolve_rows<PER_TILE>(a, k, n_o, list, w_lo, c0, c1, smem);
+  resolve_scales<PER_TILE>(cs, smem);
   lds_barrier();
 }
 
@@ -359,13 +402,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Gather the 64 rows of chunk tile `tile` into a tile buffer: wave w loads
-// rows [16 w, +16) with 8 global_load_lds_dwordx4 (2 rows each: lanes 0-31 and
-// 32-63, 16 bytes per lane; M0 = LDS destination, lane l writes base + 16 l).
-// Exactly 8 vector-memory instructions per wave, whatever the tile holds.
-// The loads are ordered only by the explicit waits of the pipeline, so the
-// compiler does not hold the other tiles' LDS reads behind them.
-__device__ __forceinline__ void gather_tile(const uint64_t* kaddr, int tile, uint8_t* tb, int w) {
+// Gather the rows of chunk tile `tile` into a tile buffer: wave w covers
+// rows [16 w, +16) with 8 instructions of 2 rows each (lanes 0-31 and 32-63,
+// 16 bytes per lane).  A pair with a row below `nrows` (the tile's valid
+// rows) is loaded with global_load_lds_dwordx4 (M0 = LDS destination, lane l
+// writes base + 16 l; a lone odd row reads the zero row); a pair past it is
+// zeroed with LDS stores, so that stale bytes never reach the MFMAs.  A full
+// tile issues exactly 8 vector-memory instructions per wave.  The loads are
+// ordered only by the explicit waits of the pipeline, so the compiler does
+// not hold the other tiles' LDS reads behind them.
+__device__ __forceinline__ void gather_tile(const uint64_t* kaddr, int tile, int nrows, uint8_t* tb, int w) {
   const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
   uint64_t src[8];
 #pragma unroll
@@ -375,10 +421,18 @@ __device__ __forceinline__ void gather_tile(const uint64_t* kaddr, int tile, uin
   }
 #pragma unroll
   for (int mi = 0; mi < 8; ++mi) {
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + (16 * w + 2 * mi) * kD));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src[mi]) : "m0");
+    const int r0 = 16 * w + 2 * mi;
+    if (r0 < nrows) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + r0 * kD));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src[mi]) : "m0");
+    } else {
+      *(v4i*)(tb + (r0 + g) * kD + 16 * li) = v4i{0, 0, 0, 0};
+    }
   }
 }
+
+// Valid rows of tile `tile` of a chunk holding nkeys keys.
+__device__ __forceinline__ int tile_rows(int nkeys, int tile) { return min(kTileKeys, nkeys - tile * kTileKeys); }
 
 __device__ __forceinline__ void wait_all_and_sync() {
   __builtin_amdgcn_s_waitcnt(0);
@@ -386,9 +440,10 @@ __device__ __forceinline__ void wait_all_and_sync() {
 }
 
 // Work-group barrier after which the older of the wave's gathers has landed:
-// with `newer` set, the 8 loads of the most recent gather may still be in flight.
-__device__ __forceinline__ void gather_barrier(bool newer) {
-  if (newer) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// with `newer_full` set, the 8 loads of the most recent gather (a full tile)
+// may still be in flight; otherwise every load is waited for.
+__device__ __forceinline__ void gather_barrier(bool newer_full) {
+  if (newer_full) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
@@ -748,7 +803,7 @@ __device__ __forceinline__ void cover_chunk(const KArgs& a, UnitState& us, int* 
 // One code path for all three buffers (the buffer offset is added to the
 // lane offsets), so that the accumulators keep their registers.
 template <int PER_TILE>
-__device__ __forceinline__ void pipeline_step(uint8_t* smem, const LaneOffsets& o_in, int tiles, int i, int bv,
+__device__ __forceinline__ void pipeline_step(uint8_t* smem, const LaneOffsets& o_in, int nkeys, int tiles, int i, int bv,
                                               const WaveCtx& c, const v8i (&qreg)[4], v16f (&oacc)[8], float Mrun,
                                               float& lsum, PTile<PER_TILE>& P, int* flag) {
   using L = Lds<PER_TILE>;
@@ -759,11 +814,13 @@ __device__ __forceinline__ void pipeline_step(uint8_t* smem, const LaneOffsets& 
   for (int k = 0; k < 4; ++k) o.tr[k] = opaque(o.tr[k]);
   const int bq = (bv == 2) ? 0 : bv + 1, bg = (bq == 2) ? 0 : bq + 1;
   const bool g2 = i + 2 < tiles;
-  if (g2) gather_tile(reinterpret_cast<const uint64_t*>(smem + L::kAddr), i + 2, smem + L::kTiles + bg * kTileBytes, c.w);
+  if (g2)
+    gather_tile(reinterpret_cast<const uint64_t*>(smem + L::kAddr), i + 2, tile_rows(nkeys, i + 2),
+                smem + L::kTiles + bg * kTileBytes, c.w);
   const TileView<PER_TILE> tv = tile_view<PER_TILE>(smem, i);
   const TrOff tro = tr_at(o, L::kTiles + bv * kTileBytes);
   pv_half<PER_TILE, 0>(smem, tro, tv, c.dh, P, c.g, oacc);
-  gather_barrier(g2);
+  gather_barrier(g2 && tile_rows(nkeys, i + 2) == kTileKeys);
   const bool has_next = i + 1 < tiles;
   const TileView<PER_TILE> tq = tile_view<PER_TILE>(smem, i + 1);
   v16f s_own, s_oth;
@@ -799,12 +856,18 @@ __device__ __forceinline__ void run_unit(KArgPtr ap, UnitState& us, int* list, i
     const int c1 = min(us.ke, c0 + L::kChunk);
     const KArgs& a = args(ap);
     cover_chunk(a, us, list, misc, c0, c1);
-    resolve_chunk<PER_TILE>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
     const int nkeys = c1 - c0, tiles = (nkeys + kTileKeys - 1) / kTileKeys;
-    const uint64_t* kaddr = reinterpret_cast<const uint64_t*>(smem + L::kAddr);
-    gather_tile(kaddr, 0, smem + L::kTiles, c.w);
-    if (tiles > 1) gather_tile(kaddr, 1, smem + L::kTiles + kTileBytes, c.w);
-    gather_barrier(tiles > 1);
+    {
+      // row addresses -> barrier -> gathers of tiles 0 and 1, then the
+      // descales, whose loads were issued with the addresses
+      const ChunkScales<PER_TILE> cs = resolve_rows<PER_TILE>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
+      lds_barrier();
+      const uint64_t* kaddr = reinterpret_cast<const uint64_t*>(smem + L::kAddr);
+      gather_tile(kaddr, 0, tile_rows(nkeys, 0), smem + L::kTiles, c.w);
+      if (tiles > 1) gather_tile(kaddr, 1, tile_rows(nkeys, 1), smem + L::kTiles + kTileBytes, c.w);
+      resolve_scales<PER_TILE>(cs, smem);
+    }
+    gather_barrier(tiles > 1 && tile_rows(nkeys, 1) == kTileKeys);
     // ---- P of tile 0 ----
     PTile<PER_TILE> P;
     {
@@ -827,7 +890,7 @@ __device__ __forceinline__ void run_unit(KArgPtr ap, UnitState& us, int* list, i
     }
     // ---- steady state ----
     for (int i = 0, bv = 0; i < tiles; ++i, bv = (bv == 2) ? 0 : bv + 1)
-      pipeline_step<PER_TILE>(smem, o, tiles, i, bv, c, qreg, oacc, Mrun, lsum, P, flag);
+      pipeline_step<PER_TILE>(smem, o, nkeys, tiles, i, bv, c, qreg, oacc, Mrun, lsum, P, flag);
   }
 }
 
@@ -845,7 +908,7 @@ __device__ __forceinline__ float unit_max(KArgPtr ap, UnitState& us, int* list, 
     resolve_chunk<PER_TILE>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
     const int nkeys = c1 - c0, tiles = (nkeys + kTileKeys - 1) / kTileKeys;
     for (int i = 0; i < tiles; ++i) {
-      gather_tile(reinterpret_cast<const uint64_t*>(smem + L::kAddr), i, smem + L::kTiles, c.w);
+      gather_tile(reinterpret_cast<const uint64_t*>(smem + L::kAddr), i, tile_rows(nkeys, i), smem + L::kTiles, c.w);
       gather_barrier(false);
       const TileView<PER_TILE> tv = tile_view<PER_TILE>(smem, i);
       v16f s_own, s_oth;
@@ -873,6 +936,13 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
   const int bid = blockIdx.x;
   const int lw = (G % 8 == 0) ? ((bid & 7) * (G >> 3) + (bid >> 3)) : bid;  // one XCD per contiguous range
   const int u_begin = ap->starts[lw], u_end = ap->starts[lw + 1];
+  {
+    // Touch every cache line of the kernel arguments up to the unit ranges
+    // in the same round trip as the ranges: the per-unit reloads through
+    // args() then hit the scalar cache.
+    const __attribute__((address_space(4))) int* kw = (const __attribute__((address_space(4))) int*)ap;
+    asm volatile("" ::"s"(kw[0]), "s"(kw[16]), "s"(kw[32]), "s"(kw[48]), "s"(kw[64]));
+  }
   int* list = reinterpret_cast<int*>(smem + L::kList);
   int* misc = reinterpret_cast<int*>(smem + L::kMisc);
   const LaneOffsets o = lane_offsets(lane, dh);
@@ -898,17 +968,21 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
     }
     const float qd = a.q_ds_per_head ? a.q_ds[(size_t)t * kN1 + h] : a.q_ds[t];
     c.qs = a.scale_log2 * qd;
+    IdxPre ip;
+    if (a.topk > 0) ip = load_indices(a, t, 0);
     us.k = token_ctx(a, t);
     if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
       if (a.splits == 1) {
-        for (int x = lane; x < 32 * 64; x += 64) {
+        for (int x = opaque(lane); x < 32 * 64; x += 64) {
           const int hr = 32 * hh + x / 64, d = 256 * dh + 4 * (x % 64);
           *(uint2*)(a.out + ((size_t)t * kN1 + hr) * kD + d) = make_uint2(0, 0);
         }
         if (a.lse && dh == 0 && g == 0) a.lse[(size_t)t * kN1 + h] = kNegInf;
-      } else if (dh == 0 && g == 0) {
-        a.ws_ml[((size_t)u * kN1 + h) * 2] = kNegInf;
-        a.ws_ml[((size_t)u * kN1 + h) * 2 + 1] = -1.0f;   // marks a padded row for the combine
+      } else {
+        if (dh == 0 && g == 0) {
+          a.ws_ml[((size_t)u * kN1 + h) * 2] = kNegInf;
+          a.ws_ml[((size_t)u * kN1 + h) * 2 + 1] = -1.0f;   // marks a padded row for the combine
+        }
       }
       continue;
     }
@@ -916,7 +990,7 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
     us.n_o = us.k.hi - us.k.lo;
     us.n_c = 0;
     us.w_lo = 0;
-    if (a.topk > 0) us.n_c = compact_indices(a, us.k, t, list, misc, 0);
+    if (a.topk > 0) us.n_c = compact_indices(a, us.k, t, list, misc, 0, ip);
     else if (a.has_cmp) us.n_c = us.k.vis;
     const int64_t n = (int64_t)us.n_o + us.n_c;
     us.kb = (int)(n * s / a.splits);
