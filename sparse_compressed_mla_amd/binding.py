@@ -253,6 +253,11 @@ class Plan:
     def grid(self) -> int:
         return int(self.metadata[7])
 
+    @property
+    def head_group(self) -> int:
+        """Heads per work unit of the head-split kernel, or 0 (key-split kernel)."""
+        return int(self.metadata[12])
+
 
 def forward(inp, out=None, lse=None, workspace=None, plan: Optional[Plan] = None, stream=None):
     """Run the attention on inputs already on the GPU.  Allocates the outputs

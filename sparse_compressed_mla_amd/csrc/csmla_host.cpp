@@ -260,8 +260,23 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
     const int64_t f = std::atoll(env);
     if (f >= 1) S = std::max(s_list, f);
   }
+  // Small decode batches with per-token descales: split the heads instead of
+  // the keys (groups of 8 heads up to 64 tokens, of 16 up to 256), so that no
+  // partial outputs need merging.  Long key lists keep the key split.
+  int hg = 0;
+  if (p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN && avg <= 8192) {
+    if (T1 <= 64) hg = 8;
+    else if (T1 <= 256) hg = 16;
+  }
+  if (const char* env = std::getenv("CSMLA_KERNEL")) {   // tuning / test override
+    if (!std::strcmp(env, "split")) hg = 0;
+    else if (!std::strcmp(env, "heads8") && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN) hg = 8;
+    else if (!std::strcmp(env, "heads16") && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN) hg = 16;
+  }
+  if (hg > 0) S = 1;
   if (S > kMaxSplits) return fail(CSMLA_ERR_UNSUPPORTED, "a token needs %lld splits; at most %d are built", (long long)S, kMaxSplits);
-  const int64_t n_units64 = (int64_t)T1 * S;
+  const int64_t per_token = hg > 0 ? kN1 / hg : S;   // units per query token
+  const int64_t n_units64 = (int64_t)T1 * per_token;
   if (n_units64 > (int64_t)1 << 30) return fail(CSMLA_ERR_UNSUPPORTED, "too many work units");
   const int n_units = (int)n_units64;
   const int G = (int)std::min<int64_t>(n_units64, kMaxGrid);
@@ -269,7 +284,7 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   // contiguous unit ranges per work-group, balanced by estimated keys
   std::vector<double> pre(n_units + 1, 0.0);
   for (int u = 0; u < n_units; ++u) {
-    const auto& c = cost[u / S];
+    const auto& c = cost[u / per_token];
     pre[u + 1] = pre[u] + (double)(c.n_o + c.n_c_up) / (double)S + 48.0;
   }
   std::vector<int32_t> starts(G + 1);
@@ -298,6 +313,7 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   md[MD_WS_LO] = (int32_t)(ws & 0x7fffffff);
   md[MD_WS_HI] = (int32_t)(ws >> 31);
   md[MD_FLAGS] = S > 1 ? 1 : 0;
+  md[MD_HEAD_GROUP] = hg;
   for (int g = 0; g <= G; ++g) md[MD_STARTS + g] = starts[g];
   if (ws_bytes) *ws_bytes = ws;
   g_last_error.clear();
@@ -354,9 +370,12 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
       return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was not written by csmla_plan of this version");
     if ((uint32_t)md[MD_PROBLEM_HASH] != problem_hash(p) || md[MD_T1] != p->t1)
       return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was planned for a different problem");
-    const int S = md[MD_SPLITS], U = md[MD_UNITS], G = md[MD_GRID];
-    if (S < 1 || U != p->t1 * S || G < 1 || G > kMaxGrid || G > U)
+    const int S = md[MD_SPLITS], U = md[MD_UNITS], G = md[MD_GRID], HG = md[MD_HEAD_GROUP];
+    const bool hg_ok = HG == 0 || ((HG == 8 || HG == 16) && S == 1 && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN);
+    const int per_token = HG > 0 ? kN1 / HG : S;
+    if (S < 1 || !hg_ok || U != p->t1 * per_token || G < 1 || G > kMaxGrid || G > U)
       return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata header is inconsistent");
+    a.hg = HG;
     for (int g = 0; g <= G; ++g) {
       const int s0 = md[MD_STARTS + g];
       if (s0 < 0 || s0 > U || (g > 0 && s0 < md[MD_STARTS + g - 1]) || (g == 0 && s0 != 0) || (g == G && s0 != U))

@@ -19,7 +19,7 @@ constexpr int32_t kMagic = 0x4C4D5343;   // "CSML"
 enum {
   MD_MAGIC = 0, MD_VERSION = 1, MD_PROBLEM_HASH = 2, MD_LENGTHS_HASH = 3, MD_T1 = 4,
   MD_SPLITS = 5, MD_UNITS = 6, MD_GRID = 7, MD_LIST_MAX = 8, MD_WS_LO = 9, MD_WS_HI = 10,
-  MD_FLAGS = 11, MD_STARTS = kHeaderWords
+  MD_FLAGS = 11, MD_HEAD_GROUP = 12, MD_STARTS = kHeaderWords
 };
 
 // Everything one kernel launch needs, passed by value in the kernarg segment.
@@ -42,6 +42,7 @@ struct KArgs {
   uint16_t* ws_o; float* ws_ml;
   // plan
   int32_t splits, n_units, grid;
+  int32_t hg;                       // > 0: head-split kernel with groups of hg heads (8 or 16)
   int32_t starts[kMaxGrid + 1];
 };
 

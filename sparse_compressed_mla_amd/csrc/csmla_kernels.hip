@@ -51,6 +51,7 @@ constexpr int kStageRow = 2 * 256 + 16;         // bytes per head row of the out
 // (row address, log2 / inverse of the row's largest V descale, descales).
 template <int PER_TILE>
 struct Lds {
+  static constexpr int kPerTile = PER_TILE;
   static constexpr int kChunk = PER_TILE ? 512 : 1024;     // keys resolved at once
   static constexpr int kNks = PER_TILE ? 8 : 1;            // descales per key
   static constexpr int kTiles = 0;                         // 3 x 32 KiB
@@ -305,20 +306,19 @@ __device__ __forceinline__ int64_t resolve_row(const KArgs& a, const Tok& k, int
 // zero descales, lam = -inf).  In between, the caller publishes the
 // addresses with a barrier and issues the first gathers, so that the rows
 // and their descales travel in the same round trip.  Whole-work-group calls.
-template <int PER_TILE>
+template <class L>
 struct ChunkScales {
-  float ds[Lds<PER_TILE>::kChunk / kThreads][Lds<PER_TILE>::kNks];
-  bool ok[Lds<PER_TILE>::kChunk / kThreads];
+  float ds[L::kChunk / kThreads][L::kNks];
+  bool ok[L::kChunk / kThreads];
 };
 
-template <int PER_TILE>
-__device__ __forceinline__ ChunkScales<PER_TILE> resolve_rows(const KArgs& a, const Tok& k, int n_o, const int* list,
+template <class L>
+__device__ __forceinline__ ChunkScales<L> resolve_rows(const KArgs& a, const Tok& k, int n_o, const int* list,
                                                               int w_lo, int c0, int c1, uint8_t* smem) {
-  using L = Lds<PER_TILE>;
   constexpr int M = L::kChunk / kThreads, NKS = L::kNks;
   uint64_t* kaddr = reinterpret_cast<uint64_t*>(smem + L::kAddr);
   const int tid = opaque((int)threadIdx.x);
-  ChunkScales<PER_TILE> cs;
+  ChunkScales<L> cs;
   int j[M], blk[M];
   bool cmp[M];
 #pragma unroll
@@ -343,7 +343,7 @@ __device__ __forceinline__ ChunkScales<PER_TILE> resolve_rows(const KArgs& a, co
       const int64_t row = row_of(a, k, cmp[m], j[m], blk[m]);
       addr = (uint64_t)(uintptr_t)((cmp[m] ? a.cmp_kv : a.ori_kv) + row * kD);
       const float* dsp = cmp[m] ? a.cmp_ds : a.ori_ds;
-      if constexpr (PER_TILE) {
+      if constexpr (L::kPerTile) {
         const v4f x0 = *(const v4f*)(dsp + row * 8);
         const v4f x1 = *(const v4f*)(dsp + row * 8 + 4);
         cs.ds[m][0] = x0[0]; cs.ds[m][1] = x0[1]; cs.ds[m][2] = x0[2]; cs.ds[m][3] = x0[3];
@@ -357,9 +357,8 @@ __device__ __forceinline__ ChunkScales<PER_TILE> resolve_rows(const KArgs& a, co
   return cs;
 }
 
-template <int PER_TILE>
-__device__ __forceinline__ void resolve_scales(const ChunkScales<PER_TILE>& cs, uint8_t* smem) {
-  using L = Lds<PER_TILE>;
+template <class L>
+__device__ __forceinline__ void resolve_scales(const ChunkScales<L>& cs, uint8_t* smem) {
   constexpr int M = L::kChunk / kThreads, NKS = L::kNks;
   float* klam = reinterpret_cast<float*>(smem + L::kLam);
   float* kinv = reinterpret_cast<float*>(smem + L::kInv);
@@ -389,11 +388,11 @@ __device__ __forceinline__ void resolve_scales(const ChunkScales<PER_TILE>& cs, 
 }
 
 // Both phases with nothing in between (ends with a barrier).
-template <int PER_TILE>
+template <class L>
 __device__ __forceinline__ void resolve_chunk(const KArgs& a, const Tok& k, int n_o, const int* list, int w_lo,
                                               int c0, int c1, uint8_t* smem) {
-  const ChunkScales<PER_TILE> cs = resolve_rows<PER_TILE>(a, k, n_o, list, w_lo, c0, c1, smem);
-  resolve_scales<PER_TILE>(cs, smem);
+  const ChunkScales<L> cs = resolve_rows<L>(a, k, n_o, list, w_lo, c0, c1, smem);
+  resolve_scales<L>(cs, smem);
   lds_barrier();
 }
 
@@ -841,10 +840,11 @@ __device__ __forceinline__ void pipeline_step(uint8_t* smem, const LaneOffsets& 
   if (has_next) probs_gather<PER_TILE>(smem, c, P);
 }
 
-// Runs the unit's keys [kb, ke) into (oacc, lsum).  Mrun enters as the preset
-// reference, or -inf: then the first tile sets it (the pair's max maps to 2^4).
+// Runs the unit's keys [kb, ke) into (oacc, lsum).  With `preset`, Mrun is the
+// reference from the redo pass; otherwise the first tile sets it (the pair's
+// max maps to 2^4).
 template <int PER_TILE>
-__device__ __forceinline__ void run_unit(KArgPtr ap, UnitState& us, int* list, int* misc, uint8_t* smem,
+__device__ __forceinline__ void run_unit(KArgPtr ap, bool preset, UnitState& us, int* list, int* misc, uint8_t* smem,
                                          const LaneOffsets& o, const WaveCtx& c, const v8i (&qreg)[4],
                                          v16f (&oacc)[8], float& Mrun, float& lsum) {
   using L = Lds<PER_TILE>;
@@ -860,12 +860,12 @@ __device__ __forceinline__ void run_unit(KArgPtr ap, UnitState& us, int* list, i
     {
       // row addresses -> barrier -> gathers of tiles 0 and 1, then the
       // descales, whose loads were issued with the addresses
-      const ChunkScales<PER_TILE> cs = resolve_rows<PER_TILE>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
+      const ChunkScales<L> cs = resolve_rows<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
       lds_barrier();
       const uint64_t* kaddr = reinterpret_cast<const uint64_t*>(smem + L::kAddr);
       gather_tile(kaddr, 0, tile_rows(nkeys, 0), smem + L::kTiles, c.w);
       if (tiles > 1) gather_tile(kaddr, 1, tile_rows(nkeys, 1), smem + L::kTiles + kTileBytes, c.w);
-      resolve_scales<PER_TILE>(cs, smem);
+      resolve_scales<L>(cs, smem);
     }
     gather_barrier(tiles > 1 && tile_rows(nkeys, 1) == kTileKeys);
     // ---- P of tile 0 ----
@@ -878,7 +878,7 @@ __device__ __forceinline__ void run_unit(KArgPtr ap, UnitState& us, int* list, i
       scores_publish<PER_TILE>(smem, c, s_oth);
       lds_barrier();
       const float mt = scores_finish<PER_TILE>(smem, kv, c, s_own);
-      if (Mrun == kNegInf) {
+      if (!preset && c0 == us.kb) {   // wave-uniform: every wave takes the same branch
         const float mx = pair_reduce(misc, c.w, c.lane, mt, true);
         Mrun = (mx == kNegInf) ? kNegInf : mx - kPShift;
       } else if (__ballot(mt > Mrun + kTau)) {
@@ -905,7 +905,7 @@ __device__ __forceinline__ float unit_max(KArgPtr ap, UnitState& us, int* list, 
     const int c1 = min(us.ke, c0 + L::kChunk);
     const KArgs& a = args(ap);
     cover_chunk(a, us, list, misc, c0, c1);
-    resolve_chunk<PER_TILE>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
+    resolve_chunk<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
     const int nkeys = c1 - c0, tiles = (nkeys + kTileKeys - 1) / kTileKeys;
     for (int i = 0; i < tiles; ++i) {
       gather_tile(reinterpret_cast<const uint64_t*>(smem + L::kAddr), i, tile_rows(nkeys, i), smem + L::kTiles, c.w);
@@ -1000,7 +1000,7 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
     float Mrun = kNegInf, lsum = 0.f;
     for (int pass = 0;; ++pass) {
       if (tid == 0) misc[4] = 0;
-      run_unit<PER_TILE>(ap, us, list, misc, smem, o, c, qreg, oacc, Mrun, lsum);
+      run_unit<PER_TILE>(ap, pass > 0, us, list, misc, smem, o, c, qreg, oacc, Mrun, lsum);
       lds_barrier();
       const int redo = misc[4];
       lds_barrier();
@@ -1063,6 +1063,389 @@ attn_kernel(const KArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds<PER_TILE>::kBytes];
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   attn_body<PER_TILE>((KArgPtr)__builtin_amdgcn_kernarg_segment_ptr(), smem, w);
+}
+
+// ---------------------------------------------------------------------------
+// head-split kernel (decode): one work unit = (query token, group of HG = 8
+// or 16 heads) over the token's whole key list, so no split partials exist.
+// ---------------------------------------------------------------------------
+//
+// For a decode batch the tokens are few, and splitting each token's keys
+// over work-groups (the kernel above) leaves 64-head partial outputs that a
+// second pass must merge.  Here the work-groups of one token divide its heads
+// instead and read the same rows, which the XCD's L2 serves after the first.
+//
+// 4 waves; 128-key tiles (2 LDS buffers).  With v_mfma_f32_16x16x128_f8f6f4
+// (A lane i+16g: row i, k = 32g..32g+31; B lane j+16g: column j; D lane
+// j+16g, reg r: element [4g+r][j]):
+//   S^T = K Q^T: wave w scores keys [32w, +32) (two 16-key blocks) against
+//   the HG heads over all of D (4 K-steps of 128), so no score exchange;
+//   P' = 2^(E - M) as an fp8 hi + lo pair goes to LDS as [head][key] bytes;
+//   O^T += V^T P^T: wave w owns output columns [128w, +128) (8 blocks of 16)
+//   over the tile's 128 keys, V^T from ds_read_b64_tr_b8.
+// Unused head columns of an 8-head group carry zero q and are not stored.
+
+constexpr int kDkRows = 128;                       // keys per tile
+constexpr int kDkTileBytes = kDkRows * kD;         // 64 KiB
+constexpr int kDkPxRow = 144;                      // bytes per head row of P (128 keys + pad)
+
+struct LdsDK {
+  static constexpr int kPerTile = 0;
+  static constexpr int kChunk = 1024;
+  static constexpr int kNks = 1;
+  static constexpr int kTiles = 0;                             // 2 x 64 KiB
+  static constexpr int kAddr = 2 * kDkTileBytes;               // uint64 [kChunk]
+  static constexpr int kLam = kAddr + 8 * kChunk;              // float [kChunk]
+  static constexpr int kInv = kLam + 4 * kChunk;               // float [kChunk]
+  static constexpr int kKs = kInv + 4 * kChunk;                // float [kChunk]
+  static constexpr int kPx = kKs + 4 * kChunk;                 // fp8 P: [hi, lo][16 heads][kDkPxRow]
+  static constexpr int kList = kPx + 2 * 16 * kDkPxRow;        // int [kListMax]
+  static constexpr int kMisc = kList + 4 * kListMax;           // [0..3] compaction, [4] redo flag, [64..] reductions
+  static constexpr int kBytes = kMisc + 4 * 64 + 4 * 4 * 64;
+};
+static_assert(LdsDK::kBytes <= 160 * 1024, "LDS");
+
+__device__ __forceinline__ v4f mma16(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Gather rows [0, 128) of chunk tile `tile` (128 keys) into a tile buffer:
+// wave w covers rows [32 w, +32) with 16 instructions of 2 rows; pairs past
+// `nrows` are zeroed.  A full tile issues exactly 16 loads per wave.
+__device__ __forceinline__ void dk_gather(const uint64_t* kaddr, int tile, int nrows, uint8_t* tb, int w) {
+  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
+  uint64_t src[16];
+#pragma unroll
+  for (int mi = 0; mi < 16; ++mi) {
+    const int r = 32 * w + 2 * mi + g;
+    src[mi] = kaddr[tile * kDkRows + r] + 16u * (uint32_t)(li ^ swz(r));
+  }
+#pragma unroll
+  for (int mi = 0; mi < 16; ++mi) {
+    const int r0 = 32 * w + 2 * mi;
+    if (r0 < nrows) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + r0 * kD));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src[mi]) : "m0");
+    } else {
+      *(v4i*)(tb + (r0 + g) * kD + 16 * li) = v4i{0, 0, 0, 0};
+    }
+  }
+}
+
+__device__ __forceinline__ int dk_rows(int nkeys, int tile) { return min(kDkRows, nkeys - tile * kDkRows); }
+
+// Per-lane LDS offsets (tile buffer 0) of the wave's K and V^T operand reads.
+struct DkOffsets {
+  int k[2][2];    // [key block b][16-byte half]: row (32 w + 16 b + i), chunk (2 g + x) ^ swz, + 128 s per K-step
+  int v[4][8];    // [m][d-block]: V^T transpose reads of keys 32 g + 8 m + .., columns 128 w + 16 db + ..
+};
+
+__device__ __forceinline__ DkOffsets dk_offsets(int lane, int w) {
+  DkOffsets o;
+  const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int row = 32 * w + 16 * b + i, f = swz(row);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) o.k[b][x] = row * kD + 16 * ((2 * g + x) ^ f);
+  }
+  const int L = lane & 15;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int row = 32 * g + 8 * m + (L >> 1), f = swz(row);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o.v[m][db] = row * kD + 128 * w + 16 * (db ^ f) + 8 * (L & 1);
+  }
+  return o;
+}
+
+// S^T blocks (16 keys x 16 heads) of the wave's 32 keys, full D.
+__device__ __forceinline__ void dk_qk(const uint8_t* tb, const DkOffsets& o, const v8i (&qreg)[4], v4f (&s)[2]) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    s[b] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const v4i lo = *(const v4i*)(tb + opaque(o.k[b][0]) + 128 * k);
+      const v4i hi = *(const v4i*)(tb + opaque(o.k[b][1]) + 128 * k);
+      s[b] = mma16(v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, qreg[k], s[b]);
+    }
+  }
+}
+
+// O^T[128 w + 16 db, +16][heads] += V^T P^T over the tile's 128 keys.
+__device__ __forceinline__ void dk_pv(const uint8_t* tb, const DkOffsets& o, const v8i& phi, const v8i& plo,
+                                      v4f (&oacc)[8]) {
+  v8i vt;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(tb + o.v[m][0]));
+    vt[2 * m] = x[0];
+    vt[2 * m + 1] = x[1];
+  }
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    v8i vn = vt;
+    if (db < 7) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(tb + o.v[m][db + 1]));
+        vn[2 * m] = x[0];
+        vn[2 * m + 1] = x[1];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    oacc[db] = mma16(vt, phi, oacc[db]);
+    oacc[db] = mma16(vt, plo, oacc[db]);
+    __builtin_amdgcn_sched_barrier(0);
+    vt = vn;
+  }
+}
+
+// Exponents of the wave's 32 keys (8 per lane: block b, reg r = key
+// 32 w + 16 b + 4 g + r of head j) in place; returns the lane's maximum.
+__device__ __forceinline__ float dk_exponents(const uint8_t* smem, int tile, int w, int g, float qs, v4f (&s)[2]) {
+  const float* lam = reinterpret_cast<const float*>(smem + LdsDK::kLam) + tile * kDkRows;
+  const float* ks = reinterpret_cast<const float*>(smem + LdsDK::kKs) + tile * kDkRows;
+  float mt = kNegInf;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int k0 = 32 * w + 16 * b + 4 * g;
+    const v4f lv = *(const v4f*)&lam[k0];
+    const v4f kv = *(const v4f*)&ks[k0];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = s[b][r] * (qs * kv[r]) + lv[r];
+      s[b][r] = e;
+      mt = fmaxf(mt, e);
+    }
+  }
+  return mt;
+}
+
+// P' = 2^(E - Mrun) as fp8 hi + lo into LDS ([head j][key] bytes); l += P' / vds_max.
+__device__ __forceinline__ void dk_probs(uint8_t* smem, int tile, int w, int j, int g, float Mrun, const v4f (&e)[2],
+                                         float& lsum) {
+  const float* inv = reinterpret_cast<const float*>(smem + LdsDK::kInv) + tile * kDkRows;
+  const float Ms = (Mrun == kNegInf) ? 0.f : Mrun;
+  uint8_t* px = smem + LdsDK::kPx + j * kDkPxRow;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int k0 = 32 * w + 16 * b + 4 * g;
+    const v4f iv = *(const v4f*)&inv[k0];
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(e[b][r] - Ms);
+      lsum += p[r] * iv[r];
+    }
+    int hv, lv;
+    split_fp8(p[0], p[1], p[2], p[3], hv, lv);
+    *(int*)(px + k0) = hv;
+    *(int*)(px + 16 * kDkPxRow + k0) = lv;
+  }
+}
+
+// B operands of P V: lane j+16g holds P[head j][keys 32 g .. +31] (hi, lo).
+__device__ __forceinline__ void dk_pread(const uint8_t* smem, int j, int g, v8i& phi, v8i& plo) {
+  const uint8_t* px = smem + LdsDK::kPx + j * kDkPxRow + 32 * g;
+  const v4i h0 = *(const v4i*)px, h1 = *(const v4i*)(px + 16);
+  const v4i l0 = *(const v4i*)(px + 16 * kDkPxRow), l1 = *(const v4i*)(px + 16 * kDkPxRow + 16);
+  phi = v8i{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  plo = v8i{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+}
+
+// Per-head value over the 4 waves (lanes j, j+16, j+32, j+48 of each wave
+// hold head j): the max or the sum.
+__device__ __forceinline__ float dk_heads_reduce(int* misc, int w, int lane, float v, bool is_max) {
+  float o1 = __shfl_xor(v, 16);
+  v = is_max ? fmaxf(v, o1) : v + o1;
+  o1 = __shfl_xor(v, 32);
+  v = is_max ? fmaxf(v, o1) : v + o1;
+  float* red = reinterpret_cast<float*>(misc + 64);
+  if (lane < 16) red[w * 16 + lane] = v;
+  lds_barrier();
+  const int j = lane & 15;
+  const float a0 = red[j], a1 = red[16 + j], a2 = red[32 + j], a3 = red[48 + j];
+  lds_barrier();
+  return is_max ? fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)) : (a0 + a1) + (a2 + a3);
+}
+
+// Runs the unit's keys into (oacc, lsum); `preset` and Mrun as in the split kernel.
+__device__ __forceinline__ void dk_run(const KArgs& a, bool preset, UnitState& us, int* list, int* misc, uint8_t* smem,
+                                       const DkOffsets& o, int w, int lane, const v8i (&qreg)[4], float qs,
+                                       v4f (&oacc)[8], float& Mrun, float& lsum) {
+  using L = LdsDK;
+  const int j = lane & 15, g = lane >> 4;
+  int* flag = misc + 4;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  lsum = 0.f;
+  const uint64_t* kaddr = reinterpret_cast<const uint64_t*>(smem + L::kAddr);
+  for (int c0 = us.kb; c0 < us.ke; c0 += L::kChunk) {
+    const int c1 = min(us.ke, c0 + L::kChunk);
+    cover_chunk(a, us, list, misc, c0, c1);
+    const int nkeys = c1 - c0, tiles = (nkeys + kDkRows - 1) / kDkRows;
+    {
+      const ChunkScales<L> cs = resolve_rows<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
+      lds_barrier();
+      dk_gather(kaddr, 0, dk_rows(nkeys, 0), smem + L::kTiles, w);
+      resolve_scales<L>(cs, smem);
+    }
+    gather_barrier(false);
+    for (int i = 0; i < tiles; ++i) {
+      uint8_t* tb = smem + L::kTiles + (i & 1) * kDkTileBytes;
+      const bool next = i + 1 < tiles;
+      if (next) dk_gather(kaddr, i + 1, dk_rows(nkeys, i + 1), smem + L::kTiles + ((i + 1) & 1) * kDkTileBytes, w);
+      v4f s[2];
+      dk_qk(tb, o, qreg, s);
+      const float mt = dk_exponents(smem, i, w, g, qs, s);
+      if (!preset && c0 == us.kb && i == 0) {   // wave-uniform
+        const float mx = dk_heads_reduce(misc, w, lane, mt, true);
+        Mrun = (mx == kNegInf) ? kNegInf : mx - kPShift;
+      } else if (__ballot(mt > Mrun + kTau)) {
+        *flag = 1;   // would overflow fp8: the unit is redone with a preset reference
+      }
+      dk_probs(smem, i, w, j, g, Mrun, s, lsum);
+      lds_barrier();
+      v8i phi, plo;
+      dk_pread(smem, j, g, phi, plo);
+      dk_pv(tb, o, phi, plo, oacc);
+      gather_barrier(false);   // tile i+1 landed; every wave is done with tile i and with P
+    }
+  }
+}
+
+// Per-head maximum exponent over the unit (S^T only), for the redo pass.
+__device__ __forceinline__ float dk_unit_max(const KArgs& a, UnitState& us, int* list, int* misc, uint8_t* smem,
+                                             const DkOffsets& o, int w, int lane, const v8i (&qreg)[4], float qs) {
+  using L = LdsDK;
+  const int g = lane >> 4;
+  float mx = kNegInf;
+  const uint64_t* kaddr = reinterpret_cast<const uint64_t*>(smem + L::kAddr);
+  for (int c0 = us.kb; c0 < us.ke; c0 += L::kChunk) {
+    const int c1 = min(us.ke, c0 + L::kChunk);
+    cover_chunk(a, us, list, misc, c0, c1);
+    resolve_chunk<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
+    const int nkeys = c1 - c0, tiles = (nkeys + kDkRows - 1) / kDkRows;
+    for (int i = 0; i < tiles; ++i) {
+      dk_gather(kaddr, i, dk_rows(nkeys, i), smem + L::kTiles, w);
+      gather_barrier(false);
+      v4f s[2];
+      dk_qk(smem + L::kTiles, o, qreg, s);
+      mx = fmaxf(mx, dk_exponents(smem, i, w, g, qs, s));
+      lds_barrier();
+    }
+  }
+  return dk_heads_reduce(misc, w, lane, mx, true);
+}
+
+__device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
+  using L = LdsDK;
+  const int lane = (int)threadIdx.x & 63;
+  const int G = ap->grid;
+  const int bid = blockIdx.x;
+  const int lw = (G % 8 == 0) ? ((bid & 7) * (G >> 3) + (bid >> 3)) : bid;  // one XCD per contiguous range
+  const int u_begin = ap->starts[lw], u_end = ap->starts[lw + 1];
+  {
+    const __attribute__((address_space(4))) int* kw = (const __attribute__((address_space(4))) int*)ap;
+    asm volatile("" ::"s"(kw[0]), "s"(kw[16]), "s"(kw[32]), "s"(kw[48]), "s"(kw[64]));
+  }
+  int* list = reinterpret_cast<int*>(smem + L::kList);
+  int* misc = reinterpret_cast<int*>(smem + L::kMisc);
+  const DkOffsets o = dk_offsets(lane, w);
+
+  for (int u = u_begin; u < u_end; ++u) {
+    const KArgs& a = args(ap);
+    const int ngroups = kN1 / a.hg;
+    const int t = u / ngroups, h0 = (u - t * ngroups) * a.hg;
+    const int j = opaque(lane) & 15, g = lane >> 4;
+    const bool real = j < a.hg;                 // head column j holds a real head
+    const int h = h0 + (real ? j : 0);
+    // q fragment: lane j+16g holds q[t, h0+j, 128 k + 32 g .. +31] for K-step k
+    v8i qreg[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qreg[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    float qs = 0.f;
+    if (real) {
+      const uint8_t* qrow = a.q + ((size_t)t * kN1 + h) * kD + 32 * g;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const v4i x0 = *(const v4i*)(qrow + 128 * k);
+        const v4i x1 = *(const v4i*)(qrow + 128 * k + 16);
+        qreg[k] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      }
+      qs = a.scale_log2 * (a.q_ds_per_head ? a.q_ds[(size_t)t * kN1 + h] : a.q_ds[t]);
+    }
+    IdxPre ip;
+    if (a.topk > 0) ip = load_indices(a, t, 0);
+    UnitState us;
+    us.t = t;
+    us.k = token_ctx(a, t);
+    if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
+      for (int x = opaque(lane); x < a.hg * 64; x += 64) {
+        const int hr = h0 + x / 64, d = 8 * (x % 64);
+        if (w == 0) *(v4i*)(a.out + ((size_t)t * kN1 + hr) * kD + d) = v4i{0, 0, 0, 0};
+      }
+      if (a.lse && w == 0 && g == 0 && real) a.lse[(size_t)t * kN1 + h] = kNegInf;
+      continue;
+    }
+    us.n_o = us.k.hi - us.k.lo;
+    us.n_c = 0;
+    us.w_lo = 0;
+    if (a.topk > 0) us.n_c = compact_indices(a, us.k, t, list, misc, 0, ip);
+    else if (a.has_cmp) us.n_c = us.k.vis;
+    us.kb = 0;
+    us.ke = us.n_o + us.n_c;
+
+    v4f oacc[8];
+    float Mrun = kNegInf, lsum = 0.f;
+    for (int pass = 0;; ++pass) {
+      if (threadIdx.x == 0) misc[4] = 0;
+      dk_run(a, pass > 0, us, list, misc, smem, o, w, lane, qreg, qs, oacc, Mrun, lsum);
+      lds_barrier();
+      const int redo = misc[4];
+      lds_barrier();
+      if (!redo || pass > 0) break;
+      const float mx = dk_unit_max(a, us, list, misc, smem, o, w, lane, qreg, qs);
+      Mrun = (mx == kNegInf) ? kNegInf : mx - kPShift;
+    }
+
+    // ---------------- epilogue: normalise, add the sink, bf16 through LDS ----------------
+    const KArgs& ae = args(ap);
+    const float lh = dk_heads_reduce(misc, w, lane, lsum, false);
+    const float sg = (ae.sinks && real) ? ae.sinks[h] * kLog2e : kNegInf;
+    const float Mf = fmaxf(Mrun, sg);
+    float lse_v = kNegInf, sc = 0.f;
+    if (Mf != kNegInf) {
+      const float af = (Mrun == kNegInf) ? 0.f : exp2f(Mrun - Mf);
+      const float Lf = af * lh + ((sg == kNegInf) ? 0.f : exp2f(sg - Mf));
+      sc = af / Lf;
+      lse_v = (Mf + __log2f(Lf)) * kLn2;
+    }
+    if (ae.lse && w == 0 && g == 0 && real) ae.lse[(size_t)t * kN1 + h] = lse_v;
+    // stage [16 heads][512 columns] bf16 (rows padded to 1040 bytes)
+    constexpr int kRow = 2 * kD + 16;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int d = 128 * w + 16 * db + 4 * g;
+      *(uint2*)(smem + j * kRow + 2 * d) = pack_bf16x4(sc * oacc[db][0], sc * oacc[db][1], sc * oacc[db][2], sc * oacc[db][3]);
+    }
+    lds_barrier();
+    // each wave stores head rows w, w+4, ...: a row is 1 KiB = 64 lanes x 16 bytes
+    for (int row = w; row < ae.hg; row += 4) {
+      const v4i x = *(const v4i*)(smem + row * kRow + 16 * lane);
+      *(v4i*)(ae.out + ((size_t)t * kN1 + h0 + row) * kD + 8 * lane) = x;
+    }
+    lds_barrier();
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+dk_kernel(const KArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LdsDK::kBytes];
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  dk_body((KArgPtr)__builtin_amdgcn_kernarg_segment_ptr(), smem, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -1204,6 +1587,10 @@ __global__ void __launch_bounds__(kThreads) debug_resolve_kernel(const KArgs a, 
 
 int launch_forward(const KArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (a.hg > 0) {
+    hipLaunchKernelGGL(dk_kernel, dim3(a.grid), dim3(kThreads), 0, st, a);
+    return (int)hipGetLastError();
+  }
   if (a.scale_mode == 1)
     hipLaunchKernelGGL(attn_kernel<1>, dim3(a.grid), dim3(kThreads), 0, st, a);
   else

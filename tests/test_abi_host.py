@@ -85,7 +85,35 @@ def test_validation_matrix(kw, status):
     assert m.csmla_validate(base_problem(**kw)) == status, m.csmla_last_error()
 
 
-def test_plan_invariants_and_determinism():
+def test_plan_head_split_for_small_decode_batches(monkeypatch):
+    """A 32-token per-token-descale decode batch is planned as 8-head groups
+    over whole key lists: 256 units, one split, no workspace."""
+    monkeypatch.delenv("CSMLA_KERNEL", raising=False)
+    _, md, ws = m.csmla_plan(base_problem())
+    assert md[12] == 8 and md[5] == 1 and md[6] == 32 * 8 and md[7] == 256 and ws == 0
+    _, md, _ = m.csmla_plan(base_problem(batch=128, t1=128))
+    assert md[12] == 16 and md[6] == 128 * 4
+    _, md, _ = m.csmla_plan(base_problem(batch=512, t1=512))
+    assert md[12] == 0                                    # large batches: key split
+    _, md, _ = m.csmla_plan(base_problem(kv_scale_mode=1))
+    assert md[12] == 0                                    # per-tile descales: key split
+    monkeypatch.setenv("CSMLA_KERNEL", "heads16")
+    _, md, _ = m.csmla_plan(base_problem())
+    assert md[12] == 16 and md[6] == 32 * 4
+
+
+def test_forward_rejects_bad_head_group(monkeypatch):
+    monkeypatch.delenv("CSMLA_KERNEL", raising=False)
+    p = base_problem()
+    _, md, ws = m.csmla_plan(p)
+    bad = md.copy(); bad[12] = 4
+    assert m.csmla_forward(p, fake_tensors(ws), bad, raise_on_error=False) == MISMATCH
+    bad = md.copy(); bad[12] = 16          # units no longer match the head group
+    assert m.csmla_forward(p, fake_tensors(ws), bad, raise_on_error=False) == MISMATCH
+
+
+def test_plan_invariants_and_determinism(monkeypatch):
+    monkeypatch.setenv("CSMLA_KERNEL", "split")
     p = base_problem()
     _, md, ws = m.csmla_plan(p)
     assert md[0] == 0x4C4D5343 and md[1] == 1
@@ -144,6 +172,7 @@ def test_plan_rejects_bad_lengths_and_buffers():
 
 
 def test_split_override_from_environment(monkeypatch):
+    monkeypatch.setenv("CSMLA_KERNEL", "split")
     monkeypatch.setenv("CSMLA_SPLITS", "3")
     _, md, ws = m.csmla_plan(base_problem())
     assert md[5] == 3 and md[6] == 96 and ws > 0
@@ -157,7 +186,8 @@ def fake_tensors(ws_bytes=0):
     return t
 
 
-def test_forward_rejects_before_launch():
+def test_forward_rejects_before_launch(monkeypatch):
+    monkeypatch.setenv("CSMLA_KERNEL", "split")   # a plan with a workspace
     p = base_problem()
     _, md, ws = m.csmla_plan(p)
     t = fake_tensors(ws)

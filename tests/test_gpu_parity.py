@@ -21,6 +21,22 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
+# Every test runs with the planner's own kernel choice ("auto": the head-split
+# kernel for small per-token batches, the key-split kernel otherwise) and with
+# each kernel forced, so that both paths meet the same bar on the same cases.
+KERNEL_MODES = ["auto", "split", "heads16"]
+
+
+@pytest.fixture(autouse=True, params=KERNEL_MODES)
+def kernel_mode(request):
+    mode = request.param
+    if mode == "auto":
+        os.environ.pop("CSMLA_KERNEL", None)
+    else:
+        os.environ["CSMLA_KERNEL"] = mode
+    yield mode
+    os.environ.pop("CSMLA_KERNEL", None)
+
 
 def say(msg):
     print(f"[gpu-test] {msg}", flush=True)
@@ -45,7 +61,7 @@ def check(inp_cpu, tokens=None, name="", inp_gpu=None, splits=None, monkeypatch=
         plan = m.Plan(g)
     finally:
         os.environ.pop("CSMLA_SPLITS", None)
-    say(f"  plan splits={plan.splits} grid={plan.grid}; launching")
+    say(f"  plan splits={plan.splits} grid={plan.grid} head_group={plan.head_group}; launching")
     o, l = run_gpu(g, plan)
     stats = compare(o, ref.out, toks, l if inp_cpu.return_lse else None,
                     ref.lse if inp_cpu.return_lse else None, name=name)
@@ -107,7 +123,9 @@ def test_cfg4_csa_mtp_long():
     check_rows(inp, tokens=range(0, 128, 3), name="cfg4")
 
 
-def test_cfg5_csa_prefill_sampled():
+def test_cfg5_csa_prefill_sampled(kernel_mode):
+    if kernel_mode != "auto":
+        pytest.skip("per-tile descales always take the key-split kernel")
     inp_g = make_config(5, device=DEV)
     inp = inp_g.to("cpu")
     T1 = inp.t1
@@ -148,6 +166,7 @@ def test_edge_invalid_duplicate_and_topk_length(kv_scale_mode):
     dict(ori_mask_mode=4, win_left=0, win_right=-1, ori=[129, 64]),
 ])
 def test_edge_mask_modes(case):
+    case = dict(case)
     ori = case.pop("ori")
     r = 7
     cmp = [o // r for o in ori]
