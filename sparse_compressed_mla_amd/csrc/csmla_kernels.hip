@@ -62,7 +62,7 @@ struct Lds {
   static constexpr int kInv = kLam + 4 * kChunk;           // float [kChunk]
   static constexpr int kKs = kInv + 4 * kChunk;            // float [kNks][kChunk]
   static constexpr int kList = kKs + 4 * kNks * kChunk;    // int [kListMax]: compacted cmp indices
-  static constexpr int kMisc = kList + 4 * kListMax;       // [0..3] compaction, [4] redo flag, [64..319] pair values
+  static constexpr int kMisc = kList + 4 * kListMax;       // [0..7] compaction, [8] redo flag, [64..319] pair values
   static constexpr int kBytes = kMisc + 4 * 64 + 4 * 4 * 64;
 };
 static_assert(Lds<0>::kBytes <= 160 * 1024 && Lds<1>::kBytes <= 160 * 1024, "LDS");
@@ -147,6 +147,17 @@ struct Tok {
   int k_eff;       // index slots read
 };
 
+// Uniform loads of the length arrays go through the constant address space
+// (scalar loads; the arrays are read-only for the whole call).  An absent
+// array reads the zero row instead, so that every load of a token's lengths
+// is issued before the first is used: one round trip, no branches.
+typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+
+__device__ __forceinline__ int ld_len(const int32_t* p, int i) {
+  const int32_t* q = p ? p : reinterpret_cast<const int32_t*>(g_zero_row);
+  return ((ConstI32)q)[p ? i : 0];
+}
+
 __device__ __forceinline__ Tok token_ctx(const KArgs& a, int t) {
   Tok k;
   int b, q0, span;
@@ -154,30 +165,33 @@ __device__ __forceinline__ Tok token_ctx(const KArgs& a, int t) {
     int lo = 0, hi = a.batch;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (a.cu_q[mid] <= t) lo = mid; else hi = mid;
+      if (((ConstI32)a.cu_q)[mid] <= t) lo = mid; else hi = mid;
     }
-    b = lo; q0 = a.cu_q[b]; span = a.cu_q[b + 1] - q0;
+    b = lo;
+    q0 = ((ConstI32)a.cu_q)[b];
+    span = ((ConstI32)a.cu_q)[b + 1] - q0;
   } else {
     b = t / a.q_s; q0 = b * a.q_s; span = a.q_s;
   }
+  const int v_su_q = ld_len(a.su_q, b), v_su_ori = ld_len(a.su_ori, b);
+  const int v_cu_o0 = ld_len(a.cu_ori, b), v_cu_o1 = ld_len(a.cu_ori, b + 1);
+  const int v_su_cmp = ld_len(a.su_cmp, b);
+  const int v_cu_c0 = ld_len(a.cu_cmp, b), v_cu_c1 = ld_len(a.cu_cmp, b + 1);
+  const int v_res = ld_len(a.res, b), v_tkl = ld_len(a.topk_len, t);
   const int i = t - q0;
-  int s1 = span;
-  if (a.su_q) s1 = min(span, a.su_q[b]);
-  int s2;
-  if (a.su_ori) s2 = a.su_ori[b];
-  else if (a.cu_ori) s2 = a.cu_ori[b + 1] - a.cu_ori[b];
-  else s2 = a.ori_s;
-  k.kv0 = (a.layout_kv == 1) ? a.cu_ori[b] : 0;
+  const int s1 = a.su_q ? min(span, v_su_q) : span;
+  const int s2 = a.su_ori ? v_su_ori : (a.cu_ori ? v_cu_o1 - v_cu_o0 : a.ori_s);
+  k.kv0 = (a.layout_kv == 1) ? v_cu_o0 : 0;
   int c = 0;
   k.cmp0 = 0;
   if (a.has_cmp) {
-    if (a.su_cmp) c = a.su_cmp[b];
-    else if (a.cu_cmp) c = a.cu_cmp[b + 1] - a.cu_cmp[b];
+    if (a.su_cmp) c = v_su_cmp;
+    else if (a.cu_cmp) c = v_cu_c1 - v_cu_c0;
     else if (a.layout_kv == 0) c = a.cmp_s;
     else c = s2 / a.cmp_ratio;
-    if (a.layout_kv == 1) k.cmp0 = a.cu_cmp[b];
+    if (a.layout_kv == 1) k.cmp0 = v_cu_c0;
   }
-  const int64_t res = a.res ? a.res[b] : 0;
+  const int64_t res = a.res ? v_res : 0;
   k.b = b; k.i = i; k.s1 = s1; k.s2 = s2; k.c = c;
   k.valid = i < s1;
   const int64_t p = (int64_t)s2 - s1 + i;  // bottom-right aligned position
@@ -196,7 +210,7 @@ __device__ __forceinline__ Tok token_ctx(const KArgs& a, int t) {
   }
   k.vis = a.has_cmp ? vis : 0;
   int ke = a.topk;
-  if (a.topk_len) ke = max(0, min(ke, a.topk_len[t]));
+  if (a.topk_len) ke = max(0, min(ke, v_tkl));
   k.k_eff = ke;
   if (!k.valid) { k.lo = k.hi = 0; k.vis = 0; k.k_eff = 0; }
   return k;
@@ -232,26 +246,29 @@ __device__ __forceinline__ int compact_indices(const KArgs& a, const Tok& k, int
                                                const IdxPre& first) {
   const int tid = opaque((int)threadIdx.x);
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int base = 0;
+  int base = 0, parity = 0;
   for (int s0 = 0; s0 < k.k_eff; s0 += kIdxPre) {
     const IdxPre cur = (s0 == 0) ? first : load_indices(a, t, s0);
 #pragma unroll
     for (int m = 0; m < kIdxRounds; ++m) {
+      if (s0 + m * kThreads >= k.k_eff) break;   // wave-uniform
       const int slot = s0 + m * kThreads + tid;
       const bool ok = (slot < k.k_eff) && (cur.v[m] >= 0) && (cur.v[m] < k.vis);
       const uint64_t bal = __ballot(ok);
       const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == 0) wtot[w] = __popcll(bal);
+      int* wt = wtot + 4 * parity;   // the wave totals alternate between two slots,
+      parity ^= 1;                   // so one barrier per round suffices
+      if (lane == 0) wt[w] = __popcll(bal);
       lds_barrier();
       int off = 0;
-      for (int j = 0; j < w; ++j) off += wtot[j];
-      const int tot = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+      for (int j = 0; j < w; ++j) off += wt[j];
+      const int tot = wt[0] + wt[1] + wt[2] + wt[3];
       const int pos = base + off + pre;
       if (ok && pos >= w_lo && pos < w_lo + kListMax) list[pos - w_lo] = cur.v[m];
       base += tot;
-      lds_barrier();
     }
   }
+  lds_barrier();   // the list is complete
   return base;
 }
 
@@ -848,7 +865,7 @@ __device__ __forceinline__ void run_unit(KArgPtr ap, bool preset, UnitState& us,
                                          const LaneOffsets& o, const WaveCtx& c, const v8i (&qreg)[4],
                                          v16f (&oacc)[8], float& Mrun, float& lsum) {
   using L = Lds<PER_TILE>;
-  int* flag = misc + 4;
+  int* flag = misc + 8;
 #pragma unroll
   for (int j = 0; j < 8; ++j) oacc[j] = v16f{};
   lsum = 0.f;
@@ -954,8 +971,11 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
     us.t = u / a.splits;
     const int s = u - us.t * a.splits;
     const int t = us.t;
-    // query fragment (B operand of S^T = K Q^T for d in [256 dh + 64 s4 + 32 g, +32))
-    // and descale: loaded before the lengths, nothing depends on them
+    // every load of the unit's prologue is issued before any is used: index
+    // slots, the query fragment (B operand of S^T = K Q^T for d in
+    // [256 dh + 64 s4 + 32 g, +32)), its descale, and the lengths
+    IdxPre ip;
+    if (a.topk > 0) ip = load_indices(a, t, 0);
     v8i qreg[4];
     {
       const uint8_t* qrow = a.q + ((size_t)t * kN1 + h) * kD + 256 * dh + 32 * g;
@@ -967,10 +987,8 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
       }
     }
     const float qd = a.q_ds_per_head ? a.q_ds[(size_t)t * kN1 + h] : a.q_ds[t];
-    c.qs = a.scale_log2 * qd;
-    IdxPre ip;
-    if (a.topk > 0) ip = load_indices(a, t, 0);
     us.k = token_ctx(a, t);
+    c.qs = a.scale_log2 * qd;
     if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
       if (a.splits == 1) {
         for (int x = opaque(lane); x < 32 * 64; x += 64) {
@@ -999,10 +1017,10 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
     v16f oacc[8];
     float Mrun = kNegInf, lsum = 0.f;
     for (int pass = 0;; ++pass) {
-      if (tid == 0) misc[4] = 0;
+      if (tid == 0) misc[8] = 0;
       run_unit<PER_TILE>(ap, pass > 0, us, list, misc, smem, o, c, qreg, oacc, Mrun, lsum);
       lds_barrier();
-      const int redo = misc[4];
+      const int redo = misc[8];
       lds_barrier();
       if (!redo || pass > 0) break;
       // recompute with the reference preset from the unit's true maximum
@@ -1100,7 +1118,7 @@ struct LdsDK {
   static constexpr int kKs = kInv + 4 * kChunk;                // float [kChunk]
   static constexpr int kPx = kKs + 4 * kChunk;                 // fp8 P: [hi, lo][16 heads][kDkPxRow]
   static constexpr int kList = kPx + 2 * 16 * kDkPxRow;        // int [kListMax]
-  static constexpr int kMisc = kList + 4 * kListMax;           // [0..3] compaction, [4] redo flag, [64..] reductions
+  static constexpr int kMisc = kList + 4 * kListMax;           // [0..7] compaction, [8] redo flag, [64..] reductions
   static constexpr int kBytes = kMisc + 4 * 64 + 4 * 4 * 64;
 };
 static_assert(LdsDK::kBytes <= 160 * 1024, "LDS");
@@ -1109,20 +1127,23 @@ __device__ __forceinline__ v4f mma16(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// Gather rows [0, 128) of chunk tile `tile` (128 keys) into a tile buffer:
-// wave w covers rows [32 w, +32) with 16 instructions of 2 rows; pairs past
-// `nrows` are zeroed.  A full tile issues exactly 16 loads per wave.
-__device__ __forceinline__ void dk_gather(const uint64_t* kaddr, int tile, int nrows, uint8_t* tb, int w) {
+// Gather half `half` (rows [64 half, +64)) of chunk tile `tile` (128 keys)
+// into a tile buffer: wave w covers rows [64 half + 16 w, +16) with 8
+// instructions of 2 rows; pairs past `nrows` are zeroed.  A tile is gathered
+// in two halves issued at different points of a step, because the hardware
+// holds back a wave's LDS-DMA loads once about a dozen are in flight.
+__device__ __forceinline__ void dk_gather(const uint64_t* kaddr, int tile, int half, int nrows, uint8_t* tb, int w) {
   const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
-  uint64_t src[16];
+  const int rb = 64 * half + 16 * w;
+  uint64_t src[8];
 #pragma unroll
-  for (int mi = 0; mi < 16; ++mi) {
-    const int r = 32 * w + 2 * mi + g;
+  for (int mi = 0; mi < 8; ++mi) {
+    const int r = rb + 2 * mi + g;
     src[mi] = kaddr[tile * kDkRows + r] + 16u * (uint32_t)(li ^ swz(r));
   }
 #pragma unroll
-  for (int mi = 0; mi < 16; ++mi) {
-    const int r0 = 32 * w + 2 * mi;
+  for (int mi = 0; mi < 8; ++mi) {
+    const int r0 = rb + 2 * mi;
     if (r0 < nrows) {
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + r0 * kD));
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src[mi]) : "m0");
@@ -1159,17 +1180,32 @@ __device__ __forceinline__ DkOffsets dk_offsets(int lane, int w) {
   return o;
 }
 
-// S^T blocks (16 keys x 16 heads) of the wave's 32 keys, full D.
+// S^T blocks (16 keys x 16 heads) of the wave's 32 keys, full D; the two
+// blocks' MFMA chains interleave, and the next K-step's operands are read
+// while the current ones multiply.
+__device__ __forceinline__ v8i dk_kop(const uint8_t* tb, const DkOffsets& o, int b, int k) {
+  const v4i lo = *(const v4i*)(tb + o.k[b][0] + 128 * k);
+  const v4i hi = *(const v4i*)(tb + o.k[b][1] + 128 * k);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 __device__ __forceinline__ void dk_qk(const uint8_t* tb, const DkOffsets& o, const v8i (&qreg)[4], v4f (&s)[2]) {
+  s[0] = v4f{0.f, 0.f, 0.f, 0.f};
+  s[1] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8i a0 = dk_kop(tb, o, 0, 0), a1 = dk_kop(tb, o, 1, 0);
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    s[b] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const v4i lo = *(const v4i*)(tb + opaque(o.k[b][0]) + 128 * k);
-      const v4i hi = *(const v4i*)(tb + opaque(o.k[b][1]) + 128 * k);
-      s[b] = mma16(v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, qreg[k], s[b]);
+  for (int k = 0; k < 4; ++k) {
+    v8i n0 = a0, n1 = a1;
+    if (k < 3) {
+      n0 = dk_kop(tb, o, 0, k + 1);
+      n1 = dk_kop(tb, o, 1, k + 1);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    s[0] = mma16(a0, qreg[k], s[0]);
+    s[1] = mma16(a1, qreg[k], s[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    a0 = n0;
+    a1 = n1;
   }
 }
 
@@ -1277,7 +1313,7 @@ __device__ __forceinline__ void dk_run(const KArgs& a, bool preset, UnitState& u
                                        v4f (&oacc)[8], float& Mrun, float& lsum) {
   using L = LdsDK;
   const int j = lane & 15, g = lane >> 4;
-  int* flag = misc + 4;
+  int* flag = misc + 8;
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db] = v4f{0.f, 0.f, 0.f, 0.f};
   lsum = 0.f;
@@ -1289,14 +1325,16 @@ __device__ __forceinline__ void dk_run(const KArgs& a, bool preset, UnitState& u
     {
       const ChunkScales<L> cs = resolve_rows<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
       lds_barrier();
-      dk_gather(kaddr, 0, dk_rows(nkeys, 0), smem + L::kTiles, w);
+      dk_gather(kaddr, 0, 0, dk_rows(nkeys, 0), smem + L::kTiles, w);
+      dk_gather(kaddr, 0, 1, dk_rows(nkeys, 0), smem + L::kTiles, w);
       resolve_scales<L>(cs, smem);
     }
     gather_barrier(false);
     for (int i = 0; i < tiles; ++i) {
       uint8_t* tb = smem + L::kTiles + (i & 1) * kDkTileBytes;
       const bool next = i + 1 < tiles;
-      if (next) dk_gather(kaddr, i + 1, dk_rows(nkeys, i + 1), smem + L::kTiles + ((i + 1) & 1) * kDkTileBytes, w);
+      uint8_t* tn = smem + L::kTiles + ((i + 1) & 1) * kDkTileBytes;
+      if (next) dk_gather(kaddr, i + 1, 0, dk_rows(nkeys, i + 1), tn, w);
       v4f s[2];
       dk_qk(tb, o, qreg, s);
       const float mt = dk_exponents(smem, i, w, g, qs, s);
@@ -1307,6 +1345,7 @@ __device__ __forceinline__ void dk_run(const KArgs& a, bool preset, UnitState& u
         *flag = 1;   // would overflow fp8: the unit is redone with a preset reference
       }
       dk_probs(smem, i, w, j, g, Mrun, s, lsum);
+      if (next) dk_gather(kaddr, i + 1, 1, dk_rows(nkeys, i + 1), tn, w);
       lds_barrier();
       v8i phi, plo;
       dk_pread(smem, j, g, phi, plo);
@@ -1329,7 +1368,8 @@ __device__ __forceinline__ float dk_unit_max(const KArgs& a, UnitState& us, int*
     resolve_chunk<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
     const int nkeys = c1 - c0, tiles = (nkeys + kDkRows - 1) / kDkRows;
     for (int i = 0; i < tiles; ++i) {
-      dk_gather(kaddr, i, dk_rows(nkeys, i), smem + L::kTiles, w);
+      dk_gather(kaddr, i, 0, dk_rows(nkeys, i), smem + L::kTiles, w);
+      dk_gather(kaddr, i, 1, dk_rows(nkeys, i), smem + L::kTiles, w);
       gather_barrier(false);
       v4f s[2];
       dk_qk(smem + L::kTiles, o, qreg, s);
@@ -1355,18 +1395,22 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
   int* misc = reinterpret_cast<int*>(smem + L::kMisc);
   const DkOffsets o = dk_offsets(lane, w);
 
+  const KArgs& a = *(const KArgs*)ap;   // few live values here: no per-unit reload needed
   for (int u = u_begin; u < u_end; ++u) {
-    const KArgs& a = args(ap);
     const int ngroups = kN1 / a.hg;
     const int t = u / ngroups, h0 = (u - t * ngroups) * a.hg;
     const int j = opaque(lane) & 15, g = lane >> 4;
     const bool real = j < a.hg;                 // head column j holds a real head
     const int h = h0 + (real ? j : 0);
-    // q fragment: lane j+16g holds q[t, h0+j, 128 k + 32 g .. +31] for K-step k
+    // every load of the unit's prologue is issued before any is used:
+    // index slots, the q fragment (lane j+16g: q[t, h0+j, 128 k + 32 g .. +31]
+    // for K-step k), its descale, and the lengths
+    IdxPre ip;
+    if (a.topk > 0) ip = load_indices(a, t, 0);
     v8i qreg[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) qreg[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    float qs = 0.f;
+    float qd = 0.f;
     if (real) {
       const uint8_t* qrow = a.q + ((size_t)t * kN1 + h) * kD + 32 * g;
 #pragma unroll
@@ -1375,13 +1419,12 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
         const v4i x1 = *(const v4i*)(qrow + 128 * k + 16);
         qreg[k] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
-      qs = a.scale_log2 * (a.q_ds_per_head ? a.q_ds[(size_t)t * kN1 + h] : a.q_ds[t]);
+      qd = a.q_ds_per_head ? a.q_ds[(size_t)t * kN1 + h] : a.q_ds[t];
     }
-    IdxPre ip;
-    if (a.topk > 0) ip = load_indices(a, t, 0);
     UnitState us;
     us.t = t;
     us.k = token_ctx(a, t);
+    const float qs = a.scale_log2 * qd;
     if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
       for (int x = opaque(lane); x < a.hg * 64; x += 64) {
         const int hr = h0 + x / 64, d = 8 * (x % 64);
@@ -1401,10 +1444,10 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     v4f oacc[8];
     float Mrun = kNegInf, lsum = 0.f;
     for (int pass = 0;; ++pass) {
-      if (threadIdx.x == 0) misc[4] = 0;
+      if (threadIdx.x == 0) misc[8] = 0;
       dk_run(a, pass > 0, us, list, misc, smem, o, w, lane, qreg, qs, oacc, Mrun, lsum);
       lds_barrier();
-      const int redo = misc[4];
+      const int redo = misc[8];
       lds_barrier();
       if (!redo || pass > 0) break;
       const float mx = dk_unit_max(a, us, list, misc, smem, o, w, lane, qreg, qs);
@@ -1412,7 +1455,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     }
 
     // ---------------- epilogue: normalise, add the sink, bf16 through LDS ----------------
-    const KArgs& ae = args(ap);
+    const KArgs& ae = a;
     const float lh = dk_heads_reduce(misc, w, lane, lsum, false);
     const float sg = (ae.sinks && real) ? ae.sinks[h] * kLog2e : kNegInf;
     const float Mf = fmaxf(Mrun, sg);
@@ -1558,7 +1601,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const KArgs a) {
 __global__ void __launch_bounds__(kThreads) debug_resolve_kernel(const KArgs a, int32_t* keys, int32_t* counts,
                                                                  int32_t max_keys) {
   __shared__ int list[kListMax];
-  __shared__ int wtot[4];
+  __shared__ int wtot[8];
   const int t = blockIdx.x;
   const Tok k = token_ctx(a, t);
   const int n_o = k.hi - k.lo;
