@@ -7,8 +7,9 @@ length 8192 with a 128-token band (left 127, right 0), cmp_ratio 4 (2048
 compressed tokens) and 512 top-k indices per token drawn uniformly without
 replacement, sinks ~ N(0,1).  Synthetic, seeded data.
 
-A step is one csmla_forward (planned split attention + split-KV combine)
-over one batch.  The KV pools are replicated over --layers distinct copies
+A step is one csmla_forward over one batch: as planned for this shape, the
+head-split kernel alone (groups of 8 heads over whole key lists), or split
+attention followed by the split-KV combine.  The KV pools are replicated over --layers distinct copies
 and step k reads copy k % layers, as consecutive layers of a model would:
 every step's KV rows come from HBM, not from the 256 MB Infinity Cache.
 Block tables, indices and q are shared by the copies.  The plan is made
@@ -62,6 +63,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing sample")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain device-to-device copies of 512 MiB (the reference kernel that scales "
+                         "the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -72,6 +76,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = 512 << 20
+        src = torch.full((n,), 7, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+        return
+
     import sparse_compressed_mla_amd as m
     from workloads import make_config
 
@@ -210,7 +225,8 @@ def main():
         "plan_host_us": round(1e6 * t_plan / reps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("csa_decode"),
-                     "kernel": "csmla_forward (attention + split-KV combine)"},
+                     "kernel": ("dk_kernel (head-split attention, whole key lists)" if plan.head_group > 0
+                                else "attn_kernel<0> + combine_kernel (split attention, split-KV combine)")},
     }
 
     # ---- CPU baseline: the oracle as it stands, on a bounded sample ----
