@@ -147,37 +147,56 @@ struct Tok {
   int k_eff;       // index slots read
 };
 
-// Uniform loads of the length arrays go through the constant address space
-// (scalar loads; the arrays are read-only for the whole call).  An absent
-// array reads the zero row instead, so that every load of a token's lengths
-// is issued before the first is used: one round trip, no branches.
+// A token's lengths: one load per array, all issued before the first is
+// used.  They are vector loads of a uniform address (the lane index is
+// laundered so that the compiler keeps them in the vector memory pipe): those
+// complete in order, so the unit's later loads need not have landed when the
+// lengths are used, which scalar loads (completing out of order) would
+// require.  An absent array reads the zero row instead.  The TND batch
+// lookup (a binary search over cu_seqlens_q) stays scalar.
 typedef const __attribute__((address_space(4))) int32_t* ConstI32;
 
-__device__ __forceinline__ int ld_len(const int32_t* p, int i) {
+__device__ __forceinline__ int ld_len(const int32_t* p, int i, int zero) {
   const int32_t* q = p ? p : reinterpret_cast<const int32_t*>(g_zero_row);
-  return ((ConstI32)q)[p ? i : 0];
+  return q[(p ? i : 0) + zero];
 }
 
-__device__ __forceinline__ Tok token_ctx(const KArgs& a, int t) {
-  Tok k;
+struct TokLens {
   int b, q0, span;
+  int su_q, su_ori, cu_o0, cu_o1, su_cmp, cu_c0, cu_c1, res, tkl;
+};
+
+__device__ __forceinline__ TokLens token_lens(const KArgs& a, int t) {
+  TokLens l;
   if (a.layout_q == 1) {  // TND: largest b with cu_q[b] <= t
     int lo = 0, hi = a.batch;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (((ConstI32)a.cu_q)[mid] <= t) lo = mid; else hi = mid;
     }
-    b = lo;
-    q0 = ((ConstI32)a.cu_q)[b];
-    span = ((ConstI32)a.cu_q)[b + 1] - q0;
+    l.b = lo;
+    l.q0 = ((ConstI32)a.cu_q)[lo];
+    l.span = ((ConstI32)a.cu_q)[lo + 1] - l.q0;
   } else {
-    b = t / a.q_s; q0 = b * a.q_s; span = a.q_s;
+    l.b = t / a.q_s; l.q0 = l.b * a.q_s; l.span = a.q_s;
   }
-  const int v_su_q = ld_len(a.su_q, b), v_su_ori = ld_len(a.su_ori, b);
-  const int v_cu_o0 = ld_len(a.cu_ori, b), v_cu_o1 = ld_len(a.cu_ori, b + 1);
-  const int v_su_cmp = ld_len(a.su_cmp, b);
-  const int v_cu_c0 = ld_len(a.cu_cmp, b), v_cu_c1 = ld_len(a.cu_cmp, b + 1);
-  const int v_res = ld_len(a.res, b), v_tkl = ld_len(a.topk_len, t);
+  const int z = opaque(0), b = l.b;
+  l.su_q = ld_len(a.su_q, b, z); l.su_ori = ld_len(a.su_ori, b, z);
+  l.cu_o0 = ld_len(a.cu_ori, b, z); l.cu_o1 = ld_len(a.cu_ori, b + 1, z);
+  l.su_cmp = ld_len(a.su_cmp, b, z);
+  l.cu_c0 = ld_len(a.cu_cmp, b, z); l.cu_c1 = ld_len(a.cu_cmp, b + 1, z);
+  l.res = ld_len(a.res, b, z); l.tkl = ld_len(a.topk_len, t, z);
+  return l;
+}
+
+__device__ __forceinline__ Tok token_ctx(const KArgs& a, int t, const TokLens& l) {
+  Tok k;
+  const int b = l.b, q0 = l.q0, span = l.span;
+  const int v_su_q = __builtin_amdgcn_readfirstlane(l.su_q), v_su_ori = __builtin_amdgcn_readfirstlane(l.su_ori);
+  const int v_cu_o0 = __builtin_amdgcn_readfirstlane(l.cu_o0), v_cu_o1 = __builtin_amdgcn_readfirstlane(l.cu_o1);
+  const int v_su_cmp = __builtin_amdgcn_readfirstlane(l.su_cmp);
+  const int v_cu_c0 = __builtin_amdgcn_readfirstlane(l.cu_c0), v_cu_c1 = __builtin_amdgcn_readfirstlane(l.cu_c1);
+  const int v_res = __builtin_amdgcn_readfirstlane(l.res), v_tkl = __builtin_amdgcn_readfirstlane(l.tkl);
   const int i = t - q0;
   const int s1 = a.su_q ? min(span, v_su_q) : span;
   const int s2 = a.su_ori ? v_su_ori : (a.cu_ori ? v_cu_o1 - v_cu_o0 : a.ori_s);
@@ -216,6 +235,8 @@ __device__ __forceinline__ Tok token_ctx(const KArgs& a, int t) {
   return k;
 }
 
+__device__ __forceinline__ Tok token_ctx(const KArgs& a, int t) { return token_ctx(a, t, token_lens(a, t)); }
+
 // The first kIdxPre index slots of token t, one value per thread per round,
 // loaded before the token's lengths are known (bounded by topk, not by the
 // effective length), so that these loads share a round trip with them.
@@ -226,14 +247,18 @@ struct IdxPre {
   int v[kIdxRounds];
 };
 
+// Branch-free: slots past topk read a valid slot (or the zero row when
+// there are no indices) and are then replaced by -1.
 __device__ __forceinline__ IdxPre load_indices(const KArgs& a, int t, int s0) {
   IdxPre p;
-  const int* row = a.idx + (size_t)t * a.topk;
+  const int* row = a.topk > 0 ? a.idx + (size_t)t * a.topk : reinterpret_cast<const int*>(g_zero_row);
+  const int last = max(a.topk - 1, 0);
   const int tid = opaque((int)threadIdx.x);
 #pragma unroll
   for (int m = 0; m < kIdxRounds; ++m) {
     const int slot = s0 + m * kThreads + tid;
-    p.v[m] = (slot < a.topk) ? row[slot] : -1;
+    const int v = row[min(slot, last)];
+    p.v[m] = (slot < a.topk) ? v : -1;
   }
   return p;
 }
@@ -290,29 +315,58 @@ __device__ __forceinline__ int key_pos(const KArgs& a, const Tok& k, int n_o, in
   return (a.topk > 0) ? list[key - n_o - w_lo] : key - n_o;
 }
 
-__device__ __forceinline__ int64_t row_of(const KArgs& a, const Tok& k, bool is_cmp, int j, int blk) {
+// The two caches' attributes as uniform registers.  A per-key choice
+// between them is then a register select; written as a choice between
+// kernel-argument fields, it compiles to a per-lane load from the argument
+// segment on every key.
+struct Side {
+  const uint8_t* kv;
+  const float* ds;
+  const int32_t* tab;
+  int bs, cols, s;
+};
+struct Sides {
+  Side o, c;   // ori_kv, cmp_kv
+};
+
+template <class T>
+__device__ __forceinline__ T pin_s(T v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+__device__ __forceinline__ Sides cache_sides(const KArgs& a) {
+  Sides x;
+  x.o.kv = pin_s(a.ori_kv); x.o.ds = pin_s(a.ori_ds); x.o.tab = pin_s(a.ori_tab);
+  x.o.bs = pin_s(a.ori_bs); x.o.cols = pin_s(a.ori_cols); x.o.s = pin_s(a.ori_s);
+  x.c.kv = pin_s(a.cmp_kv); x.c.ds = pin_s(a.cmp_ds); x.c.tab = pin_s(a.cmp_tab);
+  x.c.bs = pin_s(a.cmp_bs); x.c.cols = pin_s(a.cmp_cols); x.c.s = pin_s(a.cmp_s);
+  return x;
+}
+
+__device__ __forceinline__ int64_t row_of(const KArgs& a, const Sides& sd, const Tok& k, bool is_cmp, int j, int blk) {
   if (a.layout_kv == 2) {
-    const int bs = is_cmp ? a.cmp_bs : a.ori_bs;
+    const int bs = is_cmp ? sd.c.bs : sd.o.bs;
     return (int64_t)blk * bs + (j % bs);
   }
   if (a.layout_kv == 1) return (int64_t)(is_cmp ? k.cmp0 : k.kv0) + j;
-  return (int64_t)k.b * (is_cmp ? a.cmp_s : a.ori_s) + j;
+  return (int64_t)k.b * (is_cmp ? sd.c.s : sd.o.s) + j;
 }
 
-__device__ __forceinline__ int block_of(const KArgs& a, const Tok& k, bool is_cmp, int j) {
-  const int bs = is_cmp ? a.cmp_bs : a.ori_bs;
-  const int* tab = is_cmp ? a.cmp_tab : a.ori_tab;
-  const int cols = is_cmp ? a.cmp_cols : a.ori_cols;
+__device__ __forceinline__ int block_of(const Sides& sd, const Tok& k, bool is_cmp, int j) {
+  const int bs = is_cmp ? sd.c.bs : sd.o.bs;
+  const int32_t* tab = is_cmp ? sd.c.tab : sd.o.tab;
+  const int cols = is_cmp ? sd.c.cols : sd.o.cols;
   return tab[(size_t)k.b * cols + j / bs];
 }
 
 // Row of key `key` for the debug export (same resolution code).
-__device__ __forceinline__ int64_t resolve_row(const KArgs& a, const Tok& k, int n_o, int key, const int* list,
-                                               int w_lo) {
+__device__ __forceinline__ int64_t resolve_row(const KArgs& a, const Sides& sd, const Tok& k, int n_o, int key,
+                                               const int* list, int w_lo) {
   bool is_cmp;
   const int j = key_pos(a, k, n_o, key, list, w_lo, is_cmp);
-  const int blk = (a.layout_kv == 2) ? block_of(a, k, is_cmp, j) : 0;
-  return row_of(a, k, is_cmp, j, blk);
+  const int blk = (a.layout_kv == 2) ? block_of(sd, k, is_cmp, j) : 0;
+  return row_of(a, sd, k, is_cmp, j, blk);
 }
 
 // Resolving the keys [c0, c1) of a unit into the chunk arrays takes two
@@ -335,6 +389,7 @@ __device__ __forceinline__ ChunkScales<L> resolve_rows(const KArgs& a, const Tok
   constexpr int M = L::kChunk / kThreads, NKS = L::kNks;
   uint64_t* kaddr = reinterpret_cast<uint64_t*>(smem + L::kAddr);
   const int tid = opaque((int)threadIdx.x);
+  const Sides sd = cache_sides(a);
   ChunkScales<L> cs;
   int j[M], blk[M];
   bool cmp[M];
@@ -349,7 +404,7 @@ __device__ __forceinline__ ChunkScales<L> resolve_rows(const KArgs& a, const Tok
   if (a.layout_kv == 2) {
 #pragma unroll
     for (int m = 0; m < M; ++m)
-      if (cs.ok[m]) blk[m] = block_of(a, k, cmp[m], j[m]);
+      if (cs.ok[m]) blk[m] = block_of(sd, k, cmp[m], j[m]);
   }
 #pragma unroll
   for (int m = 0; m < M; ++m) {
@@ -357,9 +412,9 @@ __device__ __forceinline__ ChunkScales<L> resolve_rows(const KArgs& a, const Tok
 #pragma unroll
     for (int c = 0; c < NKS; ++c) cs.ds[m][c] = 0.f;
     if (cs.ok[m]) {
-      const int64_t row = row_of(a, k, cmp[m], j[m], blk[m]);
-      addr = (uint64_t)(uintptr_t)((cmp[m] ? a.cmp_kv : a.ori_kv) + row * kD);
-      const float* dsp = cmp[m] ? a.cmp_ds : a.ori_ds;
+      const int64_t row = row_of(a, sd, k, cmp[m], j[m], blk[m]);
+      addr = (uint64_t)(uintptr_t)((cmp[m] ? sd.c.kv : sd.o.kv) + row * kD);
+      const float* dsp = cmp[m] ? sd.c.ds : sd.o.ds;
       if constexpr (L::kPerTile) {
         const v4f x0 = *(const v4f*)(dsp + row * 8);
         const v4f x1 = *(const v4f*)(dsp + row * 8 + 4);
@@ -458,6 +513,9 @@ __device__ __forceinline__ void wait_all_and_sync() {
 // Work-group barrier after which the older of the wave's gathers has landed:
 // with `newer_full` set, the 8 loads of the most recent gather (a full tile)
 // may still be in flight; otherwise every load is waited for.
+// s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt unconstrained.
+constexpr int kWaitVm0 = 0x0F70;
+
 __device__ __forceinline__ void gather_barrier(bool newer_full) {
   if (newer_full) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -965,17 +1023,21 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
   const LaneOffsets o = lane_offsets(lane, dh);
 
   for (int u = u_begin; u < u_end; ++u) {
+    // Settles every load of the previous unit here, where nothing of this
+    // unit is in flight yet; without it the compiler guards registers reused
+    // across units with a wait placed after this unit's first loads.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     const KArgs& a = args(ap);
     const int h = 32 * hh + (opaque(lane) & 31);   // the lane's head, recomputed per unit
     UnitState us;
     us.t = u / a.splits;
     const int s = u - us.t * a.splits;
     const int t = us.t;
-    // every load of the unit's prologue is issued before any is used: index
-    // slots, the query fragment (B operand of S^T = K Q^T for d in
-    // [256 dh + 64 s4 + 32 g, +32)), its descale, and the lengths
-    IdxPre ip;
-    if (a.topk > 0) ip = load_indices(a, t, 0);
+    // every load of the unit's prologue is issued before any is used: the
+    // lengths, index slots, the query fragment (B operand of S^T = K Q^T for
+    // d in [256 dh + 64 s4 + 32 g, +32)) and its descale
+    const TokLens tl = token_lens(a, t);
+    const IdxPre ip = load_indices(a, t, 0);
     v8i qreg[4];
     {
       const uint8_t* qrow = a.q + ((size_t)t * kN1 + h) * kD + 256 * dh + 32 * g;
@@ -986,8 +1048,8 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
         qreg[s4] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
     }
-    const float qd = a.q_ds_per_head ? a.q_ds[(size_t)t * kN1 + h] : a.q_ds[t];
-    us.k = token_ctx(a, t);
+    const float qd = a.q_ds[a.q_ds_per_head ? (size_t)t * kN1 + h : (size_t)t];
+    us.k = token_ctx(a, t, tl);
     c.qs = a.scale_log2 * qd;
     if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
       if (a.splits == 1) {
@@ -1127,33 +1189,72 @@ __device__ __forceinline__ v4f mma16(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// Gather half `half` (rows [64 half, +64)) of chunk tile `tile` (128 keys)
-// into a tile buffer: wave w covers rows [64 half + 16 w, +16) with 8
-// instructions of 2 rows; pairs past `nrows` are zeroed.  A tile is gathered
-// in two halves issued at different points of a step, because the hardware
-// holds back a wave's LDS-DMA loads once about a dozen are in flight.
-__device__ __forceinline__ void dk_gather(const uint64_t* kaddr, int tile, int half, int nrows, uint8_t* tb, int w) {
+// Gather of chunk tile `tile` (128 keys) into a tile buffer in two halves
+// of 64 rows: in half `half`, wave w covers rows [64 half + 16 w, +16) with 8
+// instructions of 2 rows.  Every slot of a chunk holds a row address (slots
+// past the chunk end hold the zero row), so a tile is always loaded whole.
+// The source addresses are formed first (DkSrc), and the instructions are
+// then issued one at a time between the MFMAs of a step: the hardware holds
+// back a wave's LDS-DMA loads once about a dozen are in flight, and a wave
+// stalled on an issue would leave its matrix core idle.
+struct DkSrc {
+  uint64_t p[8];
+};
+
+// All LDS reads of the addresses are issued before the first is used, so
+// that forming them costs one LDS round trip.
+__device__ __forceinline__ DkSrc dk_src(const uint64_t* kaddr, int tile, int half, int w) {
   const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
   const int rb = 64 * half + 16 * w;
-  uint64_t src[8];
+  DkSrc s;
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi) s.p[mi] = kaddr[tile * kDkRows + rb + 2 * mi + g];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi) s.p[mi] += 16u * (uint32_t)(li ^ swz(rb + 2 * mi + g));
+  return s;
+}
+
+// Both halves of a tile (16 addresses per lane) with one LDS round trip.
+__device__ __forceinline__ void dk_src2(const uint64_t* kaddr, int tile, int w, DkSrc& s0, DkSrc& s1) {
+  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
 #pragma unroll
   for (int mi = 0; mi < 8; ++mi) {
-    const int r = rb + 2 * mi + g;
-    src[mi] = kaddr[tile * kDkRows + r] + 16u * (uint32_t)(li ^ swz(r));
+    s0.p[mi] = kaddr[tile * kDkRows + 16 * w + 2 * mi + g];
+    s1.p[mi] = kaddr[tile * kDkRows + 64 + 16 * w + 2 * mi + g];
   }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int mi = 0; mi < 8; ++mi) {
-    const int r0 = rb + 2 * mi;
-    if (r0 < nrows) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + r0 * kD));
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src[mi]) : "m0");
-    } else {
-      *(v4i*)(tb + (r0 + g) * kD + 16 * li) = v4i{0, 0, 0, 0};
-    }
+    const uint32_t off = 16u * (uint32_t)(li ^ swz(16 * w + 2 * mi + g));   // swz(r + 64) == swz(r)
+    s0.p[mi] += off;
+    s1.p[mi] += off;
   }
 }
 
-__device__ __forceinline__ int dk_rows(int nkeys, int tile) { return min(kDkRows, nkeys - tile * kDkRows); }
+__device__ __forceinline__ void dk_issue(const DkSrc& s, int mi, int half, uint8_t* tb, int w) {
+  const int r0 = 64 * half + 16 * w + 2 * mi;
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + r0 * kD));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(s.p[mi]) : "m0");
+}
+
+__device__ __forceinline__ void dk_gather(const uint64_t* kaddr, int tile, int half, uint8_t* tb, int w) {
+  const DkSrc s = dk_src(kaddr, tile, half, w);
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi) dk_issue(s, mi, half, tb, w);
+}
+
+// Issues the gather instructions of the next tile between MFMAs; inactive
+// (no next tile) issues nothing.
+struct DkFeed {
+  DkSrc src;
+  uint8_t* tb;
+  int half, w;
+  bool on;
+  __device__ __forceinline__ void operator()(int mi) const {
+    if (on) dk_issue(src, mi, half, tb, w);
+  }
+};
 
 // Per-lane LDS offsets (tile buffer 0) of the wave's K and V^T operand reads.
 struct DkOffsets {
@@ -1189,7 +1290,9 @@ __device__ __forceinline__ v8i dk_kop(const uint8_t* tb, const DkOffsets& o, int
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__device__ __forceinline__ void dk_qk(const uint8_t* tb, const DkOffsets& o, const v8i (&qreg)[4], v4f (&s)[2]) {
+// Two gather instructions of `feed` follow each K-step's MFMAs.
+__device__ __forceinline__ void dk_qk(const uint8_t* tb, const DkOffsets& o, const v8i (&qreg)[4], v4f (&s)[2],
+                                      const DkFeed& feed) {
   s[0] = v4f{0.f, 0.f, 0.f, 0.f};
   s[1] = v4f{0.f, 0.f, 0.f, 0.f};
   v8i a0 = dk_kop(tb, o, 0, 0), a1 = dk_kop(tb, o, 1, 0);
@@ -1203,6 +1306,9 @@ __device__ __forceinline__ void dk_qk(const uint8_t* tb, const DkOffsets& o, con
     __builtin_amdgcn_sched_barrier(0);
     s[0] = mma16(a0, qreg[k], s[0]);
     s[1] = mma16(a1, qreg[k], s[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    feed(2 * k);
+    feed(2 * k + 1);
     __builtin_amdgcn_sched_barrier(0);
     a0 = n0;
     a1 = n1;
@@ -1325,18 +1431,30 @@ __device__ __forceinline__ void dk_run(const KArgs& a, bool preset, UnitState& u
     {
       const ChunkScales<L> cs = resolve_rows<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
       lds_barrier();
-      dk_gather(kaddr, 0, 0, dk_rows(nkeys, 0), smem + L::kTiles, w);
-      dk_gather(kaddr, 0, 1, dk_rows(nkeys, 0), smem + L::kTiles, w);
+      {
+        DkSrc s0, s1;
+        dk_src2(kaddr, 0, w, s0, s1);
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) dk_issue(s0, mi, 0, smem + L::kTiles, w);
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) dk_issue(s1, mi, 1, smem + L::kTiles, w);
+      }
       resolve_scales<L>(cs, smem);
     }
     gather_barrier(false);
     for (int i = 0; i < tiles; ++i) {
       uint8_t* tb = smem + L::kTiles + (i & 1) * kDkTileBytes;
-      const bool next = i + 1 < tiles;
+      const bool next = __builtin_amdgcn_readfirstlane(i + 1 < tiles ? 1 : 0) != 0;
       uint8_t* tn = smem + L::kTiles + ((i + 1) & 1) * kDkTileBytes;
-      if (next) dk_gather(kaddr, i + 1, 0, dk_rows(nkeys, i + 1), tn, w);
+      DkFeed feed;
+      DkSrc src_b;
+      feed.tb = tn;
+      feed.w = w;
+      feed.on = next;
+      feed.half = 0;
+      if (next) dk_src2(kaddr, i + 1, w, feed.src, src_b);
       v4f s[2];
-      dk_qk(tb, o, qreg, s);
+      dk_qk(tb, o, qreg, s, feed);   // half 0 of tile i+1 goes out between the S^T MFMAs
       const float mt = dk_exponents(smem, i, w, g, qs, s);
       if (!preset && c0 == us.kb && i == 0) {   // wave-uniform
         const float mx = dk_heads_reduce(misc, w, lane, mt, true);
@@ -1344,8 +1462,11 @@ __device__ __forceinline__ void dk_run(const KArgs& a, bool preset, UnitState& u
       } else if (__ballot(mt > Mrun + kTau)) {
         *flag = 1;   // would overflow fp8: the unit is redone with a preset reference
       }
+      if (next) {   // half 1: in flight during the probabilities and P V
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) dk_issue(src_b, mi, 1, tn, w);
+      }
       dk_probs(smem, i, w, j, g, Mrun, s, lsum);
-      if (next) dk_gather(kaddr, i + 1, 1, dk_rows(nkeys, i + 1), tn, w);
       lds_barrier();
       v8i phi, plo;
       dk_pread(smem, j, g, phi, plo);
@@ -1368,11 +1489,13 @@ __device__ __forceinline__ float dk_unit_max(const KArgs& a, UnitState& us, int*
     resolve_chunk<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
     const int nkeys = c1 - c0, tiles = (nkeys + kDkRows - 1) / kDkRows;
     for (int i = 0; i < tiles; ++i) {
-      dk_gather(kaddr, i, 0, dk_rows(nkeys, i), smem + L::kTiles, w);
-      dk_gather(kaddr, i, 1, dk_rows(nkeys, i), smem + L::kTiles, w);
+      dk_gather(kaddr, i, 0, smem + L::kTiles, w);
+      dk_gather(kaddr, i, 1, smem + L::kTiles, w);
       gather_barrier(false);
       v4f s[2];
-      dk_qk(smem + L::kTiles, o, qreg, s);
+      DkFeed none;
+      none.on = false;
+      dk_qk(smem + L::kTiles, o, qreg, s, none);
       mx = fmaxf(mx, dk_exponents(smem, i, w, g, qs, s));
       lds_barrier();
     }
@@ -1397,21 +1520,23 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
 
   const KArgs& a = *(const KArgs*)ap;   // few live values here: no per-unit reload needed
   for (int u = u_begin; u < u_end; ++u) {
+    // Settles every load of the previous unit here, where nothing of this
+    // unit is in flight yet; without it the compiler guards registers reused
+    // across units with a wait placed after this unit's first loads.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     const int ngroups = kN1 / a.hg;
     const int t = u / ngroups, h0 = (u - t * ngroups) * a.hg;
     const int j = opaque(lane) & 15, g = lane >> 4;
     const bool real = j < a.hg;                 // head column j holds a real head
     const int h = h0 + (real ? j : 0);
-    // every load of the unit's prologue is issued before any is used:
-    // index slots, the q fragment (lane j+16g: q[t, h0+j, 128 k + 32 g .. +31]
-    // for K-step k), its descale, and the lengths
-    IdxPre ip;
-    if (a.topk > 0) ip = load_indices(a, t, 0);
+    // every load of the unit's prologue is issued before any is used: the
+    // lengths, index slots, the q fragment (lane j+16g: q[t, h0+j, 128 k +
+    // 32 g .. +31] for K-step k) and its descale
+    const TokLens tl = token_lens(a, t);
+    const IdxPre ip = load_indices(a, t, 0);
+    // (columns j >= hg load head h0 and are zeroed: no branch around the loads)
     v8i qreg[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) qreg[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    float qd = 0.f;
-    if (real) {
+    {
       const uint8_t* qrow = a.q + ((size_t)t * kN1 + h) * kD + 32 * g;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -1419,12 +1544,16 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
         const v4i x1 = *(const v4i*)(qrow + 128 * k + 16);
         qreg[k] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
-      qd = a.q_ds_per_head ? a.q_ds[(size_t)t * kN1 + h] : a.q_ds[t];
     }
+    const float qd_h = a.q_ds[a.q_ds_per_head ? (size_t)t * kN1 + h : (size_t)t];
     UnitState us;
     us.t = t;
-    us.k = token_ctx(a, t);
-    const float qs = a.scale_log2 * qd;
+    us.k = token_ctx(a, t, tl);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qreg[k][e] = real ? qreg[k][e] : 0;
+    const float qs = real ? a.scale_log2 * qd_h : 0.f;
     if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
       for (int x = opaque(lane); x < a.hg * 64; x += 64) {
         const int hr = h0 + x / 64, d = 8 * (x % 64);
@@ -1603,6 +1732,7 @@ __global__ void __launch_bounds__(kThreads) debug_resolve_kernel(const KArgs a, 
   __shared__ int list[kListMax];
   __shared__ int wtot[8];
   const int t = blockIdx.x;
+  const Sides sd = cache_sides(a);
   const Tok k = token_ctx(a, t);
   const int n_o = k.hi - k.lo;
   int n_c = 0;
@@ -1621,7 +1751,7 @@ __global__ void __launch_bounds__(kThreads) debug_resolve_kernel(const KArgs a, 
       }
     }
     for (int key = c0 + threadIdx.x; key < c1; key += kThreads)
-      keys[(size_t)t * max_keys + key] = (int32_t)resolve_row(a, k, n_o, key, list, w_lo);
+      keys[(size_t)t * max_keys + key] = (int32_t)resolve_row(a, sd, k, n_o, key, list, w_lo);
     __syncthreads();
   }
 }
