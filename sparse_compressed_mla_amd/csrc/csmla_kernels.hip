@@ -255,11 +255,10 @@ __device__ __forceinline__ IdxPre load_indices(const KArgs& a, int t, int s0) {
   const int last = max(a.topk - 1, 0);
   const int tid = opaque((int)threadIdx.x);
 #pragma unroll
-  for (int m = 0; m < kIdxRounds; ++m) {
-    const int slot = s0 + m * kThreads + tid;
-    const int v = row[min(slot, last)];
-    p.v[m] = (slot < a.topk) ? v : -1;
-  }
+  for (int m = 0; m < kIdxRounds; ++m) p.v[m] = row[min(s0 + m * kThreads + tid, last)];
+  __builtin_amdgcn_sched_barrier(0);   // all loads in flight before the first select
+#pragma unroll
+  for (int m = 0; m < kIdxRounds; ++m) p.v[m] = (s0 + m * kThreads + tid < a.topk) ? p.v[m] : -1;
   return p;
 }
 
@@ -393,38 +392,37 @@ __device__ __forceinline__ ChunkScales<L> resolve_rows(const KArgs& a, const Tok
   ChunkScales<L> cs;
   int j[M], blk[M];
   bool cmp[M];
+  // Slots past the chunk end resolve the chunk's last key (a chunk holds at
+  // least one) and then take the zero row: no lane-divergent branch around
+  // the loads, so that they are all in flight together.
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int key = c0 + m * kThreads + tid;
     cs.ok[m] = key < c1;
-    j[m] = cs.ok[m] ? key_pos(a, k, n_o, key, list, w_lo, cmp[m]) : 0;
-    if (!cs.ok[m]) cmp[m] = false;
+    j[m] = key_pos(a, k, n_o, cs.ok[m] ? key : c1 - 1, list, w_lo, cmp[m]);
     blk[m] = 0;
   }
   if (a.layout_kv == 2) {
 #pragma unroll
-    for (int m = 0; m < M; ++m)
-      if (cs.ok[m]) blk[m] = block_of(sd, k, cmp[m], j[m]);
+    for (int m = 0; m < M; ++m) blk[m] = block_of(sd, k, cmp[m], j[m]);
   }
+  const uint8_t* zero = g_zero_row;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    uint64_t addr = (uint64_t)(uintptr_t)g_zero_row;
-#pragma unroll
-    for (int c = 0; c < NKS; ++c) cs.ds[m][c] = 0.f;
-    if (cs.ok[m]) {
-      const int64_t row = row_of(a, sd, k, cmp[m], j[m], blk[m]);
-      addr = (uint64_t)(uintptr_t)((cmp[m] ? sd.c.kv : sd.o.kv) + row * kD);
-      const float* dsp = cmp[m] ? sd.c.ds : sd.o.ds;
-      if constexpr (L::kPerTile) {
-        const v4f x0 = *(const v4f*)(dsp + row * 8);
-        const v4f x1 = *(const v4f*)(dsp + row * 8 + 4);
-        cs.ds[m][0] = x0[0]; cs.ds[m][1] = x0[1]; cs.ds[m][2] = x0[2]; cs.ds[m][3] = x0[3];
-        cs.ds[m][4] = x1[0]; cs.ds[m][5] = x1[1]; cs.ds[m][6] = x1[2]; cs.ds[m][7] = x1[3];
-      } else {
-        cs.ds[m][0] = dsp[row];
-      }
+    const int64_t row = row_of(a, sd, k, cmp[m], j[m], blk[m]);
+    const uint8_t* kvp = (cmp[m] ? sd.c.kv : sd.o.kv) + row * kD;
+    const float* dsp = (cmp[m] ? sd.c.ds : sd.o.ds) + row * NKS;
+    kvp = cs.ok[m] ? kvp : zero;
+    dsp = cs.ok[m] ? dsp : reinterpret_cast<const float*>(zero);
+    if constexpr (L::kPerTile) {
+      const v4f x0 = *(const v4f*)dsp;
+      const v4f x1 = *(const v4f*)(dsp + 4);
+      cs.ds[m][0] = x0[0]; cs.ds[m][1] = x0[1]; cs.ds[m][2] = x0[2]; cs.ds[m][3] = x0[3];
+      cs.ds[m][4] = x1[0]; cs.ds[m][5] = x1[1]; cs.ds[m][6] = x1[2]; cs.ds[m][7] = x1[3];
+    } else {
+      cs.ds[m][0] = *dsp;
     }
-    kaddr[m * kThreads + tid] = addr;
+    kaddr[m * kThreads + tid] = (uint64_t)(uintptr_t)kvp;
   }
   return cs;
 }
