@@ -22,8 +22,9 @@ enum {
   MD_FLAGS = 11, MD_HEAD_GROUP = 12, MD_STARTS = kHeaderWords
 };
 
-// Everything one kernel launch needs, passed by value in the kernarg segment.
-struct KArgs {
+// Everything one kernel launch needs, passed by value in the kernarg segment:
+// the problem and tensors (KHdr), then the per-work-group unit ranges.
+struct KHdr {
   // problem attributes
   int32_t batch, t1, q_s, layout_q, layout_kv;
   int32_t ori_s, cmp_s, ori_bs, cmp_bs, ori_cols, cmp_cols;
@@ -43,6 +44,9 @@ struct KArgs {
   // plan
   int32_t splits, n_units, grid;
   int32_t hg;                       // > 0: head-split kernel with groups of hg heads (8 or 16)
+};
+
+struct KArgs : KHdr {
   int32_t starts[kMaxGrid + 1];
 };
 

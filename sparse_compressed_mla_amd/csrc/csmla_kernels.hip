@@ -78,6 +78,7 @@ __device__ __forceinline__ const KArgs& args(KArgPtr p) {
   return *(const KArgs*)p;
 }
 
+
 // Source of the rows of key slots past the end of a chunk: the gather always
 // issues the same number of loads per wave, so that the pipeline can count them.
 __device__ __attribute__((aligned(4096))) uint8_t g_zero_row[kD];
@@ -94,6 +95,36 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
+}
+
+// The header fields as register values.  Two vector loads bring the header
+// into two VGPRs (dword i in lane i mod 64) in one round trip; each field is
+// then a lane read.  A field read where it is used would be a scalar load
+// that waits for every scalar load in flight, one round trip each.
+// hdr_view launders the two registers first, so that the lane reads (and
+// what is computed from them) stay where a loop body uses them instead of
+// being hoisted to the kernel entry into spilled scalar registers.
+struct HdrRegs {
+  uint32_t v0, v1;
+};
+
+constexpr int kHdrWords = (int)(sizeof(KHdr) / 4);
+static_assert(sizeof(KHdr) % 4 == 0 && kHdrWords <= 128, "header size");
+
+__device__ __forceinline__ HdrRegs load_hdr_regs(KArgPtr ap) {
+  const int lane = opaque((int)threadIdx.x & 63);
+  const uint32_t* p = (const uint32_t*)ap;
+  return HdrRegs{p[min(lane, kHdrWords - 1)], p[min(64 + lane, kHdrWords - 1)]};
+}
+
+__device__ __forceinline__ KHdr hdr_view(HdrRegs r) {
+  asm volatile("" : "+v"(r.v0), "+v"(r.v1));
+  uint32_t wd[kHdrWords];
+#pragma unroll
+  for (int i = 0; i < kHdrWords; ++i) wd[i] = __builtin_amdgcn_readlane(i < 64 ? r.v0 : r.v1, i & 63);
+  KHdr h;
+  __builtin_memcpy(&h, wd, sizeof(KHdr));
+  return h;
 }
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ (((r >> 3) & 1) << 2); }
@@ -166,7 +197,7 @@ struct TokLens {
   int su_q, su_ori, cu_o0, cu_o1, su_cmp, cu_c0, cu_c1, res, tkl;
 };
 
-__device__ __forceinline__ TokLens token_lens(const KArgs& a, int t) {
+__device__ __forceinline__ TokLens token_lens(const KHdr& a, int t) {
   TokLens l;
   if (a.layout_q == 1) {  // TND: largest b with cu_q[b] <= t
     int lo = 0, hi = a.batch;
@@ -189,7 +220,7 @@ __device__ __forceinline__ TokLens token_lens(const KArgs& a, int t) {
   return l;
 }
 
-__device__ __forceinline__ Tok token_ctx(const KArgs& a, int t, const TokLens& l) {
+__device__ __forceinline__ Tok token_ctx(const KHdr& a, int t, const TokLens& l) {
   Tok k;
   const int b = l.b, q0 = l.q0, span = l.span;
   const int v_su_q = __builtin_amdgcn_readfirstlane(l.su_q), v_su_ori = __builtin_amdgcn_readfirstlane(l.su_ori);
@@ -235,7 +266,7 @@ __device__ __forceinline__ Tok token_ctx(const KArgs& a, int t, const TokLens& l
   return k;
 }
 
-__device__ __forceinline__ Tok token_ctx(const KArgs& a, int t) { return token_ctx(a, t, token_lens(a, t)); }
+__device__ __forceinline__ Tok token_ctx(const KHdr& a, int t) { return token_ctx(a, t, token_lens(a, t)); }
 
 // The first kIdxPre index slots of token t, one value per thread per round,
 // loaded before the token's lengths are known (bounded by topk, not by the
@@ -249,7 +280,7 @@ struct IdxPre {
 
 // Branch-free: slots past topk read a valid slot (or the zero row when
 // there are no indices) and are then replaced by -1.
-__device__ __forceinline__ IdxPre load_indices(const KArgs& a, int t, int s0) {
+__device__ __forceinline__ IdxPre load_indices(const KHdr& a, int t, int s0) {
   IdxPre p;
   const int* row = a.topk > 0 ? a.idx + (size_t)t * a.topk : reinterpret_cast<const int*>(g_zero_row);
   const int last = max(a.topk - 1, 0);
@@ -266,7 +297,7 @@ __device__ __forceinline__ IdxPre load_indices(const KArgs& a, int t, int s0) {
 // compacted position lies in [w_lo, w_lo + kListMax) go to list[pos - w_lo].
 // Returns the number of valid slots.  Whole-work-group call; `first` holds
 // the slots [0, kIdxPre), later rounds are loaded here.
-__device__ __forceinline__ int compact_indices(const KArgs& a, const Tok& k, int t, int* list, int* wtot, int w_lo,
+__device__ __forceinline__ int compact_indices(const KHdr& a, const Tok& k, int t, int* list, int* wtot, int w_lo,
                                                const IdxPre& first) {
   const int tid = opaque((int)threadIdx.x);
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -296,7 +327,7 @@ __device__ __forceinline__ int compact_indices(const KArgs& a, const Tok& k, int
   return base;
 }
 
-__device__ __forceinline__ int compact_indices(const KArgs& a, const Tok& k, int t, int* list, int* wtot, int w_lo) {
+__device__ __forceinline__ int compact_indices(const KHdr& a, const Tok& k, int t, int* list, int* wtot, int w_lo) {
   return compact_indices(a, k, t, list, wtot, w_lo, load_indices(a, t, 0));
 }
 
@@ -307,7 +338,7 @@ __device__ __forceinline__ int compact_indices(const KArgs& a, const Tok& k, int
 
 // Logical token position of key `key` of the token's list (ori band first,
 // then cmp entries) and whether it lives in cmp_kv.
-__device__ __forceinline__ int key_pos(const KArgs& a, const Tok& k, int n_o, int key, const int* list, int w_lo,
+__device__ __forceinline__ int key_pos(const KHdr& a, const Tok& k, int n_o, int key, const int* list, int w_lo,
                                        bool& is_cmp) {
   is_cmp = key >= n_o;
   if (!is_cmp) return k.lo + key;
@@ -334,7 +365,7 @@ __device__ __forceinline__ T pin_s(T v) {
   return v;
 }
 
-__device__ __forceinline__ Sides cache_sides(const KArgs& a) {
+__device__ __forceinline__ Sides cache_sides(const KHdr& a) {
   Sides x;
   x.o.kv = pin_s(a.ori_kv); x.o.ds = pin_s(a.ori_ds); x.o.tab = pin_s(a.ori_tab);
   x.o.bs = pin_s(a.ori_bs); x.o.cols = pin_s(a.ori_cols); x.o.s = pin_s(a.ori_s);
@@ -343,7 +374,7 @@ __device__ __forceinline__ Sides cache_sides(const KArgs& a) {
   return x;
 }
 
-__device__ __forceinline__ int64_t row_of(const KArgs& a, const Sides& sd, const Tok& k, bool is_cmp, int j, int blk) {
+__device__ __forceinline__ int64_t row_of(const KHdr& a, const Sides& sd, const Tok& k, bool is_cmp, int j, int blk) {
   if (a.layout_kv == 2) {
     const int bs = is_cmp ? sd.c.bs : sd.o.bs;
     return (int64_t)blk * bs + (j % bs);
@@ -360,7 +391,7 @@ __device__ __forceinline__ int block_of(const Sides& sd, const Tok& k, bool is_c
 }
 
 // Row of key `key` for the debug export (same resolution code).
-__device__ __forceinline__ int64_t resolve_row(const KArgs& a, const Sides& sd, const Tok& k, int n_o, int key,
+__device__ __forceinline__ int64_t resolve_row(const KHdr& a, const Sides& sd, const Tok& k, int n_o, int key,
                                                const int* list, int w_lo) {
   bool is_cmp;
   const int j = key_pos(a, k, n_o, key, list, w_lo, is_cmp);
@@ -383,7 +414,7 @@ struct ChunkScales {
 };
 
 template <class L>
-__device__ __forceinline__ ChunkScales<L> resolve_rows(const KArgs& a, const Tok& k, int n_o, const int* list,
+__device__ __forceinline__ ChunkScales<L> resolve_rows(const KHdr& a, const Tok& k, int n_o, const int* list,
                                                               int w_lo, int c0, int c1, uint8_t* smem) {
   constexpr int M = L::kChunk / kThreads, NKS = L::kNks;
   uint64_t* kaddr = reinterpret_cast<uint64_t*>(smem + L::kAddr);
@@ -459,7 +490,7 @@ __device__ __forceinline__ void resolve_scales(const ChunkScales<L>& cs, uint8_t
 
 // Both phases with nothing in between (ends with a barrier).
 template <class L>
-__device__ __forceinline__ void resolve_chunk(const KArgs& a, const Tok& k, int n_o, const int* list, int w_lo,
+__device__ __forceinline__ void resolve_chunk(const KHdr& a, const Tok& k, int n_o, const int* list, int w_lo,
                                               int c0, int c1, uint8_t* smem) {
   const ChunkScales<L> cs = resolve_rows<L>(a, k, n_o, list, w_lo, c0, c1, smem);
   resolve_scales<L>(cs, smem);
@@ -858,7 +889,7 @@ struct UnitState {
 
 // Slide the compacted index window so that it covers the cmp entries of the
 // keys [c0, c1); only a token with more than kListMax valid indices moves it.
-__device__ __forceinline__ void cover_chunk(const KArgs& a, UnitState& us, int* list, int* misc, int c0, int c1) {
+__device__ __forceinline__ void cover_chunk(const KHdr& a, UnitState& us, int* list, int* misc, int c0, int c1) {
   if (a.topk > 0 && us.n_c > kListMax) {
     const int need_lo = max(c0 - us.n_o, 0), need_hi = max(c1 - us.n_o, 0);
     if (need_hi > need_lo && (need_lo < us.w_lo || need_hi > us.w_lo + kListMax)) {
@@ -1230,10 +1261,14 @@ __device__ __forceinline__ void dk_src2(const uint64_t* kaddr, int tile, int w, 
   }
 }
 
+// M0 = the wave's row block of the half, plus the pair's offset added in
+// the same asm (per-instruction destinations would otherwise be formed once
+// for the whole kernel and held in spilled scalar registers).
 __device__ __forceinline__ void dk_issue(const DkSrc& s, int mi, int half, uint8_t* tb, int w) {
-  const int r0 = 64 * half + 16 * w + 2 * mi;
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + r0 * kD));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(s.p[mi]) : "m0");
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tb + (64 * half + 16 * w) * kD));
+  const uint32_t off = (uint32_t)(2 * mi * kD);
+  asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(s.p[mi]),
+               "s"(off) : "m0", "scc");
 }
 
 __device__ __forceinline__ void dk_gather(const uint64_t* kaddr, int tile, int half, uint8_t* tb, int w) {
@@ -1412,7 +1447,7 @@ __device__ __forceinline__ float dk_heads_reduce(int* misc, int w, int lane, flo
 }
 
 // Runs the unit's keys into (oacc, lsum); `preset` and Mrun as in the split kernel.
-__device__ __forceinline__ void dk_run(const KArgs& a, bool preset, UnitState& us, int* list, int* misc, uint8_t* smem,
+__device__ __forceinline__ void dk_run(const KHdr& a, bool preset, UnitState& us, int* list, int* misc, uint8_t* smem,
                                        const DkOffsets& o, int w, int lane, const v8i (&qreg)[4], float qs,
                                        v4f (&oacc)[8], float& Mrun, float& lsum) {
   using L = LdsDK;
@@ -1475,7 +1510,7 @@ __device__ __forceinline__ void dk_run(const KArgs& a, bool preset, UnitState& u
 }
 
 // Per-head maximum exponent over the unit (S^T only), for the redo pass.
-__device__ __forceinline__ float dk_unit_max(const KArgs& a, UnitState& us, int* list, int* misc, uint8_t* smem,
+__device__ __forceinline__ float dk_unit_max(const KHdr& a, UnitState& us, int* list, int* misc, uint8_t* smem,
                                              const DkOffsets& o, int w, int lane, const v8i (&qreg)[4], float qs) {
   using L = LdsDK;
   const int g = lane >> 4;
@@ -1504,24 +1539,29 @@ __device__ __forceinline__ float dk_unit_max(const KArgs& a, UnitState& us, int*
 __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
   using L = LdsDK;
   const int lane = (int)threadIdx.x & 63;
-  const int G = ap->grid;
+  const HdrRegs hr = load_hdr_regs(ap);
+  const KHdr a0 = hdr_view(hr);
+  const int G = a0.grid;
   const int bid = blockIdx.x;
   const int lw = (G % 8 == 0) ? ((bid & 7) * (G >> 3) + (bid >> 3)) : bid;  // one XCD per contiguous range
-  const int u_begin = ap->starts[lw], u_end = ap->starts[lw + 1];
-  {
-    const __attribute__((address_space(4))) int* kw = (const __attribute__((address_space(4))) int*)ap;
-    asm volatile("" ::"s"(kw[0]), "s"(kw[16]), "s"(kw[32]), "s"(kw[48]), "s"(kw[64]));
+  // With as many units as work-groups the planner's ranges are [g, g + 1)
+  // (any valid ranges cover each unit once, and units are independent): no
+  // load of the range table then.
+  int u_begin = lw, u_end = lw + 1;
+  if (a0.n_units != G) {
+    u_begin = ap->starts[lw];
+    u_end = ap->starts[lw + 1];
   }
   int* list = reinterpret_cast<int*>(smem + L::kList);
   int* misc = reinterpret_cast<int*>(smem + L::kMisc);
   const DkOffsets o = dk_offsets(lane, w);
 
-  const KArgs& a = *(const KArgs*)ap;   // few live values here: no per-unit reload needed
   for (int u = u_begin; u < u_end; ++u) {
     // Settles every load of the previous unit here, where nothing of this
     // unit is in flight yet; without it the compiler guards registers reused
     // across units with a wait placed after this unit's first loads.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    const KHdr a = hdr_view(hr);
     const int ngroups = kN1 / a.hg;
     const int t = u / ngroups, h0 = (u - t * ngroups) * a.hg;
     const int j = opaque(lane) & 15, g = lane >> 4;
@@ -1582,7 +1622,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     }
 
     // ---------------- epilogue: normalise, add the sink, bf16 through LDS ----------------
-    const KArgs& ae = a;
+    const KHdr& ae = a;
     const float lh = dk_heads_reduce(misc, w, lane, lsum, false);
     const float sg = (ae.sinks && real) ? ae.sinks[h] * kLog2e : kNegInf;
     const float Mf = fmaxf(Mrun, sg);
