@@ -104,6 +104,14 @@ __device__ __forceinline__ int opaque(int x) {
 // hdr_view launders the two registers first, so that the lane reads (and
 // what is computed from them) stay where a loop body uses them instead of
 // being hoisted to the kernel entry into spilled scalar registers.
+// A pointer known to address device (global) memory, rebuilt from its bits
+// so that loads through it compile to global (not flat) loads after its
+// provenance was lost in a register copy.
+template <class T>
+__device__ __forceinline__ T* gptr(T* p) {
+  return (T*)(__attribute__((address_space(1))) void*)(uintptr_t)p;
+}
+
 struct HdrRegs {
   uint32_t v0, v1;
 };
@@ -124,6 +132,16 @@ __device__ __forceinline__ KHdr hdr_view(HdrRegs r) {
   for (int i = 0; i < kHdrWords; ++i) wd[i] = __builtin_amdgcn_readlane(i < 64 ? r.v0 : r.v1, i & 63);
   KHdr h;
   __builtin_memcpy(&h, wd, sizeof(KHdr));
+  // every tensor is device (global) memory: a pointer that went through the
+  // lane reads is generic, and loads through it would be flat loads (which
+  // also count against the LDS wait counter)
+#define CSMLA_GLOBAL(f) h.f = gptr(h.f)
+  CSMLA_GLOBAL(q); CSMLA_GLOBAL(q_ds); CSMLA_GLOBAL(ori_kv); CSMLA_GLOBAL(ori_ds);
+  CSMLA_GLOBAL(cmp_kv); CSMLA_GLOBAL(cmp_ds); CSMLA_GLOBAL(idx); CSMLA_GLOBAL(ori_tab); CSMLA_GLOBAL(cmp_tab);
+  CSMLA_GLOBAL(cu_q); CSMLA_GLOBAL(cu_ori); CSMLA_GLOBAL(cu_cmp); CSMLA_GLOBAL(su_q); CSMLA_GLOBAL(su_ori);
+  CSMLA_GLOBAL(su_cmp); CSMLA_GLOBAL(res); CSMLA_GLOBAL(topk_len); CSMLA_GLOBAL(sinks); CSMLA_GLOBAL(out);
+  CSMLA_GLOBAL(lse); CSMLA_GLOBAL(ws_o); CSMLA_GLOBAL(ws_ml);
+#undef CSMLA_GLOBAL
   return h;
 }
 
@@ -367,9 +385,9 @@ __device__ __forceinline__ T pin_s(T v) {
 
 __device__ __forceinline__ Sides cache_sides(const KHdr& a) {
   Sides x;
-  x.o.kv = pin_s(a.ori_kv); x.o.ds = pin_s(a.ori_ds); x.o.tab = pin_s(a.ori_tab);
+  x.o.kv = gptr(pin_s(a.ori_kv)); x.o.ds = gptr(pin_s(a.ori_ds)); x.o.tab = gptr(pin_s(a.ori_tab));
   x.o.bs = pin_s(a.ori_bs); x.o.cols = pin_s(a.ori_cols); x.o.s = pin_s(a.ori_s);
-  x.c.kv = pin_s(a.cmp_kv); x.c.ds = pin_s(a.cmp_ds); x.c.tab = pin_s(a.cmp_tab);
+  x.c.kv = gptr(pin_s(a.cmp_kv)); x.c.ds = gptr(pin_s(a.cmp_ds)); x.c.tab = gptr(pin_s(a.cmp_tab));
   x.c.bs = pin_s(a.cmp_bs); x.c.cols = pin_s(a.cmp_cols); x.c.s = pin_s(a.cmp_s);
   return x;
 }
