@@ -52,6 +52,8 @@ constexpr int kStageRow = 2 * 256 + 16;         // bytes per head row of the out
 template <int PER_TILE>
 struct Lds {
   static constexpr int kPerTile = PER_TILE;
+  static constexpr int kNT = kThreads;                     // threads of the work-group
+  static constexpr int kFlag = 8;                          // misc word of the redo flag
   static constexpr int kChunk = PER_TILE ? 512 : 1024;     // keys resolved at once
   static constexpr int kNks = PER_TILE ? 8 : 1;            // descales per key
   static constexpr int kTiles = 0;                         // 3 x 32 KiB
@@ -286,56 +288,65 @@ __device__ __forceinline__ Tok token_ctx(const KHdr& a, int t, const TokLens& l)
 
 __device__ __forceinline__ Tok token_ctx(const KHdr& a, int t) { return token_ctx(a, t, token_lens(a, t)); }
 
-// The first kIdxPre index slots of token t, one value per thread per round,
-// loaded before the token's lengths are known (bounded by topk, not by the
-// effective length), so that these loads share a round trip with them.
-constexpr int kIdxRounds = 4;
-constexpr int kIdxPre = kIdxRounds * kThreads;
+// The first kIdxPre index slots of token t, one value per thread per round
+// (NT threads), loaded before the token's lengths are known (bounded by topk,
+// not by the effective length), so that these loads share a round trip with
+// them.
+constexpr int kIdxPre = 1024;
 
+template <int NT>
 struct IdxPre {
-  int v[kIdxRounds];
+  static constexpr int kRounds = kIdxPre / NT;
+  int v[kRounds];
 };
 
 // Branch-free: slots past topk read a valid slot (or the zero row when
 // there are no indices) and are then replaced by -1.
-__device__ __forceinline__ IdxPre load_indices(const KHdr& a, int t, int s0) {
-  IdxPre p;
+template <int NT>
+__device__ __forceinline__ IdxPre<NT> load_indices(const KHdr& a, int t, int s0) {
+  constexpr int R = IdxPre<NT>::kRounds;
+  IdxPre<NT> p;
   const int* row = a.topk > 0 ? a.idx + (size_t)t * a.topk : reinterpret_cast<const int*>(g_zero_row);
   const int last = max(a.topk - 1, 0);
   const int tid = opaque((int)threadIdx.x);
 #pragma unroll
-  for (int m = 0; m < kIdxRounds; ++m) p.v[m] = row[min(s0 + m * kThreads + tid, last)];
+  for (int m = 0; m < R; ++m) p.v[m] = row[min(s0 + m * NT + tid, last)];
   __builtin_amdgcn_sched_barrier(0);   // all loads in flight before the first select
 #pragma unroll
-  for (int m = 0; m < kIdxRounds; ++m) p.v[m] = (s0 + m * kThreads + tid < a.topk) ? p.v[m] : -1;
+  for (int m = 0; m < R; ++m) p.v[m] = (s0 + m * NT + tid < a.topk) ? p.v[m] : -1;
   return p;
 }
 
 // Compact the valid index slots of token t in slot order; entries whose
 // compacted position lies in [w_lo, w_lo + kListMax) go to list[pos - w_lo].
-// Returns the number of valid slots.  Whole-work-group call; `first` holds
-// the slots [0, kIdxPre), later rounds are loaded here.
+// Returns the number of valid slots.  Whole-work-group call (NT threads);
+// `first` holds the slots [0, kIdxPre), later rounds are loaded here; wtot
+// holds 2 NT / 64 words.
+template <int NT>
 __device__ __forceinline__ int compact_indices(const KHdr& a, const Tok& k, int t, int* list, int* wtot, int w_lo,
-                                               const IdxPre& first) {
+                                               const IdxPre<NT>& first) {
+  constexpr int NW = NT / 64, R = IdxPre<NT>::kRounds;
   const int tid = opaque((int)threadIdx.x);
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int base = 0, parity = 0;
   for (int s0 = 0; s0 < k.k_eff; s0 += kIdxPre) {
-    const IdxPre cur = (s0 == 0) ? first : load_indices(a, t, s0);
+    const IdxPre<NT> cur = (s0 == 0) ? first : load_indices<NT>(a, t, s0);
 #pragma unroll
-    for (int m = 0; m < kIdxRounds; ++m) {
-      if (s0 + m * kThreads >= k.k_eff) break;   // wave-uniform
-      const int slot = s0 + m * kThreads + tid;
+    for (int m = 0; m < R; ++m) {
+      if (s0 + m * NT >= k.k_eff) break;   // wave-uniform
+      const int slot = s0 + m * NT + tid;
       const bool ok = (slot < k.k_eff) && (cur.v[m] >= 0) && (cur.v[m] < k.vis);
       const uint64_t bal = __ballot(ok);
       const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-      int* wt = wtot + 4 * parity;   // the wave totals alternate between two slots,
+      int* wt = wtot + NW * parity;   // the wave totals alternate between two slots,
       parity ^= 1;                   // so one barrier per round suffices
       if (lane == 0) wt[w] = __popcll(bal);
       lds_barrier();
       int off = 0;
       for (int j = 0; j < w; ++j) off += wt[j];
-      const int tot = wt[0] + wt[1] + wt[2] + wt[3];
+      int tot = 0;
+#pragma unroll
+      for (int j = 0; j < NW; ++j) tot += wt[j];
       const int pos = base + off + pre;
       if (ok && pos >= w_lo && pos < w_lo + kListMax) list[pos - w_lo] = cur.v[m];
       base += tot;
@@ -345,8 +356,9 @@ __device__ __forceinline__ int compact_indices(const KHdr& a, const Tok& k, int 
   return base;
 }
 
+template <int NT>
 __device__ __forceinline__ int compact_indices(const KHdr& a, const Tok& k, int t, int* list, int* wtot, int w_lo) {
-  return compact_indices(a, k, t, list, wtot, w_lo, load_indices(a, t, 0));
+  return compact_indices<NT>(a, k, t, list, wtot, w_lo, load_indices<NT>(a, t, 0));
 }
 
 // ---------------------------------------------------------------------------
@@ -427,14 +439,14 @@ __device__ __forceinline__ int64_t resolve_row(const KHdr& a, const Sides& sd, c
 // and their descales travel in the same round trip.  Whole-work-group calls.
 template <class L>
 struct ChunkScales {
-  float ds[L::kChunk / kThreads][L::kNks];
-  bool ok[L::kChunk / kThreads];
+  float ds[L::kChunk / L::kNT][L::kNks];
+  bool ok[L::kChunk / L::kNT];
 };
 
 template <class L>
 __device__ __forceinline__ ChunkScales<L> resolve_rows(const KHdr& a, const Tok& k, int n_o, const int* list,
                                                               int w_lo, int c0, int c1, uint8_t* smem) {
-  constexpr int M = L::kChunk / kThreads, NKS = L::kNks;
+  constexpr int M = L::kChunk / L::kNT, NKS = L::kNks;
   uint64_t* kaddr = reinterpret_cast<uint64_t*>(smem + L::kAddr);
   const int tid = opaque((int)threadIdx.x);
   const Sides sd = cache_sides(a);
@@ -446,7 +458,7 @@ __device__ __forceinline__ ChunkScales<L> resolve_rows(const KHdr& a, const Tok&
   // the loads, so that they are all in flight together.
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const int key = c0 + m * kThreads + tid;
+    const int key = c0 + m * L::kNT + tid;
     cs.ok[m] = key < c1;
     j[m] = key_pos(a, k, n_o, cs.ok[m] ? key : c1 - 1, list, w_lo, cmp[m]);
     blk[m] = 0;
@@ -471,21 +483,21 @@ __device__ __forceinline__ ChunkScales<L> resolve_rows(const KHdr& a, const Tok&
     } else {
       cs.ds[m][0] = *dsp;
     }
-    kaddr[m * kThreads + tid] = (uint64_t)(uintptr_t)kvp;
+    kaddr[m * L::kNT + tid] = (uint64_t)(uintptr_t)kvp;
   }
   return cs;
 }
 
 template <class L>
 __device__ __forceinline__ void resolve_scales(const ChunkScales<L>& cs, uint8_t* smem) {
-  constexpr int M = L::kChunk / kThreads, NKS = L::kNks;
+  constexpr int M = L::kChunk / L::kNT, NKS = L::kNks;
   float* klam = reinterpret_cast<float*>(smem + L::kLam);
   float* kinv = reinterpret_cast<float*>(smem + L::kInv);
   float* kks = reinterpret_cast<float*>(smem + L::kKs);
   const int tid = opaque((int)threadIdx.x);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const int slot = m * kThreads + tid;
+    const int slot = m * L::kNT + tid;
     float lam = kNegInf, inv = 0.f;
     if (cs.ok[m]) {
       float mx = cs.ds[m][0];
@@ -907,12 +919,13 @@ struct UnitState {
 
 // Slide the compacted index window so that it covers the cmp entries of the
 // keys [c0, c1); only a token with more than kListMax valid indices moves it.
+template <int NT>
 __device__ __forceinline__ void cover_chunk(const KHdr& a, UnitState& us, int* list, int* misc, int c0, int c1) {
   if (a.topk > 0 && us.n_c > kListMax) {
     const int need_lo = max(c0 - us.n_o, 0), need_hi = max(c1 - us.n_o, 0);
     if (need_hi > need_lo && (need_lo < us.w_lo || need_hi > us.w_lo + kListMax)) {
       us.w_lo = need_lo;
-      compact_indices(a, us.k, us.t, list, misc, us.w_lo);
+      compact_indices<NT>(a, us.k, us.t, list, misc, us.w_lo);
     }
   }
 }
@@ -977,7 +990,7 @@ __device__ __forceinline__ void run_unit(KArgPtr ap, bool preset, UnitState& us,
   for (int c0 = us.kb; c0 < us.ke; c0 += L::kChunk) {
     const int c1 = min(us.ke, c0 + L::kChunk);
     const KArgs& a = args(ap);
-    cover_chunk(a, us, list, misc, c0, c1);
+    cover_chunk<kThreads>(a, us, list, misc, c0, c1);
     const int nkeys = c1 - c0, tiles = (nkeys + kTileKeys - 1) / kTileKeys;
     {
       // row addresses -> barrier -> gathers of tiles 0 and 1, then the
@@ -1026,7 +1039,7 @@ __device__ __forceinline__ float unit_max(KArgPtr ap, UnitState& us, int* list, 
   for (int c0 = us.kb; c0 < us.ke; c0 += L::kChunk) {
     const int c1 = min(us.ke, c0 + L::kChunk);
     const KArgs& a = args(ap);
-    cover_chunk(a, us, list, misc, c0, c1);
+    cover_chunk<kThreads>(a, us, list, misc, c0, c1);
     resolve_chunk<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
     const int nkeys = c1 - c0, tiles = (nkeys + kTileKeys - 1) / kTileKeys;
     for (int i = 0; i < tiles; ++i) {
@@ -1084,7 +1097,7 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
     // lengths, index slots, the query fragment (B operand of S^T = K Q^T for
     // d in [256 dh + 64 s4 + 32 g, +32)) and its descale
     const TokLens tl = token_lens(a, t);
-    const IdxPre ip = load_indices(a, t, 0);
+    const IdxPre<kThreads> ip = load_indices<kThreads>(a, t, 0);
     v8i qreg[4];
     {
       const uint8_t* qrow = a.q + ((size_t)t * kN1 + h) * kD + 256 * dh + 32 * g;
@@ -1117,7 +1130,7 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
     us.n_o = us.k.hi - us.k.lo;
     us.n_c = 0;
     us.w_lo = 0;
-    if (a.topk > 0) us.n_c = compact_indices(a, us.k, t, list, misc, 0, ip);
+    if (a.topk > 0) us.n_c = compact_indices<kThreads>(a, us.k, t, list, misc, 0, ip);
     else if (a.has_cmp) us.n_c = us.k.vis;
     const int64_t n = (int64_t)us.n_o + us.n_c;
     us.kb = (int)(n * s / a.splits);
@@ -1202,22 +1215,32 @@ attn_kernel(const KArgs a) {
 // second pass must merge.  Here the work-groups of one token divide its heads
 // instead and read the same rows, which the XCD's L2 serves after the first.
 //
-// 4 waves; 128-key tiles (2 LDS buffers).  With v_mfma_f32_16x16x128_f8f6f4
-// (A lane i+16g: row i, k = 32g..32g+31; B lane j+16g: column j; D lane
-// j+16g, reg r: element [4g+r][j]):
-//   S^T = K Q^T: wave w scores keys [32w, +32) (two 16-key blocks) against
-//   the HG heads over all of D (4 K-steps of 128), so no score exchange;
+// 8 waves (two per SIMD, so that one wave's MFMAs, LDS reads and gather
+// issues overlap the other's vector work; one wave alone issues at most one
+// instruction every four cycles); 128-key tiles (2 LDS buffers).  With
+// v_mfma_f32_16x16x128_f8f6f4 (A lane i+16g: row i, k = 32g..32g+31; B lane
+// j+16g: column j; D lane j+16g, reg r: element [4g+r][j]):
+//   S^T = K Q^T: wave w scores keys [16w, +16) against the HG heads over all
+//   of D (4 K-steps of 128), so no score exchange;
 //   P' = 2^(E - M) as an fp8 hi + lo pair goes to LDS as [head][key] bytes;
-//   O^T += V^T P^T: wave w owns output columns [128w, +128) (8 blocks of 16)
+//   O^T += V^T P^T: wave w owns output columns [64w, +64) (4 blocks of 16)
 //   over the tile's 128 keys, V^T from ds_read_b64_tr_b8.
 // Unused head columns of an 8-head group carry zero q and are not stored.
 
-constexpr int kDkRows = 128;                       // keys per tile
-constexpr int kDkTileBytes = kDkRows * kD;         // 64 KiB
-constexpr int kDkPxRow = 144;                      // bytes per head row of P (128 keys + pad)
+constexpr int kDkWaves = 8;
+constexpr int kDkThreads = 64 * kDkWaves;
+constexpr int kDkRows = 128;                          // keys per tile
+constexpr int kDkTileBytes = kDkRows * kD;            // 64 KiB
+constexpr int kDkPxRow = 144;                         // bytes per head row of P (128 keys + pad)
+constexpr int kDkKB = kDkRows / 16 / kDkWaves;        // 16-key S^T blocks per wave
+constexpr int kDkDB = kD / 16 / kDkWaves;             // 16-column O^T blocks per wave
+constexpr int kDkGI = kDkRows / 4 / kDkWaves;         // gather instructions per wave per half tile
+static_assert(kDkKB >= 1 && kDkDB >= 1 && kDkGI % 4 == 0, "wave split");
 
 struct LdsDK {
   static constexpr int kPerTile = 0;
+  static constexpr int kNT = kDkThreads;
+  static constexpr int kFlag = 2 * kDkWaves;
   static constexpr int kChunk = 1024;
   static constexpr int kNks = 1;
   static constexpr int kTiles = 0;                             // 2 x 64 KiB
@@ -1227,17 +1250,18 @@ struct LdsDK {
   static constexpr int kKs = kInv + 4 * kChunk;                // float [kChunk]
   static constexpr int kPx = kKs + 4 * kChunk;                 // fp8 P: [hi, lo][16 heads][kDkPxRow]
   static constexpr int kList = kPx + 2 * 16 * kDkPxRow;        // int [kListMax]
-  static constexpr int kMisc = kList + 4 * kListMax;           // [0..7] compaction, [8] redo flag, [64..] reductions
-  static constexpr int kBytes = kMisc + 4 * 64 + 4 * 4 * 64;
+  static constexpr int kMisc = kList + 4 * kListMax;           // [0, 2 waves) compaction, [kFlag] redo flag,
+  static constexpr int kBytes = kMisc + 4 * 64 + 4 * 4 * 64;   // [64, 64 + 16 waves) per-head reductions
 };
 static_assert(LdsDK::kBytes <= 160 * 1024, "LDS");
+static_assert(LdsDK::kFlag < 64 && 64 + 16 * kDkWaves <= 64 + 4 * 64, "misc words");
 
 __device__ __forceinline__ v4f mma16(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // Gather of chunk tile `tile` (128 keys) into a tile buffer in two halves
-// of 64 rows: in half `half`, wave w covers rows [64 half + 16 w, +16) with 8
+// of 64 rows: in half `half`, wave w covers rows [64 half + 8 w, +8) with 4
 // instructions of 2 rows.  Every slot of a chunk holds a row address (slots
 // past the chunk end hold the zero row), so a tile is always loaded whole.
 // The source addresses are formed first (DkSrc), and the instructions are
@@ -1245,35 +1269,23 @@ __device__ __forceinline__ v4f mma16(v8i a, v8i b, v4f c) {
 // back a wave's LDS-DMA loads once about a dozen are in flight, and a wave
 // stalled on an issue would leave its matrix core idle.
 struct DkSrc {
-  uint64_t p[8];
+  uint64_t p[kDkGI];
 };
 
-// All LDS reads of the addresses are issued before the first is used, so
-// that forming them costs one LDS round trip.
-__device__ __forceinline__ DkSrc dk_src(const uint64_t* kaddr, int tile, int half, int w) {
-  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
-  const int rb = 64 * half + 16 * w;
-  DkSrc s;
-#pragma unroll
-  for (int mi = 0; mi < 8; ++mi) s.p[mi] = kaddr[tile * kDkRows + rb + 2 * mi + g];
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int mi = 0; mi < 8; ++mi) s.p[mi] += 16u * (uint32_t)(li ^ swz(rb + 2 * mi + g));
-  return s;
-}
-
-// Both halves of a tile (16 addresses per lane) with one LDS round trip.
+// Both halves of a tile with one LDS round trip: every read of the
+// addresses is issued before the first is used.
 __device__ __forceinline__ void dk_src2(const uint64_t* kaddr, int tile, int w, DkSrc& s0, DkSrc& s1) {
   const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
+  constexpr int RW = 2 * kDkGI;   // rows per wave per half
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi) {
-    s0.p[mi] = kaddr[tile * kDkRows + 16 * w + 2 * mi + g];
-    s1.p[mi] = kaddr[tile * kDkRows + 64 + 16 * w + 2 * mi + g];
+  for (int mi = 0; mi < kDkGI; ++mi) {
+    s0.p[mi] = kaddr[tile * kDkRows + RW * w + 2 * mi + g];
+    s1.p[mi] = kaddr[tile * kDkRows + 64 + RW * w + 2 * mi + g];
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi) {
-    const uint32_t off = 16u * (uint32_t)(li ^ swz(16 * w + 2 * mi + g));   // swz(r + 64) == swz(r)
+  for (int mi = 0; mi < kDkGI; ++mi) {
+    const uint32_t off = 16u * (uint32_t)(li ^ swz(RW * w + 2 * mi + g));   // swz(r + 64) == swz(r)
     s0.p[mi] += off;
     s1.p[mi] += off;
   }
@@ -1283,16 +1295,20 @@ __device__ __forceinline__ void dk_src2(const uint64_t* kaddr, int tile, int w, 
 // the same asm (per-instruction destinations would otherwise be formed once
 // for the whole kernel and held in spilled scalar registers).
 __device__ __forceinline__ void dk_issue(const DkSrc& s, int mi, int half, uint8_t* tb, int w) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tb + (64 * half + 16 * w) * kD));
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tb + (64 * half + 2 * kDkGI * w) * kD));
   const uint32_t off = (uint32_t)(2 * mi * kD);
   asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(s.p[mi]),
                "s"(off) : "m0", "scc");
 }
 
-__device__ __forceinline__ void dk_gather(const uint64_t* kaddr, int tile, int half, uint8_t* tb, int w) {
-  const DkSrc s = dk_src(kaddr, tile, half, w);
+// The whole tile at once (both halves).
+__device__ __forceinline__ void dk_gather_tile(const uint64_t* kaddr, int tile, uint8_t* tb, int w) {
+  DkSrc s0, s1;
+  dk_src2(kaddr, tile, w, s0, s1);
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi) dk_issue(s, mi, half, tb, w);
+  for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s0, mi, 0, tb, w);
+#pragma unroll
+  for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s1, mi, 1, tb, w);
 }
 
 // Issues the gather instructions of the next tile between MFMAs; inactive
@@ -1308,17 +1324,18 @@ struct DkFeed {
 };
 
 // Per-lane LDS offsets (tile buffer 0) of the wave's K and V^T operand reads.
+// In a tile row, source chunk c (16 bytes) sits at chunk c ^ swz(row).
 struct DkOffsets {
-  int k[2][2];    // [key block b][16-byte half]: row (32 w + 16 b + i), chunk (2 g + x) ^ swz, + 128 s per K-step
-  int v[4][8];    // [m][d-block]: V^T transpose reads of keys 32 g + 8 m + .., columns 128 w + 16 db + ..
+  int k[kDkKB][2];    // [key block b][16-byte half]: row 16 (KB w + b) + i, chunk (2 g + x) ^ swz, + 128 per K-step
+  int v[4][kDkDB];    // [m][d-block]: V^T transpose reads of keys 32 g + 8 m + .., columns 16 (DB w + db) + ..
 };
 
 __device__ __forceinline__ DkOffsets dk_offsets(int lane, int w) {
   DkOffsets o;
   const int i = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int row = 32 * w + 16 * b + i, f = swz(row);
+  for (int b = 0; b < kDkKB; ++b) {
+    const int row = 16 * (kDkKB * w + b) + i, f = swz(row);
 #pragma unroll
     for (int x = 0; x < 2; ++x) o.k[b][x] = row * kD + 16 * ((2 * g + x) ^ f);
   }
@@ -1327,48 +1344,48 @@ __device__ __forceinline__ DkOffsets dk_offsets(int lane, int w) {
   for (int m = 0; m < 4; ++m) {
     const int row = 32 * g + 8 * m + (L >> 1), f = swz(row);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o.v[m][db] = row * kD + 128 * w + 16 * (db ^ f) + 8 * (L & 1);
+    for (int db = 0; db < kDkDB; ++db) o.v[m][db] = row * kD + 16 * ((kDkDB * w + db) ^ f) + 8 * (L & 1);
   }
   return o;
 }
 
-// S^T blocks (16 keys x 16 heads) of the wave's 32 keys, full D; the two
-// blocks' MFMA chains interleave, and the next K-step's operands are read
-// while the current ones multiply.
+// S^T blocks (16 keys x 16 heads) of the wave's keys, full D; the next
+// K-step's operands are read while the current ones multiply.
 __device__ __forceinline__ v8i dk_kop(const uint8_t* tb, const DkOffsets& o, int b, int k) {
   const v4i lo = *(const v4i*)(tb + o.k[b][0] + 128 * k);
   const v4i hi = *(const v4i*)(tb + o.k[b][1] + 128 * k);
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Two gather instructions of `feed` follow each K-step's MFMAs.
-__device__ __forceinline__ void dk_qk(const uint8_t* tb, const DkOffsets& o, const v8i (&qreg)[4], v4f (&s)[2],
+// kDkGI / 4 gather instructions of `feed` follow each K-step's MFMAs.
+__device__ __forceinline__ void dk_qk(const uint8_t* tb, const DkOffsets& o, const v8i (&qreg)[4], v4f (&s)[kDkKB],
                                       const DkFeed& feed) {
-  s[0] = v4f{0.f, 0.f, 0.f, 0.f};
-  s[1] = v4f{0.f, 0.f, 0.f, 0.f};
-  v8i a0 = dk_kop(tb, o, 0, 0), a1 = dk_kop(tb, o, 1, 0);
+  v8i a[kDkKB];
+#pragma unroll
+  for (int b = 0; b < kDkKB; ++b) {
+    s[b] = v4f{0.f, 0.f, 0.f, 0.f};
+    a[b] = dk_kop(tb, o, b, 0);
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    v8i n0 = a0, n1 = a1;
-    if (k < 3) {
-      n0 = dk_kop(tb, o, 0, k + 1);
-      n1 = dk_kop(tb, o, 1, k + 1);
-    }
+    v8i n[kDkKB];
+#pragma unroll
+    for (int b = 0; b < kDkKB; ++b) n[b] = (k < 3) ? dk_kop(tb, o, b, k + 1) : a[b];
     __builtin_amdgcn_sched_barrier(0);
-    s[0] = mma16(a0, qreg[k], s[0]);
-    s[1] = mma16(a1, qreg[k], s[1]);
+#pragma unroll
+    for (int b = 0; b < kDkKB; ++b) s[b] = mma16(a[b], qreg[k], s[b]);
     __builtin_amdgcn_sched_barrier(0);
-    feed(2 * k);
-    feed(2 * k + 1);
+#pragma unroll
+    for (int x = 0; x < kDkGI / 4; ++x) feed(k * (kDkGI / 4) + x);
     __builtin_amdgcn_sched_barrier(0);
-    a0 = n0;
-    a1 = n1;
+#pragma unroll
+    for (int b = 0; b < kDkKB; ++b) a[b] = n[b];
   }
 }
 
-// O^T[128 w + 16 db, +16][heads] += V^T P^T over the tile's 128 keys.
+// O^T[16 (DB w + db), +16][heads] += V^T P^T over the tile's 128 keys.
 __device__ __forceinline__ void dk_pv(const uint8_t* tb, const DkOffsets& o, const v8i& phi, const v8i& plo,
-                                      v4f (&oacc)[8]) {
+                                      v4f (&oacc)[kDkDB]) {
   v8i vt;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -1377,9 +1394,9 @@ __device__ __forceinline__ void dk_pv(const uint8_t* tb, const DkOffsets& o, con
     vt[2 * m + 1] = x[1];
   }
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
+  for (int db = 0; db < kDkDB; ++db) {
     v8i vn = vt;
-    if (db < 7) {
+    if (db < kDkDB - 1) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(tb + o.v[m][db + 1]));
@@ -1395,15 +1412,16 @@ __device__ __forceinline__ void dk_pv(const uint8_t* tb, const DkOffsets& o, con
   }
 }
 
-// Exponents of the wave's 32 keys (8 per lane: block b, reg r = key
-// 32 w + 16 b + 4 g + r of head j) in place; returns the lane's maximum.
-__device__ __forceinline__ float dk_exponents(const uint8_t* smem, int tile, int w, int g, float qs, v4f (&s)[2]) {
+// Exponents of the wave's keys (block b, reg r = key 16 (KB w + b) + 4 g + r
+// of head j) in place; returns the lane's maximum.
+__device__ __forceinline__ float dk_exponents(const uint8_t* smem, int tile, int w, int g, float qs,
+                                              v4f (&s)[kDkKB]) {
   const float* lam = reinterpret_cast<const float*>(smem + LdsDK::kLam) + tile * kDkRows;
   const float* ks = reinterpret_cast<const float*>(smem + LdsDK::kKs) + tile * kDkRows;
   float mt = kNegInf;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int k0 = 32 * w + 16 * b + 4 * g;
+  for (int b = 0; b < kDkKB; ++b) {
+    const int k0 = 16 * (kDkKB * w + b) + 4 * g;
     const v4f lv = *(const v4f*)&lam[k0];
     const v4f kv = *(const v4f*)&ks[k0];
 #pragma unroll
@@ -1417,14 +1435,14 @@ __device__ __forceinline__ float dk_exponents(const uint8_t* smem, int tile, int
 }
 
 // P' = 2^(E - Mrun) as fp8 hi + lo into LDS ([head j][key] bytes); l += P' / vds_max.
-__device__ __forceinline__ void dk_probs(uint8_t* smem, int tile, int w, int j, int g, float Mrun, const v4f (&e)[2],
-                                         float& lsum) {
+__device__ __forceinline__ void dk_probs(uint8_t* smem, int tile, int w, int j, int g, float Mrun,
+                                         const v4f (&e)[kDkKB], float& lsum) {
   const float* inv = reinterpret_cast<const float*>(smem + LdsDK::kInv) + tile * kDkRows;
   const float Ms = (Mrun == kNegInf) ? 0.f : Mrun;
   uint8_t* px = smem + LdsDK::kPx + j * kDkPxRow;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int k0 = 32 * w + 16 * b + 4 * g;
+  for (int b = 0; b < kDkKB; ++b) {
+    const int k0 = 16 * (kDkKB * w + b) + 4 * g;
     const v4f iv = *(const v4f*)&inv[k0];
     float p[4];
 #pragma unroll
@@ -1448,7 +1466,7 @@ __device__ __forceinline__ void dk_pread(const uint8_t* smem, int j, int g, v8i&
   plo = v8i{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
 }
 
-// Per-head value over the 4 waves (lanes j, j+16, j+32, j+48 of each wave
+// Per-head value over the waves (lanes j, j+16, j+32, j+48 of each wave
 // hold head j): the max or the sum.
 __device__ __forceinline__ float dk_heads_reduce(int* misc, int w, int lane, float v, bool is_max) {
   float o1 = __shfl_xor(v, 16);
@@ -1459,37 +1477,36 @@ __device__ __forceinline__ float dk_heads_reduce(int* misc, int w, int lane, flo
   if (lane < 16) red[w * 16 + lane] = v;
   lds_barrier();
   const int j = lane & 15;
-  const float a0 = red[j], a1 = red[16 + j], a2 = red[32 + j], a3 = red[48 + j];
+  float x[kDkWaves];
+#pragma unroll
+  for (int i = 0; i < kDkWaves; ++i) x[i] = red[16 * i + j];
   lds_barrier();
-  return is_max ? fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)) : (a0 + a1) + (a2 + a3);
+#pragma unroll
+  for (int step = kDkWaves / 2; step >= 1; step /= 2)   // pairwise tree
+#pragma unroll
+    for (int i = 0; i < step; ++i) x[i] = is_max ? fmaxf(x[i], x[i + step]) : x[i] + x[i + step];
+  return x[0];
 }
 
 // Runs the unit's keys into (oacc, lsum); `preset` and Mrun as in the split kernel.
 __device__ __forceinline__ void dk_run(const KHdr& a, bool preset, UnitState& us, int* list, int* misc, uint8_t* smem,
                                        const DkOffsets& o, int w, int lane, const v8i (&qreg)[4], float qs,
-                                       v4f (&oacc)[8], float& Mrun, float& lsum) {
+                                       v4f (&oacc)[kDkDB], float& Mrun, float& lsum) {
   using L = LdsDK;
   const int j = lane & 15, g = lane >> 4;
-  int* flag = misc + 8;
+  int* flag = misc + L::kFlag;
 #pragma unroll
-  for (int db = 0; db < 8; ++db) oacc[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < kDkDB; ++db) oacc[db] = v4f{0.f, 0.f, 0.f, 0.f};
   lsum = 0.f;
   const uint64_t* kaddr = reinterpret_cast<const uint64_t*>(smem + L::kAddr);
   for (int c0 = us.kb; c0 < us.ke; c0 += L::kChunk) {
     const int c1 = min(us.ke, c0 + L::kChunk);
-    cover_chunk(a, us, list, misc, c0, c1);
+    cover_chunk<L::kNT>(a, us, list, misc, c0, c1);
     const int nkeys = c1 - c0, tiles = (nkeys + kDkRows - 1) / kDkRows;
     {
       const ChunkScales<L> cs = resolve_rows<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
       lds_barrier();
-      {
-        DkSrc s0, s1;
-        dk_src2(kaddr, 0, w, s0, s1);
-#pragma unroll
-        for (int mi = 0; mi < 8; ++mi) dk_issue(s0, mi, 0, smem + L::kTiles, w);
-#pragma unroll
-        for (int mi = 0; mi < 8; ++mi) dk_issue(s1, mi, 1, smem + L::kTiles, w);
-      }
+      dk_gather_tile(kaddr, 0, smem + L::kTiles, w);
       resolve_scales<L>(cs, smem);
     }
     gather_barrier(false);
@@ -1504,7 +1521,7 @@ __device__ __forceinline__ void dk_run(const KHdr& a, bool preset, UnitState& us
       feed.on = next;
       feed.half = 0;
       if (next) dk_src2(kaddr, i + 1, w, feed.src, src_b);
-      v4f s[2];
+      v4f s[kDkKB];
       dk_qk(tb, o, qreg, s, feed);   // half 0 of tile i+1 goes out between the S^T MFMAs
       const float mt = dk_exponents(smem, i, w, g, qs, s);
       if (!preset && c0 == us.kb && i == 0) {   // wave-uniform
@@ -1515,7 +1532,7 @@ __device__ __forceinline__ void dk_run(const KHdr& a, bool preset, UnitState& us
       }
       if (next) {   // half 1: in flight during the probabilities and P V
 #pragma unroll
-        for (int mi = 0; mi < 8; ++mi) dk_issue(src_b, mi, 1, tn, w);
+        for (int mi = 0; mi < kDkGI; ++mi) dk_issue(src_b, mi, 1, tn, w);
       }
       dk_probs(smem, i, w, j, g, Mrun, s, lsum);
       lds_barrier();
@@ -1536,14 +1553,13 @@ __device__ __forceinline__ float dk_unit_max(const KHdr& a, UnitState& us, int* 
   const uint64_t* kaddr = reinterpret_cast<const uint64_t*>(smem + L::kAddr);
   for (int c0 = us.kb; c0 < us.ke; c0 += L::kChunk) {
     const int c1 = min(us.ke, c0 + L::kChunk);
-    cover_chunk(a, us, list, misc, c0, c1);
+    cover_chunk<L::kNT>(a, us, list, misc, c0, c1);
     resolve_chunk<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
     const int nkeys = c1 - c0, tiles = (nkeys + kDkRows - 1) / kDkRows;
     for (int i = 0; i < tiles; ++i) {
-      dk_gather(kaddr, i, 0, smem + L::kTiles, w);
-      dk_gather(kaddr, i, 1, smem + L::kTiles, w);
+      dk_gather_tile(kaddr, i, smem + L::kTiles, w);
       gather_barrier(false);
-      v4f s[2];
+      v4f s[kDkKB];
       DkFeed none;
       none.on = false;
       dk_qk(smem + L::kTiles, o, qreg, s, none);
@@ -1587,9 +1603,9 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     const int h = h0 + (real ? j : 0);
     // every load of the unit's prologue is issued before any is used: the
     // lengths, index slots, the q fragment (lane j+16g: q[t, h0+j, 128 k +
-    // 32 g .. +31] for K-step k) and its descale
+    // 32 g .. +31] for K-step k; every wave holds all of it) and its descale
     const TokLens tl = token_lens(a, t);
-    const IdxPre ip = load_indices(a, t, 0);
+    const IdxPre<L::kNT> ip = load_indices<L::kNT>(a, t, 0);
     // (columns j >= hg load head h0 and are zeroed: no branch around the loads)
     v8i qreg[4];
     {
@@ -1621,18 +1637,18 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     us.n_o = us.k.hi - us.k.lo;
     us.n_c = 0;
     us.w_lo = 0;
-    if (a.topk > 0) us.n_c = compact_indices(a, us.k, t, list, misc, 0, ip);
+    if (a.topk > 0) us.n_c = compact_indices<L::kNT>(a, us.k, t, list, misc, 0, ip);
     else if (a.has_cmp) us.n_c = us.k.vis;
     us.kb = 0;
     us.ke = us.n_o + us.n_c;
 
-    v4f oacc[8];
+    v4f oacc[kDkDB];
     float Mrun = kNegInf, lsum = 0.f;
     for (int pass = 0;; ++pass) {
-      if (threadIdx.x == 0) misc[8] = 0;
+      if (threadIdx.x == 0) misc[L::kFlag] = 0;
       dk_run(a, pass > 0, us, list, misc, smem, o, w, lane, qreg, qs, oacc, Mrun, lsum);
       lds_barrier();
-      const int redo = misc[8];
+      const int redo = misc[L::kFlag];
       lds_barrier();
       if (!redo || pass > 0) break;
       const float mx = dk_unit_max(a, us, list, misc, smem, o, w, lane, qreg, qs);
@@ -1655,13 +1671,13 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     // stage [16 heads][512 columns] bf16 (rows padded to 1040 bytes)
     constexpr int kRow = 2 * kD + 16;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const int d = 128 * w + 16 * db + 4 * g;
+    for (int db = 0; db < kDkDB; ++db) {
+      const int d = 16 * (kDkDB * w + db) + 4 * g;
       *(uint2*)(smem + j * kRow + 2 * d) = pack_bf16x4(sc * oacc[db][0], sc * oacc[db][1], sc * oacc[db][2], sc * oacc[db][3]);
     }
     lds_barrier();
-    // each wave stores head rows w, w+4, ...: a row is 1 KiB = 64 lanes x 16 bytes
-    for (int row = w; row < ae.hg; row += 4) {
+    // wave w stores head rows w, w + waves, ...: a row is 1 KiB = 64 lanes x 16 bytes
+    for (int row = w; row < ae.hg; row += kDkWaves) {
       const v4i x = *(const v4i*)(smem + row * kRow + 16 * lane);
       *(v4i*)(ae.out + ((size_t)t * kN1 + h0 + row) * kD + 8 * lane) = x;
     }
@@ -1669,7 +1685,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
   }
 }
 
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kDkThreads) __attribute__((amdgpu_waves_per_eu(kDkWaves / 4, kDkWaves / 4)))
 dk_kernel(const KArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LdsDK::kBytes];
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -1792,7 +1808,7 @@ __global__ void __launch_bounds__(kThreads) debug_resolve_kernel(const KArgs a, 
   const Tok k = token_ctx(a, t);
   const int n_o = k.hi - k.lo;
   int n_c = 0;
-  if (a.topk > 0) n_c = compact_indices(a, k, t, list, wtot, 0);
+  if (a.topk > 0) n_c = compact_indices<kThreads>(a, k, t, list, wtot, 0);
   else if (a.has_cmp) n_c = k.vis;
   if (threadIdx.x == 0) { counts[2 * t] = n_o; counts[2 * t + 1] = n_c; }
   const int n = min(n_o + n_c, max_keys);
@@ -1803,7 +1819,7 @@ __global__ void __launch_bounds__(kThreads) debug_resolve_kernel(const KArgs a, 
       const int need_lo = max(c0 - n_o, 0), need_hi = max(c1 - n_o, 0);
       if (need_hi > need_lo && (need_lo < w_lo || need_hi > w_lo + kListMax)) {
         w_lo = need_lo;
-        compact_indices(a, k, t, list, wtot, w_lo);
+        compact_indices<kThreads>(a, k, t, list, wtot, w_lo);
       }
     }
     for (int key = c0 + threadIdx.x; key < c1; key += kThreads)
@@ -1817,7 +1833,7 @@ __global__ void __launch_bounds__(kThreads) debug_resolve_kernel(const KArgs a, 
 int launch_forward(const KArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (a.hg > 0) {
-    hipLaunchKernelGGL(dk_kernel, dim3(a.grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(dk_kernel, dim3(a.grid), dim3(kDkThreads), 0, st, a);
     return (int)hipGetLastError();
   }
   if (a.scale_mode == 1)
