@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0   # dense fp8 MFMA, MI355X
 METRIC = "CSA decode query-tokens/s + effective KV HBM GB/s (% roofline), 1 MI355X"
 
 
@@ -63,6 +64,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing sample")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--workload", choices=["csa_decode", "csa_prefill"], default="csa_decode",
+                    help="csa_decode (default, the headline line) or csa_prefill (fp8 MFMA utilisation)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device-to-device copies of 512 MiB (the reference kernel that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -89,6 +92,10 @@ def main():
 
     import sparse_compressed_mla_amd as m
     from workloads import make_config
+
+    if args.workload == "csa_prefill":
+        prefill(args, m, make_config, torch, np)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -248,6 +255,70 @@ def main():
                                "kind": "oracle",
                                "sample": f"{done} csa_decode query tokens (640 keys each) in {dt:.1f} s, "
                                          f"float64 NumPy oracle on the host"}
+    print(json.dumps(res), flush=True)
+
+
+def prefill(args, m, make_config, torch, np):
+    """CSA prefill (TND, B=4 x 4096 query tokens, per-tile-64 descales,
+    return_softmax_lse): fp8 MFMA utilisation on the algorithmic flops
+    4 * 64 * 512 per (query token, key) pair (S = Q K^T and O = P V over the
+    64 heads).  The KV of one batch (4 x 4096 rows) is reused by every query
+    token of the batch, so no layer rotation: the bound is the matrix cores."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] building inputs: csa_prefill", file=sys.stderr, flush=True)
+    inp = make_config(5, device=dev)
+    T1 = inp.t1
+    if not args.no_parity:
+        from oracle import oracle_forward
+        from tests.parity_util import compare
+        toks = [0, 1500, T1 // 2 + 7, T1 - 1]
+        cpu = inp.to("cpu")
+        ref = oracle_forward(cpu, toks)
+        o, _ = m.forward(inp)
+        torch.cuda.synchronize()
+        compare(o.float().cpu().numpy(), ref.out, toks, name="bench precheck", verbose=False)
+        print("[bench] parity precheck ok", file=sys.stderr, flush=True)
+    _, counts = m.debug_resolve(inp, 1024)
+    torch.cuda.synchronize()
+    pairs = int(counts.sum().item())
+    flops = 4.0 * 64 * 512 * pairs
+    plan = m.Plan(inp)
+    out = torch.empty(inp.q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T1, 64), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    tens = m.tensors_from(inp, out, lse, ws if plan.workspace_bytes else None)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    steps = max(1, min(args.steps, 50))
+    warm = max(1, min(args.warmup, 10))
+    for _ in range(warm):
+        m.csmla_forward(plan.problem, tens, plan.metadata, sp)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        m.csmla_forward(plan.problem, tens, plan.metadata, sp)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    tflops = flops / (ms / 1e3) / 1e12
+    print(f"[bench] prefill forward {ms * 1e3:.1f} us, {pairs} pairs, {tflops:.1f} TFLOP/s; "
+          f"splits {plan.splits} grid {plan.grid}", file=sys.stderr, flush=True)
+    res = {
+        "metric": "CSA prefill query-tokens/s + fp8 MFMA TFLOP/s (% dense peak), 1 MI355X",
+        "value": round(T1 / (ms / 1e3), 1), "unit": "query-tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)",
+        "data": "synthetic, seeded (workloads.make_config(5))",
+        "config": {"workload": "csa_prefill", "batch": 4, "q_tokens_per_batch": 4096, "n1": 64, "d": 512,
+                   "band": 128, "cmp_ratio": 4, "topk": 512, "kv_scale": "per-tile-64", "lse": True,
+                   "splits": plan.splits, "grid": plan.grid},
+        "pairs_per_step": pairs,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_kernel<1> (split attention, per-tile descales)"},
+    }
     print(json.dumps(res), flush=True)
 
 
