@@ -1311,15 +1311,16 @@ __device__ __forceinline__ void dk_gather_tile(const uint64_t* kaddr, int tile, 
   for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s1, mi, 1, tb, w);
 }
 
-// Issues the gather instructions of the next tile between MFMAs; inactive
-// (no next tile) issues nothing.
+// The next tile's gather: src[h] holds half h's source addresses; half 0 is
+// issued between the S^T MFMAs (operator()), half 1 after the exponents.
+// Inactive (no next tile) issues nothing.
 struct DkFeed {
-  DkSrc src;
+  DkSrc src[2];
   uint8_t* tb;
-  int half, w;
+  int w;
   bool on;
-  __device__ __forceinline__ void operator()(int mi) const {
-    if (on) dk_issue(src, mi, half, tb, w);
+  __device__ __forceinline__ void operator()(int x) const {
+    if (on) dk_issue(src[x / kDkGI], x % kDkGI, x / kDkGI, tb, w);
   }
 };
 
@@ -1509,18 +1510,17 @@ __device__ __forceinline__ void dk_run(const KHdr& a, bool preset, UnitState& us
       dk_gather_tile(kaddr, 0, smem + L::kTiles, w);
       resolve_scales<L>(cs, smem);
     }
+    // source addresses of the next tile's gather, formed a step ahead (their
+    // LDS round trip overlaps the end of the previous step)
+    DkFeed feed;
+    feed.w = w;
+    if (tiles > 1) dk_src2(kaddr, 1, w, feed.src[0], feed.src[1]);
     gather_barrier(false);
     for (int i = 0; i < tiles; ++i) {
       uint8_t* tb = smem + L::kTiles + (i & 1) * kDkTileBytes;
       const bool next = __builtin_amdgcn_readfirstlane(i + 1 < tiles ? 1 : 0) != 0;
-      uint8_t* tn = smem + L::kTiles + ((i + 1) & 1) * kDkTileBytes;
-      DkFeed feed;
-      DkSrc src_b;
-      feed.tb = tn;
-      feed.w = w;
+      feed.tb = smem + L::kTiles + ((i + 1) & 1) * kDkTileBytes;
       feed.on = next;
-      feed.half = 0;
-      if (next) dk_src2(kaddr, i + 1, w, feed.src, src_b);
       v4f s[kDkKB];
       dk_qk(tb, o, qreg, s, feed);   // half 0 of tile i+1 goes out between the S^T MFMAs
       const float mt = dk_exponents(smem, i, w, g, qs, s);
@@ -1532,13 +1532,14 @@ __device__ __forceinline__ void dk_run(const KHdr& a, bool preset, UnitState& us
       }
       if (next) {   // half 1: in flight during the probabilities and P V
 #pragma unroll
-        for (int mi = 0; mi < kDkGI; ++mi) dk_issue(src_b, mi, 1, tn, w);
+        for (int mi = 0; mi < kDkGI; ++mi) dk_issue(feed.src[1], mi, 1, feed.tb, w);
       }
       dk_probs(smem, i, w, j, g, Mrun, s, lsum);
       lds_barrier();
       v8i phi, plo;
       dk_pread(smem, j, g, phi, plo);
       dk_pv(tb, o, phi, plo, oacc);
+      if (i + 2 < tiles) dk_src2(kaddr, i + 2, w, feed.src[0], feed.src[1]);
       gather_barrier(false);   // tile i+1 landed; every wave is done with tile i and with P
     }
   }
