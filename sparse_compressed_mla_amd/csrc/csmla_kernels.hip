@@ -229,7 +229,8 @@ __device__ __forceinline__ TokLens token_lens(const KHdr& a, int t) {
     l.q0 = ((ConstI32)a.cu_q)[lo];
     l.span = ((ConstI32)a.cu_q)[lo + 1] - l.q0;
   } else {
-    l.b = t / a.q_s; l.q0 = l.b * a.q_s; l.span = a.q_s;
+    l.b = (a.q_s == 1) ? t : t / a.q_s;   // (uniform) decode rows: no division
+    l.q0 = l.b * a.q_s; l.span = a.q_s;
   }
   const int z = opaque(0), b = l.b;
   l.su_q = ld_len(a.su_q, b, z); l.su_ori = ld_len(a.su_ori, b, z);
@@ -387,6 +388,8 @@ struct Side {
 };
 struct Sides {
   Side o, c;   // ori_kv, cmp_kv
+  bool pow2;   // both block sizes are powers of two: shifts instead of divisions
+  int osh, csh;
 };
 
 template <class T>
@@ -401,23 +404,43 @@ __device__ __forceinline__ Sides cache_sides(const KHdr& a) {
   x.o.bs = pin_s(a.ori_bs); x.o.cols = pin_s(a.ori_cols); x.o.s = pin_s(a.ori_s);
   x.c.kv = gptr(pin_s(a.cmp_kv)); x.c.ds = gptr(pin_s(a.cmp_ds)); x.c.tab = gptr(pin_s(a.cmp_tab));
   x.c.bs = pin_s(a.cmp_bs); x.c.cols = pin_s(a.cmp_cols); x.c.s = pin_s(a.cmp_s);
+  const bool op = x.o.bs > 0 && (x.o.bs & (x.o.bs - 1)) == 0, cp = x.c.bs > 0 && (x.c.bs & (x.c.bs - 1)) == 0;
+  x.pow2 = op && cp;
+  x.osh = op ? __builtin_ctz((unsigned)x.o.bs) : 0;
+  x.csh = cp ? __builtin_ctz((unsigned)x.c.bs) : 0;
   return x;
 }
 
-__device__ __forceinline__ int64_t row_of(const KHdr& a, const Sides& sd, const Tok& k, bool is_cmp, int j, int blk) {
+// Block index and offset of position j in a paged cache.
+struct BlockPos {
+  int q, r;
+};
+
+__device__ __forceinline__ BlockPos block_pos(const Sides& sd, bool is_cmp, int j) {
+  if (sd.pow2) {   // uniform
+    const int sh = is_cmp ? sd.csh : sd.osh;
+    return BlockPos{j >> sh, j & ((1 << sh) - 1)};
+  }
+  const int bs = is_cmp ? sd.c.bs : sd.o.bs;
+  const int q = j / bs;
+  return BlockPos{q, j - q * bs};
+}
+
+// blk: the table entry of the position's block; r: its offset in the block.
+__device__ __forceinline__ int64_t row_of(const KHdr& a, const Sides& sd, const Tok& k, bool is_cmp, int j, int blk,
+                                          int r) {
   if (a.layout_kv == 2) {
     const int bs = is_cmp ? sd.c.bs : sd.o.bs;
-    return (int64_t)blk * bs + (j % bs);
+    return (int64_t)blk * bs + r;
   }
   if (a.layout_kv == 1) return (int64_t)(is_cmp ? k.cmp0 : k.kv0) + j;
   return (int64_t)k.b * (is_cmp ? sd.c.s : sd.o.s) + j;
 }
 
-__device__ __forceinline__ int block_of(const Sides& sd, const Tok& k, bool is_cmp, int j) {
-  const int bs = is_cmp ? sd.c.bs : sd.o.bs;
+__device__ __forceinline__ int block_of(const Sides& sd, const Tok& k, bool is_cmp, int q) {
   const int32_t* tab = is_cmp ? sd.c.tab : sd.o.tab;
   const int cols = is_cmp ? sd.c.cols : sd.o.cols;
-  return tab[(size_t)k.b * cols + j / bs];
+  return tab[(size_t)k.b * cols + q];
 }
 
 // Row of key `key` for the debug export (same resolution code).
@@ -425,8 +448,10 @@ __device__ __forceinline__ int64_t resolve_row(const KHdr& a, const Sides& sd, c
                                                const int* list, int w_lo) {
   bool is_cmp;
   const int j = key_pos(a, k, n_o, key, list, w_lo, is_cmp);
-  const int blk = (a.layout_kv == 2) ? block_of(sd, k, is_cmp, j) : 0;
-  return row_of(a, sd, k, is_cmp, j, blk);
+  BlockPos bp{0, 0};
+  if (a.layout_kv == 2) bp = block_pos(sd, is_cmp, j);
+  const int blk = (a.layout_kv == 2) ? block_of(sd, k, is_cmp, bp.q) : 0;
+  return row_of(a, sd, k, is_cmp, j, blk, bp.r);
 }
 
 // Resolving the keys [c0, c1) of a unit into the chunk arrays takes two
@@ -451,7 +476,7 @@ __device__ __forceinline__ ChunkScales<L> resolve_rows(const KHdr& a, const Tok&
   const int tid = opaque((int)threadIdx.x);
   const Sides sd = cache_sides(a);
   ChunkScales<L> cs;
-  int j[M], blk[M];
+  int j[M], blk[M], off[M];
   bool cmp[M];
   // Slots past the chunk end resolve the chunk's last key (a chunk holds at
   // least one) and then take the zero row: no lane-divergent branch around
@@ -462,15 +487,20 @@ __device__ __forceinline__ ChunkScales<L> resolve_rows(const KHdr& a, const Tok&
     cs.ok[m] = key < c1;
     j[m] = key_pos(a, k, n_o, cs.ok[m] ? key : c1 - 1, list, w_lo, cmp[m]);
     blk[m] = 0;
+    off[m] = 0;
   }
   if (a.layout_kv == 2) {
 #pragma unroll
-    for (int m = 0; m < M; ++m) blk[m] = block_of(sd, k, cmp[m], j[m]);
+    for (int m = 0; m < M; ++m) {
+      const BlockPos bp = block_pos(sd, cmp[m], j[m]);
+      blk[m] = block_of(sd, k, cmp[m], bp.q);
+      off[m] = bp.r;
+    }
   }
   const uint8_t* zero = g_zero_row;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const int64_t row = row_of(a, sd, k, cmp[m], j[m], blk[m]);
+    const int64_t row = row_of(a, sd, k, cmp[m], j[m], blk[m], off[m]);
     const uint8_t* kvp = (cmp[m] ? sd.c.kv : sd.o.kv) + row * kD;
     const float* dsp = (cmp[m] ? sd.c.ds : sd.o.ds) + row * NKS;
     kvp = cs.ok[m] ? kvp : zero;
@@ -1597,8 +1627,8 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     // across units with a wait placed after this unit's first loads.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     const KHdr a = hdr_view(hr);
-    const int ngroups = kN1 / a.hg;
-    const int t = u / ngroups, h0 = (u - t * ngroups) * a.hg;
+    const int lg = (a.hg == 8) ? 3 : 4;          // head groups of 8 or 16
+    const int t = u >> (6 - lg), h0 = (u & ((kN1 >> lg) - 1)) << lg;
     const int j = opaque(lane) & 15, g = lane >> 4;
     const bool real = j < a.hg;                 // head column j holds a real head
     const int h = h0 + (real ? j : 0);
@@ -1682,7 +1712,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
       const v4i x = *(const v4i*)(smem + row * kRow + 16 * lane);
       *(v4i*)(ae.out + ((size_t)t * kN1 + h0 + row) * kD + 8 * lane) = x;
     }
-    lds_barrier();
+    if (u + 1 < u_end) lds_barrier();   // the staging area is read before the next unit's gathers
   }
 }
 
