@@ -199,7 +199,7 @@ def test_edge_contiguous_kv_layouts(layout_kv):
     check_rows(inp, name=f"kv layout {layout_kv}")
 
 
-@pytest.mark.parametrize("bs,r", [(16, 1), (64, 128), (1, 2), (1024, 3)])
+@pytest.mark.parametrize("bs,r", [(16, 1), (64, 128), (1, 2), (1024, 3), (96, 4), (100, 1)])
 def test_edge_block_sizes_and_ratios(bs, r):
     rng = np.random.default_rng(51)
     ori = [1100, 517]
@@ -209,6 +209,20 @@ def test_edge_block_sizes_and_ratios(bs, r):
                       residual=[o % r for o in ori], indices=idx, block_size=bs, return_lse=True)
     check(inp, name=f"block {bs} ratio {r}")
     check_rows(inp, name=f"block {bs} ratio {r}")
+
+
+def test_edge_mixed_block_sizes():
+    """ori blocks of 128 (a power of two) and cmp blocks of 24 (not one): the
+    block position of each key takes the division path."""
+    rng = np.random.default_rng(53)
+    ori = [900, 2049]
+    cmp = [o // 4 for o in ori]
+    idx = _rand_idx(rng, 4, 96, max(cmp), 0.2)
+    inp = make_custom(seed=54, q_lens=[2, 2], ori_lens=ori, cmp_lens=cmp, cmp_ratio=4,
+                      residual=[o % 4 for o in ori], indices=idx, block_size=128, cmp_block_size=24,
+                      return_lse=True)
+    check(inp, name="ori blocks 128, cmp blocks 24")
+    check_rows(inp, name="ori blocks 128, cmp blocks 24")
 
 
 def test_edge_topk_beyond_list_window():
