@@ -70,15 +70,9 @@ struct Lds {
 static_assert(Lds<0>::kBytes <= 160 * 1024 && Lds<1>::kBytes <= 160 * 1024, "LDS");
 
 // The kernel arguments live in the kernarg segment (constant address space).
-// args() re-derives a view of them through an opaque copy of the pointer, so
-// that fields are reloaded with scalar loads where they are used instead of
-// being held in scalar registers across the whole kernel.
+// The kernels read the header once into two VGPRs (load_hdr_regs) and the
+// per-work-group unit ranges directly from the segment.
 typedef const __attribute__((address_space(4))) KArgs* KArgPtr;
-
-__device__ __forceinline__ const KArgs& args(KArgPtr p) {
-  asm volatile("" : "+s"(p));
-  return *(const KArgs*)p;
-}
 
 
 // Source of the rows of key slots past the end of a chunk: the gather always
@@ -1009,7 +1003,7 @@ __device__ __forceinline__ void pipeline_step(uint8_t* smem, const LaneOffsets& 
 // reference from the redo pass; otherwise the first tile sets it (the pair's
 // max maps to 2^4).
 template <int PER_TILE>
-__device__ __forceinline__ void run_unit(KArgPtr ap, bool preset, UnitState& us, int* list, int* misc, uint8_t* smem,
+__device__ __forceinline__ void run_unit(HdrRegs hr, bool preset, UnitState& us, int* list, int* misc, uint8_t* smem,
                                          const LaneOffsets& o, const WaveCtx& c, const v8i (&qreg)[4],
                                          v16f (&oacc)[8], float& Mrun, float& lsum) {
   using L = Lds<PER_TILE>;
@@ -1019,7 +1013,7 @@ __device__ __forceinline__ void run_unit(KArgPtr ap, bool preset, UnitState& us,
   lsum = 0.f;
   for (int c0 = us.kb; c0 < us.ke; c0 += L::kChunk) {
     const int c1 = min(us.ke, c0 + L::kChunk);
-    const KArgs& a = args(ap);
+    const KHdr a = hdr_view(hr);
     cover_chunk<kThreads>(a, us, list, misc, c0, c1);
     const int nkeys = c1 - c0, tiles = (nkeys + kTileKeys - 1) / kTileKeys;
     {
@@ -1062,13 +1056,13 @@ __device__ __forceinline__ void run_unit(KArgPtr ap, bool preset, UnitState& us,
 // Per-head maximum exponent over the unit (S^T only, not pipelined), for the
 // rare unit where a later tile outgrows the first tile's fp8 window.
 template <int PER_TILE>
-__device__ __forceinline__ float unit_max(KArgPtr ap, UnitState& us, int* list, int* misc, uint8_t* smem,
+__device__ __forceinline__ float unit_max(HdrRegs hr, UnitState& us, int* list, int* misc, uint8_t* smem,
                                           const LaneOffsets& o, const WaveCtx& c, const v8i (&qreg)[4]) {
   using L = Lds<PER_TILE>;
   float mx = kNegInf;
   for (int c0 = us.kb; c0 < us.ke; c0 += L::kChunk) {
     const int c1 = min(us.ke, c0 + L::kChunk);
-    const KArgs& a = args(ap);
+    const KHdr a = hdr_view(hr);
     cover_chunk<kThreads>(a, us, list, misc, c0, c1);
     resolve_chunk<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
     const int nkeys = c1 - c0, tiles = (nkeys + kTileKeys - 1) / kTileKeys;
@@ -1097,16 +1091,15 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
   c.g = lane >> 5;
   c.dh = w >> 1;
   const int hh = w & 1, g = c.g, dh = c.dh;
-  const int G = ap->grid;
+  const HdrRegs hr = load_hdr_regs(ap);
+  const KHdr a0 = hdr_view(hr);
+  const int G = a0.grid;
   const int bid = blockIdx.x;
   const int lw = (G % 8 == 0) ? ((bid & 7) * (G >> 3) + (bid >> 3)) : bid;  // one XCD per contiguous range
-  const int u_begin = ap->starts[lw], u_end = ap->starts[lw + 1];
-  {
-    // Touch every cache line of the kernel arguments up to the unit ranges
-    // in the same round trip as the ranges: the per-unit reloads through
-    // args() then hit the scalar cache.
-    const __attribute__((address_space(4))) int* kw = (const __attribute__((address_space(4))) int*)ap;
-    asm volatile("" ::"s"(kw[0]), "s"(kw[16]), "s"(kw[32]), "s"(kw[48]), "s"(kw[64]));
+  int u_begin = lw, u_end = lw + 1;
+  if (a0.n_units != G) {
+    u_begin = ap->starts[lw];
+    u_end = ap->starts[lw + 1];
   }
   int* list = reinterpret_cast<int*>(smem + L::kList);
   int* misc = reinterpret_cast<int*>(smem + L::kMisc);
@@ -1117,10 +1110,10 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
     // unit is in flight yet; without it the compiler guards registers reused
     // across units with a wait placed after this unit's first loads.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    const KArgs& a = args(ap);
+    const KHdr a = hdr_view(hr);
     const int h = 32 * hh + (opaque(lane) & 31);   // the lane's head, recomputed per unit
     UnitState us;
-    us.t = u / a.splits;
+    us.t = (a.splits == 1) ? u : u / a.splits;
     const int s = u - us.t * a.splits;
     const int t = us.t;
     // every load of the unit's prologue is issued before any is used: the
@@ -1170,18 +1163,18 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
     float Mrun = kNegInf, lsum = 0.f;
     for (int pass = 0;; ++pass) {
       if (tid == 0) misc[8] = 0;
-      run_unit<PER_TILE>(ap, pass > 0, us, list, misc, smem, o, c, qreg, oacc, Mrun, lsum);
+      run_unit<PER_TILE>(hr, pass > 0, us, list, misc, smem, o, c, qreg, oacc, Mrun, lsum);
       lds_barrier();
       const int redo = misc[8];
       lds_barrier();
       if (!redo || pass > 0) break;
       // recompute with the reference preset from the unit's true maximum
-      const float mx = unit_max<PER_TILE>(ap, us, list, misc, smem, o, c, qreg);
+      const float mx = unit_max<PER_TILE>(hr, us, list, misc, smem, o, c, qreg);
       Mrun = (mx == kNegInf) ? kNegInf : mx - kPShift;
     }
 
     // ---------------- write: final output (one split) or partial state ----------------
-    const KArgs& ae = args(ap);
+    const KHdr ae = hdr_view(hr);
     float lh = lsum + __shfl_xor(lsum, 32);
     lh = pair_reduce(misc, w, lane, lh, false);   // both key halves
     float sc;
