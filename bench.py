@@ -64,8 +64,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing sample")
     ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--workload", choices=["csa_decode", "csa_prefill"], default="csa_decode",
-                    help="csa_decode (default, the headline line) or csa_prefill (fp8 MFMA utilisation)")
+    ap.add_argument("--workload", choices=["csa_decode", "csa_prefill", "swa_tiny", "hca_decode", "csa_mtp"],
+                    default="csa_decode",
+                    help="csa_decode (default, the headline line), csa_prefill (fp8 MFMA utilisation), or one of "
+                         "the other configurations (forward time and effective KV bytes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device-to-device copies of 512 MiB (the reference kernel that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -95,6 +97,9 @@ def main():
 
     if args.workload == "csa_prefill":
         prefill(args, m, make_config, torch, np)
+        return
+    if args.workload != "csa_decode":
+        other(args, m, make_config, torch, np)
         return
 
     dev = torch.device("cuda:0")
@@ -256,6 +261,73 @@ def main():
                                "sample": f"{done} csa_decode query tokens (640 keys each) in {dt:.1f} s, "
                                          f"float64 NumPy oracle on the host"}
     print(json.dumps(res), flush=True)
+
+
+OTHER = {"swa_tiny": 1, "hca_decode": 3, "csa_mtp": 4}
+
+
+def other(args, m, make_config, torch, np):
+    """Forward time of another configuration (inputs resident, one KV pool,
+    eager launches timed with HIP events on the kernels' stream), effective
+    KV bytes = unique (row) keys of each batch x 516 B."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    k = OTHER[args.workload]
+    print(f"[bench] building inputs: {args.workload}", file=sys.stderr, flush=True)
+    inp = make_config(k, device=dev)
+    T1 = inp.t1
+    if not args.no_parity:
+        from oracle import oracle_forward
+        from tests.parity_util import compare
+        toks = sorted({0, T1 // 2, T1 - 1})
+        cpu = inp.to("cpu")
+        ref = oracle_forward(cpu, toks)
+        o, _ = m.forward(inp)
+        torch.cuda.synchronize()
+        compare(o.float().cpu().numpy(), ref.out, toks, name="bench precheck", verbose=False)
+        print("[bench] parity precheck ok", file=sys.stderr, flush=True)
+    keys, counts = m.debug_resolve(inp, 1024)
+    torch.cuda.synchronize()
+    keys, counts = keys.cpu().numpy(), counts.cpu().numpy()
+    pairs = int(counts.sum())
+    rows = set()
+    for t in range(T1):
+        n_o, n_c = counts[t]
+        rows.update(("o", int(x)) for x in keys[t, :n_o])
+        rows.update(("c", int(x)) for x in keys[t, n_o:n_o + n_c])
+    kv_bytes = len(rows) * 516
+    plan = m.Plan(inp)
+    out = torch.empty(inp.q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T1, 64), dtype=torch.float32, device=dev) if getattr(inp, "return_lse", False) else None
+    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    tens = m.tensors_from(inp, out, lse, ws if plan.workspace_bytes else None)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    steps = max(1, min(args.steps, 200))
+    for _ in range(max(1, min(args.warmup, 20))):
+        m.csmla_forward(plan.problem, tens, plan.metadata, sp)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        m.csmla_forward(plan.problem, tens, plan.metadata, sp)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    gbs = kv_bytes / (ms / 1e3) / 1e9
+    kernel = (f"dk_kernel (head groups of {plan.head_group})" if plan.head_group > 0
+              else f"attn_kernel (splits {plan.splits})" + (" + combine_kernel" if plan.splits > 1 else ""))
+    print(f"[bench] {args.workload} forward {ms * 1e3:.2f} us, {T1} query tokens, {pairs} pairs, "
+          f"{gbs:.1f} GB/s effective KV; {kernel}, grid {plan.grid}", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": f"{args.workload} query-tokens/s + effective KV HBM GB/s, 1 MI355X",
+        "value": round(T1 / (ms / 1e3), 1), "unit": "query-tokens/s", "n_gpus": 1, "steps": steps,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "data": f"synthetic, seeded (workloads.make_config({k}))",
+        "config": {"workload": args.workload, "t1": T1, "splits": plan.splits, "grid": plan.grid,
+                   "head_group": plan.head_group},
+        "pairs_per_step": pairs, "kv_bytes_per_step": kv_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel}}), flush=True)
 
 
 def prefill(args, m, make_config, torch, np):
