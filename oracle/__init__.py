@@ -1,4 +1,5 @@
-"""CPU oracle for quantized sparse shared-KV MLA attention (test infrastructure).
+"""CPU oracle for quantized sparse shared-KV MLA attention and for the
+lightning-indexer top-k that feeds it (test infrastructure).
 
 This package is TEST INFRASTRUCTURE ONLY.  It is a plain, slow, float64
 NumPy restatement of what the pages define, used to check the HIP path.
@@ -6,7 +7,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import it.  The library under ``sparse_compressed_mla_amd/``
 never imports it and never falls back to it.
 
-Every function is pinned by ``tests/test_oracle_*.py`` against something other
+``oracle.indexer`` holds the indexer oracle.  Every function is pinned by
+``tests/test_oracle_*.py`` against something other
 than itself (library routines, closed forms, brute-force masks, invariants).
 """
 from .fp8 import decode_e4m3, E4M3_LUT  # noqa: F401
