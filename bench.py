@@ -64,10 +64,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing sample")
     ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--workload", choices=["csa_decode", "csa_prefill", "swa_tiny", "hca_decode", "csa_mtp"],
+    ap.add_argument("--workload", choices=["csa_decode", "csa_prefill", "swa_tiny", "hca_decode", "csa_mtp",
+                                           "idx_csa_decode", "idx_csa_mtp_long", "idx_csa_prefill"],
                     default="csa_decode",
-                    help="csa_decode (default, the headline line), csa_prefill (fp8 MFMA utilisation), or one of "
-                         "the other configurations (forward time and effective KV bytes)")
+                    help="csa_decode (default, the headline line), csa_prefill (fp8 MFMA utilisation), one of "
+                         "the other attention configurations (forward time and effective KV bytes), or an "
+                         "indexer top-k workload (idx_*)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device-to-device copies of 512 MiB (the reference kernel that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -95,6 +97,9 @@ def main():
     import sparse_compressed_mla_amd as m
     from workloads import make_config
 
+    if args.workload.startswith("idx_"):
+        indexer(args, m, torch, np)
+        return
     if args.workload == "csa_prefill":
         prefill(args, m, make_config, torch, np)
         return
@@ -391,6 +396,119 @@ def prefill(args, m, make_config, torch, np):
                      "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "attn_kernel<1> (split attention, per-tile descales)"},
     }
+    print(json.dumps(res), flush=True)
+
+
+def indexer(args, m, torch, np):
+    """Lightning-indexer top-k (csmla_indexer_forward: score kernel + top-k
+    kernel) on one of the indexer workloads.  Decode-shaped workloads are
+    bound by HBM: algorithmic bytes = every batch's keys once (128 fp8 bytes
+    + a 4-byte scale each) + the query rows (g x 128 bytes + 8 bytes of
+    weight and scale per head) + the int32 index rows written.  The key pools
+    are replicated over copies (read round-robin) so that no step finds them
+    in the Infinity Cache.  Prefill is bound by the matrix cores: algorithmic
+    flops = 2 x g x 128 per (query row, visible key) pair."""
+    from workloads.indexer_gen import make_indexer_workload
+    from oracle.indexer import token_context
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = args.workload
+    print(f"[bench] building inputs: {name}", file=sys.stderr, flush=True)
+    cpu = make_indexer_workload(name)
+    inp = cpu.to(dev)
+    T1, g = inp.t1, inp.g
+    vis = np.array([max(token_context(cpu, t)[4], 0) for t in range(T1)], dtype=np.int64)
+    nkeys = np.array([token_context(cpu, t)[3] for t in range(T1)], dtype=np.int64)
+    plan = m.IndexerPlan(inp)
+    out = torch.empty((T1, 1, inp.topk), dtype=torch.int32, device=dev)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    if not args.no_parity:
+        from oracle.indexer import oracle_scores, topk_positions
+        rows = sorted({0, T1 // 2, T1 - 1})
+        m.indexer_forward(inp, out=out, workspace=ws, plan=plan)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().reshape(T1, -1)
+        sc = ws.view(torch.float32)[: T1 * plan.stride].view(T1, plan.stride).cpu().numpy()
+        for t in rows:
+            v = int(vis[t])
+            ref = oracle_scores(cpu, t)
+            assert np.allclose(sc[t, :v], ref, rtol=1e-3, atol=1e-3 * np.abs(ref).max()), f"row {t} scores"
+            assert np.array_equal(got[t], topk_positions(sc[t, :v], inp.topk)), f"row {t} selection"
+        print("[bench] parity precheck ok", file=sys.stderr, flush=True)
+    decode_like = name != "idx_csa_prefill"
+    copies = 1
+    if decode_like:
+        key_bytes = int(inp.key.numel()) + 4 * int(inp.key_scale.numel())
+        copies = max(1, min(48, (1 << 30) // max(key_bytes, 1)))
+    keys = [inp.key] + [inp.key.clone() for _ in range(copies - 1)]
+    scales = [inp.key_scale] + [inp.key_scale.clone() for _ in range(copies - 1)]
+    tens = []
+    for c in range(copies):
+        t = m.indexer_tensors_from(inp, out, ws)
+        t.key, t.key_dequant_scale = keys[c].data_ptr(), scales[c].data_ptr()
+        tens.append(t)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    steps = max(1, min(args.steps, 200))
+    warm = max(1, min(args.warmup, 20))
+    for i in range(warm):
+        m.csmla_indexer_forward(plan.problem, tens[i % copies], plan.metadata, sp)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        m.csmla_indexer_forward(plan.problem, tens[i % copies], plan.metadata, sp)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    # keys each batch holds (every key of a batch is read once per call)
+    per_batch = {}
+    for t in range(T1):
+        b = token_context(cpu, t)[0]
+        per_batch[b] = int(nkeys[t]) if vis[t] > 0 else per_batch.get(b, 0)
+    key_bytes = sum(per_batch.values()) * (128 + 4)
+    alg_bytes = key_bytes + T1 * g * (128 + 8) + T1 * inp.topk * 4
+    flops = 2.0 * g * 128 * float(vis.sum())
+    gbs = alg_bytes / (ms / 1e3) / 1e9
+    tflops = flops / (ms / 1e3) / 1e12
+    kern = "idx_score_kernel + idx_topk_kernel (one csmla_indexer_forward)"
+    if decode_like:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kern}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "traffic": None, "kernel": kern}
+    print(f"[bench] {name}: {ms * 1e3:.2f} us per call, {T1} rows, {gbs:.1f} GB/s algorithmic, "
+          f"{tflops:.1f} TFLOP/s; tile tw={plan.metadata[4]} wt={plan.metadata[5]} kc={plan.metadata[6]}, "
+          f"stride {plan.stride}, key copies {copies}", file=sys.stderr, flush=True)
+    res = {
+        "metric": f"{name} indexer query-rows/s, 1 MI355X", "value": round(T1 / (ms / 1e3), 1),
+        "unit": "query-rows/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)",
+        "data": f"synthetic, seeded (workloads.indexer_gen, {name})",
+        "config": {"workload": name, "t1": T1, "g": g, "d": 128, "topk": int(inp.topk),
+                   "layout_q": cpu.layout_q, "layout_k": cpu.layout_k, "visible_pairs": int(vis.sum())},
+        "alg_bytes_per_step": alg_bytes, "flops_per_step": flops, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle.indexer import oracle_indexer
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            cores = len(os.sched_getaffinity(0))
+        order = np.random.default_rng(0).permutation(T1)
+        t0 = time.time()
+        done = 0
+        for t in order:
+            oracle_indexer(cpu, [int(t)])
+            done += 1
+            if time.time() - t0 > args.cpu_seconds:
+                break
+        dt = time.time() - t0
+        res["cpu_baseline"] = {"value": round(done / dt, 3), "unit": "query-rows/s",
+                               "cores": int(cores), "kind": "oracle",
+                               "sample": f"{done} random rows of {name} in {dt:.1f} s, NumPy oracle on the host"}
     print(json.dumps(res), flush=True)
 
 

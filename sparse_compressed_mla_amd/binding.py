@@ -289,3 +289,170 @@ def debug_resolve(inp, max_keys: int, stream=None):
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
     csmla_debug_resolve(p, t, _ptr(keys), _ptr(counts), max_keys, s)
     return keys, counts
+
+
+# ---------------------------------------------------------------------------
+# the lightning-indexer top-k (include/csmla_indexer.h)
+# ---------------------------------------------------------------------------
+
+CSMLA_INDEXER_METADATA_WORDS = 32
+
+
+class CsmlaIndexerProblem(ctypes.Structure):
+    _fields_ = [(n, _i32) for n in (
+        "batch", "g", "n2", "d", "layout_q", "layout_k", "q_s", "t1", "k_s", "block_size", "num_blocks",
+        "table_cols", "topk", "mask_mode", "cmp_ratio", "quant_mode")]
+
+
+class CsmlaIndexerHostLengths(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("cu_seqlens_q", "seqused_q", "cu_seqlens_k", "seqused_k", "cmp_residual_k")]
+
+
+INDEXER_TENSOR_FIELDS = ("query", "key", "weights", "query_dequant_scale", "key_dequant_scale", "cu_seqlens_q",
+                         "cu_seqlens_k", "seqused_q", "seqused_k", "cmp_residual_k", "block_table",
+                         "sparse_indices", "workspace")
+
+
+class CsmlaIndexerTensors(ctypes.Structure):
+    _fields_ = [(n, _p) for n in INDEXER_TENSOR_FIELDS] + [("workspace_bytes", ctypes.c_size_t)]
+
+
+def _load_indexer():
+    lib = load()
+    if not getattr(lib, "_indexer_ready", False):
+        lib.csmla_indexer_metadata_words.restype = ctypes.c_size_t
+        lib.csmla_indexer_validate.restype = ctypes.c_int
+        lib.csmla_indexer_validate.argtypes = [ctypes.POINTER(CsmlaIndexerProblem)]
+        lib.csmla_indexer_plan.restype = ctypes.c_int
+        lib.csmla_indexer_plan.argtypes = [ctypes.POINTER(CsmlaIndexerProblem),
+                                           ctypes.POINTER(CsmlaIndexerHostLengths), ctypes.POINTER(_i32),
+                                           ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
+        lib.csmla_indexer_forward.restype = ctypes.c_int
+        lib.csmla_indexer_forward.argtypes = [ctypes.POINTER(CsmlaIndexerProblem),
+                                              ctypes.POINTER(CsmlaIndexerTensors), ctypes.POINTER(_i32), _p]
+        lib._indexer_ready = True
+    return lib
+
+
+def csmla_indexer_metadata_words() -> int:
+    return int(_load_indexer().csmla_indexer_metadata_words())
+
+
+def csmla_indexer_validate(problem: CsmlaIndexerProblem) -> int:
+    return _load_indexer().csmla_indexer_validate(ctypes.byref(problem))
+
+
+def csmla_indexer_plan(problem: CsmlaIndexerProblem, lengths: Optional[CsmlaIndexerHostLengths] = None,
+                       raise_on_error: bool = True) -> Tuple[int, np.ndarray, int]:
+    """Returns (status, int32 plan, workspace bytes)."""
+    md = np.zeros(CSMLA_INDEXER_METADATA_WORDS, dtype=np.int32)
+    ws = ctypes.c_size_t(0)
+    st = _load_indexer().csmla_indexer_plan(ctypes.byref(problem),
+                                            ctypes.byref(lengths) if lengths is not None else None,
+                                            md.ctypes.data_as(ctypes.POINTER(_i32)), md.size, ctypes.byref(ws))
+    if raise_on_error:
+        _check(st, "csmla_indexer_plan")
+    return st, md, int(ws.value)
+
+
+def csmla_indexer_forward(problem: CsmlaIndexerProblem, tensors: CsmlaIndexerTensors, metadata: np.ndarray,
+                          stream: int = 0, raise_on_error: bool = True) -> int:
+    md = np.ascontiguousarray(metadata, dtype=np.int32)
+    st = _load_indexer().csmla_indexer_forward(ctypes.byref(problem), ctypes.byref(tensors),
+                                               md.ctypes.data_as(ctypes.POINTER(_i32)), _p(stream))
+    if raise_on_error:
+        _check(st, "csmla_indexer_forward")
+    return st
+
+
+def indexer_problem_from(inp) -> CsmlaIndexerProblem:
+    """Problem struct of an object carrying the page's indexer tensors (q,
+    q_scale, weights, key, key_scale, ... as torch tensors) and attributes."""
+    p = CsmlaIndexerProblem()
+    p.batch = int(inp.batch)
+    p.g = int(inp.q.shape[1])
+    p.n2 = 1
+    p.d = int(inp.q.shape[2])
+    p.layout_q = LAYOUTS[inp.layout_q]
+    p.layout_k = LAYOUTS[inp.layout_k]
+    p.q_s = int(inp.q_s)
+    p.t1 = int(inp.q.shape[0])
+    if inp.layout_k == "PA_BBND":
+        p.block_size = int(inp.key.shape[1])
+        p.num_blocks = int(inp.key.shape[0])
+        p.table_cols = int(inp.block_table.shape[1])
+    elif inp.layout_k == "BSND":
+        p.k_s = int(inp.key.shape[1])
+    else:
+        p.k_s = int(inp.key.shape[0])
+    p.topk = int(inp.topk)
+    p.mask_mode = int(inp.mask_mode)
+    p.cmp_ratio = int(inp.cmp_ratio)
+    p.quant_mode = 1
+    return p
+
+
+_IDX_LEN_NAMES = ("cu_seqlens_q", "seqused_q", "cu_seqlens_k", "seqused_k", "cmp_residual_k")
+
+
+def indexer_host_lengths_from(inp):
+    keep = []
+    hl = CsmlaIndexerHostLengths()
+    for n in _IDX_LEN_NAMES:
+        x = getattr(inp, n, None)
+        if x is None:
+            continue
+        arr = np.ascontiguousarray(x.detach().cpu().numpy().astype(np.int32))
+        keep.append(arr)
+        setattr(hl, n, arr.ctypes.data)
+    return hl, keep
+
+
+def indexer_tensors_from(inp, sparse_indices, workspace) -> CsmlaIndexerTensors:
+    t = CsmlaIndexerTensors()
+    t.query = _ptr(inp.q)
+    t.key = _ptr(inp.key)
+    t.weights = _ptr(inp.weights)
+    t.query_dequant_scale = _ptr(inp.q_scale)
+    t.key_dequant_scale = _ptr(inp.key_scale)
+    for n in ("cu_seqlens_q", "cu_seqlens_k", "seqused_q", "seqused_k", "cmp_residual_k", "block_table"):
+        v = getattr(inp, n, None)
+        if v is not None:
+            setattr(t, n, _ptr(v))
+    t.sparse_indices = _ptr(sparse_indices)
+    if workspace is not None:
+        t.workspace = _ptr(workspace)
+        t.workspace_bytes = int(workspace.numel() * workspace.element_size())
+    return t
+
+
+class IndexerPlan:
+    """A planned indexer call: problem struct, plan words and workspace size."""
+
+    def __init__(self, inp, lengths: bool = True):
+        self.problem = indexer_problem_from(inp)
+        hl, keep = indexer_host_lengths_from(inp) if lengths else (None, [])
+        _, self.metadata, self.workspace_bytes = csmla_indexer_plan(self.problem, hl)
+        self._keep = keep
+
+    @property
+    def stride(self) -> int:
+        """floats per score row in the workspace"""
+        return int(self.metadata[9])
+
+
+def indexer_forward(inp, out=None, workspace=None, plan: Optional[IndexerPlan] = None, stream=None):
+    """Run the indexer on inputs already on the GPU.  Returns (sparse_indices
+    int32 [t1, 1, topk], workspace); the workspace holds the float32 scores,
+    row t at t * plan.stride floats."""
+    import torch
+    plan = plan or IndexerPlan(inp)
+    dev = inp.q.device
+    if out is None:
+        out = torch.empty((inp.q.shape[0], 1, int(inp.topk)), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    t = indexer_tensors_from(inp, out, workspace)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
+    csmla_indexer_forward(plan.problem, t, plan.metadata, s)
+    return out, workspace

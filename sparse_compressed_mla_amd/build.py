@@ -1,8 +1,9 @@
 """Build the HIP library libcsmla.so in-tree for gfx950 (MI355X).
 
-The library is the product's only compute path: the C ABI in include/csmla.h
-implemented by csrc/csmla_host.cpp (validation, planner, launches) and
-csrc/csmla_kernels.hip (the kernels).  Built with hipcc; no JIT cache.
+The library is the product's only compute path: the C ABIs in include/csmla.h
+(attention) and include/csmla_indexer.h (indexer top-k), implemented by
+csrc/csmla_host.cpp and csrc/csmla_indexer_host.cpp (validation, planners,
+launches) and csrc/csmla_kernels.hip / csrc/csmla_indexer_kernels.hip.  Built with hipcc; no JIT cache.
 """
 import os
 import subprocess
@@ -34,16 +35,20 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, save_temps: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     common = ["-std=c++17", "-O3", "-fPIC", "-Wall", "-Wno-unused-function"]
-    host_o = os.path.join(BUILD, "csmla_host.o")
-    kern_o = os.path.join(BUILD, "csmla_kernels.o")
-    _run([HIPCC, *common, "-x", "c++", "-c", os.path.join(CSRC, "csmla_host.cpp"), "-o", host_o], verbose)
-    kcmd = [HIPCC, *common, f"--offload-arch={ARCH}", *DEVICE_FLAGS, "-c",
-            os.path.join(CSRC, "csmla_kernels.hip"), "-o", kern_o]
-    if save_temps:
-        kcmd += ["-save-temps=obj"]
-    _run(kcmd, verbose)
+    objs = []
+    for src in ("csmla_host.cpp", "csmla_indexer_host.cpp"):
+        o = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        _run([HIPCC, *common, "-x", "c++", "-c", os.path.join(CSRC, src), "-o", o], verbose)
+        objs.append(o)
+    for src in ("csmla_kernels.hip", "csmla_indexer_kernels.hip"):
+        o = os.path.join(BUILD, src.replace(".hip", ".o"))
+        kcmd = [HIPCC, *common, f"--offload-arch={ARCH}", *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", o]
+        if save_temps:
+            kcmd += ["-save-temps=obj"]
+        _run(kcmd, verbose)
+        objs.append(o)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", host_o, kern_o, "-o", tmp], verbose)
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

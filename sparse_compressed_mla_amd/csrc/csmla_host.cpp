@@ -138,6 +138,21 @@ bool is_win(int w) { return w == -1 || w >= 0; }
 
 }  // namespace
 
+// Error reporting shared with the indexer's host code (csmla_indexer_host.cpp).
+int csmla::fail_with(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+void csmla::clear_last_error() { g_last_error.clear(); }
+
+uint32_t csmla::hash_bytes(const void* data, size_t n, uint32_t seed) { return fnv1a(data, n, seed); }
+
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of a split plan: bf16 partial outputs [units, 64, 512], then

@@ -52,6 +52,13 @@ struct KArgs : KHdr {
 
 size_t workspace_bytes_for(int n_units, int splits);
 
+// Host helpers shared by the two halves of the library (csmla_host.cpp):
+// set the calling thread's last-error message and return `status`; clear it;
+// FNV-1a over bytes.
+int fail_with(int status, const char* fmt, ...);
+void clear_last_error();
+uint32_t hash_bytes(const void* data, size_t n, uint32_t seed = 2166136261u);
+
 // launchers (csmla_kernels.hip); return a hipError_t as int
 int launch_forward(const KArgs& a, void* stream);
 int launch_debug_resolve(const KArgs& a, int32_t* keys, int32_t* counts, int32_t max_keys, void* stream);
