@@ -424,13 +424,16 @@ def indexer(args, m, torch, np):
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     if not args.no_parity:
         from oracle.indexer import oracle_scores, topk_positions
-        rows = sorted({0, T1 // 2, T1 - 1})
+        rows = sorted({0, T1 // 2, T1 // 2 + 1, T1 - 1})
         m.indexer_forward(inp, out=out, workspace=ws, plan=plan)
         torch.cuda.synchronize()
         got = out.cpu().numpy().reshape(T1, -1)
         sc = ws.view(torch.float32)[: T1 * plan.stride].view(T1, plan.stride).cpu().numpy()
         for t in rows:
             v = int(vis[t])
+            if v == 0:
+                assert (got[t] == -1).all(), f"row {t} sees no key"
+                continue
             ref = oracle_scores(cpu, t)
             assert np.allclose(sc[t, :v], ref, rtol=1e-3, atol=1e-3 * np.abs(ref).max()), f"row {t} scores"
             assert np.array_equal(got[t], topk_positions(sc[t, :v], inp.topk)), f"row {t} selection"

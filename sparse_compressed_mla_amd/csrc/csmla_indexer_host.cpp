@@ -8,6 +8,7 @@
 #include "csmla_internal.h"
 
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -57,6 +58,20 @@ int64_t key_capacity(const csmla_indexer_problem* p) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Top-k work-group shapes built (threads, float4 chunks kept in registers).
+bool topk_shape_ok(int nt, int cc) {
+  return (nt == 256 && (cc == 1 || cc == 4)) || (nt == 1024 && (cc == 2 || cc == 4 || cc == 8));
+}
+
+// Most blocks a wave's `part` keys starting at a multiple of 64 can touch.
+int block_span(int part, int bs) {
+  int worst = 0;
+  const int period = 64 * bs;
+  for (int k0 = 0; k0 < period; k0 += 64)
+    worst = std::max(worst, (k0 + part - 1) / bs - k0 / bs + 1);
+  return worst;
+}
+
 }  // namespace
 
 extern "C" {
@@ -89,6 +104,10 @@ csmla_status csmla_indexer_validate(const csmla_indexer_problem* p) {
   }
   if (p->cmp_ratio < 1 || p->cmp_ratio > 128) return fail(CSMLA_ERR_INVALID_ARG, "cmp_ratio must be in 1..128");
   if (p->mask_mode != 0 && p->mask_mode != 3) return fail(CSMLA_ERR_INVALID_ARG, "mask_mode must be 0 or 3");
+  const int64_t rows = p->layout_k == CSMLA_LAYOUT_PA_BBND ? (int64_t)p->num_blocks * p->block_size
+                       : p->layout_k == CSMLA_LAYOUT_BSND  ? (int64_t)p->batch * p->k_s
+                                                           : (int64_t)p->k_s;
+  if (rows >= ((int64_t)1 << 31)) return fail(CSMLA_ERR_UNSUPPORTED, "key caches of 2^31 rows or more are not built");
   csmla::clear_last_error();
   return CSMLA_OK;
 }
@@ -146,12 +165,28 @@ csmla_status csmla_indexer_plan(const csmla_indexer_problem* p, const csmla_inde
   if (max_s1 <= 1) { tw = 1; wt = 1; }
   else if (max_s1 == 2) { tw = 2; wt = 1; }
   else if (max_s1 <= 8) { tw = 4; wt = 1; }
-  else { tw = 4; wt = 4; }
-  if (wt == 1) kc = max_n <= 4096 ? 256 : 1024;
-  else kc = 512;
+  else { tw = 2; wt = 4; }
+  if (const char* env = std::getenv("CSMLA_IDX_TILE")) {   // tuning override "tw,wt"
+    int a = 0, b = 0;
+    if (std::sscanf(env, "%d,%d", &a, &b) == 2 && ((a == 1 && b == 1) || (a == 2 && (b == 1 || b == 4)) ||
+                                                   (a == 4 && (b == 1 || b == 4)))) {
+      tw = a;
+      wt = b;
+    }
+  }
+  if (wt == 1) kc = max_n <= 4096 ? 256 : 4096;
+  else kc = 1024;
   if (const char* env = std::getenv("CSMLA_IDX_KC")) {   // tuning override: a multiple of 256
     const int f = std::atoi(env);
     if (f >= 256 && f % 256 == 0) kc = f;
+  }
+  // A wave reads the block-table entries of its keys with one load per lane:
+  // its keys may span at most 64 blocks.
+  if (p->layout_k == CSMLA_LAYOUT_PA_BBND) {
+    while (block_span(kc / (4 / wt), p->block_size) > 64) {
+      if (kc > 256) kc -= 256;
+      else wt = 1;
+    }
   }
   const int64_t rows_per_tile = (int64_t)tw * wt;
   const int64_t nqt = std::max<int64_t>(1, (max_s1 + rows_per_tile - 1) / rows_per_tile);
@@ -166,6 +201,13 @@ csmla_status csmla_indexer_plan(const csmla_indexer_problem* p, const csmla_inde
   else if (stride <= 16384) { nt = 1024; cc = 4; }
   else { nt = 1024; cc = 8; }
 
+  if (const char* env = std::getenv("CSMLA_IDX_TOPK")) {   // tuning override "threads,chunks"
+    int a = 0, b = 0;
+    if (std::sscanf(env, "%d,%d", &a, &b) == 2 && topk_shape_ok(a, b)) {
+      nt = a;
+      cc = b;
+    }
+  }
   const size_t ws = align256((size_t)p->t1 * (size_t)stride * sizeof(float));
   std::memset(md, 0, sizeof(int32_t) * CSMLA_INDEXER_METADATA_WORDS);
   md[IM_MAGIC] = kMagic;
@@ -198,11 +240,13 @@ csmla_status csmla_indexer_forward(const csmla_indexer_problem* p, const csmla_i
   if (md[IM_PROBLEM_HASH] != (int32_t)problem_hash(p))
     return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was planned for another problem");
   const int tw = md[IM_TW], wt = md[IM_WT], kc = md[IM_KC], nt = md[IM_TOPK_NT], cc = md[IM_TOPK_C];
-  const bool tile_ok = (tw == 1 && wt == 1) || (tw == 2 && wt == 1) || (tw == 4 && (wt == 1 || wt == 4));
-  const bool topk_ok = (nt == 256 && (cc == 1 || cc == 4)) || (nt == 1024 && (cc == 2 || cc == 4 || cc == 8));
+  const bool tile_ok = (tw == 1 && wt == 1) || (tw == 2 && (wt == 1 || wt == 4)) || (tw == 4 && (wt == 1 || wt == 4));
+  const bool topk_ok = topk_shape_ok(nt, cc);
   if (!tile_ok || !topk_ok || kc < 256 || kc % 256 != 0 || md[IM_NQT] < 1 || md[IM_NKC] < 1 || md[IM_STRIDE] < kStep ||
       md[IM_STRIDE] % kStep != 0)
     return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata fields are inconsistent");
+  if (p->layout_k == CSMLA_LAYOUT_PA_BBND && block_span(kc / (4 / wt), p->block_size) > 64)
+    return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata key chunk spans more than 64 blocks per wave");
   if (!t->query || !t->key || !t->weights || !t->query_dequant_scale || !t->key_dequant_scale || !t->sparse_indices)
     return fail(CSMLA_ERR_INVALID_ARG, "query, key, weights, both dequant scales and sparse_indices are required");
   if (p->layout_q == CSMLA_LAYOUT_TND && !t->cu_seqlens_q) return fail(CSMLA_ERR_INVALID_ARG, "TND query needs cu_seqlens_q");
@@ -228,11 +272,23 @@ csmla_status csmla_indexer_forward(const csmla_indexer_problem* p, const csmla_i
   for (int s = 0; s < 11; ++s)
     if (a.bs == (1 << s)) a.bs_shift = s;
   a.cols = p->table_cols;
+  if (p->layout_k == CSMLA_LAYOUT_PA_BBND) {
+    a.nrows = (int32_t)std::min<int64_t>((int64_t)p->num_blocks * p->block_size, INT32_MAX);
+    a.tab_ld = p->table_cols;
+    a.tab_cols = p->table_cols;
+  } else {
+    a.nrows = p->layout_k == CSMLA_LAYOUT_TND ? p->k_s
+                                              : (int32_t)std::min<int64_t>((int64_t)p->batch * p->k_s, INT32_MAX);
+    a.tab_ld = 0;
+    a.tab_cols = 1;
+  }
   a.topk = p->topk; a.mask = p->mask_mode; a.ratio = p->cmp_ratio;
   a.tw = tw; a.wt = wt; a.kc = kc; a.nqt = md[IM_NQT]; a.nkc = md[IM_NKC]; a.stride = md[IM_STRIDE];
   a.q = (const uint8_t*)t->query; a.qs = t->query_dequant_scale; a.w = t->weights;
   a.key = (const uint8_t*)t->key; a.ks = t->key_dequant_scale;
-  a.tab = t->block_table; a.cu_q = t->cu_seqlens_q; a.cu_k = t->cu_seqlens_k;
+  // without paging the kernel's one table read per lane lands on the first key scale
+  a.tab = t->block_table ? t->block_table : (const int32_t*)t->key_dequant_scale;
+  a.cu_q = t->cu_seqlens_q; a.cu_k = t->cu_seqlens_k;
   a.su_q = t->seqused_q; a.su_k = t->seqused_k; a.res = t->cmp_residual_k;
   a.scores = (float*)t->workspace; a.out = t->sparse_indices;
   const int e = launch_indexer(a, nt, cc, stream);

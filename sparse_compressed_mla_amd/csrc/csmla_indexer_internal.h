@@ -28,6 +28,8 @@ enum {
 
 struct IArgs {
   int32_t batch, t1, g, q_s, layout_q, layout_k, k_s, bs, bs_shift, cols;
+  int32_t nrows;             // rows of the key cache (PA: blocks * block_size)
+  int32_t tab_ld, tab_cols;  // block-table row stride and width as read (0 and 1 without paging)
   int32_t topk, mask, ratio;
   int32_t tw, wt, kc, nqt, nkc, stride;
   const uint8_t* q; const float* qs; const float* w;

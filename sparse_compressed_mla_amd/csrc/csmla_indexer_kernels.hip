@@ -81,33 +81,33 @@ __device__ __forceinline__ int visible(const IArgs& a, const Batch& c, int i) {
   return min(v, a.stride);
 }
 
-// Row of the key cache holding key s of batch b.
-__device__ __forceinline__ long long key_row(const IArgs& a, int b, int s) {
-  if (a.layout_k == CSMLA_LAYOUT_PA_BBND) {
-    int blk, off;
-    if (a.bs_shift >= 0) {
-      blk = s >> a.bs_shift;
-      off = s & (a.bs - 1);
-    } else {
-      blk = s / a.bs;
-      off = s - blk * a.bs;
-    }
-    return (long long)a.tab[(long long)b * a.cols + blk] * a.bs + off;
-  }
-  if (a.layout_k == CSMLA_LAYOUT_TND) return (long long)a.cu_k[b] + s;
-  return (long long)b * a.k_s + s;
-}
-
 // ---------------------------------------------------------------------------
 // scores
 // ---------------------------------------------------------------------------
+
+// The fp8 key operands (4 groups of 16 keys) and the key scale of one step.
+struct Step {
+  v8i k[4];
+  float s;
+};
 
 template <int TW, int WT>
 __global__ __launch_bounds__(256) void idx_score_kernel(IArgs a) {
   constexpr int KP = 4 / WT;                 // waves of a work-group that split the keys
   const int b = blockIdx.z;
-  const Batch c = batch_of(a, b);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hi = lane & 15, grp = lane >> 4;
+  const int part = a.kc / KP;
+  const int k0 = blockIdx.x * a.kc + (w / WT) * part;
+  const bool paged = a.layout_k == CSMLA_LAYOUT_PA_BBND;
+
+  // Block-table entries of the blocks the wave's keys can touch (at most 64,
+  // as planned), one per lane, read before any length is known; later rows
+  // come from a lane shuffle.  Without paging the read is a harmless word.
+  const int blk0 = paged ? (a.bs_shift >= 0 ? k0 >> a.bs_shift : k0 / a.bs) : 0;
+  const int tabreg = a.tab[(long long)b * a.tab_ld + min(blk0 + lane, a.tab_cols - 1)];
+
+  const Batch c = batch_of(a, b);
   const int i0 = (blockIdx.y * WT + w % WT) * TW;
   if (i0 >= c.s1) return;
   const int nt = min(TW, c.s1 - i0);
@@ -118,67 +118,95 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IArgs a) {
     vis[r] = r < nt ? visible(a, c, i0 + r) : 0;
     vmax = max(vmax, vis[r]);
   }
-  const int part = a.kc / KP;
-  const int k0 = blockIdx.x * a.kc + (w / WT) * part;
   const int k1 = min(k0 + part, vmax);
   if (k0 >= k1) return;
-  const int hi = lane & 15, grp = lane >> 4;
+  const int kbase = a.layout_k == CSMLA_LAYOUT_TND ? a.cu_k[b] : b * a.k_s;
+
+  // Row of key s (k0 <= s < k1) in the cache, clamped into the cache.
+  auto row_of = [&](int s) -> int {
+    const int bi = a.bs_shift >= 0 ? s >> a.bs_shift : s / a.bs;
+    const int blk = __shfl(tabreg, bi - blk0);
+    const int pr = min(max(blk, 0) * a.bs + (s - bi * a.bs), a.nrows - 1);
+    const int cr = min(kbase + s, a.nrows - 1);
+    return paged ? pr : cr;
+  };
+  // Issue the loads of the step at `base`; keys past k1 repeat key k1 - 1.
+  auto issue = [&](int base, Step& st) {
+    int myrow = 0;
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const int row = row_of(min(base + 16 * kg + hi, k1 - 1));
+      st.k[kg] = load32(a.key + (long long)row * kD + 32 * grp);
+      myrow = kg == grp ? row : myrow;                   // key base + lane after the reduction
+    }
+    st.s = a.ks[myrow];
+  };
+
+  Step A, B;
+  issue(k0, A);
 
   // query operands and the per-head factors W * scale_q of this lane's heads
+  // (rows past the batch and heads past g read a valid row, then count zero)
   v8i qa[TW][4];
   float wq[TW][4][4];
 #pragma unroll
   for (int r = 0; r < TW; ++r) {
-    const long long t = c.q0 + i0 + r;
+    const long long t = c.q0 + i0 + min(r, nt - 1);
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
       const int head = 16 * hb + hi;
-      qa[r][hb] = (r < nt && head < a.g) ? load32(a.q + (t * a.g + head) * kD + 32 * grp) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      const v8i x = load32(a.q + (t * a.g + min(head, a.g - 1)) * kD + 32 * grp);
+      const bool on = r < nt && head < a.g;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qa[r][hb][e] = on ? x[e] : 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int h2 = 16 * hb + 4 * grp + e;
-        wq[r][hb][e] = (r < nt && h2 < a.g) ? a.w[t * a.g + h2] * a.qs[t * a.g + h2] : 0.f;
+        const long long j = t * a.g + min(h2, a.g - 1);
+        const float f = a.w[j] * a.qs[j];
+        wq[r][hb][e] = (r < nt && h2 < a.g) ? f : 0.f;
       }
     }
   }
 
-  for (int base = k0; base < k1; base += kStep) {
-    v8i kb[4];
-    long long myrow = 0;
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg) {
-      const int s = min(base + 16 * kg + hi, k1 - 1);   // keys past the range repeat the last one
-      const long long row = key_row(a, b, s);
-      kb[kg] = load32(a.key + row * kD + 32 * grp);
-      if (kg == grp) myrow = row;                       // key base + lane after the reduction
-    }
-    const float ksc = a.ks[myrow];
+  auto compute = [&](int base, const Step& st) {
 #pragma unroll
     for (int r = 0; r < TW; ++r) {
-      if (r >= nt) break;
-      float p[4];
+      if (r < nt) {
+        float p[4];
 #pragma unroll
-      for (int kg = 0; kg < 4; ++kg) {
-        v4f acc[4];
+        for (int kg = 0; kg < 4; ++kg) {
+          v4f acc[4];
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) acc[hb] = mma16(qa[r][hb], kb[kg], v4f{0.f, 0.f, 0.f, 0.f});
-        float s = 0.f;
+          for (int hb = 0; hb < 4; ++hb) acc[hb] = mma16(qa[r][hb], st.k[kg], v4f{0.f, 0.f, 0.f, 0.f});
+          float s = 0.f;
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
+          for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s = fmaf(wq[r][hb][e], fmaxf(acc[hb][e], 0.f), s);
-        p[kg] = s;
+            for (int e = 0; e < 4; ++e) s = fmaf(wq[r][hb][e], fmaxf(acc[hb][e], 0.f), s);
+          p[kg] = s;
+        }
+        // reduce-scatter over lane groups g = lane / 16: afterwards lane l
+        // holds the sum over all 64 heads for key 16 (l / 16) + l % 16 = l
+        const bool upper = lane >= 32;
+        const float a0 = (upper ? p[2] : p[0]) + __shfl_xor(upper ? p[0] : p[2], 32);
+        const float a1 = (upper ? p[3] : p[1]) + __shfl_xor(upper ? p[1] : p[3], 32);
+        const bool odd = (lane >> 4) & 1;
+        const float tot = (odd ? a1 : a0) + __shfl_xor(odd ? a0 : a1, 16);
+        const int key = base + lane;
+        if (key < vis[r]) a.scores[(long long)(c.q0 + i0 + r) * a.stride + key] = st.s * tot;
       }
-      // reduce-scatter over lane groups g = lane / 16: afterwards lane l holds
-      // the sum over all 64 heads for key 16 (l / 16) + l % 16 = l
-      const bool upper = lane >= 32;
-      const float a0 = (upper ? p[2] : p[0]) + __shfl_xor(upper ? p[0] : p[2], 32);
-      const float a1 = (upper ? p[3] : p[1]) + __shfl_xor(upper ? p[1] : p[3], 32);
-      const bool odd = (lane >> 4) & 1;
-      const float tot = (odd ? a1 : a0) + __shfl_xor(odd ? a0 : a1, 16);
-      const int key = base + lane;
-      if (key < vis[r]) a.scores[(long long)(c.q0 + i0 + r) * a.stride + key] = ksc * tot;
     }
+  };
+
+  // two buffers: the next step's keys are in flight while this one multiplies
+  const int nsteps = (k1 - k0 + kStep - 1) / kStep;
+  for (int st = 0; st < nsteps; st += 2) {
+    issue(k0 + (st + 1) * kStep, B);
+    compute(k0 + st * kStep, A);
+    if (st + 1 >= nsteps) break;
+    issue(k0 + (st + 2) * kStep, A);
+    compute(k0 + (st + 1) * kStep, B);
   }
 }
 
@@ -216,25 +244,42 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   return before + x - v;
 }
 
+// Batch of query row t: t / S1 (BSND), or the last batch whose
+// cu_seqlens_q entry is <= t (TND), found 64 entries per load.
+__device__ __forceinline__ int batch_of_row(const IArgs& a, int t) {
+  if (a.layout_q != CSMLA_LAYOUT_TND) return t / a.q_s;
+  const int lane = threadIdx.x & 63;
+  int b = 0;
+  for (int j0 = 0; j0 < a.batch; j0 += 64) {
+    const int cv = a.cu_q[min(j0 + lane, a.batch - 1)];
+    const bool le = (j0 + lane < a.batch) & (cv <= t);
+    b += __popcll(__ballot(le));
+  }
+  return b - 1;
+}
+
 template <int NT, int C>
 __global__ __launch_bounds__(NT) void idx_topk_kernel(IArgs a) {
-  __shared__ uint32_t hist[256];
+  constexpr int NB = 2048;                   // bins of an 11-bit digit
+  constexpr int BPT = NB / NT;               // bins per thread in the scan
+  __shared__ uint32_t hist[NB];
   __shared__ uint32_t wsum[2][NT / 64];
-  __shared__ int32_t pick[2];
+  __shared__ int32_t pick[3];
   constexpr int CH = 4 * NT;                 // scores per chunk; thread tid holds [4 tid, 4 tid + 4)
   const int t = blockIdx.x, tid = threadIdx.x;
-  int b;
-  if (a.layout_q == CSMLA_LAYOUT_TND) {     // largest b with cu_seqlens_q[b] <= t
-    int lo = 0, hi = a.batch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.cu_q[mid] <= t) lo = mid;
-      else hi = mid - 1;
-    }
-    b = lo;
-  } else {
-    b = t / a.q_s;
-  }
+  const float* row = a.scores + (long long)t * a.stride;
+  auto load = [&](int cc, uint32_t (&u)[4]) {
+    const int j0 = min(cc * CH + 4 * tid, a.stride - 4);   // stays in the row; masked by vis below
+    const v4f x = *(const v4f*)(row + j0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = order_key(x[e]);
+  };
+  // the cached part of the row is read before the row's length is known
+  uint32_t cache[C][4];
+#pragma unroll
+  for (int cc = 0; cc < C; ++cc) load(cc, cache[cc]);
+
+  const int b = batch_of_row(a, t);
   const Batch c = batch_of(a, b);
   const int i = t - c.q0;
   int32_t* out = a.out + (long long)t * a.topk;
@@ -243,33 +288,24 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(IArgs a) {
     for (int j = tid; j < a.topk; j += NT) out[j] = j < vis ? j : -1;
     return;
   }
-  const float* row = a.scores + (long long)t * a.stride;
   const int nch = (vis + CH - 1) / CH;
-  auto load = [&](int cc, uint32_t (&u)[4]) {
-    const int j0 = cc * CH + 4 * tid;
-    v4f x = v4f{0.f, 0.f, 0.f, 0.f};
-    if (j0 < vis) x = *(const v4f*)(row + j0);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = order_key(x[e]);
-  };
-  uint32_t cache[C][4];
-#pragma unroll
-  for (int cc = 0; cc < C; ++cc) load(cc, cache[cc]);
 
-  // radix selection of the topk-th largest key, 8 bits a round
+  // radix selection of the topk-th largest key: digits of 11, 11 and 10
+  // bits; stop early once the chosen bin is taken whole
   uint32_t prefix = 0;
-  int need = a.topk;
-  int sb = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int j = tid; j < 256; j += NT) hist[j] = 0;
+  int need = a.topk, sh = 0, sb = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t hmask = pass == 0 ? 0u : (pass == 1 ? 0xFFFFFFFFu << 21 : 0xFFFFFFFFu << 10);
+    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0;
     __syncthreads();
     auto count = [&](int cc, const uint32_t (&u)[4]) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int idx = cc * CH + 4 * tid + e;
-        if (idx < vis && (u[e] & hmask) == prefix) atomicAdd(&hist[(u[e] >> shift) & 255u], 1u);
+        if (idx < vis && (u[e] & hmask) == prefix) atomicAdd(&hist[(u[e] >> shift) & dmask], 1u);
       }
     };
 #pragma unroll
@@ -281,23 +317,35 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(IArgs a) {
       count(cc, u);
     }
     __syncthreads();
-    // thread tid takes digit 255 - tid: inclusive prefix = keys with digit >= it
-    const uint32_t h = tid < 256 ? hist[255 - tid] : 0u;
+    // thread tid holds digits NB-1 - (tid*BPT + j), j = 0..BPT-1 (descending)
+    uint32_t hv[BPT], local = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      hv[j] = hist[NB - 1 - (tid * BPT + j)];
+      local += hv[j];
+    }
     uint32_t total;
-    const uint32_t incl = block_exclusive_scan<NT>(h, wsum[sb++ & 1], total) + h;
-    if (tid < 256 && incl >= (uint32_t)need && incl - h < (uint32_t)need) {
-      pick[0] = 255 - tid;
-      pick[1] = need - (int)(incl - h);
+    uint32_t run = block_exclusive_scan<NT>(local, wsum[sb++ & 1], total);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      if (run < (uint32_t)need && run + hv[j] >= (uint32_t)need) {
+        pick[0] = NB - 1 - (tid * BPT + j);
+        pick[1] = need - (int)run;
+        pick[2] = (int)hv[j];
+      }
+      run += hv[j];
     }
     __syncthreads();
     prefix |= (uint32_t)pick[0] << shift;
     need = pick[1];
+    sh = shift;
+    if (pick[2] == need) break;              // the whole bin is taken: no finer digit matters
   }
 
-  // index-order compaction: keys above the threshold, then the first `need`
-  // keys equal to it; the output position of key s is (keys above before s)
-  // + min(keys equal before s, need)
-  const uint32_t T = prefix;
+  // index-order compaction at the resolved digits: keys above the prefix,
+  // then the first `need` keys equal to it; the output position of key s is
+  // (keys above before s) + min(keys equal before s, need)
+  const uint32_t T = prefix >> sh;
   uint32_t GT = 0, EQ = 0;
   auto emit = [&](int cc, const uint32_t (&u)[4]) {
     uint32_t ng = 0, ne = 0;
@@ -305,8 +353,8 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(IArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int idx = cc * CH + 4 * tid + e;
       if (idx < vis) {
-        ng += u[e] > T;
-        ne += u[e] == T;
+        ng += (u[e] >> sh) > T;
+        ne += (u[e] >> sh) == T;
       }
     }
     uint32_t total;
@@ -316,11 +364,12 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(IArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int idx = cc * CH + 4 * tid + e;
       if (idx < vis) {
-        if (u[e] > T) {
+        const uint32_t v = u[e] >> sh;
+        if (v > T) {
           const uint32_t pos = lg + min(le, (uint32_t)need);
           if (pos < (uint32_t)a.topk) out[pos] = idx;     // always true; keeps every store in the row
           ++lg;
-        } else if (u[e] == T) {
+        } else if (v == T) {
           if (le < (uint32_t)need && lg + le < (uint32_t)a.topk) out[lg + le] = idx;
           ++le;
         }
@@ -345,7 +394,8 @@ int launch_indexer(const IArgs& a, int nt, int cc, void* stream) {
   const hipStream_t s = (hipStream_t)stream;
   const dim3 g1(a.nkc, a.nqt, a.batch);
   if (a.tw == 1) hipLaunchKernelGGL((idx_score_kernel<1, 1>), g1, dim3(256), 0, s, a);
-  else if (a.tw == 2) hipLaunchKernelGGL((idx_score_kernel<2, 1>), g1, dim3(256), 0, s, a);
+  else if (a.tw == 2 && a.wt == 1) hipLaunchKernelGGL((idx_score_kernel<2, 1>), g1, dim3(256), 0, s, a);
+  else if (a.tw == 2) hipLaunchKernelGGL((idx_score_kernel<2, 4>), g1, dim3(256), 0, s, a);
   else if (a.wt == 1) hipLaunchKernelGGL((idx_score_kernel<4, 1>), g1, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((idx_score_kernel<4, 4>), g1, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();

@@ -62,18 +62,20 @@ def test_plan_decode_prefill_and_mtp_shapes():
     _, md, ws = m.csmla_indexer_plan(problem(), hl)
     assert md[0] == 0x58444943 and (md[4], md[5], md[6]) == (1, 1, 256)
     assert (md[7], md[8], md[9]) == (1, 8, 2048) and ws == 32 * 2048 * 4
+    assert (md[10], md[11]) == (256, 4)
     # two rows per batch (MTP), long keys
     hl, _k = lengths(seqused_k=list(range(20000, 20064)))
     _, md, ws = m.csmla_indexer_plan(problem(batch=64, q_s=2, t1=128, table_cols=200), hl)
-    assert (md[4], md[5], md[6]) == (2, 1, 1024) and md[9] == 20096 and md[8] == 20
+    assert (md[4], md[5], md[6]) == (2, 1, 4096) and md[9] == 20096 and md[8] == 5
     assert (md[10], md[11]) == (1024, 8)
     # prefill: 16 rows per work-group
     hl, _k = lengths(cu_seqlens_q=[0, 4096, 8192], seqused_k=[1024, 1024])
     _, md, ws = m.csmla_indexer_plan(problem(batch=2, layout_q=1, q_s=0, t1=8192, table_cols=8), hl)
-    assert (md[4], md[5]) == (4, 4) and md[7] == 256 and md[9] == 1024 and (md[10], md[11]) == (256, 1)
+    assert (md[4], md[5], md[6]) == (2, 4, 1024) and md[7] == 512 and md[8] == 1 and md[9] == 1024
+    assert (md[10], md[11]) == (256, 1)
     # the same problem without host lengths plans from the shapes
     _, md2, ws2 = m.csmla_indexer_plan(problem(batch=2, layout_q=1, q_s=0, t1=8192, table_cols=8))
-    assert md2[7] == 512 and md2[9] == 1024 and md2[3] == 0 and md[3] != 0
+    assert md2[7] == 1024 and md2[9] == 1024 and md2[3] == 0 and md[3] != 0
     assert ws2 == 8192 * 1024 * 4
 
 
@@ -139,6 +141,8 @@ def test_forward_rejects_before_launch():
     assert f(fake_tensors(ws), bad) == MISMATCH                   # stride not a multiple of 64
     bad = md.copy(); bad[10] = 512
     assert f(fake_tensors(ws), bad) == MISMATCH                   # no such top-k shape
+    bad = md.copy(); bad[10], bad[11] = 256, 2
+    assert f(fake_tensors(ws), bad) == MISMATCH
     assert f(fake_tensors(ws - 4)) == WORKSPACE
     assert f(fake_tensors(ws, workspace=0x200010)) == WORKSPACE   # misaligned
     assert f(fake_tensors(ws, query=None)) == INVALID
@@ -154,3 +158,28 @@ def test_forward_rejects_before_launch():
     lib = m.load()
     assert lib.csmla_indexer_forward(ctypes.byref(p), ctypes.byref(fake_tensors(ws)), None, None) == INVALID
     assert "metadata" in m.csmla_last_error()
+
+
+def test_paged_tiny_blocks_shrink_the_key_chunk():
+    """A wave reads its block-table entries with one load per lane: its keys
+    may span at most 64 blocks, so tiny blocks shrink the chunk (and fall back
+    to waves that split keys)."""
+    for bs in (1, 2, 3, 7, 48, 128, 1024):
+        hl, _k = lengths(cu_seqlens_q=[0, 40], seqused_k=[600])
+        _, md, _ = m.csmla_indexer_plan(problem(batch=1, layout_q=1, q_s=0, t1=40, block_size=bs,
+                                                table_cols=(600 + bs - 1) // bs), hl)
+        part = md[6] // (4 // md[5])
+        worst = max((k0 + part - 1) // bs - k0 // bs + 1 for k0 in range(0, 64 * bs, 64))
+        assert worst <= 64 and part >= 64, (bs, md[4:7])
+
+
+def test_tuning_overrides(monkeypatch):
+    monkeypatch.setenv("CSMLA_IDX_TILE", "2,4")
+    monkeypatch.setenv("CSMLA_IDX_KC", "512")
+    monkeypatch.setenv("CSMLA_IDX_TOPK", "1024,2")
+    _, md, _ = m.csmla_indexer_plan(problem())
+    assert (md[4], md[5], md[6], md[10], md[11]) == (2, 4, 512, 1024, 2)
+    monkeypatch.setenv("CSMLA_IDX_TILE", "3,3")      # not a built shape: ignored
+    monkeypatch.setenv("CSMLA_IDX_TOPK", "128,1")
+    _, md, _ = m.csmla_indexer_plan(problem())
+    assert (md[4], md[5]) == (1, 1) and (md[10], md[11]) != (128, 1)

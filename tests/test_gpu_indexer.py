@@ -226,3 +226,36 @@ def test_full_prefill_sampled_rows():
     inp = make_indexer_workload("idx_csa_prefill")
     rows = _sample(inp, 40, 2) + [2047, 2048, 2049, 4095, 4096]   # around the topk = visible boundary
     check(inp, rows=sorted(set(rows)), name="idx_csa_prefill")
+
+
+@pytest.mark.parametrize("tile", ["1,1", "2,1", "2,4", "4,1", "4,4"])
+def test_every_tile_shape(tile, monkeypatch):
+    # the planner's tile choice forced: rows per wave x waves across rows
+    monkeypatch.setenv("CSMLA_IDX_TILE", tile)
+    inp = make_indexer(seed=40, q_lens=[37, 11, 2], k_lens=[700, 150, 1300], layout_q="TND",
+                       residual=[1, 2, 0], topk=64, cmp_ratio=4, block_size=64)
+    check(inp, name=f"tile_{tile}")
+
+
+@pytest.mark.parametrize("bs", [1, 3, 48])
+def test_small_and_odd_block_sizes(bs):
+    # a wave's keys span at most 64 blocks: tiny blocks shrink the key chunk
+    inp = make_indexer(seed=41, q_lens=[20, 1], k_lens=[600, 333], layout_q="TND", residual=[0, 3], topk=50,
+                       block_size=bs, g=16)
+    check(inp, name=f"block_size_{bs}")
+
+
+def test_key_chunk_override(monkeypatch):
+    monkeypatch.setenv("CSMLA_IDX_KC", "1024")
+    inp = make_indexer(seed=42, q_lens=[1] * 4, k_lens=[5000, 3000, 64, 1], layout_q="BSND", residual=[0] * 4,
+                       topk=512)
+    check(inp, name="kc1024")
+
+
+@pytest.mark.parametrize("shape", ["256,1", "256,4", "1024,2", "1024,4", "1024,8"])
+def test_every_topk_shape(shape, monkeypatch):
+    # rows of 700 to 40000 keys: most shapes also re-read chunks past the registers
+    monkeypatch.setenv("CSMLA_IDX_TOPK", shape)
+    inp = make_indexer(seed=43, q_lens=[1] * 5, k_lens=[700, 1100, 2100, 9000, 40000], layout_q="BSND",
+                       residual=[0] * 5, topk=512, g=8)
+    check(inp, name=f"topk_{shape}")
