@@ -320,7 +320,8 @@ def other(args, m, make_config, torch, np):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
     gbs = kv_bytes / (ms / 1e3) / 1e9
-    kernel = (f"dk_kernel (head groups of {plan.head_group})" if plan.head_group > 0
+    kernel = ("pf_kernel (whole-token prefill)" if plan.head_group == 64
+              else f"dk_kernel (head groups of {plan.head_group})" if plan.head_group > 0
               else f"attn_kernel (splits {plan.splits})" + (" + combine_kernel" if plan.splits > 1 else ""))
     print(f"[bench] {args.workload} forward {ms * 1e3:.2f} us, {T1} query tokens, {pairs} pairs, "
           f"{gbs:.1f} GB/s effective KV; {kernel}, grid {plan.grid}", file=sys.stderr, flush=True)
@@ -381,7 +382,7 @@ def prefill(args, m, make_config, torch, np):
     ms = start.elapsed_time(stop) / steps
     tflops = flops / (ms / 1e3) / 1e12
     print(f"[bench] prefill forward {ms * 1e3:.1f} us, {pairs} pairs, {tflops:.1f} TFLOP/s; "
-          f"splits {plan.splits} grid {plan.grid}", file=sys.stderr, flush=True)
+          f"splits {plan.splits} grid {plan.grid} head_group {plan.head_group}", file=sys.stderr, flush=True)
     res = {
         "metric": "CSA prefill query-tokens/s + fp8 MFMA TFLOP/s (% dense peak), 1 MI355X",
         "value": round(T1 / (ms / 1e3), 1), "unit": "query-tokens/s", "n_gpus": 1, "steps": steps,
@@ -394,7 +395,9 @@ def prefill(args, m, make_config, torch, np):
         "pairs_per_step": pairs,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "attn_kernel<1> (split attention, per-tile descales)"},
+                     "kernel": ("pf_kernel<1> (whole-token prefill: fp8 S^T, f16 P V, per-tile descales)"
+                                if plan.head_group == 64 else
+                                "attn_kernel<1> (split attention, per-tile descales)")},
     }
     print(json.dumps(res), flush=True)
 

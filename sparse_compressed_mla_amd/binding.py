@@ -255,7 +255,8 @@ class Plan:
 
     @property
     def head_group(self) -> int:
-        """Heads per work unit of the head-split kernel, or 0 (key-split kernel)."""
+        """Heads per work unit: 8 or 16 (head-split decode kernel), 64 (whole-token
+        prefill kernel), or 0 (key-split kernel)."""
         return int(self.metadata[12])
 
 

@@ -278,15 +278,20 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   // Small decode batches with per-token descales: split the heads instead of
   // the keys (groups of 8 heads up to 64 tokens, of 16 up to 256), so that no
   // partial outputs need merging.  Long key lists keep the key split.
+  // Prefill-sized batches (more tokens than CUs) with at most kListMax index
+  // slots per token: whole tokens per unit (all 64 heads, hg = kN1), no splits.
   int hg = 0;
   if (p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN && avg <= 8192) {
     if (T1 <= 64) hg = 8;
     else if (T1 <= 256) hg = 16;
   }
+  const bool pf_ok = p->topk <= kListMax;
+  if (T1 > 256 && pf_ok) hg = kN1;
   if (const char* env = std::getenv("CSMLA_KERNEL")) {   // tuning / test override
     if (!std::strcmp(env, "split")) hg = 0;
     else if (!std::strcmp(env, "heads8") && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN) hg = 8;
     else if (!std::strcmp(env, "heads16") && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN) hg = 16;
+    else if (!std::strcmp(env, "prefill") && pf_ok) hg = kN1;
   }
   if (hg > 0) S = 1;
   if (S > kMaxSplits) return fail(CSMLA_ERR_UNSUPPORTED, "a token needs %lld splits; at most %d are built", (long long)S, kMaxSplits);
@@ -386,7 +391,8 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
     if ((uint32_t)md[MD_PROBLEM_HASH] != problem_hash(p) || md[MD_T1] != p->t1)
       return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was planned for a different problem");
     const int S = md[MD_SPLITS], U = md[MD_UNITS], G = md[MD_GRID], HG = md[MD_HEAD_GROUP];
-    const bool hg_ok = HG == 0 || ((HG == 8 || HG == 16) && S == 1 && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN);
+    const bool hg_ok = HG == 0 || ((HG == 8 || HG == 16) && S == 1 && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN) ||
+                       (HG == kN1 && S == 1 && p->topk <= kListMax);
     const int per_token = HG > 0 ? kN1 / HG : S;
     if (S < 1 || !hg_ok || U != p->t1 * per_token || G < 1 || G > kMaxGrid || G > U)
       return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata header is inconsistent");

@@ -1852,10 +1852,619 @@ __global__ void __launch_bounds__(kThreads) debug_resolve_kernel(const KArgs a, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// prefill kernel: one work unit = one query token, all 64 heads, over the
+// token's whole key list (ori band positions, then the compacted cmp
+// entries), so no split partials exist.  QuantSparseFlashMla, 功能说明 (the
+// formula and the SWA / CSA / HCA key sets); KvQuantSparseAttnSharedkv,
+// 参数说明 (per-64-column KV descales).
+// ---------------------------------------------------------------------------
+//
+// 8 waves (two per SIMD).  The work-group walks its range of tokens as one
+// stream of 64-key tiles.  Step s computes tile s from LDS only:
+//   S^T = K Q^T in fp8 (v_mfma_f32_32x32x64_f8f6f4): wave w = kb + 2 hb + 4 dh
+//     scores keys [32 kb, +32) against heads [32 hb, +32) over D half dh, one
+//     64-wide D tile per MFMA, so that a per-tile K descale multiplies an
+//     exact fp32 partial; the two D halves meet in LDS and each wave finishes
+//     16 of its 32 keys,
+//   the softmax in log2 units against a per-head reference that moves only
+//     when a tile's maximum passes it by 2^8 (every wave then rescales its
+//     accumulators by the same factor),
+//   O^T += V^T P^T in f16 (v_mfma_f32_32x32x16_f16): wave w owns output
+//     columns [64 w, +64), which is exactly D tile w, so each V value is
+//     dequantized once, in registers, after the LDS transpose read
+//     (ds_read_b64_tr_b8): V' = e4m3 value * vds[key][w] / vmax[key] in f16,
+//     with log2 vmax[key] folded into the exponent of P.
+// At the boundary after step s one wait covers every vector-memory access of
+// the last boundary; then tile s+2 goes HBM -> LDS (global_load_lds_dwordx4
+// into the buffer tile s used) with its descales, the row addresses of tile
+// s+3 are formed from its block-table entries, and tile s+4's key positions
+// are resolved and its block-table loads issued.  Every global load is
+// consumed one boundary after it is issued.
+// The K side stays fp8 (exact products); V' and P carry f16 rounding
+// (relative 2^-11).
+//
+// MFMA operand k-slots: in the P V product, lane group g (lanes 32 g..) slot i
+// of the 16-key step rho stands for key 16 rho + 8 (i >> 2) + 4 g + (i & 3):
+// the byte order of the transpose read, and the order in which the S^T
+// accumulator holds a wave's keys (D layout of the 32x32 MFMA: lane l, reg r
+// = column l % 32, row 8 (r >> 2) + 4 (l >> 5) + (r & 3)).
+
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr float kPfTau = 8.0f;   // a tile maximum above the reference + 8 moves the reference
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+struct LdsPF {
+  static constexpr int kTiles = 0;                          // 2 x 32 KiB fp8 tiles (XOR-swizzled chunks)
+  static constexpr int kXch = 2 * kTileBytes;               // f32 [8 waves][64 lanes][8]: S^T halves for the partner
+  static constexpr int kP = kXch + kPfThreads * 32;         // f16 P [64 heads][8 groups of 8 keys], groups swizzled
+  static constexpr int kSc = kP + 64 * 64 * 2;              // 2 sets of per-key scales (tile parity)
+  static constexpr int kScKs = 0;                           //   f32 [8 D tiles][64 keys]: K descales (per-tile mode)
+  static constexpr int kScVs = 2048;                        //   f16 [8 D tiles][64 slots]: vds / vmax (per-tile mode)
+  static constexpr int kScLam = 3072;                       //   f32 [64]: log2 vmax (-inf: empty slot)
+  static constexpr int kScInv = 3328;                       //   f32 [64]: 1 / vmax
+  static constexpr int kScKd = 3584;                        //   f32 [64]: the key's descale (per-token mode)
+  static constexpr int kScBytes = 3840;
+  static constexpr int kList = kSc + 2 * kScBytes;          // int [kListMax]: compacted cmp indices (cursor token)
+  static constexpr int kMax = kList + 4 * kListMax;         // f32 [8 waves][64]: tile maxima per head
+  static constexpr int kL = kMax + 4 * kPfThreads;          // f32 [8 waves][64]: row sums per head (epilogue)
+  static constexpr int kMisc = kL + 4 * kPfThreads;         // int: [0,16) compaction, [16,18) flags, [24,32) tiles ring
+  // The cursor is at most 5 tokens ahead of the token whose successor's entry
+  // is read (it resolves 4 tiles ahead and enters the next token as soon as
+  // one is done), so 8 entries are never overwritten before they are read.
+  static constexpr int kFlag = 16, kRing = 24, kRingMask = 7;
+  static constexpr int kQ = kMisc + 4 * 64;                 // fp8 q of the current token [64 heads][512], swizzled like a tile
+  static constexpr int kBytes = kQ + kN1 * kD;
+};
+static_assert(LdsPF::kBytes <= 160 * 1024, "LDS");
+
+__device__ __forceinline__ v16f mma_f16(h8_t a, h8_t b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Eight e4m3 codes (two dwords, byte order) as f16 (exact: every e4m3 value
+// is an f16 value).
+__device__ __forceinline__ h8_t e4m3x8_f16(v2i x) {
+  const h2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, false);
+  const h2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, true);
+  const h2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, false);
+  const h2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, true);
+  return h8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// Slot of key k (0..63) in the P-V operand order: 16 rho + 8 g + i.
+__device__ __forceinline__ int pf_slot(int k) {
+  const int kk = k & 15;
+  return (k & 48) + 8 * ((kk >> 2) & 1) + (kk & 3) + 4 * (kk >> 3);
+}
+
+// The resolution cursor: the token whose tiles are being resolved, and the
+// prefetched lengths and first index slots of the token after it.
+struct PfCursor {
+  int u, tile, tiles, n_o, n_c;
+  Tok k;
+  TokLens nl;
+  IdxPre<kPfThreads> nip;
+};
+
+// Index slots [0, kIdxPre) of token t as loaded (slots past topk read the
+// last slot); pf_idx_fix replaces those by -1 where they are used, so that
+// the loads stay in flight until then.
+__device__ __forceinline__ IdxPre<kPfThreads> pf_idx_raw(const KHdr& a, int t) {
+  IdxPre<kPfThreads> p;
+  const int* row = a.topk > 0 ? a.idx + (size_t)t * a.topk : reinterpret_cast<const int*>(g_zero_row);
+  const int last = max(a.topk - 1, 0);
+  const int tid = opaque((int)threadIdx.x);
+#pragma unroll
+  for (int m = 0; m < IdxPre<kPfThreads>::kRounds; ++m) p.v[m] = row[min(m * kPfThreads + tid, last)];
+  return p;
+}
+
+__device__ __forceinline__ IdxPre<kPfThreads> pf_idx_fix(const KHdr& a, IdxPre<kPfThreads> p) {
+  const int tid = opaque((int)threadIdx.x);
+#pragma unroll
+  for (int m = 0; m < IdxPre<kPfThreads>::kRounds; ++m) p.v[m] = (m * kPfThreads + tid < a.topk) ? p.v[m] : -1;
+  return p;
+}
+
+// Enter token c.u (whole-work-group call): its context, the compaction of
+// its index slots into `list`, its tile count (at least one: a token with no
+// keys still takes one step, which writes its output) into the tiles ring,
+// and the prefetch of the next token's lengths and index slots.
+__device__ __forceinline__ void pf_enter(const KHdr& a, PfCursor& c, int u_end, int* list, int* misc) {
+  c.k = token_ctx(a, c.u, c.nl);
+  c.n_o = c.k.hi - c.k.lo;
+  c.n_c = 0;
+  if (a.topk > 0) c.n_c = compact_indices<kPfThreads>(a, c.k, c.u, list, misc, 0, pf_idx_fix(a, c.nip));
+  else if (a.has_cmp) c.n_c = c.k.vis;
+  c.n_c = __builtin_amdgcn_readfirstlane(c.n_c);
+  c.tiles = max(1, (c.n_o + c.n_c + kTileKeys - 1) / kTileKeys);
+  c.tile = 0;
+  if (threadIdx.x == 0) misc[LdsPF::kRing + (c.u & LdsPF::kRingMask)] = c.tiles | (c.k.valid ? 0 : 0x10000);
+  if (c.u + 1 < u_end) {
+    c.nl = token_lens(a, c.u + 1);
+    c.nip = pf_idx_raw(a, c.u + 1);
+  }
+}
+
+// One key slot of a tile (thread tid serves key tid >> 3 and its 64-byte
+// part tid & 7): the block-table entry (in flight) and what locates the row.
+struct PfKey {
+  int blk;
+  int64_t rc;   // paged: offset in the block; else the row
+  bool cmp, ok;
+};
+
+__device__ __forceinline__ PfKey pf_resolve(const KHdr& a, const Sides& sd, const PfCursor& c, const int* list,
+                                            bool live) {
+  // Branch-free around the table load (a branch would make the compiler wait
+  // for it at the join): without a paged key it reads the zero row.
+  PfKey r;
+  const int n = c.n_o + c.n_c;
+  const int key = kTileKeys * c.tile + (opaque((int)threadIdx.x) >> 3);
+  const bool any = live && n > 0;   // uniform
+  r.ok = live && key < n;
+  bool is_cmp = false;
+  int j = 0;
+  if (any) j = key_pos(a, c.k, c.n_o, min(key, n - 1), list, 0, is_cmp);
+  r.cmp = is_cmp;
+  const bool paged = a.layout_kv == 2;
+  const BlockPos bp = block_pos(sd, is_cmp, j);
+  const int32_t* tab = is_cmp ? sd.c.tab : sd.o.tab;
+  const int cols = is_cmp ? sd.c.cols : sd.o.cols;
+  const int32_t* tp = (paged && any) ? tab + (size_t)c.k.b * cols + bp.q : reinterpret_cast<const int32_t*>(g_zero_row);
+  r.blk = *tp;
+  r.rc = paged ? (int64_t)bp.r : row_of(a, sd, c.k, is_cmp, j, 0, 0);
+  return r;
+}
+
+// Next tile of the stream: resolve it, then advance the cursor (entering
+// the next token when this one is done).
+__device__ __forceinline__ PfKey pf_next(const KHdr& a, const Sides& sd, PfCursor& c, int u_end, int* list,
+                                         int* misc) {
+  const bool live = c.u < u_end;
+  const PfKey r = pf_resolve(a, sd, c, list, live);
+  if (live) {
+    if (++c.tile == c.tiles) {
+      if (++c.u < u_end) pf_enter(a, c, u_end, list, misc);
+    }
+  }
+  return r;
+}
+
+// A key row's source address and the address of this thread's descale of
+// it (per-tile: the one of D tile tid & 7), from the block-table entry
+// (which must have landed).  No loads.
+struct PfSrc {
+  uint64_t addr;
+  const float* ds;
+  bool ok;
+};
+
+template <int PER_TILE>
+__device__ __forceinline__ PfSrc pf_src(const Sides& sd, int layout_kv, const PfKey& k) {
+  const int part = opaque((int)threadIdx.x) & 7;
+  int64_t row = k.rc;
+  if (layout_kv == 2) row += (int64_t)k.blk * (k.cmp ? sd.c.bs : sd.o.bs);
+  const uint8_t* src = (k.cmp ? sd.c.kv : sd.o.kv) + row * kD;
+  const float* dsp = (k.cmp ? sd.c.ds : sd.o.ds) + row * (PER_TILE ? 8 : 1) + (PER_TILE ? part : 0);
+  PfSrc r;
+  r.addr = (uint64_t)(uintptr_t)(k.ok ? src : g_zero_row);
+  r.ds = gptr(k.ok ? dsp : reinterpret_cast<const float*>(g_zero_row));
+  r.ok = k.ok;
+  return r;
+}
+
+// Row tid >> 3, bytes [64 (tid & 7), +64), into a swizzled 64-row buffer.
+__device__ __forceinline__ void pf_put_row(uint8_t* base, const v4i (&x)[4]) {
+  const int tid = opaque((int)threadIdx.x), row = tid >> 3, part = tid & 7, f = swz(row);
+  uint8_t* tr = base + row * kD;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) *(v4i*)(tr + 16 * ((4 * part + c) ^ f)) = x[c];
+}
+
+// The tile's 64 rows HBM -> LDS (global_load_lds_dwordx4, M0 = LDS row pair,
+// lane l writes chunk l % 32 of row 2 mi + l / 32 and reads source chunk
+// (l % 32) ^ swz(row)).  Wave w moves its own keys [8 w, +8), whose addresses
+// its lanes already hold (lane 8 k has key 8 w + k).  Not ordered by the
+// compiler: the step ends with a wait for every vector-memory access.
+__device__ __forceinline__ void pf_issue(uint8_t* tb, const PfSrc& r, int w) {
+  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int k = 2 * mi + g, row = 8 * w + k;
+    const int lo = __shfl((int)(uint32_t)r.addr, 8 * k), hi = __shfl((int)(uint32_t)(r.addr >> 32), 8 * k);
+    const uint64_t src = (((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo) + 16u * (uint32_t)(li ^ swz(row));
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + (8 * w + 2 * mi) * kD));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "m0");
+  }
+}
+
+// The tile's per-key scales into scale set `set`.  Empty slots: zero
+// descales, lam = -inf.
+template <int PER_TILE>
+__device__ __forceinline__ void pf_scales(uint8_t* set, float s, bool ok) {
+  using L = LdsPF;
+  const int tid = opaque((int)threadIdx.x), key = tid >> 3, part = tid & 7;
+  float mx = s;
+  int nan = (s != s) ? 1 : 0;
+  if constexpr (PER_TILE) {   // the key's 8 descales sit in 8 consecutive lanes
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, m));
+      nan |= __shfl_xor(nan, m);
+    }
+  }
+  float mxd = (mx == 0.f) ? kMinDescale : mx;
+  if (nan) mxd = __builtin_nanf("");        // a NaN descale poisons the key
+  const float lam = ok ? __log2f(mxd) : kNegInf;
+  const float inv = ok ? 1.0f / mxd : 0.f;
+  if constexpr (PER_TILE) {
+    reinterpret_cast<float*>(set + L::kScKs)[part * 64 + key] = s;
+    reinterpret_cast<_Float16*>(set + L::kScVs)[part * 64 + pf_slot(key)] = (_Float16)(s * inv);
+  }
+  if (part == 0) {
+    reinterpret_cast<float*>(set + L::kScLam)[key] = lam;
+    reinterpret_cast<float*>(set + L::kScInv)[key] = inv;
+    reinterpret_cast<float*>(set + L::kScKd)[key] = s;
+  }
+}
+
+// S^T of the wave's 32 keys x 32 heads over D half dh (per-tile: each D
+// tile's exact partial times that tile's K descale).
+// The 32 bytes [256 dh + 64 s4 + 32 g, +32) of row r of a swizzled buffer
+// (an MFMA operand of 32x32x64: lane group g holds k = 32 g .. 32 g + 31).
+__device__ __forceinline__ v8i pf_op(const uint8_t* buf, int r, int dh, int s4, int g) {
+  const uint8_t* row = buf + r * kD;
+  const int f = swz(r), cb = 16 * dh + 8 * (s4 >> 1), cl = 4 * (s4 & 1) + 2 * g;
+  const v4i lo = *(const v4i*)(row + 16 * (cb + (cl ^ f)));
+  const v4i hi = *(const v4i*)(row + 16 * (cb + ((cl + 1) ^ f)));
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <int PER_TILE>
+__device__ __forceinline__ v16f pf_qk(const uint8_t* tb, const uint8_t* qb, const float* ks, int kb, int hb, int dh,
+                                      int lane_in) {
+  const int lane = opaque(lane_in), g = lane >> 5, kr = 32 * kb + (lane & 31), hr = 32 * hb + (lane & 31);
+  v8i ka = pf_op(tb, kr, dh, 0, g), qa = pf_op(qb, hr, dh, 0, g);
+  v16f S = v16f{};
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    v8i kn = ka, qn = qa;
+    if (s4 < 3) {
+      kn = pf_op(tb, kr, dh, s4 + 1, g);
+      qn = pf_op(qb, hr, dh, s4 + 1, g);
+    }
+    const v8i kop = ka, qop = qa;
+    ka = kn;
+    qa = qn;
+    if constexpr (PER_TILE) {
+      const v16f p = mma(kop, qop, v16f{});
+      const float* kst = ks + (4 * dh + s4) * 64 + 32 * kb + 4 * g;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const v4f kv = *(const v4f*)(kst + 8 * q4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[4 * q4 + r] += kv[r] * p[4 * q4 + r];
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one D tile's partial live at a time
+    } else {
+      S = mma(kop, qop, S);
+    }
+  }
+  return S;
+}
+
+// O^T[64 w + 32 db + .., heads] += V'^T P^T over the tile's 64 keys.
+template <int PER_TILE>
+__device__ __forceinline__ void pf_pv(const uint8_t* tb, const _Float16* vs, const uint8_t* pb, int w, int lane_in,
+                                      v16f (&acc)[2][2]) {
+  const int lane = opaque(lane_in), g = lane >> 5, trx = (lane >> 4) & 1;
+  const int vkey = 8 * ((lane >> 3) & 1) + 4 * g + ((lane >> 1) & 3);
+#pragma unroll
+  for (int rho = 0; rho < 4; ++rho) {
+    h8_t pop[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int h = 32 * hb + (lane & 31);
+      pop[hb] = __builtin_bit_cast(h8_t, *(const v4i*)(pb + h * 128 + 16 * ((2 * rho + g) ^ (h & 7))));
+    }
+    h8_t vsc;
+    if constexpr (PER_TILE) vsc = *(const h8_t*)(vs + w * 64 + 16 * rho + 8 * g);
+    const int key = 16 * rho + vkey, f = swz(key);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int J = 2 * w + db;
+      const uint8_t* src = tb + key * kD + 16 * ((2 * J + trx) ^ f) + 8 * (lane & 1);
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)src);
+      h8_t va = e4m3x8_f16(x);
+      if constexpr (PER_TILE) va = va * vsc;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) acc[db][hb] = mma_f16(va, pop[hb], acc[db][hb]);
+    }
+  }
+}
+
+// Token t's query: this thread's 64 bytes of head tid >> 3 (for the LDS
+// copy), and the lane's exponent factor softmax_scale * log2(e) * q_descale
+// of head h.
+struct PfQ {
+  v4i x[4];
+  float qd;   // q descale of head h (the factor is formed where it is used)
+};
+
+__device__ __forceinline__ PfQ pf_load_q(const KHdr& a, int t, int h) {
+  PfQ r;
+  const int tid = opaque((int)threadIdx.x);
+  const uint8_t* src = a.q + ((size_t)t * kN1 + (tid >> 3)) * kD + 64 * (tid & 7);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r.x[c] = *(const v4i*)(src + 16 * c);
+  r.qd = a.q_ds[a.q_ds_per_head ? (size_t)t * kN1 + h : (size_t)t];
+  return r;
+}
+
+template <int PER_TILE>
+__device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
+  using L = LdsPF;
+  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5;
+  const int kb = w & 1, hb = (w >> 1) & 1, dh = w >> 2;
+  const HdrRegs hr = load_hdr_regs(ap);
+  const KHdr a0 = hdr_view(hr);
+  const int G = a0.grid, bid = blockIdx.x;
+  const int lw = (G % 8 == 0) ? ((bid & 7) * (G >> 3) + (bid >> 3)) : bid;   // one XCD per contiguous range
+  int u_begin = lw, u_end = lw + 1;
+  if (a0.n_units != G) {
+    u_begin = ap->starts[lw];
+    u_end = ap->starts[lw + 1];
+  }
+  if (u_begin >= u_end) return;   // uniform over the work-group
+  int* list = reinterpret_cast<int*>(smem + L::kList);
+  int* misc = reinterpret_cast<int*>(smem + L::kMisc);
+  float* xch = reinterpret_cast<float*>(smem + L::kXch);
+  float* maxb = reinterpret_cast<float*>(smem + L::kMax);
+  float* lbuf = reinterpret_cast<float*>(smem + L::kL);
+  uint8_t* pbuf = smem + L::kP;
+  if (threadIdx.x < 2) misc[L::kFlag + threadIdx.x] = 0;
+
+  // sink logits (log2 units) of the lane's two output heads
+  float sink[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) sink[x] = a0.sinks ? a0.sinks[32 * x + (lane & 31)] * kLog2e : kNegInf;
+
+  // ---- fill the pipeline ----
+  // In the loop, every global load is issued right after a step boundary
+  // (after that boundary's DMA) and consumed only at the next boundary,
+  // after its wait for every vector-memory access: a compiler-placed wait
+  // between the two would also wait for the DMA, which it does not count.
+  PfCursor cur;
+  cur.u = u_begin;
+  cur.nl = token_lens(a0, u_begin);
+  cur.nip = pf_idx_raw(a0, u_begin);
+  pf_enter(a0, cur, u_end, list, misc);
+  PfKey kC;        // tile s+3: block-table entry in flight
+  PfSrc rB;        // tile s+2: row address
+  float sB;        // tile s+2: descale in flight
+  {
+    const Sides sd = cache_sides(a0);
+    const PfKey k0 = pf_next(a0, sd, cur, u_end, list, misc);
+    const PfSrc r0 = pf_src<PER_TILE>(sd, a0.layout_kv, k0);
+    const float s0 = *r0.ds;
+    const PfKey k1 = pf_next(a0, sd, cur, u_end, list, misc);
+    const PfSrc r1 = pf_src<PER_TILE>(sd, a0.layout_kv, k1);
+    const float s1 = *r1.ds;
+    const PfKey k2 = pf_next(a0, sd, cur, u_end, list, misc);
+    rB = pf_src<PER_TILE>(sd, a0.layout_kv, k2);
+    sB = *rB.ds;
+    kC = pf_next(a0, sd, cur, u_end, list, misc);
+    pf_issue(smem + L::kTiles, r0, w);
+    pf_issue(smem + L::kTiles + kTileBytes, r1, w);
+    pf_scales<PER_TILE>(smem + L::kSc, s0, r0.ok);
+    pf_scales<PER_TILE>(smem + L::kSc + L::kScBytes, s1, r1.ok);
+  }
+  const int hq0 = 32 * hb + (lane & 31);   // the lane's head in S^T and the softmax
+  PfQ qn = pf_load_q(a0, u_begin, hq0);
+  pf_put_row(smem + L::kQ, qn.x);
+  float qc = a0.scale_log2 * qn.qd;
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // tiles 0 and 1 landed
+  lds_barrier();
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) acc[db][x] = v16f{};
+  float Macc[2] = {kNegInf, kNegInf};
+  float lsum = 0.f;
+  int u = u_begin, ti = 0;
+  int ring = __builtin_amdgcn_readfirstlane(misc[L::kRing + (u & L::kRingMask)]);
+  int tiles_u = ring & 0xffff;
+  bool valid_u = (ring >> 16) == 0;
+  // qn holds the q of the token that begins with the next tile (loaded after
+  // the last boundary, written to LDS at the next one)
+  bool qpend = tiles_u == 1 && u + 1 < u_end;
+  if (qpend) qn = pf_load_q(a0, u + 1, hq0);
+
+  for (int s = 0;; ++s) {
+    const int buf = s & 1, par = s & 1;
+    const int ln = opaque(lane), gg = ln >> 5, hq = 32 * hb + (ln & 31);
+    const uint8_t* tb = smem + L::kTiles + buf * kTileBytes;
+    const uint8_t* set = smem + L::kSc + buf * L::kScBytes;
+    // ---- S^T, the D halves exchanged ----
+    const v16f S = pf_qk<PER_TILE>(tb, smem + L::kQ, reinterpret_cast<const float*>(set + L::kScKs), kb, hb, dh, ln);
+    {
+      float* dst = xch + (w * 64 + ln) * 8;
+      if (dh) {
+        *(v4f*)dst = v4f{S[0], S[1], S[2], S[3]};
+        *(v4f*)(dst + 4) = v4f{S[4], S[5], S[6], S[7]};
+      } else {
+        *(v4f*)dst = v4f{S[8], S[9], S[10], S[11]};
+        *(v4f*)(dst + 4) = v4f{S[12], S[13], S[14], S[15]};
+      }
+    }
+    lds_barrier();
+    if (threadIdx.x == 0) misc[L::kFlag + (par ^ 1)] = 0;   // the previous step's flag was read by all
+    float E[8];
+    {
+      const float* src = xch + ((w ^ 4) * 64 + ln) * 8;
+      const v4f x0 = *(const v4f*)src, x1 = *(const v4f*)(src + 4);
+      const int kt = 32 * kb + 16 * dh + 4 * gg;
+      const float* lamp = reinterpret_cast<const float*>(set + L::kScLam) + kt;
+      const float* kdp = reinterpret_cast<const float*>(set + L::kScKd) + kt;
+      const v4f la0 = *(const v4f*)lamp, la1 = *(const v4f*)(lamp + 8);
+      v4f kd0 = v4f{1.f, 1.f, 1.f, 1.f}, kd1 = kd0;
+      if constexpr (!PER_TILE) {
+        kd0 = *(const v4f*)kdp;
+        kd1 = *(const v4f*)(kdp + 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s0 = (dh ? S[8 + i] : S[i]) + x0[i];
+        const float s1 = (dh ? S[12 + i] : S[4 + i]) + x1[i];
+        E[i] = s0 * (qc * kd0[i]) + la0[i];
+        E[4 + i] = s1 * (qc * kd1[i]) + la1[i];
+      }
+    }
+    float m = E[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = fmaxf(m, E[i]);
+    m = fmaxf(m, __shfl_xor(m, 32));
+    maxb[w * 64 + ln] = m;
+    const float Ms = hb ? Macc[1] : Macc[0];
+    if (__ballot(m > Ms + kPfTau) && ln == 0) misc[L::kFlag + par] = 1;
+    lds_barrier();
+    if (__builtin_amdgcn_readfirstlane(misc[L::kFlag + par])) {   // rare: the reference moves
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        float mn = Macc[x];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) mn = fmaxf(mn, maxb[((y & 1) + 2 * x + 4 * (y >> 1)) * 64 + (ln & 31)]);
+        const float fa = (Macc[x] == kNegInf) ? 0.f : exp2f(Macc[x] - mn);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) acc[db][x] *= fa;
+        if (x == hb) lsum *= fa;
+        Macc[x] = mn;
+      }
+    }
+    // ---- P ----
+    {
+      const float* invp = reinterpret_cast<const float*>(set + L::kScInv) + 32 * kb + 16 * dh + 4 * gg;
+      const v4f iv0 = *(const v4f*)invp, iv1 = *(const v4f*)(invp + 8);
+      const float Mh = hb ? Macc[1] : Macc[0];
+      const float Mz = (Mh == kNegInf) ? 0.f : Mh;
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(E[i] - Mz);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lsum += p[i] * iv0[i] + p[4 + i] * iv1[i];
+      const v4i pk = v4i{(int)pk_f16(p[0], p[1]), (int)pk_f16(p[2], p[3]), (int)pk_f16(p[4], p[5]),
+                         (int)pk_f16(p[6], p[7])};
+      const int q = 2 * (2 * kb + dh) + gg;
+      *(v4i*)(pbuf + hq * 128 + 16 * (q ^ (hq & 7))) = pk;
+    }
+    lds_barrier();
+    // ---- O^T += V'^T P^T ----
+    pf_pv<PER_TILE>(tb, reinterpret_cast<const _Float16*>(set + L::kScVs), pbuf, w, ln, acc);
+
+    // ---- step boundary: every vector-memory access of the last boundary
+    // (tile s+1's DMA, descales, table entries, q, prefetches, stores) done ----
+    const bool last = ti + 1 == tiles_u;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    {
+      const KHdr a = hdr_view(hr);
+      const Sides sd = cache_sides(a);
+      if (qpend) pf_put_row(smem + L::kQ, qn.x);                      // token of tile s+1 (S^T of s is done)
+      const PfSrc rC = pf_src<PER_TILE>(sd, a.layout_kv, kC);         // tile s+3: address
+      lds_barrier();                                                  // tile s is done in every wave
+      pf_issue(smem + L::kTiles + buf * kTileBytes, rB, w);          // tile s+2 into the buffer tile s leaves
+      pf_scales<PER_TILE>(smem + L::kSc + buf * L::kScBytes, sB, rB.ok);   // and into its scale set
+      sB = *rC.ds;                                                    // tile s+3: descale load
+      rB = rC;
+      kC = pf_next(a, sd, cur, u_end, list, misc);                    // tile s+4: block-table loads
+    }
+    if (last) {
+      // ---- epilogue of token u ----
+      const KHdr ae = hdr_view(hr);
+      lbuf[w * 64 + ln] = lsum + __shfl_xor(lsum, 32);
+      lds_barrier();
+      const int t = u;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int h = 32 * x + (ln & 31);
+        float Ls = 0.f;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) Ls += lbuf[((y & 1) + 2 * x + 4 * (y >> 1)) * 64 + (ln & 31)];
+        const float M = Macc[x], sg = sink[x];
+        const float Mf = fmaxf(M, sg);
+        float sc = 0.f, lse_v = kNegInf;
+        if (valid_u && Mf != kNegInf) {
+          const float af = (M == kNegInf) ? 0.f : exp2f(M - Mf);
+          const float Lf = af * Ls + ((sg == kNegInf) ? 0.f : exp2f(sg - Mf));
+          sc = af / Lf;
+          lse_v = (Mf + __log2f(Lf)) * kLn2;
+        }
+        if (ae.lse && w == 0 && gg == 0) ae.lse[(size_t)t * kN1 + h] = lse_v;
+        uint16_t* orow = ae.out + ((size_t)t * kN1 + h) * kD + 64 * w + 4 * gg;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v16f& o = acc[db][x];
+            *(uint2*)(orow + 32 * db + 8 * q) =
+                pack_bf16x4(sc * o[4 * q], sc * o[4 * q + 1], sc * o[4 * q + 2], sc * o[4 * q + 3]);
+          }
+      }
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) acc[db][x] = v16f{};
+      Macc[0] = Macc[1] = kNegInf;
+      lsum = 0.f;
+      if (++u == u_end) break;
+      ti = 0;
+      ring = __builtin_amdgcn_readfirstlane(misc[L::kRing + (u & L::kRingMask)]);
+      tiles_u = ring & 0xffff;
+      valid_u = (ring >> 16) == 0;
+      qc = ae.scale_log2 * qn.qd;
+    } else {
+      ++ti;
+    }
+    // the token after u begins with tile s+2: its q now, written at the next boundary
+    qpend = (ti + 1 == tiles_u) && u + 1 < u_end;
+    if (qpend) {
+      const KHdr a = hdr_view(hr);
+      qn = pf_load_q(a, u + 1, 32 * hb + (opaque(lane) & 31));
+    }
+  }
+  // every wave's last loads (of the stream past its end) settle before exit
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+}
+
+template <int PER_TILE>
+__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(kPfWaves / 4, kPfWaves / 4)))
+pf_kernel(const KArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LdsPF::kBytes];
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  pf_body<PER_TILE>((KArgPtr)__builtin_amdgcn_kernarg_segment_ptr(), smem, w);
+}
+
 }  // namespace
 
 int launch_forward(const KArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (a.hg == kN1) {
+    if (a.scale_mode == 1)
+      hipLaunchKernelGGL(pf_kernel<1>, dim3(a.grid), dim3(kPfThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(pf_kernel<0>, dim3(a.grid), dim3(kPfThreads), 0, st, a);
+    return (int)hipGetLastError();
+  }
   if (a.hg > 0) {
     hipLaunchKernelGGL(dk_kernel, dim3(a.grid), dim3(kDkThreads), 0, st, a);
     return (int)hipGetLastError();

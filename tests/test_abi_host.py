@@ -98,9 +98,17 @@ def test_plan_head_split_for_small_decode_batches(monkeypatch):
     _, md, _ = m.csmla_plan(base_problem(batch=128, t1=128))
     assert md[12] == 16 and md[6] == 128 * 4
     _, md, _ = m.csmla_plan(base_problem(batch=512, t1=512))
-    assert md[12] == 0                                    # large batches: key split
+    assert md[12] == 64 and md[5] == 1 and md[6] == 512   # prefill-sized batches: whole tokens
+    _, md, _ = m.csmla_plan(base_problem(batch=512, t1=512, kv_scale_mode=1))
+    assert md[12] == 64 and md[6] == 512                  # also with per-tile descales
     _, md, _ = m.csmla_plan(base_problem(kv_scale_mode=1))
-    assert md[12] == 0                                    # per-tile descales: key split
+    assert md[12] == 0                                    # small per-tile batches: key split
+    monkeypatch.setenv("CSMLA_KERNEL", "prefill")
+    _, md, _ = m.csmla_plan(base_problem())
+    assert md[12] == 64 and md[6] == 32 and md[7] == 32
+    monkeypatch.setenv("CSMLA_KERNEL", "split")
+    _, md, _ = m.csmla_plan(base_problem(batch=512, t1=512))
+    assert md[12] == 0
     monkeypatch.setenv("CSMLA_KERNEL", "heads16")
     _, md, _ = m.csmla_plan(base_problem())
     assert md[12] == 16 and md[6] == 32 * 4

@@ -22,9 +22,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 # Every test runs with the planner's own kernel choice ("auto": the head-split
-# kernel for small per-token batches, the key-split kernel otherwise) and with
-# each kernel forced, so that both paths meet the same bar on the same cases.
-KERNEL_MODES = ["auto", "split", "heads16"]
+# kernel for small per-token batches, the whole-token prefill kernel for more
+# than 256 query tokens, the key-split kernel otherwise) and with each kernel
+# forced, so that every path meets the same bar on the same cases.
+KERNEL_MODES = ["auto", "split", "heads16", "prefill"]
 
 
 @pytest.fixture(autouse=True, params=KERNEL_MODES)
@@ -124,8 +125,8 @@ def test_cfg4_csa_mtp_long():
 
 
 def test_cfg5_csa_prefill_sampled(kernel_mode):
-    if kernel_mode != "auto":
-        pytest.skip("per-tile descales always take the key-split kernel")
+    if kernel_mode not in ("auto", "split"):
+        pytest.skip("auto is the prefill kernel here; heads16 does not take per-tile descales")
     inp_g = make_config(5, device=DEV)
     inp = inp_g.to("cpu")
     T1 = inp.t1
