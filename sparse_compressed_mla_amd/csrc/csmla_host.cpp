@@ -305,7 +305,15 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   std::vector<double> pre(n_units + 1, 0.0);
   for (int u = 0; u < n_units; ++u) {
     const auto& c = cost[u / per_token];
-    pre[u + 1] = pre[u] + (double)(c.n_o + c.n_c_up) / (double)S + 48.0;
+    if (hg == kN1) {
+      // whole-token prefill kernel: a token takes at least one 64-key tile, and
+      // its output, sink and lse plus the next token's set-up cost about 1.2
+      // tiles more (measured on MI355X)
+      const int64_t tiles = std::max<int64_t>(1, (c.n_o + c.n_c_up + kTileKeys - 1) / kTileKeys);
+      pre[u + 1] = pre[u] + (double)(tiles * kTileKeys) + 80.0;
+    } else {
+      pre[u + 1] = pre[u] + (double)(c.n_o + c.n_c_up) / (double)S + 48.0;
+    }
   }
   std::vector<int32_t> starts(G + 1);
   starts[0] = 0;

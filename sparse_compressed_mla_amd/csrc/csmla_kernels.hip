@@ -1917,7 +1917,10 @@ struct LdsPF {
   // one is done), so 8 entries are never overwritten before they are read.
   static constexpr int kFlag = 16, kRing = 24, kRingMask = 7;
   static constexpr int kQ = kMisc + 4 * 64;                 // fp8 q of the current token [64 heads][512], swizzled like a tile
-  static constexpr int kBytes = kQ + kN1 * kD;
+  static constexpr int kKaddr = kQ + kN1 * kD;              // u64 [2][64]: row addresses (tile parity), from wave 0
+  static constexpr int kKds = kKaddr + 2 * 64 * 8;          // u64 [2][64]: descale addresses (tile parity), from wave 0
+  static constexpr int kNvalid = kKds + 2 * 64 * 8;         // int [2]: keys of the tile (tile parity)
+  static constexpr int kBytes = kNvalid + 16;
 };
 static_assert(LdsPF::kBytes <= 160 * 1024, "LDS");
 
@@ -1994,8 +1997,8 @@ __device__ __forceinline__ void pf_enter(const KHdr& a, PfCursor& c, int u_end, 
   }
 }
 
-// One key slot of a tile (thread tid serves key tid >> 3 and its 64-byte
-// part tid & 7): the block-table entry (in flight) and what locates the row.
+// Key resolution runs in wave 0 only, one key of a tile per lane: the
+// block-table entry (in flight) and what locates the row.
 struct PfKey {
   int blk;
   int64_t rc;   // paged: offset in the block; else the row
@@ -2008,7 +2011,7 @@ __device__ __forceinline__ PfKey pf_resolve(const KHdr& a, const Sides& sd, cons
   // for it at the join): without a paged key it reads the zero row.
   PfKey r;
   const int n = c.n_o + c.n_c;
-  const int key = kTileKeys * c.tile + (opaque((int)threadIdx.x) >> 3);
+  const int key = kTileKeys * c.tile + (opaque((int)threadIdx.x) & 63);
   const bool any = live && n > 0;   // uniform
   r.ok = live && key < n;
   bool is_cmp = false;
@@ -2025,23 +2028,18 @@ __device__ __forceinline__ PfKey pf_resolve(const KHdr& a, const Sides& sd, cons
   return r;
 }
 
-// Next tile of the stream: resolve it, then advance the cursor (entering
-// the next token when this one is done).
-__device__ __forceinline__ PfKey pf_next(const KHdr& a, const Sides& sd, PfCursor& c, int u_end, int* list,
-                                         int* misc) {
-  const bool live = c.u < u_end;
-  const PfKey r = pf_resolve(a, sd, c, list, live);
-  if (live) {
+// Move the cursor past its tile (every wave: entering a token compacts its
+// index slots with the whole work-group).
+__device__ __forceinline__ void pf_advance(const KHdr& a, PfCursor& c, int u_end, int* list, int* misc) {
+  if (c.u < u_end) {
     if (++c.tile == c.tiles) {
       if (++c.u < u_end) pf_enter(a, c, u_end, list, misc);
     }
   }
-  return r;
 }
 
-// A key row's source address and the address of this thread's descale of
-// it (per-tile: the one of D tile tid & 7), from the block-table entry
-// (which must have landed).  No loads.
+// A key's row address and the address of its descales (per-tile: all eight),
+// from its block-table entry (which must have landed).  No loads.
 struct PfSrc {
   uint64_t addr;
   const float* ds;
@@ -2050,11 +2048,10 @@ struct PfSrc {
 
 template <int PER_TILE>
 __device__ __forceinline__ PfSrc pf_src(const Sides& sd, int layout_kv, const PfKey& k) {
-  const int part = opaque((int)threadIdx.x) & 7;
   int64_t row = k.rc;
   if (layout_kv == 2) row += (int64_t)k.blk * (k.cmp ? sd.c.bs : sd.o.bs);
   const uint8_t* src = (k.cmp ? sd.c.kv : sd.o.kv) + row * kD;
-  const float* dsp = (k.cmp ? sd.c.ds : sd.o.ds) + row * (PER_TILE ? 8 : 1) + (PER_TILE ? part : 0);
+  const float* dsp = (k.cmp ? sd.c.ds : sd.o.ds) + row * (PER_TILE ? 8 : 1);
   PfSrc r;
   r.addr = (uint64_t)(uintptr_t)(k.ok ? src : g_zero_row);
   r.ds = gptr(k.ok ? dsp : reinterpret_cast<const float*>(g_zero_row));
@@ -2070,40 +2067,65 @@ __device__ __forceinline__ void pf_put_row(uint8_t* base, const v4i (&x)[4]) {
   for (int c = 0; c < 4; ++c) *(v4i*)(tr + 16 * ((4 * part + c) ^ f)) = x[c];
 }
 
-// The tile's 64 rows HBM -> LDS (global_load_lds_dwordx4, M0 = LDS row pair,
-// lane l writes chunk l % 32 of row 2 mi + l / 32 and reads source chunk
-// (l % 32) ^ swz(row)).  Wave w moves its own keys [8 w, +8), whose addresses
-// its lanes already hold (lane 8 k has key 8 w + k).  Not ordered by the
-// compiler: the step ends with a wait for every vector-memory access.
-__device__ __forceinline__ void pf_issue(uint8_t* tb, const PfSrc& r, int w) {
-  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int k = 2 * mi + g, row = 8 * w + k;
-    const int lo = __shfl((int)(uint32_t)r.addr, 8 * k), hi = __shfl((int)(uint32_t)(r.addr >> 32), 8 * k);
-    const uint64_t src = (((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo) + 16u * (uint32_t)(li ^ swz(row));
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(tb + (8 * w + 2 * mi) * kD));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "m0");
-  }
+// One LDS-DMA instruction: lane l's 16 (or 4) source bytes to M0 + 16 l (or 4 l).
+__device__ __forceinline__ void pf_dma16(uint32_t dst, uint64_t src) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "m0");
+}
+__device__ __forceinline__ void pf_dma4(uint32_t dst, uint64_t src) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(dst), "v"(src) : "m0");
 }
 
-// The tile's per-key scales into scale set `set`.  Empty slots: zero
-// descales, lam = -inf.
+// The tile's 64 rows HBM -> LDS (global_load_lds_dwordx4, M0 = LDS row pair,
+// lane l writes chunk l % 32 of row 2 mi + l / 32 and reads source chunk
+// (l % 32) ^ swz(row)).  Wave w moves the keys [8 w, +8), whose row addresses
+// wave 0 left in `kaddr`.  Not ordered by the compiler: a step boundary waits
+// for every vector-memory access.
+__device__ __forceinline__ void pf_issue(uint8_t* tb, const uint64_t* kaddr, int w) {
+  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
+  uint64_t src[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int row = 8 * w + 2 * mi + g;
+    src[mi] = kaddr[row] + 16u * (uint32_t)(li ^ swz(row));
+  }
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+    pf_dma16(__builtin_amdgcn_readfirstlane(lds_addr(tb + (8 * w + 2 * mi) * kD)), src[mi]);
+}
+
+// This thread's descale of its key (tid >> 3) of a tile (per-tile: the one of
+// D tile tid & 7), from the descale address wave 0 left in `kds`.
 template <int PER_TILE>
-__device__ __forceinline__ void pf_scales(uint8_t* set, float s, bool ok) {
+__device__ __forceinline__ float pf_load_scale(const uint64_t* kds) {
+  const int tid = opaque((int)threadIdx.x);
+  const float* p = gptr(reinterpret_cast<const float*>(kds[tid >> 3]));
+  return p[PER_TILE ? (tid & 7) : 0];
+}
+
+// The tile's per-key scales into scale set `set` (thread: key tid >> 3, part
+// tid & 7; the key's 8 descales sit in 8 consecutive lanes).  Slots past the
+// tile's `nvalid` keys hold zero descales and lam = -inf; a NaN descale
+// poisons the key.
+// Largest of 8 consecutive lanes' values (DPP: swap lanes 1 apart, 2 apart,
+// then mirror within 8).
+__device__ __forceinline__ uint32_t max8_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  return x;
+}
+
+template <int PER_TILE>
+__device__ __forceinline__ void pf_scales(uint8_t* set, float s, int nvalid) {
   using L = LdsPF;
   const int tid = opaque((int)threadIdx.x), key = tid >> 3, part = tid & 7;
+  const bool ok = key < nvalid;
+  // per-tile: the largest |descale| of the key's 8 (as unsigned integers the
+  // magnitudes of floats order like the floats, and a NaN orders above every
+  // one of them); per-token: the descale itself
   float mx = s;
-  int nan = (s != s) ? 1 : 0;
-  if constexpr (PER_TILE) {   // the key's 8 descales sit in 8 consecutive lanes
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) {
-      mx = fmaxf(mx, __shfl_xor(mx, m));
-      nan |= __shfl_xor(nan, m);
-    }
-  }
-  float mxd = (mx == 0.f) ? kMinDescale : mx;
-  if (nan) mxd = __builtin_nanf("");        // a NaN descale poisons the key
+  if constexpr (PER_TILE) mx = __uint_as_float(max8_u32(__float_as_uint(s) & 0x7fffffffu));
+  const float mxd = (mx == 0.f) ? kMinDescale : mx;
   const float lam = ok ? __log2f(mxd) : kNegInf;
   const float inv = ok ? 1.0f / mxd : 0.f;
   if constexpr (PER_TILE) {
@@ -2210,6 +2232,20 @@ __device__ __forceinline__ PfQ pf_load_q(const KHdr& a, int t, int h) {
   return r;
 }
 
+// P' = 2^(E - M) of the lane's 8 keys (M = -inf: no key seen yet, read as 0),
+// written as f16 to the lane's 16-byte group of P; returns sum P' / vmax.
+__device__ __forceinline__ float pf_probs(const float (&E)[8], float Mh, v4f iv0, v4f iv1, uint8_t* prow) {
+  const float Mz = (Mh == kNegInf) ? 0.f : Mh;
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(E[i] - Mz);
+  float ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ls += p[i] * iv0[i] + p[4 + i] * iv1[i];
+  *(v4i*)prow = v4i{(int)pk_f16(p[0], p[1]), (int)pk_f16(p[2], p[3]), (int)pk_f16(p[4], p[5]), (int)pk_f16(p[6], p[7])};
+  return ls;
+}
+
 template <int PER_TILE>
 __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
   using L = LdsPF;
@@ -2248,25 +2284,38 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
   cur.nl = token_lens(a0, u_begin);
   cur.nip = pf_idx_raw(a0, u_begin);
   pf_enter(a0, cur, u_end, list, misc);
-  PfKey kC;        // tile s+3: block-table entry in flight
-  PfSrc rB;        // tile s+2: row address
-  float sB;        // tile s+2: descale in flight
+  // Tile stages: in step s wave 0 resolves tile s+2 (block-table loads,
+  // during its S^T MFMAs); at the boundary after step s it forms tile s+2's
+  // row and descale addresses, then every wave starts tile s+2's DMA and
+  // descale loads and turns tile s+1's descales (loaded one boundary
+  // earlier) into its scale set.
+  const bool w0 = w == 0;
+  uint64_t* kaddr = reinterpret_cast<uint64_t*>(smem + L::kKaddr);
+  uint64_t* kds = reinterpret_cast<uint64_t*>(smem + L::kKds);
+  int* nvalid = reinterpret_cast<int*>(smem + L::kNvalid);
+  PfKey kR;          // wave 0: tile s+2's block-table entries (in flight)
+  float sB;          // tile s+1's descale of this thread (in flight)
   {
     const Sides sd = cache_sides(a0);
-    const PfKey k0 = pf_next(a0, sd, cur, u_end, list, misc);
-    const PfSrc r0 = pf_src<PER_TILE>(sd, a0.layout_kv, k0);
-    const float s0 = *r0.ds;
-    const PfKey k1 = pf_next(a0, sd, cur, u_end, list, misc);
-    const PfSrc r1 = pf_src<PER_TILE>(sd, a0.layout_kv, k1);
-    const float s1 = *r1.ds;
-    const PfKey k2 = pf_next(a0, sd, cur, u_end, list, misc);
-    rB = pf_src<PER_TILE>(sd, a0.layout_kv, k2);
-    sB = *rB.ds;
-    kC = pf_next(a0, sd, cur, u_end, list, misc);
-    pf_issue(smem + L::kTiles, r0, w);
-    pf_issue(smem + L::kTiles + kTileBytes, r1, w);
-    pf_scales<PER_TILE>(smem + L::kSc, s0, r0.ok);
-    pf_scales<PER_TILE>(smem + L::kSc + L::kScBytes, s1, r1.ok);
+    // tiles 0 and 1: resolved, addressed, loaded
+#pragma unroll 1
+    for (int x = 0; x < 2; ++x) {
+      if (w0) {
+        const PfKey k = pf_resolve(a0, sd, cur, list, cur.u < u_end);
+        const PfSrc r = pf_src<PER_TILE>(sd, a0.layout_kv, k);
+        kaddr[64 * x + lane] = r.addr;
+        kds[64 * x + lane] = (uint64_t)(uintptr_t)r.ds;
+        const int nv = (int)__popcll(__ballot(r.ok));   // the whole wave votes
+        if (lane == 0) nvalid[x] = nv;
+      }
+      pf_advance(a0, cur, u_end, list, misc);
+    }
+    lds_barrier();
+    pf_issue(smem + L::kTiles, kaddr, w);
+    pf_issue(smem + L::kTiles + kTileBytes, kaddr + 64, w);
+    const float s0 = pf_load_scale<PER_TILE>(kds);
+    sB = pf_load_scale<PER_TILE>(kds + 64);
+    pf_scales<PER_TILE>(smem + L::kSc, s0, nvalid[0]);
   }
   const int hq0 = 32 * hb + (lane & 31);   // the lane's head in S^T and the softmax
   PfQ qn = pf_load_q(a0, u_begin, hq0);
@@ -2297,6 +2346,10 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     const uint8_t* tb = smem + L::kTiles + buf * kTileBytes;
     const uint8_t* set = smem + L::kSc + buf * L::kScBytes;
     // ---- S^T, the D halves exchanged ----
+    if (w0) {   // tile s+2: block-table loads (in flight until the boundary)
+      const KHdr a = hdr_view(hr);
+      kR = pf_resolve(a, cache_sides(a), cur, list, cur.u < u_end);
+    }
     const v16f S = pf_qk<PER_TILE>(tb, smem + L::kQ, reinterpret_cast<const float*>(set + L::kScKs), kb, hb, dh, ln);
     {
       float* dst = xch + (w * 64 + ln) * 8;
@@ -2338,37 +2391,29 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     maxb[w * 64 + ln] = m;
     const float Ms = hb ? Macc[1] : Macc[0];
     if (__ballot(m > Ms + kPfTau) && ln == 0) misc[L::kFlag + par] = 1;
+    // ---- P against the current reference; redone if any wave moves it ----
+    const float* invp = reinterpret_cast<const float*>(set + L::kScInv) + 32 * kb + 16 * dh + 4 * gg;
+    const v4f iv0 = *(const v4f*)invp, iv1 = *(const v4f*)(invp + 8);
+    const int pq = 2 * (2 * kb + dh) + gg;
+    uint8_t* prow = pbuf + hq * 128 + 16 * (pq ^ (hq & 7));
+    float lt = pf_probs(E, Ms, iv0, iv1, prow);
     lds_barrier();
-    if (__builtin_amdgcn_readfirstlane(misc[L::kFlag + par])) {   // rare: the reference moves
+    if (__builtin_amdgcn_readfirstlane(misc[L::kFlag + par])) {   // first tile of a token, or a jump
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         float mn = Macc[x];
 #pragma unroll
         for (int y = 0; y < 4; ++y) mn = fmaxf(mn, maxb[((y & 1) + 2 * x + 4 * (y >> 1)) * 64 + (ln & 31)]);
-        const float fa = (Macc[x] == kNegInf) ? 0.f : exp2f(Macc[x] - mn);
+        const float fa = (Macc[x] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(Macc[x] - mn);
 #pragma unroll
         for (int db = 0; db < 2; ++db) acc[db][x] *= fa;
         if (x == hb) lsum *= fa;
         Macc[x] = mn;
       }
+      lt = pf_probs(E, hb ? Macc[1] : Macc[0], iv0, iv1, prow);
+      lds_barrier();
     }
-    // ---- P ----
-    {
-      const float* invp = reinterpret_cast<const float*>(set + L::kScInv) + 32 * kb + 16 * dh + 4 * gg;
-      const v4f iv0 = *(const v4f*)invp, iv1 = *(const v4f*)(invp + 8);
-      const float Mh = hb ? Macc[1] : Macc[0];
-      const float Mz = (Mh == kNegInf) ? 0.f : Mh;
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(E[i] - Mz);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lsum += p[i] * iv0[i] + p[4 + i] * iv1[i];
-      const v4i pk = v4i{(int)pk_f16(p[0], p[1]), (int)pk_f16(p[2], p[3]), (int)pk_f16(p[4], p[5]),
-                         (int)pk_f16(p[6], p[7])};
-      const int q = 2 * (2 * kb + dh) + gg;
-      *(v4i*)(pbuf + hq * 128 + 16 * (q ^ (hq & 7))) = pk;
-    }
-    lds_barrier();
+    lsum += lt;
     // ---- O^T += V'^T P^T ----
     pf_pv<PER_TILE>(tb, reinterpret_cast<const _Float16*>(set + L::kScVs), pbuf, w, ln, acc);
 
@@ -2377,22 +2422,27 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     const bool last = ti + 1 == tiles_u;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     {
+      // tile s+1 uses parity buf ^ 1, tile s+2 parity buf
       const KHdr a = hdr_view(hr);
-      const Sides sd = cache_sides(a);
+      pf_scales<PER_TILE>(smem + L::kSc + (buf ^ 1) * L::kScBytes, sB, nvalid[buf ^ 1]);   // tile s+1
       if (qpend) pf_put_row(smem + L::kQ, qn.x);                      // token of tile s+1 (S^T of s is done)
-      const PfSrc rC = pf_src<PER_TILE>(sd, a.layout_kv, kC);         // tile s+3: address
+      if (w0) {                                                       // tile s+2: addresses
+        const PfSrc r = pf_src<PER_TILE>(cache_sides(a), a.layout_kv, kR);
+        const int key = opaque(lane) & 63;
+        kaddr[64 * buf + key] = r.addr;
+        kds[64 * buf + key] = (uint64_t)(uintptr_t)r.ds;
+        const int nv = (int)__popcll(__ballot(r.ok));
+        if (key == 0) nvalid[buf] = nv;
+      }
+      if (last) lbuf[w * 64 + ln] = lsum + __shfl_xor(lsum, 32);     // row sums of the ending token
       lds_barrier();                                                  // tile s is done in every wave
-      pf_issue(smem + L::kTiles + buf * kTileBytes, rB, w);          // tile s+2 into the buffer tile s leaves
-      pf_scales<PER_TILE>(smem + L::kSc + buf * L::kScBytes, sB, rB.ok);   // and into its scale set
-      sB = *rC.ds;                                                    // tile s+3: descale load
-      rB = rC;
-      kC = pf_next(a, sd, cur, u_end, list, misc);                    // tile s+4: block-table loads
+      pf_issue(smem + L::kTiles + buf * kTileBytes, kaddr + 64 * buf, w);   // tile s+2 into tile s's buffer
+      sB = pf_load_scale<PER_TILE>(kds + 64 * buf);                   // and its descales
+      pf_advance(a, cur, u_end, list, misc);
     }
     if (last) {
       // ---- epilogue of token u ----
       const KHdr ae = hdr_view(hr);
-      lbuf[w * 64 + ln] = lsum + __shfl_xor(lsum, 32);
-      lds_barrier();
       const int t = u;
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
@@ -2404,9 +2454,9 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
         const float Mf = fmaxf(M, sg);
         float sc = 0.f, lse_v = kNegInf;
         if (valid_u && Mf != kNegInf) {
-          const float af = (M == kNegInf) ? 0.f : exp2f(M - Mf);
-          const float Lf = af * Ls + ((sg == kNegInf) ? 0.f : exp2f(sg - Mf));
-          sc = af / Lf;
+          const float af = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - Mf);
+          const float Lf = af * Ls + ((sg == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sg - Mf));
+          sc = af * __builtin_amdgcn_rcpf(Lf);
           lse_v = (Mf + __log2f(Lf)) * kLn2;
         }
         if (ae.lse && w == 0 && gg == 0) ae.lse[(size_t)t * kN1 + h] = lse_v;
