@@ -387,7 +387,9 @@ def prefill(args, m, make_config, torch, np):
         "metric": "CSA prefill query-tokens/s + fp8 MFMA TFLOP/s (% dense peak), 1 MI355X",
         "value": round(T1 / (ms / 1e3), 1), "unit": "query-tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warm, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)",
+        "vs_baseline": None,
+        "dtype": ("fp8e4m3 S^T, f16 P V (fp32 accumulate)" if plan.head_group == 64
+                  else "fp8e4m3 (fp32 accumulate)"),
         "data": "synthetic, seeded (workloads.make_config(5))",
         "config": {"workload": "csa_prefill", "batch": 4, "q_tokens_per_batch": 4096, "n1": 64, "d": 512,
                    "band": 128, "cmp_ratio": 4, "topk": 512, "kv_scale": "per-tile-64", "lse": True,
