@@ -1916,7 +1916,7 @@ struct LdsPF {
   // is read (it resolves 4 tiles ahead and enters the next token as soon as
   // one is done), so 8 entries are never overwritten before they are read.
   static constexpr int kFlag = 16, kRing = 24, kRingMask = 7;
-  static constexpr int kQ = kMisc + 4 * 64;                 // fp8 q of the current token [64 heads][512], swizzled like a tile
+  static constexpr int kQ = kMisc + 4 * 64;                 // fp8 q staging [64 heads][512], swizzled like a tile
   static constexpr int kKaddr = kQ + kN1 * kD;              // u64 [2][64]: row addresses (tile parity), from wave 0
   static constexpr int kKds = kKaddr + 2 * 64 * 8;          // u64 [2][64]: descale addresses (tile parity), from wave 0
   static constexpr int kNvalid = kKds + 2 * 64 * 8;         // int [2]: keys of the tile (tile parity)
@@ -2059,14 +2059,6 @@ __device__ __forceinline__ PfSrc pf_src(const Sides& sd, int layout_kv, const Pf
   return r;
 }
 
-// Row tid >> 3, bytes [64 (tid & 7), +64), into a swizzled 64-row buffer.
-__device__ __forceinline__ void pf_put_row(uint8_t* base, const v4i (&x)[4]) {
-  const int tid = opaque((int)threadIdx.x), row = tid >> 3, part = tid & 7, f = swz(row);
-  uint8_t* tr = base + row * kD;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) *(v4i*)(tr + 16 * ((4 * part + c) ^ f)) = x[c];
-}
-
 // One LDS-DMA instruction: lane l's 16 (or 4) source bytes to M0 + 16 l (or 4 l).
 __device__ __forceinline__ void pf_dma16(uint32_t dst, uint64_t src) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "m0");
@@ -2152,21 +2144,17 @@ __device__ __forceinline__ v8i pf_op(const uint8_t* buf, int r, int dh, int s4, 
 }
 
 template <int PER_TILE>
-__device__ __forceinline__ v16f pf_qk(const uint8_t* tb, const uint8_t* qb, const float* ks, int kb, int hb, int dh,
+__device__ __forceinline__ v16f pf_qk(const uint8_t* tb, const v8i (&qf)[4], const float* ks, int kb, int dh,
                                       int lane_in) {
-  const int lane = opaque(lane_in), g = lane >> 5, kr = 32 * kb + (lane & 31), hr = 32 * hb + (lane & 31);
-  v8i ka = pf_op(tb, kr, dh, 0, g), qa = pf_op(qb, hr, dh, 0, g);
+  const int lane = opaque(lane_in), g = lane >> 5, kr = 32 * kb + (lane & 31);
+  v8i ka = pf_op(tb, kr, dh, 0, g);
   v16f S = v16f{};
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) {
-    v8i kn = ka, qn = qa;
-    if (s4 < 3) {
-      kn = pf_op(tb, kr, dh, s4 + 1, g);
-      qn = pf_op(qb, hr, dh, s4 + 1, g);
-    }
-    const v8i kop = ka, qop = qa;
+    v8i kn = ka;
+    if (s4 < 3) kn = pf_op(tb, kr, dh, s4 + 1, g);
+    const v8i kop = ka, qop = qf[s4];
     ka = kn;
-    qa = qn;
     if constexpr (PER_TILE) {
       const v16f p = mma(kop, qop, v16f{});
       const float* kst = ks + (4 * dh + s4) * 64 + 32 * kb + 4 * g;
@@ -2214,22 +2202,29 @@ __device__ __forceinline__ void pf_pv(const uint8_t* tb, const _Float16* vs, con
   }
 }
 
-// Token t's query: this thread's 64 bytes of head tid >> 3 (for the LDS
-// copy), and the lane's exponent factor softmax_scale * log2(e) * q_descale
-// of head h.
-struct PfQ {
-  v4i x[4];
-  float qd;   // q descale of head h (the factor is formed where it is used)
-};
-
-__device__ __forceinline__ PfQ pf_load_q(const KHdr& a, int t, int h) {
-  PfQ r;
-  const int tid = opaque((int)threadIdx.x);
-  const uint8_t* src = a.q + ((size_t)t * kN1 + (tid >> 3)) * kD + 64 * (tid & 7);
+// Token t's query rows HBM -> the LDS staging buffer (laid out like a key
+// tile): wave w moves heads [8 w, +8) by LDS-DMA.
+__device__ __forceinline__ void pf_issue_q(uint8_t* qb, const uint8_t* q, int t, int w) {
+  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) r.x[c] = *(const v4i*)(src + 16 * c);
-  r.qd = a.q_ds[a.q_ds_per_head ? (size_t)t * kN1 + h : (size_t)t];
-  return r;
+  for (int mi = 0; mi < 4; ++mi) {
+    const int h = 8 * w + 2 * mi + g;
+    const uint64_t src = (uint64_t)(uintptr_t)(q + ((size_t)t * kN1 + h) * kD) + 16u * (uint32_t)(li ^ swz(h));
+    pf_dma16(__builtin_amdgcn_readfirstlane(lds_addr(qb + (8 * w + 2 * mi) * kD)), src);
+  }
+}
+
+// The wave's query fragments from the staging buffer: the B operands of
+// S^T = K Q^T for heads [32 hb, +32), D half dh (held for the whole token).
+__device__ __forceinline__ void pf_q_frag(const uint8_t* qb, int hb, int dh, int lane_in, v8i (&qf)[4]) {
+  const int lane = opaque(lane_in), g = lane >> 5, hr = 32 * hb + (lane & 31);
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) qf[s4] = pf_op(qb, hr, dh, s4, g);
+}
+
+// The q descale of head h of token t.
+__device__ __forceinline__ float pf_qds(const KHdr& a, int t, int h) {
+  return a.q_ds[a.q_ds_per_head ? (size_t)t * kN1 + h : (size_t)t];
 }
 
 // P' = 2^(E - M) of the lane's 8 keys (M = -inf: no key seen yet, read as 0),
@@ -2318,10 +2313,11 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     pf_scales<PER_TILE>(smem + L::kSc, s0, nvalid[0]);
   }
   const int hq0 = 32 * hb + (lane & 31);   // the lane's head in S^T and the softmax
-  PfQ qn = pf_load_q(a0, u_begin, hq0);
-  pf_put_row(smem + L::kQ, qn.x);
-  float qc = a0.scale_log2 * qn.qd;
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // tiles 0 and 1 landed
+  pf_issue_q(smem + L::kQ, a0.q, u_begin, w);
+  float qc = a0.scale_log2 * pf_qds(a0, u_begin, hq0);
+  float qd_next = 0.f;
+  v8i qf[4];
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // tiles 0 and 1 and the first token's q landed
   lds_barrier();
 
   v16f acc[2][2];
@@ -2335,22 +2331,22 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
   int ring = __builtin_amdgcn_readfirstlane(misc[L::kRing + (u & L::kRingMask)]);
   int tiles_u = ring & 0xffff;
   bool valid_u = (ring >> 16) == 0;
-  // qn holds the q of the token that begins with the next tile (loaded after
-  // the last boundary, written to LDS at the next one)
-  bool qpend = tiles_u == 1 && u + 1 < u_end;
-  if (qpend) qn = pf_load_q(a0, u + 1, hq0);
+  // q of a token: LDS-DMA into the staging buffer during the previous
+  // token's last step (after its first barrier, when every wave holds its
+  // fragments), read into registers at the token's first step
 
   for (int s = 0;; ++s) {
     const int buf = s & 1, par = s & 1;
     const int ln = opaque(lane), gg = ln >> 5, hq = 32 * hb + (ln & 31);
     const uint8_t* tb = smem + L::kTiles + buf * kTileBytes;
     const uint8_t* set = smem + L::kSc + buf * L::kScBytes;
+    if (ti == 0) pf_q_frag(smem + L::kQ, hb, dh, ln, qf);   // a new token's q
     // ---- S^T, the D halves exchanged ----
     if (w0) {   // tile s+2: block-table loads (in flight until the boundary)
       const KHdr a = hdr_view(hr);
       kR = pf_resolve(a, cache_sides(a), cur, list, cur.u < u_end);
     }
-    const v16f S = pf_qk<PER_TILE>(tb, smem + L::kQ, reinterpret_cast<const float*>(set + L::kScKs), kb, hb, dh, ln);
+    const v16f S = pf_qk<PER_TILE>(tb, qf, reinterpret_cast<const float*>(set + L::kScKs), kb, dh, ln);
     {
       float* dst = xch + (w * 64 + ln) * 8;
       if (dh) {
@@ -2363,6 +2359,11 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     }
     lds_barrier();
     if (threadIdx.x == 0) misc[L::kFlag + (par ^ 1)] = 0;   // the previous step's flag was read by all
+    if (ti + 1 == tiles_u && u + 1 < u_end) {   // the next token's q (every wave holds this token's)
+      const KHdr a = hdr_view(hr);
+      pf_issue_q(smem + L::kQ, a.q, u + 1, w);
+      qd_next = pf_qds(a, u + 1, hq);
+    }
     float E[8];
     {
       const float* src = xch + ((w ^ 4) * 64 + ln) * 8;
@@ -2425,7 +2426,6 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
       // tile s+1 uses parity buf ^ 1, tile s+2 parity buf
       const KHdr a = hdr_view(hr);
       pf_scales<PER_TILE>(smem + L::kSc + (buf ^ 1) * L::kScBytes, sB, nvalid[buf ^ 1]);   // tile s+1
-      if (qpend) pf_put_row(smem + L::kQ, qn.x);                      // token of tile s+1 (S^T of s is done)
       if (w0) {                                                       // tile s+2: addresses
         const PfSrc r = pf_src<PER_TILE>(cache_sides(a), a.layout_kv, kR);
         const int key = opaque(lane) & 63;
@@ -2481,15 +2481,9 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
       ring = __builtin_amdgcn_readfirstlane(misc[L::kRing + (u & L::kRingMask)]);
       tiles_u = ring & 0xffff;
       valid_u = (ring >> 16) == 0;
-      qc = ae.scale_log2 * qn.qd;
+      qc = ae.scale_log2 * qd_next;
     } else {
       ++ti;
-    }
-    // the token after u begins with tile s+2: its q now, written at the next boundary
-    qpend = (ti + 1 == tiles_u) && u + 1 < u_end;
-    if (qpend) {
-      const KHdr a = hdr_view(hr);
-      qn = pf_load_q(a, u + 1, 32 * hb + (opaque(lane) & 31));
     }
   }
   // every wave's last loads (of the stream past its end) settle before exit

@@ -241,6 +241,24 @@ def test_edge_topk_beyond_list_window():
     check_rows(inp, name="topk 2500")
 
 
+@pytest.mark.parametrize("kv_scale_mode", [0, 1])
+def test_prefill_stream_many_tokens_per_workgroup(kv_scale_mode):
+    """1100 query tokens over 256 work-groups: the whole-token kernel streams
+    4-5 tokens per work-group (tiles of consecutive tokens back to back), with
+    token lists from 1 to 4 tiles, rows past seqused_q, rows that see no key
+    (more query rows than keys), -1 / out-of-range index slots and both
+    descale modes."""
+    rng = np.random.default_rng(81 + kv_scale_mode)
+    q_lens = [500, 380, 180, 40]
+    ori = [700, 520, 250, 20]
+    cmp = [o // 4 for o in ori]
+    idx = _rand_idx(rng, sum(q_lens), 96, max(cmp), 0.25)
+    inp = make_custom(seed=82 + kv_scale_mode, q_lens=q_lens, ori_lens=ori, cmp_lens=cmp, cmp_ratio=4,
+                      residual=[o % 4 for o in ori], indices=idx, seqused_q=[500, 361, 177, 40],
+                      kv_scale_mode=kv_scale_mode, return_lse=True)
+    check(inp, name=f"prefill stream, scale mode {kv_scale_mode}")
+
+
 def test_edge_per_token_q_descale_and_zero_descale_row():
     inp = make_custom(seed=71, q_lens=[3], ori_lens=[200], cmp_lens=[50], cmp_ratio=4, residual=[0],
                       indices=np.tile(np.arange(50), (3, 1)), q_descale_per_head=False, return_lse=True)
