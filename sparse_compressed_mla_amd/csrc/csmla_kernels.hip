@@ -2460,14 +2460,22 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
           lse_v = (Mf + __log2f(Lf)) * kLn2;
         }
         if (ae.lse && w == 0 && gg == 0) ae.lse[(size_t)t * kN1 + h] = lse_v;
-        uint16_t* orow = ae.out + ((size_t)t * kN1 + h) * kD + 64 * w + 4 * gg;
+        // lane (h, g) holds columns 8 q + 4 g + [0, 4) of each 32-column block;
+        // lanes l and l + 32 swap one half of each q pair, so that each lane
+        // stores 16 contiguous bytes: columns 16 k + 8 g + [0, 8)
+        uint16_t* orow = ae.out + ((size_t)t * kN1 + h) * kD + 64 * w + 8 * gg;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int k2 = 0; k2 < 2; ++k2) {
             const v16f& o = acc[db][x];
-            *(uint2*)(orow + 32 * db + 8 * q) =
-                pack_bf16x4(sc * o[4 * q], sc * o[4 * q + 1], sc * o[4 * q + 2], sc * o[4 * q + 3]);
+            const int q0 = 2 * k2, q1 = 2 * k2 + 1;
+            const uint2 A = pack_bf16x4(sc * o[4 * q0], sc * o[4 * q0 + 1], sc * o[4 * q0 + 2], sc * o[4 * q0 + 3]);
+            const uint2 B = pack_bf16x4(sc * o[4 * q1], sc * o[4 * q1 + 1], sc * o[4 * q1 + 2], sc * o[4 * q1 + 3]);
+            const uint2 X = gg ? A : B;
+            const uint2 Y = make_uint2((uint32_t)__shfl_xor((int)X.x, 32), (uint32_t)__shfl_xor((int)X.y, 32));
+            const uint4 v = gg ? make_uint4(Y.x, Y.y, B.x, B.y) : make_uint4(A.x, A.y, Y.x, Y.y);
+            *(uint4*)(orow + 32 * db + 16 * k2) = v;
           }
       }
 #pragma unroll
