@@ -2290,6 +2290,7 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
   int* nvalid = reinterpret_cast<int*>(smem + L::kNvalid);
   PfKey kR;          // wave 0: tile s+2's block-table entries (in flight)
   float sB;          // tile s+1's descale of this thread (in flight)
+  int nvB;           // tile s+1's key count
   {
     const Sides sd = cache_sides(a0);
     // tiles 0 and 1: resolved, addressed, loaded
@@ -2310,6 +2311,7 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     pf_issue(smem + L::kTiles + kTileBytes, kaddr + 64, w);
     const float s0 = pf_load_scale<PER_TILE>(kds);
     sB = pf_load_scale<PER_TILE>(kds + 64);
+    nvB = nvalid[1];
     pf_scales<PER_TILE>(smem + L::kSc, s0, nvalid[0]);
   }
   const int hq0 = 32 * hb + (lane & 31);   // the lane's head in S^T and the softmax
@@ -2425,7 +2427,7 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     {
       // tile s+1 uses parity buf ^ 1, tile s+2 parity buf
       const KHdr a = hdr_view(hr);
-      pf_scales<PER_TILE>(smem + L::kSc + (buf ^ 1) * L::kScBytes, sB, nvalid[buf ^ 1]);   // tile s+1
+      pf_scales<PER_TILE>(smem + L::kSc + (buf ^ 1) * L::kScBytes, sB, nvB);   // tile s+1
       if (w0) {                                                       // tile s+2: addresses
         const PfSrc r = pf_src<PER_TILE>(cache_sides(a), a.layout_kv, kR);
         const int key = opaque(lane) & 63;
@@ -2438,6 +2440,7 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
       lds_barrier();                                                  // tile s is done in every wave
       pf_issue(smem + L::kTiles + buf * kTileBytes, kaddr + 64 * buf, w);   // tile s+2 into tile s's buffer
       sB = pf_load_scale<PER_TILE>(kds + 64 * buf);                   // and its descales
+      nvB = nvalid[buf];
       pf_advance(a, cur, u_end, list, misc);
     }
     if (last) {
