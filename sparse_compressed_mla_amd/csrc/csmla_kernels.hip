@@ -2059,6 +2059,11 @@ __device__ __forceinline__ PfSrc pf_src(const Sides& sd, int layout_kv, const Pf
   return r;
 }
 
+// Swizzle of the prefill kernel's 512-byte LDS rows (key tiles, q staging):
+// 16-byte chunk c of row r sits at chunk c ^ (r & 15), so 16 lanes reading
+// the same chunk of 16 consecutive rows touch 16 different chunks (256 bytes).
+__device__ __forceinline__ int pf_swz(int r) { return r & 15; }
+
 // One LDS-DMA instruction: lane l's 16 (or 4) source bytes to M0 + 16 l (or 4 l).
 __device__ __forceinline__ void pf_dma16(uint32_t dst, uint64_t src) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "m0");
@@ -2069,7 +2074,7 @@ __device__ __forceinline__ void pf_dma4(uint32_t dst, uint64_t src) {
 
 // The tile's 64 rows HBM -> LDS (global_load_lds_dwordx4, M0 = LDS row pair,
 // lane l writes chunk l % 32 of row 2 mi + l / 32 and reads source chunk
-// (l % 32) ^ swz(row)).  Wave w moves the keys [8 w, +8), whose row addresses
+// (l % 32) ^ pf_swz(row)).  Wave w moves the keys [8 w, +8), whose row addresses
 // wave 0 left in `kaddr`.  Not ordered by the compiler: a step boundary waits
 // for every vector-memory access.
 __device__ __forceinline__ void pf_issue(uint8_t* tb, const uint64_t* kaddr, int w) {
@@ -2078,7 +2083,7 @@ __device__ __forceinline__ void pf_issue(uint8_t* tb, const uint64_t* kaddr, int
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int row = 8 * w + 2 * mi + g;
-    src[mi] = kaddr[row] + 16u * (uint32_t)(li ^ swz(row));
+    src[mi] = kaddr[row] + 16u * (uint32_t)(li ^ pf_swz(row));
   }
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
@@ -2137,9 +2142,9 @@ __device__ __forceinline__ void pf_scales(uint8_t* set, float s, int nvalid) {
 // (an MFMA operand of 32x32x64: lane group g holds k = 32 g .. 32 g + 31).
 __device__ __forceinline__ v8i pf_op(const uint8_t* buf, int r, int dh, int s4, int g) {
   const uint8_t* row = buf + r * kD;
-  const int f = swz(r), cb = 16 * dh + 8 * (s4 >> 1), cl = 4 * (s4 & 1) + 2 * g;
-  const v4i lo = *(const v4i*)(row + 16 * (cb + (cl ^ f)));
-  const v4i hi = *(const v4i*)(row + 16 * (cb + ((cl + 1) ^ f)));
+  const int f = pf_swz(r), c = 16 * dh + 8 * (s4 >> 1) + 4 * (s4 & 1) + 2 * g;
+  const v4i lo = *(const v4i*)(row + 16 * (c ^ f));
+  const v4i hi = *(const v4i*)(row + 16 * ((c + 1) ^ f));
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -2188,7 +2193,7 @@ __device__ __forceinline__ void pf_pv(const uint8_t* tb, const _Float16* vs, con
     }
     h8_t vsc;
     if constexpr (PER_TILE) vsc = *(const h8_t*)(vs + w * 64 + 16 * rho + 8 * g);
-    const int key = 16 * rho + vkey, f = swz(key);
+    const int key = 16 * rho + vkey, f = pf_swz(key);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int J = 2 * w + db;
@@ -2209,7 +2214,7 @@ __device__ __forceinline__ void pf_issue_q(uint8_t* qb, const uint8_t* q, int t,
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int h = 8 * w + 2 * mi + g;
-    const uint64_t src = (uint64_t)(uintptr_t)(q + ((size_t)t * kN1 + h) * kD) + 16u * (uint32_t)(li ^ swz(h));
+    const uint64_t src = (uint64_t)(uintptr_t)(q + ((size_t)t * kN1 + h) * kD) + 16u * (uint32_t)(li ^ pf_swz(h));
     pf_dma16(__builtin_amdgcn_readfirstlane(lds_addr(qb + (8 * w + 2 * mi) * kD)), src);
   }
 }
