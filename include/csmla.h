@@ -68,7 +68,9 @@ enum { CSMLA_KV_SCALE_PER_TOKEN = 0, CSMLA_KV_SCALE_PER_TILE64 = 1 };
 /* Shapes and attributes; host values.  Field order is part of the ABI. */
 typedef struct {
   int32_t batch;              /* B >= 1 */
-  int32_t n1;                 /* query heads; 64 (SparseCompressedFlashAttention: N1 = 64) */
+  int32_t n1;                 /* query heads: 64 (SparseCompressedFlashAttention: N1 = 64) or 128
+                                 (KvQuantSparseAttnSharedkv, 约束说明); 128 runs as two 64-head
+                                 launches on the stream, sharing the plan and the workspace */
   int32_t n2;                 /* KV heads; must be 1 */
   int32_t d;                  /* head dim; must be 512 */
   int32_t layout_q;           /* CSMLA_LAYOUT_BSND or _TND */
@@ -170,7 +172,7 @@ size_t csmla_metadata_words(void);
  * 1 without cmp_kv; mask modes {0,3,4}/{0,3}; windows -1 or >= 0, and >= 0
  * only with band mode; the allowed layout pairs; block sizes 1..1024; no
  * empty tensors.  Returns CSMLA_OK, CSMLA_ERR_INVALID_ARG or
- * CSMLA_ERR_UNSUPPORTED (n1 != 64, topk_value_mode != 0). */
+ * CSMLA_ERR_UNSUPPORTED (n1 other than 64 or 128, topk_value_mode != 0). */
 csmla_status csmla_validate(const csmla_problem* problem);
 
 /* Split planner, the counterpart of QuantSparseFlashMlaMetadata

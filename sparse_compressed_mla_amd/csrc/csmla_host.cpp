@@ -191,7 +191,8 @@ csmla_status csmla_validate(const csmla_problem* p) {
   if (p->n2 != 1) return fail(CSMLA_ERR_INVALID_ARG, "n2 must be 1, got %d", p->n2);
   if (p->d != 512) return fail(CSMLA_ERR_INVALID_ARG, "d must be 512, got %d", p->d);
   if (p->n1 < 1) return fail(CSMLA_ERR_INVALID_ARG, "n1 must be >= 1");
-  if (p->n1 != kN1) return fail(CSMLA_ERR_UNSUPPORTED, "only n1 = 64 query heads are built, got %d", p->n1);
+  if (p->n1 != kN1 && p->n1 != 2 * kN1)
+    return fail(CSMLA_ERR_UNSUPPORTED, "only n1 = 64 or 128 query heads are built, got %d", p->n1);
   if (p->layout_q != CSMLA_LAYOUT_BSND && p->layout_q != CSMLA_LAYOUT_TND)
     return fail(CSMLA_ERR_INVALID_ARG, "layout_q must be BSND or TND");
   if (p->layout_kv != CSMLA_LAYOUT_BSND && p->layout_kv != CSMLA_LAYOUT_TND && p->layout_kv != CSMLA_LAYOUT_PA_BBND)
@@ -381,6 +382,7 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
   a.win_left = p->ori_mask_mode == CSMLA_MASK_BAND ? p->ori_win_left : -1;
   a.win_right = p->ori_mask_mode == CSMLA_MASK_BAND ? p->ori_win_right : -1;
   a.scale_mode = p->kv_scale_mode; a.q_ds_per_head = p->q_descale_per_head; a.ret_lse = p->return_softmax_lse;
+  a.n1 = p->n1;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   a.q = (const uint8_t*)t->q; a.q_ds = t->q_descale;
   a.ori_kv = (const uint8_t*)t->ori_kv; a.ori_ds = t->ori_kv_descale;
@@ -429,8 +431,19 @@ csmla_status csmla_forward(const csmla_problem* p, const csmla_tensors* t, const
   KArgs a;
   csmla_status st = build_args(p, t, md, a, true);
   if (st != CSMLA_OK) return st;
-  const int e = launch_forward(a, stream);
-  if (e != 0) return fail(CSMLA_ERR_HIP, "kernel launch failed (hipError %d)", e);
+  // The kernels cover 64 heads per launch: n1 = 128 runs the two halves one
+  // after the other on the stream (same plan, same workspace), each with its
+  // pointers at the half's first head and the token stride of n1 heads.
+  for (int h0 = 0; h0 < p->n1; h0 += kN1) {
+    KArgs ah = a;
+    ah.q = a.q + (size_t)h0 * kD;
+    ah.out = a.out + (size_t)h0 * kD;
+    if (a.lse) ah.lse = a.lse + h0;
+    if (a.q_ds_per_head) ah.q_ds = a.q_ds + h0;
+    if (a.sinks) ah.sinks = a.sinks + h0;
+    const int e = launch_forward(ah, stream);
+    if (e != 0) return fail(CSMLA_ERR_HIP, "kernel launch failed (hipError %d)", e);
+  }
   g_last_error.clear();
   return CSMLA_OK;
 }

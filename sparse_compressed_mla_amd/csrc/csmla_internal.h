@@ -30,6 +30,8 @@ struct KHdr {
   int32_t ori_s, cmp_s, ori_bs, cmp_bs, ori_cols, cmp_cols;
   int32_t has_cmp, topk, cmp_ratio, ori_mask, cmp_mask, win_left, win_right;
   int32_t scale_mode, q_ds_per_head, ret_lse;
+  int32_t n1;                       // query heads per token: the token stride of q, q_descale, out, lse
+                                    // (one launch covers 64 of them; pointers start at its first head)
   float scale_log2;                 // softmax_scale * log2(e)
   // tensors
   const uint8_t* q; const float* q_ds;

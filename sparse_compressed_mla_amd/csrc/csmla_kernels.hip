@@ -1123,7 +1123,7 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
     const IdxPre<kThreads> ip = load_indices<kThreads>(a, t, 0);
     v8i qreg[4];
     {
-      const uint8_t* qrow = a.q + ((size_t)t * kN1 + h) * kD + 256 * dh + 32 * g;
+      const uint8_t* qrow = a.q + ((size_t)t * a.n1 + h) * kD + 256 * dh + 32 * g;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const v4i x0 = *(const v4i*)(qrow + 64 * s4);
@@ -1131,16 +1131,16 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
         qreg[s4] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
     }
-    const float qd = a.q_ds[a.q_ds_per_head ? (size_t)t * kN1 + h : (size_t)t];
+    const float qd = a.q_ds[a.q_ds_per_head ? (size_t)t * a.n1 + h : (size_t)t];
     us.k = token_ctx(a, t, tl);
     c.qs = a.scale_log2 * qd;
     if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
       if (a.splits == 1) {
         for (int x = opaque(lane); x < 32 * 64; x += 64) {
           const int hr = 32 * hh + x / 64, d = 256 * dh + 4 * (x % 64);
-          *(uint2*)(a.out + ((size_t)t * kN1 + hr) * kD + d) = make_uint2(0, 0);
+          *(uint2*)(a.out + ((size_t)t * a.n1 + hr) * kD + d) = make_uint2(0, 0);
         }
-        if (a.lse && dh == 0 && g == 0) a.lse[(size_t)t * kN1 + h] = kNegInf;
+        if (a.lse && dh == 0 && g == 0) a.lse[(size_t)t * a.n1 + h] = kNegInf;
       } else {
         if (dh == 0 && g == 0) {
           a.ws_ml[((size_t)u * kN1 + h) * 2] = kNegInf;
@@ -1189,7 +1189,7 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
         sc = af / Lf;
         lse_v = (Mf + __log2f(Lf)) * kLn2;
       }
-      if (ae.lse && dh == 0 && g == 0) ae.lse[(size_t)t * kN1 + h] = lse_v;
+      if (ae.lse && dh == 0 && g == 0) ae.lse[(size_t)t * ae.n1 + h] = lse_v;
     } else {
       sc = (lh > 0.f) ? 1.0f / lh : 0.f;
       if (dh == 0 && g == 0) {
@@ -1210,7 +1210,7 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
             pack_bf16x4(sc * ov[4 * r4], sc * ov[4 * r4 + 1], sc * ov[4 * r4 + 2], sc * ov[4 * r4 + 3]);
       }
     }
-    uint16_t* dst = (ae.splits == 1) ? ae.out + (size_t)t * kN1 * kD : ae.ws_o + (size_t)u * kN1 * kD;
+    uint16_t* dst = (ae.splits == 1) ? ae.out + (size_t)t * ae.n1 * kD : ae.ws_o + (size_t)u * kN1 * kD;
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int row = 2 * it + g;   // head 32 hh + row
@@ -1633,7 +1633,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     // (columns j >= hg load head h0 and are zeroed: no branch around the loads)
     v8i qreg[4];
     {
-      const uint8_t* qrow = a.q + ((size_t)t * kN1 + h) * kD + 32 * g;
+      const uint8_t* qrow = a.q + ((size_t)t * a.n1 + h) * kD + 32 * g;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const v4i x0 = *(const v4i*)(qrow + 128 * k);
@@ -1641,7 +1641,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
         qreg[k] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
     }
-    const float qd_h = a.q_ds[a.q_ds_per_head ? (size_t)t * kN1 + h : (size_t)t];
+    const float qd_h = a.q_ds[a.q_ds_per_head ? (size_t)t * a.n1 + h : (size_t)t];
     UnitState us;
     us.t = t;
     us.k = token_ctx(a, t, tl);
@@ -1653,9 +1653,9 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
       for (int x = opaque(lane); x < a.hg * 64; x += 64) {
         const int hr = h0 + x / 64, d = 8 * (x % 64);
-        if (w == 0) *(v4i*)(a.out + ((size_t)t * kN1 + hr) * kD + d) = v4i{0, 0, 0, 0};
+        if (w == 0) *(v4i*)(a.out + ((size_t)t * a.n1 + hr) * kD + d) = v4i{0, 0, 0, 0};
       }
-      if (a.lse && w == 0 && g == 0 && real) a.lse[(size_t)t * kN1 + h] = kNegInf;
+      if (a.lse && w == 0 && g == 0 && real) a.lse[(size_t)t * a.n1 + h] = kNegInf;
       continue;
     }
     us.n_o = us.k.hi - us.k.lo;
@@ -1691,7 +1691,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
       sc = af / Lf;
       lse_v = (Mf + __log2f(Lf)) * kLn2;
     }
-    if (ae.lse && w == 0 && g == 0 && real) ae.lse[(size_t)t * kN1 + h] = lse_v;
+    if (ae.lse && w == 0 && g == 0 && real) ae.lse[(size_t)t * ae.n1 + h] = lse_v;
     // stage [16 heads][512 columns] bf16 (rows padded to 1040 bytes)
     constexpr int kRow = 2 * kD + 16;
 #pragma unroll
@@ -1703,7 +1703,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     // wave w stores head rows w, w + waves, ...: a row is 1 KiB = 64 lanes x 16 bytes
     for (int row = w; row < ae.hg; row += kDkWaves) {
       const v4i x = *(const v4i*)(smem + row * kRow + 16 * lane);
-      *(v4i*)(ae.out + ((size_t)t * kN1 + h0 + row) * kD + 8 * lane) = x;
+      *(v4i*)(ae.out + ((size_t)t * ae.n1 + h0 + row) * kD + 8 * lane) = x;
     }
     if (u + 1 < u_end) lds_barrier();   // the staging area is read before the next unit's gathers
   }
@@ -1754,7 +1754,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const KArgs a) {
   const int h = hg * 8 + (threadIdx.x >> 5);
   const int col = (threadIdx.x & 31) * 16;
   const int S = a.splits;
-  uint16_t* dst = a.out + ((size_t)t * kN1 + h) * kD + col;
+  uint16_t* dst = a.out + ((size_t)t * a.n1 + h) * kD + col;
   const float* ml = a.ws_ml + ((size_t)t * S * kN1 + h) * 2;   // split s at + s * kN1 * 2
   const size_t ostride = (size_t)kN1 * kD;
   const uint16_t* op = a.ws_o + ((size_t)t * S * kN1 + h) * kD + col;
@@ -1817,7 +1817,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const KArgs a) {
   *(uint4*)dst = make_uint4(o[0], o[1], o[2], o[3]);
   *(uint4*)(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
   if (a.lse && (threadIdx.x & 31) == 0)
-    a.lse[(size_t)t * kN1 + h] = (!padded && L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
+    a.lse[(size_t)t * a.n1 + h] = (!padded && L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
@@ -2209,12 +2209,12 @@ __device__ __forceinline__ void pf_pv(const uint8_t* tb, const _Float16* vs, con
 
 // Token t's query rows HBM -> the LDS staging buffer (laid out like a key
 // tile): wave w moves heads [8 w, +8) by LDS-DMA.
-__device__ __forceinline__ void pf_issue_q(uint8_t* qb, const uint8_t* q, int t, int w) {
+__device__ __forceinline__ void pf_issue_q(uint8_t* qb, const uint8_t* q, int n1, int t, int w) {
   const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int h = 8 * w + 2 * mi + g;
-    const uint64_t src = (uint64_t)(uintptr_t)(q + ((size_t)t * kN1 + h) * kD) + 16u * (uint32_t)(li ^ pf_swz(h));
+    const uint64_t src = (uint64_t)(uintptr_t)(q + ((size_t)t * n1 + h) * kD) + 16u * (uint32_t)(li ^ pf_swz(h));
     pf_dma16(__builtin_amdgcn_readfirstlane(lds_addr(qb + (8 * w + 2 * mi) * kD)), src);
   }
 }
@@ -2229,7 +2229,7 @@ __device__ __forceinline__ void pf_q_frag(const uint8_t* qb, int hb, int dh, int
 
 // The q descale of head h of token t.
 __device__ __forceinline__ float pf_qds(const KHdr& a, int t, int h) {
-  return a.q_ds[a.q_ds_per_head ? (size_t)t * kN1 + h : (size_t)t];
+  return a.q_ds[a.q_ds_per_head ? (size_t)t * a.n1 + h : (size_t)t];
 }
 
 // P' = 2^(E - M) of the lane's 8 keys (M = -inf: no key seen yet, read as 0),
@@ -2320,7 +2320,7 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     pf_scales<PER_TILE>(smem + L::kSc, s0, nvalid[0]);
   }
   const int hq0 = 32 * hb + (lane & 31);   // the lane's head in S^T and the softmax
-  pf_issue_q(smem + L::kQ, a0.q, u_begin, w);
+  pf_issue_q(smem + L::kQ, a0.q, a0.n1, u_begin, w);
   float qc = a0.scale_log2 * pf_qds(a0, u_begin, hq0);
   float qd_next = 0.f;
   v8i qf[4];
@@ -2368,7 +2368,7 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     if (threadIdx.x == 0) misc[L::kFlag + (par ^ 1)] = 0;   // the previous step's flag was read by all
     if (ti + 1 == tiles_u && u + 1 < u_end) {   // the next token's q (every wave holds this token's)
       const KHdr a = hdr_view(hr);
-      pf_issue_q(smem + L::kQ, a.q, u + 1, w);
+      pf_issue_q(smem + L::kQ, a.q, a.n1, u + 1, w);
       qd_next = pf_qds(a, u + 1, hq);
     }
     float E[8];
@@ -2467,11 +2467,11 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
           sc = af * __builtin_amdgcn_rcpf(Lf);
           lse_v = (Mf + __log2f(Lf)) * kLn2;
         }
-        if (ae.lse && w == 0 && gg == 0) ae.lse[(size_t)t * kN1 + h] = lse_v;
+        if (ae.lse && w == 0 && gg == 0) ae.lse[(size_t)t * ae.n1 + h] = lse_v;
         // lane (h, g) holds columns 8 q + 4 g + [0, 4) of each 32-column block;
         // lanes l and l + 32 swap one half of each q pair, so that each lane
         // stores 16 contiguous bytes: columns 16 k + 8 g + [0, 8)
-        uint16_t* orow = ae.out + ((size_t)t * kN1 + h) * kD + 64 * w + 8 * gg;
+        uint16_t* orow = ae.out + ((size_t)t * ae.n1 + h) * kD + 64 * w + 8 * gg;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll

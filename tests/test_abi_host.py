@@ -60,7 +60,9 @@ def base_problem(**kw):
     (dict(), OK),
     (dict(n2=2), INVALID),                      # N2 only 1
     (dict(d=576), INVALID),                     # D only 512
-    (dict(n1=128), UNSUPPORTED),                # N1 = 128 allowed by KvQuantSparseAttnSharedkv, not built
+    (dict(n1=128), OK),                         # N1 = 128 (KvQuantSparseAttnSharedkv): two 64-head launches
+    (dict(n1=96), UNSUPPORTED),                 # only 64 and 128 are built
+    (dict(n1=32), UNSUPPORTED),
     (dict(batch=0, t1=0), INVALID),             # empty tensors
     (dict(cmp_ratio=0), INVALID),
     (dict(cmp_ratio=129), INVALID),             # 1..128

@@ -259,6 +259,30 @@ def test_prefill_stream_many_tokens_per_workgroup(kv_scale_mode):
     check(inp, name=f"prefill stream, scale mode {kv_scale_mode}")
 
 
+@pytest.mark.parametrize("kv_scale_mode", [0, 1])
+def test_n1_128_heads(kv_scale_mode):
+    """128 query heads (KvQuantSparseAttnSharedkv): the two 64-head halves run
+    as separate launches over the same plan; a decode-shaped batch and a
+    prefill-sized one (more than 256 tokens), with per-head q descales, sinks
+    and lse, both descale modes."""
+    rng = np.random.default_rng(91 + kv_scale_mode)
+    ori = [900, 400]
+    cmp = [o // 4 for o in ori]
+    idx = _rand_idx(rng, 6, 80, max(cmp), 0.2)
+    inp = make_custom(seed=92 + kv_scale_mode, q_lens=[3, 3], ori_lens=ori, cmp_lens=cmp, cmp_ratio=4,
+                      residual=[o % 4 for o in ori], indices=idx, n1=128, kv_scale_mode=kv_scale_mode,
+                      return_lse=True)
+    check(inp, name=f"n1 128 decode, scale mode {kv_scale_mode}")
+    q_lens = [200, 120]
+    ori = [260, 150]
+    cmp = [o // 4 for o in ori]
+    idx = _rand_idx(rng, sum(q_lens), 48, max(cmp), 0.2)
+    inp = make_custom(seed=93 + kv_scale_mode, q_lens=q_lens, ori_lens=ori, cmp_lens=cmp, cmp_ratio=4,
+                      residual=[o % 4 for o in ori], indices=idx, n1=128, kv_scale_mode=kv_scale_mode,
+                      seqused_q=[200, 117], return_lse=True)
+    check(inp, name=f"n1 128 prefill-sized, scale mode {kv_scale_mode}")
+
+
 def test_edge_per_token_q_descale_and_zero_descale_row():
     inp = make_custom(seed=71, q_lens=[3], ori_lens=[200], cmp_lens=[50], cmp_ratio=4, residual=[0],
                       indices=np.tile(np.arange(50), (3, 1)), q_descale_per_head=False, return_lse=True)
