@@ -308,10 +308,11 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
     const auto& c = cost[u / per_token];
     if (hg == kN1) {
       // whole-token prefill kernel: a token takes at least one 64-key tile, and
-      // its output, sink and lse plus the next token's set-up cost about 1.2
-      // tiles more (measured on MI355X)
+      // its first-tile reference move, output, sink and lse plus the next
+      // token's set-up cost about 2.5 tiles more (swept on MI355X: 112 to 176
+      // keys balance equally well; 56 runs 12% slower, 400 runs 3% slower)
       const int64_t tiles = std::max<int64_t>(1, (c.n_o + c.n_c_up + kTileKeys - 1) / kTileKeys);
-      pre[u + 1] = pre[u] + (double)(tiles * kTileKeys) + 80.0;
+      pre[u + 1] = pre[u] + (double)(tiles * kTileKeys) + 160.0;
     } else {
       pre[u + 1] = pre[u] + (double)(c.n_o + c.n_c_up) / (double)S + 48.0;
     }
