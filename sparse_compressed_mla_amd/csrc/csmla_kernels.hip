@@ -2005,8 +2005,9 @@ struct PfKey {
   bool cmp, ok;
 };
 
-__device__ __forceinline__ PfKey pf_resolve(const KHdr& a, const Sides& sd, const PfCursor& c, const int* list,
-                                            bool live) {
+// It reads only the header fields it uses (no cache_sides, which pins all of
+// them in scalar registers): this runs in every step.
+__device__ __forceinline__ PfKey pf_resolve(const KHdr& a, const PfCursor& c, const int* list, bool live) {
   // Branch-free around the table load (a branch would make the compiler wait
   // for it at the join): without a paged key it reads the zero row.
   PfKey r;
@@ -2019,21 +2020,33 @@ __device__ __forceinline__ PfKey pf_resolve(const KHdr& a, const Sides& sd, cons
   if (any) j = key_pos(a, c.k, c.n_o, min(key, n - 1), list, 0, is_cmp);
   r.cmp = is_cmp;
   const bool paged = a.layout_kv == 2;
-  const BlockPos bp = block_pos(sd, is_cmp, j);
-  const int32_t* tab = is_cmp ? sd.c.tab : sd.o.tab;
-  const int cols = is_cmp ? sd.c.cols : sd.o.cols;
-  const int32_t* tp = (paged && any) ? tab + (size_t)c.k.b * cols + bp.q : reinterpret_cast<const int32_t*>(g_zero_row);
-  r.blk = *tp;
-  r.rc = paged ? (int64_t)bp.r : row_of(a, sd, c.k, is_cmp, j, 0, 0);
+  int bq = 0, br = j;
+  if (paged) {   // uniform
+    const int bs = is_cmp ? a.cmp_bs : a.ori_bs;
+    if (((a.cmp_bs & (a.cmp_bs - 1)) | (a.ori_bs & (a.ori_bs - 1))) == 0) {   // both powers of two
+      bq = j >> __builtin_ctz((unsigned)bs);
+      br = j & (bs - 1);
+    } else {
+      bq = j / bs;
+      br = j - bq * bs;
+    }
+  }
+  const int32_t* tab = is_cmp ? a.cmp_tab : a.ori_tab;
+  const int cols = is_cmp ? a.cmp_cols : a.ori_cols;
+  const int32_t* tp = (paged && any) ? tab + (size_t)c.k.b * cols + bq : reinterpret_cast<const int32_t*>(g_zero_row);
+  r.blk = *gptr(tp);
+  if (paged) r.rc = br;
+  else if (a.layout_kv == 1) r.rc = (int64_t)(is_cmp ? c.k.cmp0 : c.k.kv0) + j;
+  else r.rc = (int64_t)c.k.b * (is_cmp ? a.cmp_s : a.ori_s) + j;
   return r;
 }
 
 // Move the cursor past its tile (every wave: entering a token compacts its
-// index slots with the whole work-group).
-__device__ __forceinline__ void pf_advance(const KHdr& a, PfCursor& c, int u_end, int* list, int* misc) {
+// index slots with the whole work-group).  The header is read only on entry.
+__device__ __forceinline__ void pf_advance(HdrRegs hr, PfCursor& c, int u_end, int* list, int* misc) {
   if (c.u < u_end) {
     if (++c.tile == c.tiles) {
-      if (++c.u < u_end) pf_enter(a, c, u_end, list, misc);
+      if (++c.u < u_end) pf_enter(hdr_view(hr), c, u_end, list, misc);
     }
   }
 }
@@ -2047,11 +2060,11 @@ struct PfSrc {
 };
 
 template <int PER_TILE>
-__device__ __forceinline__ PfSrc pf_src(const Sides& sd, int layout_kv, const PfKey& k) {
+__device__ __forceinline__ PfSrc pf_src(const KHdr& a, const PfKey& k) {
   int64_t row = k.rc;
-  if (layout_kv == 2) row += (int64_t)k.blk * (k.cmp ? sd.c.bs : sd.o.bs);
-  const uint8_t* src = (k.cmp ? sd.c.kv : sd.o.kv) + row * kD;
-  const float* dsp = (k.cmp ? sd.c.ds : sd.o.ds) + row * (PER_TILE ? 8 : 1);
+  if (a.layout_kv == 2) row += (int64_t)k.blk * (k.cmp ? a.cmp_bs : a.ori_bs);
+  const uint8_t* src = (k.cmp ? a.cmp_kv : a.ori_kv) + row * kD;
+  const float* dsp = (k.cmp ? a.cmp_ds : a.ori_ds) + row * (PER_TILE ? 8 : 1);
   PfSrc r;
   r.addr = (uint64_t)(uintptr_t)(k.ok ? src : g_zero_row);
   r.ds = gptr(k.ok ? dsp : reinterpret_cast<const float*>(g_zero_row));
@@ -2124,7 +2137,7 @@ __device__ __forceinline__ void pf_scales(uint8_t* set, float s, int nvalid) {
   if constexpr (PER_TILE) mx = __uint_as_float(max8_u32(__float_as_uint(s) & 0x7fffffffu));
   const float mxd = (mx == 0.f) ? kMinDescale : mx;
   const float lam = ok ? __log2f(mxd) : kNegInf;
-  const float inv = ok ? 1.0f / mxd : 0.f;
+  const float inv = ok ? __builtin_amdgcn_rcpf(mxd) : 0.f;   // mxd is a normal float, NaN or inf
   if constexpr (PER_TILE) {
     reinterpret_cast<float*>(set + L::kScKs)[part * 64 + key] = s;
     reinterpret_cast<_Float16*>(set + L::kScVs)[part * 64 + pf_slot(key)] = (_Float16)(s * inv);
@@ -2297,19 +2310,18 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
   float sB;          // tile s+1's descale of this thread (in flight)
   int nvB;           // tile s+1's key count
   {
-    const Sides sd = cache_sides(a0);
     // tiles 0 and 1: resolved, addressed, loaded
 #pragma unroll 1
     for (int x = 0; x < 2; ++x) {
       if (w0) {
-        const PfKey k = pf_resolve(a0, sd, cur, list, cur.u < u_end);
-        const PfSrc r = pf_src<PER_TILE>(sd, a0.layout_kv, k);
+        const PfKey k = pf_resolve(a0, cur, list, cur.u < u_end);
+        const PfSrc r = pf_src<PER_TILE>(a0, k);
         kaddr[64 * x + lane] = r.addr;
         kds[64 * x + lane] = (uint64_t)(uintptr_t)r.ds;
         const int nv = (int)__popcll(__ballot(r.ok));   // the whole wave votes
         if (lane == 0) nvalid[x] = nv;
       }
-      pf_advance(a0, cur, u_end, list, misc);
+      pf_advance(hr, cur, u_end, list, misc);
     }
     lds_barrier();
     pf_issue(smem + L::kTiles, kaddr, w);
@@ -2351,7 +2363,7 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     // ---- S^T, the D halves exchanged ----
     if (w0) {   // tile s+2: block-table loads (in flight until the boundary)
       const KHdr a = hdr_view(hr);
-      kR = pf_resolve(a, cache_sides(a), cur, list, cur.u < u_end);
+      kR = pf_resolve(a, cur, list, cur.u < u_end);
     }
     const v16f S = pf_qk<PER_TILE>(tb, qf, reinterpret_cast<const float*>(set + L::kScKs), kb, dh, ln);
     {
@@ -2398,13 +2410,15 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     m = fmaxf(m, __shfl_xor(m, 32));
     maxb[w * 64 + ln] = m;
     const float Ms = hb ? Macc[1] : Macc[0];
-    if (__ballot(m > Ms + kPfTau) && ln == 0) misc[L::kFlag + par] = 1;
-    // ---- P against the current reference; redone if any wave moves it ----
+    if ((ti == 0 || __ballot(m > Ms + kPfTau)) && ln == 0) misc[L::kFlag + par] = 1;   // ti uniform
+    // ---- P against the current reference; redone if any wave moves it (a
+    // token's first tile has no reference yet: P is written only then) ----
     const float* invp = reinterpret_cast<const float*>(set + L::kScInv) + 32 * kb + 16 * dh + 4 * gg;
     const v4f iv0 = *(const v4f*)invp, iv1 = *(const v4f*)(invp + 8);
     const int pq = 2 * (2 * kb + dh) + gg;
     uint8_t* prow = pbuf + hq * 128 + 16 * (pq ^ (hq & 7));
-    float lt = pf_probs(E, Ms, iv0, iv1, prow);
+    float lt = 0.f;
+    if (ti != 0) lt = pf_probs(E, Ms, iv0, iv1, prow);
     lds_barrier();
     if (__builtin_amdgcn_readfirstlane(misc[L::kFlag + par])) {   // first tile of a token, or a jump
 #pragma unroll
@@ -2431,10 +2445,9 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     {
       // tile s+1 uses parity buf ^ 1, tile s+2 parity buf
-      const KHdr a = hdr_view(hr);
       pf_scales<PER_TILE>(smem + L::kSc + (buf ^ 1) * L::kScBytes, sB, nvB);   // tile s+1
       if (w0) {                                                       // tile s+2: addresses
-        const PfSrc r = pf_src<PER_TILE>(cache_sides(a), a.layout_kv, kR);
+        const PfSrc r = pf_src<PER_TILE>(hdr_view(hr), kR);
         const int key = opaque(lane) & 63;
         kaddr[64 * buf + key] = r.addr;
         kds[64 * buf + key] = (uint64_t)(uintptr_t)r.ds;
@@ -2446,7 +2459,7 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
       pf_issue(smem + L::kTiles + buf * kTileBytes, kaddr + 64 * buf, w);   // tile s+2 into tile s's buffer
       sB = pf_load_scale<PER_TILE>(kds + 64 * buf);                   // and its descales
       nvB = nvalid[buf];
-      pf_advance(a, cur, u_end, list, misc);
+      pf_advance(hr, cur, u_end, list, misc);
     }
     if (last) {
       // ---- epilogue of token u ----
