@@ -2427,9 +2427,11 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
 #pragma unroll
         for (int y = 0; y < 4; ++y) mn = fmaxf(mn, maxb[((y & 1) + 2 * x + 4 * (y >> 1)) * 64 + (ln & 31)]);
         const float fa = (Macc[x] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(Macc[x] - mn);
+        if (ti != 0) {   // uniform; on a token's first tile acc and lsum are zero
 #pragma unroll
-        for (int db = 0; db < 2; ++db) acc[db][x] *= fa;
-        if (x == hb) lsum *= fa;
+          for (int db = 0; db < 2; ++db) acc[db][x] *= fa;
+          if (x == hb) lsum *= fa;
+        }
         Macc[x] = mn;
       }
       lt = pf_probs(E, hb ? Macc[1] : Macc[0], iv0, iv1, prow);
@@ -2482,8 +2484,9 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
         }
         if (ae.lse && w == 0 && gg == 0) ae.lse[(size_t)t * ae.n1 + h] = lse_v;
         // lane (h, g) holds columns 8 q + 4 g + [0, 4) of each 32-column block;
-        // lanes l and l + 32 swap one half of each q pair, so that each lane
-        // stores 16 contiguous bytes: columns 16 k + 8 g + [0, 8)
+        // v_permlane32_swap trades the upper lanes' even-q half with the lower
+        // lanes' odd-q half of each q pair, so that each lane stores 16
+        // contiguous bytes: columns 16 k + 8 g + [0, 8)
         uint16_t* orow = ae.out + ((size_t)t * ae.n1 + h) * kD + 64 * w + 8 * gg;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -2493,10 +2496,12 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
             const int q0 = 2 * k2, q1 = 2 * k2 + 1;
             const uint2 A = pack_bf16x4(sc * o[4 * q0], sc * o[4 * q0 + 1], sc * o[4 * q0 + 2], sc * o[4 * q0 + 3]);
             const uint2 B = pack_bf16x4(sc * o[4 * q1], sc * o[4 * q1 + 1], sc * o[4 * q1 + 2], sc * o[4 * q1 + 3]);
-            const uint2 X = gg ? A : B;
-            const uint2 Y = make_uint2((uint32_t)__shfl_xor((int)X.x, 32), (uint32_t)__shfl_xor((int)X.y, 32));
-            const uint4 v = gg ? make_uint4(Y.x, Y.y, B.x, B.y) : make_uint4(A.x, A.y, Y.x, Y.y);
-            *(uint4*)(orow + 32 * db + 16 * k2) = v;
+            // lanes 32..63 of the first operand <-> lanes 0..31 of the second:
+            // lower lanes end with (A own, A of lane + 32), upper lanes with
+            // (B of lane - 32, B own)
+            const auto sx = __builtin_amdgcn_permlane32_swap(A.x, B.x, false, false);
+            const auto sy = __builtin_amdgcn_permlane32_swap(A.y, B.y, false, false);
+            *(uint4*)(orow + 32 * db + 16 * k2) = make_uint4(sx[0], sy[0], sx[1], sy[1]);
           }
       }
 #pragma unroll
