@@ -100,6 +100,23 @@ __device__ __forceinline__ int opaque(int x) {
 // hdr_view launders the two registers first, so that the lane reads (and
 // what is computed from them) stay where a loop body uses them instead of
 // being hoisted to the kernel entry into spilled scalar registers.
+// v combined (max or sum) with the value of lane l ^ 32, or of lane l ^ 16,
+// on the vector ALU: v_permlane32_swap (v_permlane16_swap) of v with itself
+// leaves lane l's own value in one result and its partner's in the other, so
+// no LDS round trip (as a ds_bpermute would take) is needed.
+__device__ __forceinline__ float xor32_reduce(float v, bool is_max) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return is_max ? fmaxf(a, b) : a + b;
+}
+__device__ __forceinline__ float xor16_reduce(float v, bool is_max) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return is_max ? fmaxf(a, b) : a + b;
+}
+
 // A pointer known to address device (global) memory, rebuilt from its bits
 // so that loads through it compile to global (not flat) loads after its
 // provenance was lost in a register copy.
@@ -877,7 +894,7 @@ __device__ __forceinline__ float scores_finish(const uint8_t* smem, const KeyVal
       mt = fmaxf(mt, e);
     }
   }
-  return fmaxf(mt, __shfl_xor(mt, 32));
+  return xor32_reduce(mt, true);
 }
 
 // P' = 2^(E - Mrun) of the own half; accumulates l += P' / vds_max and
@@ -1175,7 +1192,7 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
 
     // ---------------- write: final output (one split) or partial state ----------------
     const KHdr ae = hdr_view(hr);
-    float lh = lsum + __shfl_xor(lsum, 32);
+    float lh = xor32_reduce(lsum, false);
     lh = pair_reduce(misc, w, lane, lh, false);   // both key halves
     float sc;
     if (ae.splits == 1) {
@@ -1493,10 +1510,7 @@ __device__ __forceinline__ void dk_pread(const uint8_t* smem, int j, int g, v8i&
 // Per-head value over the waves (lanes j, j+16, j+32, j+48 of each wave
 // hold head j): the max or the sum.
 __device__ __forceinline__ float dk_heads_reduce(int* misc, int w, int lane, float v, bool is_max) {
-  float o1 = __shfl_xor(v, 16);
-  v = is_max ? fmaxf(v, o1) : v + o1;
-  o1 = __shfl_xor(v, 32);
-  v = is_max ? fmaxf(v, o1) : v + o1;
+  v = xor32_reduce(xor16_reduce(v, is_max), is_max);
   float* red = reinterpret_cast<float*>(misc + 64);
   if (lane < 16) red[w * 16 + lane] = v;
   lds_barrier();
@@ -2407,7 +2421,7 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     float m = E[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) m = fmaxf(m, E[i]);
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = xor32_reduce(m, true);
     maxb[w * 64 + ln] = m;
     const float Ms = hb ? Macc[1] : Macc[0];
     if ((ti == 0 || __ballot(m > Ms + kPfTau)) && ln == 0) misc[L::kFlag + par] = 1;   // ti uniform
@@ -2456,7 +2470,7 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
         const int nv = (int)__popcll(__ballot(r.ok));
         if (key == 0) nvalid[buf] = nv;
       }
-      if (last) lbuf[w * 64 + ln] = lsum + __shfl_xor(lsum, 32);     // row sums of the ending token
+      if (last) lbuf[w * 64 + ln] = xor32_reduce(lsum, false);       // row sums of the ending token
       lds_barrier();                                                  // tile s is done in every wave
       pf_issue(smem + L::kTiles + buf * kTileBytes, kaddr + 64 * buf, w);   // tile s+2 into tile s's buffer
       sB = pf_load_scale<PER_TILE>(kds + 64 * buf);                   // and its descales
