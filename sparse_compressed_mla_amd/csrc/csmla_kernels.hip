@@ -2118,12 +2118,15 @@ __device__ __forceinline__ void pf_issue(uint8_t* tb, const uint64_t* kaddr, int
 }
 
 // This thread's descale of its key (tid >> 3) of a tile (per-tile: the one of
-// D tile tid & 7), from the descale address wave 0 left in `kds`.
+// D tile tid & 7), from the descale address wave 0 left in `kds` (read with
+// pf_scale_addr, which can go ahead of the tile's DMA issue).
+__device__ __forceinline__ uint64_t pf_scale_addr(const uint64_t* kds) {
+  return kds[opaque((int)threadIdx.x) >> 3];
+}
 template <int PER_TILE>
-__device__ __forceinline__ float pf_load_scale(const uint64_t* kds) {
-  const int tid = opaque((int)threadIdx.x);
-  const float* p = gptr(reinterpret_cast<const float*>(kds[tid >> 3]));
-  return p[PER_TILE ? (tid & 7) : 0];
+__device__ __forceinline__ float pf_load_scale(uint64_t addr) {
+  const float* p = gptr(reinterpret_cast<const float*>(addr));
+  return p[PER_TILE ? (opaque((int)threadIdx.x) & 7) : 0];
 }
 
 // The tile's per-key scales into scale set `set` (thread: key tid >> 3, part
@@ -2340,8 +2343,8 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
     lds_barrier();
     pf_issue(smem + L::kTiles, kaddr, w);
     pf_issue(smem + L::kTiles + kTileBytes, kaddr + 64, w);
-    const float s0 = pf_load_scale<PER_TILE>(kds);
-    sB = pf_load_scale<PER_TILE>(kds + 64);
+    const float s0 = pf_load_scale<PER_TILE>(pf_scale_addr(kds));
+    sB = pf_load_scale<PER_TILE>(pf_scale_addr(kds + 64));
     nvB = nvalid[1];
     pf_scales<PER_TILE>(smem + L::kSc, s0, nvalid[0]);
   }
@@ -2472,9 +2475,10 @@ __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
       }
       if (last) lbuf[w * 64 + ln] = xor32_reduce(lsum, false);       // row sums of the ending token
       lds_barrier();                                                  // tile s is done in every wave
-      pf_issue(smem + L::kTiles + buf * kTileBytes, kaddr + 64 * buf, w);   // tile s+2 into tile s's buffer
-      sB = pf_load_scale<PER_TILE>(kds + 64 * buf);                   // and its descales
+      const uint64_t dsa = pf_scale_addr(kds + 64 * buf);
       nvB = nvalid[buf];
+      pf_issue(smem + L::kTiles + buf * kTileBytes, kaddr + 64 * buf, w);   // tile s+2 into tile s's buffer
+      sB = pf_load_scale<PER_TILE>(dsa);                              // and its descales
       pf_advance(hr, cur, u_end, list, misc);
     }
     if (last) {
