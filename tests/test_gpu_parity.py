@@ -350,3 +350,69 @@ def test_sensitivity_sink_dominance():
     inp.sinks = torch.full((64,), 30.0)
     _, o, l, ref = check(inp, name="sink dominates")
     assert np.abs(ref.out).max() < 1e-6 and np.abs(o).max() < 1e-6
+
+
+def test_topk_1024_full_list():
+    """top-k = 1024, the longest index list the whole-token kernel keeps in
+    LDS: the rows sit at the end of 4400- and 4300-token sequences, so nearly
+    every slot is a visible compressed token and the compacted list is full
+    (2% -1 slots, a few out-of-range ones); 270 query tokens, so the planner's
+    own choice is the whole-token kernel."""
+    rng = np.random.default_rng(91)
+    q_lens, ori = [140, 130], [4400, 4300]
+    cmp = [o // 4 for o in ori]
+    idx = _rand_idx(rng, sum(q_lens), 1024, max(cmp), 0.02)
+    inp = make_custom(seed=92, q_lens=q_lens, ori_lens=ori, cmp_lens=cmp, cmp_ratio=4,
+                      residual=[0, 0], indices=idx, return_lse=True)
+    check(inp, tokens=list(range(0, inp.t1, 3)) + [inp.t1 - 1], name="topk 1024")
+
+
+@pytest.mark.parametrize("n_splits", [None, 3])
+def test_graph_capture_replays_match_eager(n_splits):
+    """The plan is made once on the host; csmla_forward (which allocates
+    nothing and records no memset) is captured in a HIP graph and replayed
+    three times, with eager forwards of another input and host
+    synchronisations in between: every replay equals the eager forward bit
+    for bit, and the eager forward meets the oracle."""
+    rng = np.random.default_rng(95)
+    q_lens, ori = [3, 2, 4], [900, 400, 1300]
+    cmp = [o // 4 for o in ori]
+    mk = lambda seed: make_custom(seed=seed, q_lens=q_lens, ori_lens=ori, cmp_lens=cmp, cmp_ratio=4,
+                                  residual=[0, 0, 0], indices=_rand_idx(rng, sum(q_lens), 80, max(cmp), 0.1),
+                                  return_lse=True)
+    inp, other = mk(96), mk(97)
+    check(inp, name=f"graph case, splits {n_splits}", splits=n_splits)
+    g, g2 = inp.to(DEV), other.to(DEV)
+    if n_splits is not None:
+        os.environ["CSMLA_SPLITS"] = str(n_splits)
+    try:
+        plan = m.Plan(g)
+    finally:
+        os.environ.pop("CSMLA_SPLITS", None)
+    say(f"  graph plan splits={plan.splits} head_group={plan.head_group}")
+    out = torch.empty(g.q.shape, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((g.t1, 64), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
+    tens = m.tensors_from(g, out, lse, ws if plan.workspace_bytes else None)
+    cap = torch.cuda.Stream(DEV)
+    cap.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(cap):
+        m.csmla_forward(plan.problem, tens, plan.metadata, cap.cuda_stream)
+    torch.cuda.synchronize()
+    eo, el = out.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        m.csmla_forward(plan.problem, tens, plan.metadata, cap.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(7.0)
+        lse.fill_(7.0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cap):
+            graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eo), f"replay {rep}: output differs from the eager forward"
+        assert torch.equal(lse, el), f"replay {rep}: lse differs from the eager forward"
+        m.forward(g2)                       # eager work between the replays
+        torch.cuda.synchronize()
+    say(f"graph case, splits {n_splits}: 3 replays equal the eager forward")
