@@ -276,17 +276,24 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
     const int64_t f = std::atoll(env);
     if (f >= 1) S = std::max(s_list, f);
   }
-  // Small decode batches with per-token descales: split the heads instead of
-  // the keys (groups of 8 heads up to 64 tokens, of 16 up to 256), so that no
-  // partial outputs need merging.  Long key lists keep the key split.
+  // Decode batches with per-token descales: split the heads instead of the
+  // keys, so that no partial outputs need merging.  Groups of 8 heads while
+  // their units fit one round of the work-groups (T1 <= 32), else groups of
+  // 16 up to 128 tokens; from 129 tokens whole tokens per unit (all 64 heads,
+  // hg = kN1) when the index list fits the list buffer.  Measured on MI355X
+  // with 640 keys per token: 48 tokens take 17.1 us in 16-head groups and
+  // 29.3 us in 8-head groups; 128 tokens 34.5 us in 16-head groups and
+  // 38.2 us as whole tokens; 160 tokens 47.3 us and 39.1 us.  Long key lists
+  // and per-tile descales keep the key split up to 256 tokens.
   // Prefill-sized batches (more tokens than CUs) with at most kListMax index
-  // slots per token: whole tokens per unit (all 64 heads, hg = kN1), no splits.
+  // slots per token: whole tokens per unit, no splits.
+  const bool pf_ok = p->topk <= kListMax;
   int hg = 0;
   if (p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN && avg <= 8192) {
-    if (T1 <= 64) hg = 8;
-    else if (T1 <= 256) hg = 16;
+    if (T1 * (kN1 / 8) <= kMaxGrid) hg = 8;
+    else if (T1 <= 128 || (T1 <= 256 && !pf_ok)) hg = 16;
+    else if (pf_ok) hg = kN1;
   }
-  const bool pf_ok = p->topk <= kListMax;
   if (T1 > 256 && pf_ok) hg = kN1;
   if (const char* env = std::getenv("CSMLA_KERNEL")) {   // tuning / test override
     if (!std::strcmp(env, "split")) hg = 0;

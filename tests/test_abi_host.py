@@ -97,8 +97,14 @@ def test_plan_head_split_for_small_decode_batches(monkeypatch):
     monkeypatch.delenv("CSMLA_KERNEL", raising=False)
     _, md, ws = m.csmla_plan(base_problem())
     assert md[12] == 8 and md[5] == 1 and md[6] == 32 * 8 and md[7] == 256 and ws == 0
+    _, md, _ = m.csmla_plan(base_problem(batch=48, t1=48))
+    assert md[12] == 16 and md[6] == 48 * 4               # 8-head groups would need two rounds
     _, md, _ = m.csmla_plan(base_problem(batch=128, t1=128))
     assert md[12] == 16 and md[6] == 128 * 4
+    _, md, _ = m.csmla_plan(base_problem(batch=160, t1=160))
+    assert md[12] == 64 and md[6] == 160                  # whole tokens from 129 tokens
+    _, md, _ = m.csmla_plan(base_problem(batch=160, t1=160, kv_scale_mode=1))
+    assert md[12] == 0                                    # per-tile below 257 tokens: key split
     _, md, _ = m.csmla_plan(base_problem(batch=512, t1=512))
     assert md[12] == 64 and md[5] == 1 and md[6] == 512   # prefill-sized batches: whole tokens
     _, md, _ = m.csmla_plan(base_problem(batch=512, t1=512, kv_scale_mode=1))
