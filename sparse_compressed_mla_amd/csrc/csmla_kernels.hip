@@ -1290,7 +1290,7 @@ struct LdsDK {
   static constexpr int kKs = kInv + 4 * kChunk;                // float [kChunk]
   static constexpr int kPx = kKs + 4 * kChunk;                 // fp8 P: [hi, lo][16 heads][kDkPxRow]
   static constexpr int kList = kPx + 2 * 16 * kDkPxRow;        // int [kListMax]
-  static constexpr int kMisc = kList + 4 * kListMax;           // [0, 2 waves) compaction, [kFlag] redo flag,
+  static constexpr int kMisc = kList + 4 * kListMax;           // [0, 2 waves) compaction, [kFlag, +2) reference flags,
   static constexpr int kBytes = kMisc + 4 * 64 + 4 * 4 * 64;   // [64, 64 + 16 waves) per-head reductions
 };
 static_assert(LdsDK::kBytes <= 160 * 1024, "LDS");
@@ -1526,13 +1526,19 @@ __device__ __forceinline__ float dk_heads_reduce(int* misc, int w, int lane, flo
   return x[0];
 }
 
-// Runs the unit's keys into (oacc, lsum); `preset` and Mrun as in the split kernel.
-__device__ __forceinline__ void dk_run(const KHdr& a, bool preset, UnitState& us, int* list, int* misc, uint8_t* smem,
+// Runs the unit's keys into (oacc, lsum) against the reference Mrun, which the
+// first tile sets (its maximum maps to 2^kPShift) and a later tile moves when
+// one of its P' would pass 2^kTau: that tile's waves vote through a flag
+// (one word per tile parity, read with the P operands after the P barrier),
+// then every wave takes the new per-head maximum, rescales its accumulators
+// and row sums, and rewrites the tile's P.  Flags start at zero.
+__device__ __forceinline__ void dk_run(const KHdr& a, UnitState& us, int* list, int* misc, uint8_t* smem,
                                        const DkOffsets& o, int w, int lane, const v8i (&qreg)[4], float qs,
                                        v4f (&oacc)[kDkDB], float& Mrun, float& lsum) {
   using L = LdsDK;
   const int j = lane & 15, g = lane >> 4;
-  int* flag = misc + L::kFlag;
+  int* flag = misc + L::kFlag;   // [2]: by tile parity
+  int it = 0;                    // tiles run so far (over the chunks)
 #pragma unroll
   for (int db = 0; db < kDkDB; ++db) oacc[db] = v4f{0.f, 0.f, 0.f, 0.f};
   lsum = 0.f;
@@ -1553,59 +1559,49 @@ __device__ __forceinline__ void dk_run(const KHdr& a, bool preset, UnitState& us
     feed.w = w;
     if (tiles > 1) dk_src2(kaddr, 1, w, feed.src[0], feed.src[1]);
     gather_barrier(false);
-    for (int i = 0; i < tiles; ++i) {
+    for (int i = 0; i < tiles; ++i, ++it) {
       uint8_t* tb = smem + L::kTiles + (i & 1) * kDkTileBytes;
       const bool next = __builtin_amdgcn_readfirstlane(i + 1 < tiles ? 1 : 0) != 0;
+      if (threadIdx.x == 0) flag[(it & 1) ^ 1] = 0;   // the previous tile's flag was read by all
       feed.tb = smem + L::kTiles + ((i + 1) & 1) * kDkTileBytes;
       feed.on = next;
       v4f s[kDkKB];
       dk_qk(tb, o, qreg, s, feed);   // half 0 of tile i+1 goes out between the S^T MFMAs
       const float mt = dk_exponents(smem, i, w, g, qs, s);
-      if (!preset && c0 == us.kb && i == 0) {   // wave-uniform
+      if (c0 == us.kb && i == 0) {   // wave-uniform
         const float mx = dk_heads_reduce(misc, w, lane, mt, true);
         Mrun = (mx == kNegInf) ? kNegInf : mx - kPShift;
       } else if (__ballot(mt > Mrun + kTau)) {
-        *flag = 1;   // would overflow fp8: the unit is redone with a preset reference
+        flag[it & 1] = 1;   // would pass the fp8 range: the reference moves
       }
       if (next) {   // half 1: in flight during the probabilities and P V
 #pragma unroll
         for (int mi = 0; mi < kDkGI; ++mi) dk_issue(feed.src[1], mi, 1, feed.tb, w);
       }
+      const float lprev = lsum;
       dk_probs(smem, i, w, j, g, Mrun, s, lsum);
       lds_barrier();
       v8i phi, plo;
       dk_pread(smem, j, g, phi, plo);
+      if (__builtin_amdgcn_readfirstlane(flag[it & 1])) {
+        // every wave's P reads are done at the reduction's first barrier
+        const float mx = dk_heads_reduce(misc, w, lane, mt, true);
+        const float Mnew = mx - kPShift;                       // mx > Mrun + kTau: finite
+        const float Mold = (Mrun == kNegInf) ? 0.f : Mrun;     // the reference the sums were taken against
+        const float fa = __builtin_amdgcn_exp2f(Mold - Mnew);
+#pragma unroll
+        for (int db = 0; db < kDkDB; ++db) oacc[db] *= fa;
+        lsum = lprev * fa;
+        Mrun = Mnew;
+        dk_probs(smem, i, w, j, g, Mrun, s, lsum);
+        lds_barrier();
+        dk_pread(smem, j, g, phi, plo);
+      }
       dk_pv(tb, o, phi, plo, oacc);
       if (i + 2 < tiles) dk_src2(kaddr, i + 2, w, feed.src[0], feed.src[1]);
       gather_barrier(false);   // tile i+1 landed; every wave is done with tile i and with P
     }
   }
-}
-
-// Per-head maximum exponent over the unit (S^T only), for the redo pass.
-__device__ __forceinline__ float dk_unit_max(const KHdr& a, UnitState& us, int* list, int* misc, uint8_t* smem,
-                                             const DkOffsets& o, int w, int lane, const v8i (&qreg)[4], float qs) {
-  using L = LdsDK;
-  const int g = lane >> 4;
-  float mx = kNegInf;
-  const uint64_t* kaddr = reinterpret_cast<const uint64_t*>(smem + L::kAddr);
-  for (int c0 = us.kb; c0 < us.ke; c0 += L::kChunk) {
-    const int c1 = min(us.ke, c0 + L::kChunk);
-    cover_chunk<L::kNT>(a, us, list, misc, c0, c1);
-    resolve_chunk<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
-    const int nkeys = c1 - c0, tiles = (nkeys + kDkRows - 1) / kDkRows;
-    for (int i = 0; i < tiles; ++i) {
-      dk_gather_tile(kaddr, i, smem + L::kTiles, w);
-      gather_barrier(false);
-      v4f s[kDkKB];
-      DkFeed none;
-      none.on = false;
-      dk_qk(smem + L::kTiles, o, qreg, s, none);
-      mx = fmaxf(mx, dk_exponents(smem, i, w, g, qs, s));
-      lds_barrier();
-    }
-  }
-  return dk_heads_reduce(misc, w, lane, mx, true);
 }
 
 __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
@@ -1682,16 +1678,8 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
 
     v4f oacc[kDkDB];
     float Mrun = kNegInf, lsum = 0.f;
-    for (int pass = 0;; ++pass) {
-      if (threadIdx.x == 0) misc[L::kFlag] = 0;
-      dk_run(a, pass > 0, us, list, misc, smem, o, w, lane, qreg, qs, oacc, Mrun, lsum);
-      lds_barrier();
-      const int redo = misc[L::kFlag];
-      lds_barrier();
-      if (!redo || pass > 0) break;
-      const float mx = dk_unit_max(a, us, list, misc, smem, o, w, lane, qreg, qs);
-      Mrun = (mx == kNegInf) ? kNegInf : mx - kPShift;
-    }
+    if (threadIdx.x < 2) misc[L::kFlag + threadIdx.x] = 0;   // seen at dk_run's first barrier
+    dk_run(a, us, list, misc, smem, o, w, lane, qreg, qs, oacc, Mrun, lsum);
 
     // ---------------- epilogue: normalise, add the sink, bf16 through LDS ----------------
     const KHdr& ae = a;
