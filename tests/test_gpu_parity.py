@@ -304,9 +304,9 @@ def test_determinism_and_nan_canaries():
 
 # ---------------------------------------------------------------- sensitivity
 
-def _dominant_key_case(pos_offset, which="ori"):
-    """One key whose score is ~40 above the rest: query row 0 must return that
-    key's value row iff the key is visible.  Row 0 of a 2-row batch sits at
+def _dominant_key_case(pos_offset, which="ori", score=40.0):
+    """One key whose score is `score` (default ~40) above the rest: query row 0
+    must return that key's value row iff the key is visible (for score 40).  Row 0 of a 2-row batch sits at
     p = S2 - 2; its band is [p - 127, p] and its compressed prefix [0, (p+1)//r)."""
     s2, s1, r = 400, 2, 4
     c = s2 // r
@@ -318,7 +318,7 @@ def _dominant_key_case(pos_offset, which="ori"):
     inp.q_descale[0] = inp.q_descale[0, 0]
     p = s2 - s1
     qq = float((q[0].view(torch.float8_e4m3fn).float() ** 2).sum())
-    kds = 40.0 / (float(inp.q_descale[0, 0]) * 512 ** -0.5 * qq)
+    kds = score / (float(inp.q_descale[0, 0]) * 512 ** -0.5 * qq)
     if which == "ori":
         j = p + pos_offset
         kv, ds, tab = inp.ori_kv, inp.ori_kv_descale, inp.ori_block_table
@@ -416,3 +416,15 @@ def test_graph_capture_replays_match_eager(n_splits):
         m.forward(g2)                       # eager work between the replays
         torch.cuda.synchronize()
     say(f"graph case, splits {n_splits}: 3 replays equal the eager forward")
+
+
+@pytest.mark.parametrize("score,off", [(6.0, -1), (6.0, -40), (9.0, -1)])
+def test_reference_move_with_live_history(score, off):
+    """A compressed key (after the 128-key band, so in a later tile) scores 6
+    or 9 above the others: it passes the fp8 range of P' set by the first
+    tile, so the softmax reference moves mid-unit, while the band's keys
+    still carry a weight comparable to it (about e^-6 each over ~230 keys):
+    the accumulators' and row sums' rescale must be exact for the output and
+    lse to meet the oracle."""
+    inp, _ = _dominant_key_case(off, "cmp", score=score)
+    check(inp, tokens=[0, 1], name=f"reference move, score {score}, cmp {off}")
