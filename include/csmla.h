@@ -194,16 +194,27 @@ csmla_status csmla_plan(const csmla_problem* problem, const csmla_host_lengths* 
 csmla_status csmla_forward(const csmla_problem* problem, const csmla_tensors* tensors,
                            const int32_t* metadata, void* stream);
 
-/* Resolved key list of every query row, as the attention kernel resolves it
- * (same device code): for row t, keys[t*max_keys + k] for k < counts[2t] +
- * counts[2t+1] holds the physical cache row of the k-th key — ori band rows in
- * position order first (counts[2t] of them), then cmp rows in index-slot order
- * (counts[2t+1]); entries past max_keys are not written (counts are exact).
+/* Resolved key list of every query row (QuantSparseFlashMla, 参数说明: the
+ * band window, cmp_sparse_indices with -1 skipped, the block tables), as the
+ * key-split and head-split kernels resolve it: their resolution functions
+ * (key position, block position, table entry, row) run on every key.  For
+ * row t, keys[t*max_keys + k] for k < counts[2t] + counts[2t+1] holds the
+ * physical cache row of the k-th key — ori band rows in position order first
+ * (counts[2t] of them), then cmp rows in index-slot order (counts[2t+1]);
+ * entries past max_keys are not written (counts are exact).
  *   keys    device int32 [t1, max_keys]
  *   counts  device int32 [t1, 2]
  * Used to check the gather sets bit for bit. */
 csmla_status csmla_debug_resolve(const csmla_problem* problem, const csmla_tensors* tensors,
                                  int32_t* keys, int32_t* counts, int32_t max_keys, void* stream);
+
+/* The same export through the whole-token (prefill) kernel's own resolution:
+ * its token entry (lengths, index compaction), per-tile key resolution and
+ * row-address functions, with the row recovered from the address its LDS-DMA
+ * would read.  Same arguments and output as csmla_debug_resolve;
+ * CSMLA_ERR_UNSUPPORTED when topk > 1024 (that kernel's index-list limit). */
+csmla_status csmla_debug_resolve_whole_token(const csmla_problem* problem, const csmla_tensors* tensors,
+                                             int32_t* keys, int32_t* counts, int32_t max_keys, void* stream);
 
 #ifdef __cplusplus
 }

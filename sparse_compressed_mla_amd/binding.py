@@ -81,9 +81,9 @@ def load(path: str = LIB_PATH):
     lib.csmla_forward.restype = ctypes.c_int
     lib.csmla_forward.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaTensors),
                                   ctypes.POINTER(_i32), _p]
-    lib.csmla_debug_resolve.restype = ctypes.c_int
-    lib.csmla_debug_resolve.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaTensors),
-                                        _p, _p, _i32, _p]
+    for fn in (lib.csmla_debug_resolve, lib.csmla_debug_resolve_whole_token):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaTensors), _p, _p, _i32, _p]
     _lib = lib
     return lib
 
@@ -144,6 +144,14 @@ def csmla_debug_resolve(problem: CsmlaProblem, tensors: CsmlaTensors, keys_ptr: 
     st = load().csmla_debug_resolve(ctypes.byref(problem), ctypes.byref(tensors), _p(keys_ptr), _p(counts_ptr),
                                     max_keys, _p(stream))
     _check(st, "csmla_debug_resolve")
+    return st
+
+
+def csmla_debug_resolve_whole_token(problem: CsmlaProblem, tensors: CsmlaTensors, keys_ptr: int, counts_ptr: int,
+                                    max_keys: int, stream: int = 0) -> int:
+    st = load().csmla_debug_resolve_whole_token(ctypes.byref(problem), ctypes.byref(tensors), _p(keys_ptr),
+                                                _p(counts_ptr), max_keys, _p(stream))
+    _check(st, "csmla_debug_resolve_whole_token")
     return st
 
 
@@ -278,9 +286,11 @@ def forward(inp, out=None, lse=None, workspace=None, plan: Optional[Plan] = None
     return out, lse
 
 
-def debug_resolve(inp, max_keys: int, stream=None):
-    """Resolved physical rows per query token (the kernels' resolution code).
-    Returns (keys int32 [t1, max_keys], counts int32 [t1, 2]) on the GPU."""
+def debug_resolve(inp, max_keys: int, stream=None, whole_token: bool = False):
+    """Resolved physical rows per query token (the kernels' resolution code:
+    the key-split / head-split kernels' functions, or with whole_token the
+    whole-token kernel's own).  Returns (keys int32 [t1, max_keys], counts
+    int32 [t1, 2]) on the GPU."""
     import torch
     dev = inp.q.device
     keys = torch.full((inp.q.shape[0], max_keys), -1, dtype=torch.int32, device=dev)
@@ -288,7 +298,8 @@ def debug_resolve(inp, max_keys: int, stream=None):
     p = problem_from(inp)
     t = tensors_from(inp, None, None)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
-    csmla_debug_resolve(p, t, _ptr(keys), _ptr(counts), max_keys, s)
+    fn = csmla_debug_resolve_whole_token if whole_token else csmla_debug_resolve
+    fn(p, t, _ptr(keys), _ptr(counts), max_keys, s)
     return keys, counts
 
 

@@ -456,16 +456,29 @@ csmla_status csmla_forward(const csmla_problem* p, const csmla_tensors* t, const
   return CSMLA_OK;
 }
 
-csmla_status csmla_debug_resolve(const csmla_problem* p, const csmla_tensors* t, int32_t* keys, int32_t* counts,
-                                 int32_t max_keys, void* stream) {
+static csmla_status debug_resolve(const csmla_problem* p, const csmla_tensors* t, int32_t* keys, int32_t* counts,
+                                  int32_t max_keys, int whole_token, void* stream) {
   KArgs a;
   csmla_status st = build_args(p, t, nullptr, a, false);
   if (st != CSMLA_OK) return st;
   if (!keys || !counts || max_keys < 0) return fail(CSMLA_ERR_INVALID_ARG, "keys/counts buffers are required");
-  const int e = launch_debug_resolve(a, keys, counts, max_keys, stream);
+  if (whole_token && p->topk > kListMax)
+    return fail(CSMLA_ERR_UNSUPPORTED, "the whole-token kernel keeps at most %d index slots (topk %d)", kListMax,
+                p->topk);
+  const int e = launch_debug_resolve(a, keys, counts, max_keys, whole_token, stream);
   if (e != 0) return fail(CSMLA_ERR_HIP, "kernel launch failed (hipError %d)", e);
   g_last_error.clear();
   return CSMLA_OK;
+}
+
+csmla_status csmla_debug_resolve(const csmla_problem* p, const csmla_tensors* t, int32_t* keys, int32_t* counts,
+                                 int32_t max_keys, void* stream) {
+  return debug_resolve(p, t, keys, counts, max_keys, 0, stream);
+}
+
+csmla_status csmla_debug_resolve_whole_token(const csmla_problem* p, const csmla_tensors* t, int32_t* keys,
+                                             int32_t* counts, int32_t max_keys, void* stream) {
+  return debug_resolve(p, t, keys, counts, max_keys, 1, stream);
 }
 
 }  // extern "C"

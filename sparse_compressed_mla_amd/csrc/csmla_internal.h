@@ -63,6 +63,7 @@ uint32_t hash_bytes(const void* data, size_t n, uint32_t seed = 2166136261u);
 
 // launchers (csmla_kernels.hip); return a hipError_t as int
 int launch_forward(const KArgs& a, void* stream);
-int launch_debug_resolve(const KArgs& a, int32_t* keys, int32_t* counts, int32_t max_keys, void* stream);
+int launch_debug_resolve(const KArgs& a, int32_t* keys, int32_t* counts, int32_t max_keys, int whole_token,
+                         void* stream);
 
 }  // namespace csmla

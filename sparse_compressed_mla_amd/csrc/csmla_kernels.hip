@@ -1584,11 +1584,15 @@ __device__ __forceinline__ void dk_run(const KHdr& a, UnitState& us, int* list, 
       v8i phi, plo;
       dk_pread(smem, j, g, phi, plo);
       if (__builtin_amdgcn_readfirstlane(flag[it & 1])) {
-        // every wave's P reads are done at the reduction's first barrier
+        // every wave's P reads are done at the reduction's first barrier.  The
+        // vote is shared by all heads, so a head whose tile maximum stays
+        // below its reference keeps it (the reference never moves down: a
+        // downward move would scale the history by 2^(Mrun - Mnew), which
+        // overflows once a head's earlier maximum is far above this tile's).
+        // A head with no finite exponent so far has an empty history.
         const float mx = dk_heads_reduce(misc, w, lane, mt, true);
-        const float Mnew = mx - kPShift;                       // mx > Mrun + kTau: finite
-        const float Mold = (Mrun == kNegInf) ? 0.f : Mrun;     // the reference the sums were taken against
-        const float fa = __builtin_amdgcn_exp2f(Mold - Mnew);
+        const float Mnew = fmaxf(Mrun, mx - kPShift);
+        const float fa = (Mrun == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(Mrun - Mnew);
 #pragma unroll
         for (int db = 0; db < kDkDB; ++db) oacc[db] *= fa;
         lsum = lprev * fa;
@@ -2540,6 +2544,36 @@ pf_kernel(const KArgs a) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// debug export of the whole-token kernel's resolved key rows: the token entry
+// (pf_enter: lengths, index compaction), the per-tile key resolution
+// (pf_resolve) and the row address (pf_src) that feeds the tile's LDS-DMA,
+// each the same function pf_kernel runs; the row is recovered from the address.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kPfThreads) pf_debug_resolve_kernel(const KArgs a, int32_t* keys, int32_t* counts,
+                                                                      int32_t max_keys) {
+  __shared__ int list[kListMax];
+  __shared__ int misc[64];
+  const int t = blockIdx.x;
+  PfCursor c;
+  c.u = t;
+  c.nl = token_lens(a, t);
+  c.nip = pf_idx_raw(a, t);
+  pf_enter(a, c, t + 1, list, misc);
+  if (threadIdx.x == 0) { counts[2 * t] = c.n_o; counts[2 * t + 1] = c.n_c; }
+  const int n = min(c.n_o + c.n_c, max_keys);
+  if (threadIdx.x >= 64) return;
+  for (c.tile = 0; c.tile * kTileKeys < n; ++c.tile) {
+    const PfKey k = pf_resolve(a, c, list, true);
+    const PfSrc src = pf_src<0>(a, k);
+    const int key = kTileKeys * c.tile + (int)threadIdx.x;
+    if (key < n && src.ok) {
+      const uint8_t* base = k.cmp ? a.cmp_kv : a.ori_kv;
+      keys[(size_t)t * max_keys + key] = (int32_t)(((const uint8_t*)(uintptr_t)src.addr - base) / kD);
+    }
+  }
+}
+
 int launch_forward(const KArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (a.hg == kN1) {
@@ -2576,9 +2610,14 @@ int launch_forward(const KArgs& a, void* stream) {
   return (int)e;
 }
 
-int launch_debug_resolve(const KArgs& a, int32_t* keys, int32_t* counts, int32_t max_keys, void* stream) {
-  hipLaunchKernelGGL(debug_resolve_kernel, dim3(a.t1), dim3(kThreads), 0, (hipStream_t)stream, a, keys, counts,
-                     max_keys);
+int launch_debug_resolve(const KArgs& a, int32_t* keys, int32_t* counts, int32_t max_keys, int whole_token,
+                         void* stream) {
+  if (whole_token)
+    hipLaunchKernelGGL(pf_debug_resolve_kernel, dim3(a.t1), dim3(kPfThreads), 0, (hipStream_t)stream, a, keys, counts,
+                       max_keys);
+  else
+    hipLaunchKernelGGL(debug_resolve_kernel, dim3(a.t1), dim3(kThreads), 0, (hipStream_t)stream, a, keys, counts,
+                       max_keys);
   return (int)hipGetLastError();
 }
 

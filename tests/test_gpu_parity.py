@@ -69,22 +69,27 @@ def check(inp_cpu, tokens=None, name="", inp_gpu=None, splits=None, monkeypatch=
     return stats, o, l, ref
 
 
-def check_rows(inp_cpu, tokens=None, name=""):
-    """csmla_debug_resolve row lists == the oracle's, bit for bit and in order."""
+def check_rows(inp_cpu, tokens=None, name="", inp_gpu=None):
+    """The resolved row lists == the oracle's, bit for bit and in order, through
+    both resolution paths: the key-split / head-split kernels' functions
+    (csmla_debug_resolve) and the whole-token kernel's own
+    (csmla_debug_resolve_whole_token; that kernel takes top-k <= 1024)."""
     toks = list(range(inp_cpu.t1)) if tokens is None else list(tokens)
     tt = token_table(inp_cpu)
     want = {t: token_rows(inp_cpu, t, tt) for t in toks}
     max_keys = max([len(v) for v in want.values()] + [1])
-    say(f"rows {name}: max_keys={max_keys}")
-    keys, counts = m.debug_resolve(inp_cpu.to(DEV), max_keys)
-    torch.cuda.synchronize()
-    keys, counts = keys.cpu().numpy(), counts.cpu().numpy()
-    for t in toks:
-        w = want[t]
-        n_o = sum(1 for k, _ in w if k == 0)
-        n_c = len(w) - n_o
-        assert counts[t, 0] == n_o and counts[t, 1] == n_c, (name, t, counts[t], n_o, n_c)
-        assert np.array_equal(keys[t, :len(w)], np.array([r for _, r in w], dtype=np.int32)), (name, t)
+    g = inp_gpu if inp_gpu is not None else inp_cpu.to(DEV)
+    for whole in ((False, True) if inp_cpu.topk <= 1024 else (False,)):
+        say(f"rows {name}: max_keys={max_keys} whole_token={whole}")
+        keys, counts = m.debug_resolve(g, max_keys, whole_token=whole)
+        torch.cuda.synchronize()
+        keys, counts = keys.cpu().numpy(), counts.cpu().numpy()
+        for t in toks:
+            w = want[t]
+            n_o = sum(1 for k, _ in w if k == 0)
+            n_c = len(w) - n_o
+            assert counts[t, 0] == n_o and counts[t, 1] == n_c, (name, whole, t, counts[t], n_o, n_c)
+            assert np.array_equal(keys[t, :len(w)], np.array([r for _, r in w], dtype=np.int32)), (name, whole, t)
 
 
 # ---------------------------------------------------------------- the five workloads
@@ -125,15 +130,21 @@ def test_cfg4_csa_mtp_long():
 
 
 def test_cfg5_csa_prefill_sampled(kernel_mode):
+    """All of the first 2048 query tokens of the first sequence (early rows see
+    few compressed tokens and fewer than 512 valid slots), every 8th token
+    after, the last 40 and the batch edges; the resolved rows of every token
+    through both resolution paths (auto mode only: they do not depend on the
+    kernel choice)."""
     if kernel_mode not in ("auto", "split"):
         pytest.skip("auto is the prefill kernel here; heads16 does not take per-tile descales")
     inp_g = make_config(5, device=DEV)
     inp = inp_g.to("cpu")
     T1 = inp.t1
-    toks = sorted(set(list(range(0, 160)) + list(range(160, T1, 211)) + list(range(T1 - 40, T1))
+    toks = sorted(set(list(range(0, 2048)) + list(range(2048, T1, 8)) + list(range(T1 - 40, T1))
                       + [4095, 4096, 8191, 8192, 12287, 12288]))
-    check(inp, tokens=toks, name="cfg5 csa prefill (sampled rows)", inp_gpu=inp_g)
-    check_rows(inp, tokens=toks[::4], name="cfg5")
+    check(inp, tokens=toks, name=f"cfg5 csa prefill ({len(toks)} rows)", inp_gpu=inp_g)
+    if kernel_mode == "auto":
+        check_rows(inp, name="cfg5 (all tokens)", inp_gpu=inp_g)
 
 
 # ---------------------------------------------------------------- edge cases
@@ -257,6 +268,7 @@ def test_prefill_stream_many_tokens_per_workgroup(kv_scale_mode):
                       residual=[o % 4 for o in ori], indices=idx, seqused_q=[500, 361, 177, 40],
                       kv_scale_mode=kv_scale_mode, return_lse=True)
     check(inp, name=f"prefill stream, scale mode {kv_scale_mode}")
+    check_rows(inp, name=f"prefill stream, scale mode {kv_scale_mode}")
 
 
 @pytest.mark.parametrize("kv_scale_mode", [0, 1])
@@ -304,14 +316,22 @@ def test_determinism_and_nan_canaries():
 
 # ---------------------------------------------------------------- sensitivity
 
-def _dominant_key_case(pos_offset, which="ori", score=40.0):
+def _dominant_key_case(pos_offset, which="ori", score=40.0, residual=0, s1=2, indices_of=None):
     """One key whose score is `score` (default ~40) above the rest: query row 0
-    must return that key's value row iff the key is visible (for score 40).  Row 0 of a 2-row batch sits at
-    p = S2 - 2; its band is [p - 127, p] and its compressed prefix [0, (p+1)//r)."""
-    s2, s1, r = 400, 2, 4
+    must return that key's value row iff the key is visible (for score 40).
+    Row 0 of an s1-row batch over S2 = 400 ori tokens sits at p = S2 - s1; its
+    band is [p - 127, p].  The compressed cache holds C = 100 tokens with
+    `residual`, so row 0's restored position is p_cmp = 4 C + residual - s1 and
+    its compressed prefix is [0, (p_cmp + 1) // 4).  indices_of(vis, j) gives
+    the CSA index row (None: HCA, every visible compressed token)."""
+    s2, r = 400, 4
     c = s2 // r
-    inp = make_custom(seed=81, q_lens=[s1], ori_lens=[s2], cmp_lens=[c], cmp_ratio=r, residual=[0],
-                      indices=None, return_lse=True)
+    p_cmp = c * r + residual - s1
+    vis = (p_cmp + 1) // r
+    j_cmp = vis + pos_offset
+    idx = None if indices_of is None else np.tile(np.asarray(indices_of(vis, j_cmp)), (s1, 1))
+    inp = make_custom(seed=81, q_lens=[s1], ori_lens=[s2], cmp_lens=[c], cmp_ratio=r, residual=[residual],
+                      indices=idx, return_lse=True)
     q = inp.q[0].clone()
     q[:] = q[0]                        # every head uses the same query vector
     inp.q[0] = q
@@ -323,7 +343,7 @@ def _dominant_key_case(pos_offset, which="ori", score=40.0):
         j = p + pos_offset
         kv, ds, tab = inp.ori_kv, inp.ori_kv_descale, inp.ori_block_table
     else:
-        j = (p + 1) // r + pos_offset
+        j = j_cmp
         kv, ds, tab = inp.cmp_kv, inp.cmp_kv_descale, inp.cmp_block_table
     bs = kv.shape[1]
     blk = int(tab[0, j // bs])
@@ -343,6 +363,60 @@ def test_sensitivity_dominant_key(which, off):
     near = np.abs(ref.out[0] - value[None, :]).max() < 1e-3
     assert near == visible, (which, off)
     assert (np.abs(o[0] - value[None, :]).max() < 0.05) == visible, (which, off)
+
+
+@pytest.mark.parametrize("off", [-1, 0])
+def test_sensitivity_cmp_edge_with_residual(off):
+    """Compressed visibility edge with residual r - 1 = 3 and 8 query rows: row
+    0's restored position is 4 * 100 + 3 - 8 = 395, so it sees 99 compressed
+    tokens; the key at 98 (vis - 1) decides the output, the key at 99 (vis)
+    must not.  With residual 0 the same row would see only 98."""
+    inp, value = _dominant_key_case(off, "cmp", residual=3, s1=8)
+    _, o, l, ref = check(inp, tokens=[0], name=f"dominant cmp {off}, residual 3")
+    visible = off < 0
+    assert (np.abs(ref.out[0] - value[None, :]).max() < 1e-3) == visible
+    assert (np.abs(o[0] - value[None, :]).max() < 0.05) == visible
+
+
+def _csa_rows_without(vis, j):
+    """Every visible compressed token but j, shuffled, with j's slot (the
+    first) holding -1 and a -1 tail."""
+    rng = np.random.default_rng(vis)
+    rest = [c for c in range(vis) if c != j]
+    row = np.full(128, -1)
+    row[1:1 + len(rest)] = rng.permutation(rest)
+    return row
+
+
+def _csa_rows_duplicated(vis, j):
+    """j listed twice (slots 0 and 5) among the other visible tokens."""
+    row = _csa_rows_without(vis, j)
+    row[0] = j
+    row[5] = j
+    return row
+
+
+def test_sensitivity_dominant_behind_invalid_slot():
+    """CSA: the dominant compressed token is causally visible but its slot holds
+    -1 (and it is listed nowhere else), so it is not a key; the output must
+    not follow it (QuantSparseFlashMla, 参数说明: -1 marks an invalid slot)."""
+    inp, value = _dominant_key_case(-3, "cmp", indices_of=_csa_rows_without)
+    _, o, l, ref = check(inp, tokens=[0, 1], name="dominant behind a -1 slot")
+    assert np.abs(ref.out[0] - value[None, :]).max() > 0.1
+    assert np.abs(o[0] - value[None, :]).max() > 0.1
+
+
+def test_sensitivity_dominant_in_duplicate_slot():
+    """CSA: the dominant token listed in two slots counts as two keys, so the
+    normaliser holds it twice: lse rises by ~log 2 over a single listing, far
+    past the lse tolerance, while the output still follows the key."""
+    inp, value = _dominant_key_case(-3, "cmp", indices_of=_csa_rows_duplicated)
+    _, o, l, ref = check(inp, tokens=[0, 1], name="dominant in a duplicate slot")
+    single, _ = _dominant_key_case(-3, "cmp", indices_of=lambda v, j: np.where(
+        np.arange(128) == 5, -1, _csa_rows_duplicated(v, j)))
+    ref1 = oracle_forward(single, [0])
+    assert np.all(np.abs(ref.lse[0] - ref1.lse[0] - np.log(2.0)) < 1e-3)
+    assert np.abs(o[0] - value[None, :]).max() < 0.05
 
 
 def test_sensitivity_sink_dominance():
@@ -365,6 +439,7 @@ def test_topk_1024_full_list():
     inp = make_custom(seed=92, q_lens=q_lens, ori_lens=ori, cmp_lens=cmp, cmp_ratio=4,
                       residual=[0, 0], indices=idx, return_lse=True)
     check(inp, tokens=list(range(0, inp.t1, 3)) + [inp.t1 - 1], name="topk 1024")
+    check_rows(inp, name="topk 1024")
 
 
 @pytest.mark.parametrize("n_splits", [None, 3])
@@ -428,3 +503,37 @@ def test_reference_move_with_live_history(score, off):
     lse to meet the oracle."""
     inp, _ = _dominant_key_case(off, "cmp", score=score)
     check(inp, tokens=[0, 1], name=f"reference move, score {score}, cmp {off}")
+
+
+def test_reference_move_heads_diverge():
+    """The reference-move vote is shared by the heads of a unit, but each head
+    keeps its own reference.  Head 3's query is a scaled copy of a band key
+    (first tile) and scores ~100 nats (~144 log2 units) on it; head 9's query
+    copies a compressed key (a later tile) and scores ~15 nats on it, so that
+    later tile moves head 9's reference while head 3's tile maximum there is
+    ~140 log2 units below its own.  A head whose reference moved down would
+    scale its history by 2^140 (inf in fp32) and return NaN."""
+    s2, s1, r = 400, 2, 4
+    c = s2 // r
+    inp = make_custom(seed=83, q_lens=[s1], ori_lens=[s2], cmp_lens=[c], cmp_ratio=r, residual=[0],
+                      indices=None, return_lse=True)
+    p = s2 - s1                                  # row 0's position
+    picks = {3: ("ori", p - 5, 100.0), 9: ("cmp", (p + 1) // r - 7, 15.0)}
+    for h, (which, j, score) in picks.items():
+        kv, ds, tab = ((inp.ori_kv, inp.ori_kv_descale, inp.ori_block_table) if which == "ori"
+                       else (inp.cmp_kv, inp.cmp_kv_descale, inp.cmp_block_table))
+        bs = kv.shape[1]
+        blk = int(tab[0, j // bs])
+        row = kv[blk, j % bs, 0].clone()
+        kk = float((row.view(torch.float8_e4m3fn).double() ** 2).sum())
+        inp.q[0, h] = row
+        inp.q_descale[0, h] = score / (512 ** -0.5 * float(ds[blk, j % bs]) * kk)
+    _, o, l, ref = check(inp, tokens=[0, 1], name="per-head reference moves")
+    for h, (which, j, _) in picks.items():
+        kv, ds, tab = ((inp.ori_kv, inp.ori_kv_descale, inp.ori_block_table) if which == "ori"
+                       else (inp.cmp_kv, inp.cmp_kv_descale, inp.cmp_block_table))
+        bs = kv.shape[1]
+        blk = int(tab[0, j // bs])
+        value = kv[blk, j % bs, 0].view(torch.float8_e4m3fn).double().numpy() * float(ds[blk, j % bs])
+        assert np.abs(ref.out[0, h] - value).max() < 1e-3, (h, "the oracle's head follows its key")
+        assert np.abs(o[0, h] - value).max() < 0.05, (h, "the kernel's head follows its key")

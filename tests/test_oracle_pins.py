@@ -100,10 +100,33 @@ def _logical_cache(kv, ds, table, b, length, per_tile):
     return vals * ds[blocks].reshape(-1)[:length].to(torch.float64)[:, None]
 
 
-def _brute_force(inp):
+def _logical_rows(inp, which, b, length, per_tile):
+    """Logical rows [0, length) of batch b's ori or cmp cache in any layout:
+    paged (table order), TND (the batch's run of a [T, 1, D] cache, found by
+    summing the earlier batches' lengths from the cu_seqlens input) or BSND
+    (row b of a [B, S, 1, D] cache)."""
+    kv = getattr(inp, f"{which}_kv")
+    ds = getattr(inp, f"{which}_kv_descale")
+    if inp.layout_kv == "PA_BBND":
+        return _logical_cache(kv, ds, getattr(inp, f"{which}_block_table"), b, length, per_tile)
+    if inp.layout_kv == "TND":
+        cu = getattr(inp, f"cu_seqlens_{which}_kv")
+        start = int(cu[b])
+        codes, sc = kv[start:start + length, 0], ds[start:start + length]
+    else:
+        codes, sc = kv[b, :length, 0], ds[b, :length]
+    vals = _dec_torch(codes)
+    if per_tile:
+        return vals * sc.to(torch.float64).repeat_interleave(64, dim=1)
+    return vals * sc.to(torch.float64)[:, None]
+
+
+def _brute_force(inp, s2_of=None, c_of=None, r_of=None):
     """Dense masked softmax over every logical row of the batch, with the mask
     written cell by cell from the alignment rules (last query row aligned with
-    the last kv token / the last restored token)."""
+    the last kv token / the last restored token).  Lengths come from
+    seqused_ori_kv / seqused_cmp_kv / cmp_residual_kv, unless the caller
+    states them (s2_of / c_of / r_of: per-batch lists)."""
     T1, n1, d = inp.t1, inp.n1, inp.d
     per_tile = inp.kv_scale_mode == 1
     out = torch.zeros(T1, n1, d, dtype=torch.float64)
@@ -115,14 +138,17 @@ def _brute_force(inp):
         else:
             span = inp.q_s
         s1 = span if inp.seqused_q is None else min(span, int(inp.seqused_q[b]))
-        s2 = int(inp.seqused_ori_kv[b])
-        ori = _logical_cache(inp.ori_kv, inp.ori_kv_descale, inp.ori_block_table, b, s2, per_tile)
+        s2 = int(inp.seqused_ori_kv[b]) if s2_of is None else int(s2_of[b])
+        ori = _logical_rows(inp, "ori", b, s2, per_tile)
         r = inp.cmp_ratio
         if inp.cmp_kv is not None:
-            C = int(inp.seqused_cmp_kv[b])
-            R = int(inp.cmp_residual_kv[b]) if inp.cmp_residual_kv is not None else 0
+            C = int(inp.seqused_cmp_kv[b]) if c_of is None else int(c_of[b])
+            if r_of is not None:
+                R = int(r_of[b])
+            else:
+                R = int(inp.cmp_residual_kv[b]) if inp.cmp_residual_kv is not None else 0
             L = C * r + R
-            cmp = _logical_cache(inp.cmp_kv, inp.cmp_kv_descale, inp.cmp_block_table, b, C, per_tile)
+            cmp = _logical_rows(inp, "cmp", b, C, per_tile)
         for i in range(span):
             t = q_off + i
             if i >= s1:
@@ -239,6 +265,129 @@ def test_oracle_vs_brute_force_topk_length_and_swa():
     swa = make_custom(seed=22, q_lens=[3, 5], ori_lens=[70, 33], n1=4, d=128, block_size=16,
                       win_left=10, win_right=2, cmp_mask_mode=0)
     _assert_close(oracle_forward(swa).out, _brute_force(swa)[0].numpy())
+
+
+@pytest.mark.parametrize("layout_kv,kw", [
+    ("TND", dict(q_lens=[3, 1, 4], ori_lens=[150, 37, 260])),
+    ("TND", dict(q_lens=[2, 5], ori_lens=[9, 300], kv_scale_mode=1)),
+    ("BSND", dict(q_lens=[3, 3, 3], ori_lens=[150, 37, 260], layout_q="BSND")),
+    ("BSND", dict(q_lens=[2, 2], ori_lens=[300, 120], layout_q="BSND", kv_scale_mode=1)),
+    ("BSND", dict(q_lens=[2, 2], ori_lens=[203, 201], layout_q="BSND")),   # equal cmp lengths (50)
+])
+def test_oracle_vs_brute_force_contiguous_kv(layout_kv, kw):
+    """Contiguous KV caches (QuantSparseFlashMla, 参数说明 layout_kv TND / BSND
+    with cu_seqlens_ori_kv / cu_seqlens_cmp_kv): the TND case passes no
+    seqused_ori_kv, so the ori length is the cu_seqlens difference; the brute
+    force reads each batch's run of the cache itself and is told the lengths
+    the cache was built with.  The caches' spare slots hold NaN, so a row
+    read from the wrong batch or offset shows.  The compressed length comes
+    from cu_seqlens_cmp_kv (TND), from seqused_cmp_kv (BSND, unequal
+    lengths), or from the BSND shape when every batch has the same number."""
+    kw = dict(kw)
+    r = 4
+    ori = kw.pop("ori_lens")
+    res = [o % r for o in ori]
+    cmp = [o // r for o in ori]
+    rng = np.random.default_rng(sum(ori))
+    T1 = sum(kw["q_lens"])
+    idx = rng.integers(-2, max(cmp) + 3, size=(T1, 24))
+    idx[rng.random(idx.shape) < 0.2] = -1
+    by_shape = layout_kv == "BSND" and len(set(cmp)) == 1
+    inp = make_custom(seed=len(ori) + ori[0], ori_lens=ori, cmp_lens=cmp, cmp_ratio=r, residual=res,
+                      indices=idx, n1=4, d=128, layout_kv=layout_kv,
+                      pass_seqused_cmp=(layout_kv == "BSND" and not by_shape), **kw)
+    if layout_kv == "TND" or by_shape:
+        assert inp.seqused_cmp_kv is None
+    if layout_kv == "TND":
+        assert inp.seqused_ori_kv is None and inp.cu_seqlens_ori_kv is not None
+    got = oracle_forward(inp)
+    out, lse = _brute_force(inp, s2_of=ori, c_of=cmp, r_of=res)
+    _assert_close(got.out, out.numpy())
+    _assert_close(got.lse, lse.numpy())
+
+
+def _relayout(inp, layout_kv):
+    """The same logical caches (the rows of each batch in order, and their
+    descales) laid out as a TND ([T, 1, D] + cu_seqlens) or BSND
+    ([B, S, 1, D], NaN past each batch's length) cache."""
+    out = {}
+    B = inp.batch
+    s2 = [int(x) for x in inp.seqused_ori_kv]
+    cl = [int(x) for x in inp.seqused_cmp_kv]
+    for which, lens in (("ori", s2), ("cmp", cl)):
+        kv = getattr(inp, f"{which}_kv")
+        ds = getattr(inp, f"{which}_kv_descale")
+        tab = getattr(inp, f"{which}_block_table")
+        bs = kv.shape[1]
+        rows_kv, rows_ds = [], []
+        for b in range(B):
+            nb = (lens[b] + bs - 1) // bs
+            blocks = tab[b, :nb].long()
+            rows_kv.append(kv[blocks].reshape(nb * bs, 1, -1)[:lens[b]])
+            rows_ds.append(ds[blocks].reshape((nb * bs,) + tuple(ds.shape[2:]))[:lens[b]])
+        if layout_kv == "TND":
+            out[f"{which}_kv"] = torch.cat(rows_kv)
+            out[f"{which}_kv_descale"] = torch.cat(rows_ds)
+            out[f"cu_seqlens_{which}_kv"] = torch.as_tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+        else:
+            S = max(lens)
+            k = torch.full((B, S, 1, kv.shape[-1]), 0x7F, dtype=torch.uint8)
+            d_ = torch.full((B, S) + tuple(ds.shape[2:]), float("nan"))
+            for b in range(B):
+                k[b, :lens[b]] = rows_kv[b]
+                d_[b, :lens[b]] = rows_ds[b]
+            out[f"{which}_kv"], out[f"{which}_kv_descale"] = k, d_
+        out[f"{which}_block_table"] = None
+    from dataclasses import replace
+    return replace(inp, layout_kv=layout_kv, **out)
+
+
+@pytest.mark.parametrize("kv_scale_mode", [0, 1])
+def test_oracle_layouts_agree(kv_scale_mode):
+    """One logical problem as paged, TND and BSND caches: the oracle's result
+    is bit-identical (K~ depends only on the logical rows; QuantSparseFlashMla,
+    参数说明 layout_kv).  A TND offset or a BSND batch stride that is off by
+    one reads another row (or a NaN pad) and fails here."""
+    inp = _cmp_case(71, q_lens=[3, 2, 4], ori_lens=[130, 61, 222], B=3, kv_scale_mode=kv_scale_mode)
+    base = oracle_forward(inp)
+    for lay in ("TND", "BSND"):
+        alt = _relayout(inp, lay)
+        res = oracle_forward(alt)
+        assert np.array_equal(res.out, base.out), lay
+        assert np.array_equal(res.lse, base.lse), lay
+
+
+def test_default_cmp_length_and_residual():
+    """Paged caches with neither seqused_cmp_kv nor cmp_residual_kv: the
+    reading of QuantSparseFlashMla 约束说明 (the compressed length derived from
+    the shapes) takes C = floor(S2 / cmp_ratio) and residual 0.  The brute
+    force is told exactly those lengths; a batch whose S2 is not a multiple
+    of the ratio makes the restored length L = C r differ from S2."""
+    r = 4
+    ori = [203, 130]
+    cmp_true = [o // r for o in ori]
+    rng = np.random.default_rng(5)
+    idx = rng.integers(-1, max(cmp_true) + 2, size=(5, 20))
+    idx[0:2, 0] = 49     # the last compressed token of batch 0: visible to its rows 0 and 1 only with residual 3
+    inp = make_custom(seed=73, q_lens=[3, 2], ori_lens=ori, cmp_lens=cmp_true, cmp_ratio=r,
+                      residual=[o % r for o in ori], indices=idx, n1=4, d=128, block_size=16,
+                      pass_seqused_cmp=False, pass_residual=False, return_lse=True)
+    assert inp.seqused_cmp_kv is None and inp.cmp_residual_kv is None
+    got = oracle_forward(inp)
+    for b in range(2):
+        bl = batch_lengths(inp, b)
+        assert (bl["c"], bl["res"], bl["L"]) == (ori[b] // r, 0, (ori[b] // r) * r)
+    out, lse = _brute_force(inp, s2_of=ori, c_of=cmp_true, r_of=[0, 0])
+    _assert_close(got.out, out.numpy())
+    _assert_close(got.lse, lse.numpy())
+    # the same problem with the residual passed: the cmp visibility moves for
+    # batch 0 (203 = 50 * 4 + 3), so the results differ
+    inp_r = make_custom(seed=73, q_lens=[3, 2], ori_lens=ori, cmp_lens=cmp_true, cmp_ratio=r,
+                        residual=[o % r for o in ori], indices=idx, n1=4, d=128, block_size=16,
+                        pass_seqused_cmp=False, pass_residual=True, return_lse=True)
+    out_r, _ = _brute_force(inp_r, s2_of=ori, c_of=cmp_true)
+    _assert_close(oracle_forward(inp_r).out, out_r.numpy())
+    assert not np.allclose(got.out, oracle_forward(inp_r).out)
 
 
 def test_oracle_vs_sdpa_float64():
