@@ -194,6 +194,20 @@ csmla_status csmla_plan(const csmla_problem* problem, const csmla_host_lengths* 
 csmla_status csmla_forward(const csmla_problem* problem, const csmla_tensors* tensors,
                            const int32_t* metadata, void* stream);
 
+/* csmla_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels, with tensors->workspace / workspace_bytes ignored and the
+ * split partials kept in the library's static device scratch instead, 64 MiB
+ * per GPU (CSMLA_NOALLOC_SCRATCH_BYTES), held from the first call on a device
+ * until the process ends.  A plan needing more workspace than that returns
+ * CSMLA_ERR_WORKSPACE before any device work.  Allocates nothing and records
+ * no memset.  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (two streams, two threads) race and must be
+ * serialised by the caller. */
+#define CSMLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+csmla_status csmla_forward_noalloc(const csmla_problem* problem, const csmla_tensors* tensors,
+                                   const int32_t* metadata, void* stream);
+
 /* Resolved key list of every query row (QuantSparseFlashMla, 参数说明: the
  * band window, cmp_sparse_indices with -1 skipped, the block tables), as the
  * key-split and head-split kernels resolve it: their resolution functions

@@ -78,9 +78,9 @@ def load(path: str = LIB_PATH):
     lib.csmla_plan.restype = ctypes.c_int
     lib.csmla_plan.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaHostLengths),
                                ctypes.POINTER(_i32), ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
-    lib.csmla_forward.restype = ctypes.c_int
-    lib.csmla_forward.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaTensors),
-                                  ctypes.POINTER(_i32), _p]
+    for fn in (lib.csmla_forward, lib.csmla_forward_noalloc):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaTensors), ctypes.POINTER(_i32), _p]
     for fn in (lib.csmla_debug_resolve, lib.csmla_debug_resolve_whole_token):
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaTensors), _p, _p, _i32, _p]
@@ -136,6 +136,18 @@ def csmla_forward(problem: CsmlaProblem, tensors: CsmlaTensors, metadata: np.nda
                               md.ctypes.data_as(ctypes.POINTER(_i32)), _p(stream))
     if raise_on_error:
         _check(st, "csmla_forward")
+    return st
+
+
+def csmla_forward_noalloc(problem: CsmlaProblem, tensors: CsmlaTensors, metadata: np.ndarray, stream: int = 0,
+                          raise_on_error: bool = True) -> int:
+    """csmla_forward with the split partials in the library's static device
+    scratch (tensors.workspace is ignored); allocates nothing."""
+    md = np.ascontiguousarray(metadata, dtype=np.int32)
+    st = load().csmla_forward_noalloc(ctypes.byref(problem), ctypes.byref(tensors),
+                                      md.ctypes.data_as(ctypes.POINTER(_i32)), _p(stream))
+    if raise_on_error:
+        _check(st, "csmla_forward_noalloc")
     return st
 
 

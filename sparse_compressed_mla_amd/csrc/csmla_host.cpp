@@ -16,6 +16,8 @@
 
 using namespace csmla;
 
+static_assert(CSMLA_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "static scratch size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -454,6 +456,32 @@ csmla_status csmla_forward(const csmla_problem* p, const csmla_tensors* t, const
   }
   g_last_error.clear();
   return CSMLA_OK;
+}
+
+csmla_status csmla_forward_noalloc(const csmla_problem* p, const csmla_tensors* t, const int32_t* md, void* stream) {
+  if (!t) return fail(CSMLA_ERR_INVALID_ARG, "tensors is NULL");
+  csmla_tensors ts = *t;
+  ts.workspace = nullptr;
+  ts.workspace_bytes = 0;
+  // the plan's workspace size, checked against the static scratch before any
+  // HIP call (a plan that is not csmla_plan's is rejected by csmla_forward)
+  if (md && md[MD_MAGIC] == kMagic && md[MD_VERSION] == CSMLA_ABI_VERSION && md[MD_UNITS] >= 0 &&
+      md[MD_SPLITS] >= 1) {
+    const size_t need = workspace_bytes_for(md[MD_UNITS], md[MD_SPLITS]);
+    if (need > kNoAllocScratchBytes)
+      return fail(CSMLA_ERR_WORKSPACE,
+                  "the plan needs %zu bytes of workspace; csmla_forward_noalloc holds %zu (use csmla_forward with "
+                  "a workspace, or a plan with fewer key splits)",
+                  need, kNoAllocScratchBytes);
+    if (need > 0) {
+      void* ptr = nullptr;
+      const int e = noalloc_scratch(&ptr);
+      if (e != 0) return fail(CSMLA_ERR_HIP, "static scratch lookup failed (hipError %d)", e);
+      ts.workspace = ptr;
+      ts.workspace_bytes = kNoAllocScratchBytes;
+    }
+  }
+  return csmla_forward(p, &ts, md, stream);
 }
 
 static csmla_status debug_resolve(const csmla_problem* p, const csmla_tensors* t, int32_t* keys, int32_t* counts,

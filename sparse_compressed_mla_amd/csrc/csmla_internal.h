@@ -61,6 +61,14 @@ int fail_with(int status, const char* fmt, ...);
 void clear_last_error();
 uint32_t hash_bytes(const void* data, size_t n, uint32_t seed = 2166136261u);
 
+// Size of the library's static device scratch (csmla_forward_noalloc's
+// workspace): 64 MiB per GPU, enough for ~1000 split units.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+
+// Device address of that scratch on the current device (looked up once per
+// device, then cached); returns a hipError_t as int.
+int noalloc_scratch(void** ptr);
+
 // launchers (csmla_kernels.hip); return a hipError_t as int
 int launch_forward(const KArgs& a, void* stream);
 int launch_debug_resolve(const KArgs& a, int32_t* keys, int32_t* counts, int32_t max_keys, int whole_token,

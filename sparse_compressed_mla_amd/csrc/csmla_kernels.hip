@@ -21,6 +21,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "csmla_internal.h"
 
@@ -2572,6 +2573,36 @@ __global__ void __launch_bounds__(kPfThreads) pf_debug_resolve_kernel(const KArg
       keys[(size_t)t * max_keys + key] = (int32_t)(((const uint8_t*)(uintptr_t)src.addr - base) / kD);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// static scratch for callers that cannot allocate (csmla_forward_noalloc):
+// the split partials and their (max, sum) live here instead of in a
+// caller-provided workspace.  Each GPU holds its own copy of the array at its
+// own address; host code uses only the address hipGetSymbolAddress returns
+// for the current device (the array's name is a host-side stand-in).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+int noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 int launch_forward(const KArgs& a, void* stream) {

@@ -257,3 +257,17 @@ def test_problem_struct_layout_matches_header():
     body_t = src[src.index("typedef struct {", src.index("Device pointers")):src.index("} csmla_tensors;")]
     tnames = re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+);", body_t, flags=re.M)
     assert tnames == [f[0] for f in CsmlaTensors._fields_]
+
+
+def test_noalloc_rejects_plans_beyond_the_static_scratch(monkeypatch):
+    """csmla_forward_noalloc holds 64 MiB of static scratch per GPU; a plan
+    whose split partials need more is refused on the host, before any HIP
+    call (no GPU is needed to see the refusal)."""
+    monkeypatch.setenv("CSMLA_KERNEL", "split")
+    monkeypatch.setenv("CSMLA_SPLITS", "64")
+    p = base_problem()
+    _, md, ws = m.csmla_plan(p)
+    assert ws > 64 << 20
+    st = m.csmla_forward_noalloc(p, fake_tensors(0), md, raise_on_error=False)
+    assert st == 3, (st, m.csmla_last_error())          # CSMLA_ERR_WORKSPACE
+    assert "64" in m.csmla_last_error() or "67108864" in m.csmla_last_error()
