@@ -7,16 +7,17 @@ length 8192 with a 128-token band (left 127, right 0), cmp_ratio 4 (2048
 compressed tokens) and 512 top-k indices per token drawn uniformly without
 replacement, sinks ~ N(0,1).  Synthetic, seeded data.
 
-A step is one csmla_forward over one batch: as planned for this shape, the
-head-split kernel alone (groups of 8 heads over whole key lists), or split
-attention followed by the split-KV combine.  The KV pools are replicated over --layers distinct copies
-and step k reads copy k % layers, as consecutive layers of a model would:
-every step's KV rows come from HBM, not from the 256 MB Infinity Cache.
-Block tables, indices and q are shared by the copies.  The plan is made
-once per pass over the layers, as a model plans once per decode step.
+A step is one csmla_forward over one batch (the whole path: key resolution,
+gather, QK^T, masks and sink, softmax, P V, epilogue, and the split-KV combine
+when the plan splits keys).  The decode-shaped workloads run as consecutive
+model layers would: --layers copies of the KV pools, each layer with its own
+q, q descales, top-k index rows and output (block tables, lengths and sinks
+shared); step k runs layer k % layers, so every step's rows come from HBM,
+not from the 256 MB Infinity Cache.  Exactly --steps forwards are timed
+after --warmup untimed ones (HIP graphs over the layers, HIP events on the
+stream the kernels run on).  The plan is made once per pass over the layers.
 
-Prints one JSON line (rank 0).  --gpus above 1 is refused: this build runs
-on one GPU.
+Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
 import argparse
 import hashlib
@@ -58,11 +59,15 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--layers", type=int, default=48)
-    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=48)
+    ap.add_argument("--layers", type=int, default=48,
+                    help="model layers rotated through (each its own KV pool copy, q, indices and output)")
+    ap.add_argument("--copy-budget-gb", type=float, default=96.0,
+                    help="device memory the KV pool copies may take (caps --layers for large caches)")
+    ap.add_argument("--batch", type=int, default=0, help="batch of the decode workloads (0: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="budget of each oracle timing sample (one thread, then all threads)")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--workload", choices=["csa_decode", "csa_prefill", "swa_tiny", "hca_decode", "csa_mtp",
                                            "idx_csa_decode", "idx_csa_mtp_long", "idx_csa_prefill"],
@@ -103,183 +108,170 @@ def main():
     if args.workload == "csa_prefill":
         prefill(args, m, make_config, torch, np)
         return
-    if args.workload != "csa_decode":
-        other(args, m, make_config, torch, np)
-        return
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    print(f"[bench] building inputs: csa_decode batch={args.batch} layers={args.layers}", file=sys.stderr, flush=True)
-    inp = make_config(2, device=dev, batch=args.batch)
-    T1 = inp.t1
+    rotated(args, m, make_config, torch, np)
 
-    # ---- parity precheck on a few rows (the oracle is the CPU reference) ----
-    if not args.no_parity:
-        from oracle import oracle_forward
-        from tests.parity_util import compare
-        toks = [0, T1 // 2, T1 - 1]
-        cpu = inp.to("cpu")
-        ref = oracle_forward(cpu, toks)
-        o, _ = m.forward(inp)
-        torch.cuda.synchronize()
-        compare(o.float().cpu().numpy(), ref.out, toks, name="bench precheck", verbose=False)
-        print("[bench] parity precheck ok", file=sys.stderr, flush=True)
-        del cpu
 
-    # ---- algorithmic bytes: unique KV rows per batch x (512 B + 4 B descale) ----
-    nmax = 1024
-    keys, counts = m.debug_resolve(inp, nmax)
+# ---------------------------------------------------------------------------
+# helpers shared by the workloads
+# ---------------------------------------------------------------------------
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(run_one, n_items, seconds, unit, what):
+    """The oracle as it stands, timed on the host on a bounded sample: items
+    (query tokens or rows) run one at a time in a fixed shuffled order until
+    `seconds` have passed, once with BLAS on one thread and once on all the
+    threads the BLAS pool holds.  The all-threads figure is `value`."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    order = np.random.default_rng(0).permutation(n_items)
+
+    def timed():
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds or done == 0:
+            run_one(int(order[done % n_items]))
+            done += 1
+        return done, time.perf_counter() - t0
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    with threadpool_limits(limits=1):
+        d1, s1 = timed()
+    dn, sn = timed()
+    return {"value": round(dn / sn, 3), "unit": unit, "cores": int(threads), "kind": "oracle",
+            "sample": f"{dn} {what} in {sn:.1f} s on {threads} BLAS threads (float64 NumPy oracle, "
+                      f"{cpu_model()})",
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": round(d1 / s1, 3), "unit": unit, "cores": 1,
+                              "sample": f"{d1} {what} in {s1:.1f} s on one thread"}}
+
+
+def unique_rows(m, inp, np, torch):
+    """(token, key) pairs and rows unique per batch of the resolved key lists
+    (csmla_debug_resolve; bit-exact against the oracle in the GPU tests)."""
+    keys, counts = m.debug_resolve(inp, 1024 if inp.topk <= 1024 else 4096)
     torch.cuda.synchronize()
     keys, counts = keys.cpu().numpy(), counts.cpu().numpy()
-    uniq = 0
-    tt = np.repeat(np.arange(args.batch), T1 // args.batch)
-    for b in range(args.batch):
-        ts = np.nonzero(tt == b)[0]
-        ori = set(); cmp = set()
-        for t in ts:
-            n_o, n_c = counts[t]
-            ori.update(keys[t, :n_o].tolist())
-            cmp.update(keys[t, n_o:n_o + n_c].tolist())
-        uniq += len(ori) + len(cmp)
-    kv_bytes = uniq * (512 + 4)
-    pairs = int(counts.sum())
-    other_bytes = T1 * 64 * 512 + T1 * 64 * 4 + T1 * 64 * 512 * 2 + int(inp.cmp_sparse_indices.numel()) * 4
+    from oracle.attention import token_table
+    tt = token_table(inp)
+    per_batch = {}
+    for t in range(inp.t1):
+        n_o, n_c = counts[t]
+        s = per_batch.setdefault(tt[t][0], set())
+        s.update(("o", int(x)) for x in keys[t, :n_o])
+        s.update(("c", int(x)) for x in keys[t, n_o:n_o + n_c])
+    return int(counts.sum()), sum(len(v) for v in per_batch.values())
 
-    # ---- layer copies of the KV pools ----
-    layers = []
-    for l in range(args.layers):
-        if l == 0:
-            layers.append(inp)
-            continue
-        c = type(inp)(**{k: v for k, v in inp.__dict__.items()})
-        c.ori_kv = inp.ori_kv.clone(); c.ori_kv_descale = inp.ori_kv_descale.clone()
-        c.cmp_kv = inp.cmp_kv.clone(); c.cmp_kv_descale = inp.cmp_kv_descale.clone()
-        layers.append(c)
-    pool_gb = sum(x.ori_kv.numel() + x.cmp_kv.numel() for x in layers) / 1e9
-    print(f"[bench] KV pools resident: {pool_gb:.1f} GB over {args.layers} layers", file=sys.stderr, flush=True)
 
-    plan = m.Plan(inp)
-    out = torch.empty(inp.q.shape, dtype=torch.bfloat16, device=dev)
-    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
-    tens = [m.tensors_from(x, out, None, ws if plan.workspace_bytes else None) for x in layers]
-    stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
-    hl, keep = m.host_lengths_from(inp)
-
-    # ---- one HIP graph holding a forward per layer (no host work per step) ----
-    L = args.layers
+def timed_graph_steps(m, torch, plan, tens, dev, steps, warmup):
+    """Forward i of a pass uses layer i's tensors.  Graphs of forwards over
+    the layers are captured once (a full pass, and the partial passes the
+    step counts need); every replay is checked equal to the eager forwards.
+    Warm-up runs `warmup` untimed forwards on the last layers; the timed
+    region runs exactly `steps` forwards from layer 0 on, with HIP events
+    on the stream the kernels run on.  The host planner runs once per full
+    pass (its host time is reported apart).  Returns (ms for the steps,
+    host planner seconds, passes)."""
+    L = len(tens)
     cap = torch.cuda.Stream(dev)
-    cap.wait_stream(stream)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+
+    def fwd(l):
+        m.csmla_forward(plan.problem, tens[l][0], plan.metadata, cap.cuda_stream)
+
     with torch.cuda.stream(cap):
-        for l in range(L):                       # eager warm-up on the capture stream
-            m.csmla_forward(plan.problem, tens[l], plan.metadata, cap.cuda_stream)
-    torch.cuda.synchronize()
-    eager = out.clone()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cap):
         for l in range(L):
-            m.csmla_forward(plan.problem, tens[l], plan.metadata, cap.cuda_stream)
+            fwd(l)
     torch.cuda.synchronize()
-    for rep in range(2):                          # replays must equal the eager result
-        out.zero_()
+    eager = [t[1].clone() for t in tens]
+
+    def capture(layers):
+        if not layers:
+            return None
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for l in layers:
+                fwd(l)
+        torch.cuda.synchronize()
+        return g
+
+    full = capture(list(range(L)))
+    part_k = capture(list(range(steps % L)))
+    part_w = capture(list(range(L - warmup % L, L)) if warmup % L else [])
+    for g in (full,):
+        for t in tens:
+            t[1].zero_()
         torch.cuda.synchronize()
         with torch.cuda.stream(cap):
-            graph.replay()
+            g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(out, eager), "graph replay differs from the eager forward"
-
-    reps_w = max(1, -(-args.warmup // L))
-    reps = max(1, -(-args.steps // L))
-    K = reps * L
+        for l, t in enumerate(tens):
+            assert torch.equal(t[1], eager[l]), f"graph replay differs from the eager forward (layer {l})"
     with torch.cuda.stream(cap):
-        for _ in range(reps_w):
-            graph.replay()
+        if part_w is not None:
+            part_w.replay()
+        for _ in range(warmup // L):
+            full.replay()
     torch.cuda.synchronize()
-
-    # ---- timed region: K steps (reps x L layers), events on the kernels' stream ----
+    hl, keep = m.host_lengths_from(tens[0][2])
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_plan = 0.0
-    with torch.cuda.stream(cap):                  # replay() launches on the current stream
+    with torch.cuda.stream(cap):
         start.record(cap)
-        for r in range(reps):
+        for _ in range(steps // L):
             t0 = time.perf_counter()
-            m.csmla_plan(plan.problem, hl)       # the planner runs once per pass over the layers
+            m.csmla_plan(plan.problem, hl)
             t_plan += time.perf_counter() - t0
-            graph.replay()
+            full.replay()
+        if part_k is not None:
+            part_k.replay()
         stop.record(cap)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    fwd_ms = total_ms / K
-    ms_per_step = fwd_ms
-    value = T1 * K / (total_ms / 1e3)
-    achieved = kv_bytes / (fwd_ms / 1e3) / 1e9
-    print(f"[bench] forward {fwd_ms * 1e3:.2f} us per step over {K} steps (graph of {L} layers); "
-          f"splits {plan.splits} grid {plan.grid}; plan {1e6 * t_plan / reps:.0f} us host per pass",
-          file=sys.stderr, flush=True)
-
-    res = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "query-tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": reps_w * L,
-        "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8e4m3 (fp32 accumulate)",
-        "data": "synthetic, seeded (workloads.make_config(2))",
-        "config": {"workload": "csa_decode", "batch": args.batch, "q_tokens_per_batch": 1, "n1": 64, "d": 512,
-                   "ori_len": 8192, "band": 128, "cmp_ratio": 4, "topk": 512, "block_size": 128,
-                   "layers_rotated": args.layers, "splits": plan.splits, "grid": plan.grid},
-        "effective_kv_gbs": round(achieved, 1),
-        "kv_bytes_per_step": kv_bytes,
-        "total_bytes_per_step": kv_bytes + other_bytes,
-        "pairs_per_step": pairs,
-        "forward_us": round(fwd_ms * 1e3, 3),
-        "plan_host_us": round(1e6 * t_plan / reps, 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("csa_decode"),
-                     "kernel": ("dk_kernel (head-split attention, whole key lists)" if plan.head_group > 0
-                                else "attn_kernel<0> + combine_kernel (split attention, split-KV combine)")},
-    }
-
-    # ---- CPU baseline: the oracle as it stands, on a bounded sample ----
-    if not args.no_cpu_baseline:
-        from oracle import oracle_forward
-        cpu = inp.to("cpu")
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:
-            cores = len(os.sched_getaffinity(0))
-        done = 0
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < args.cpu_seconds or done == 0:
-            oracle_forward(cpu, [done % T1])
-            done += 1
-        dt = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": round(done / dt, 2), "unit": "query-tokens/s", "cores": int(cores),
-                               "kind": "oracle",
-                               "sample": f"{done} csa_decode query tokens (640 keys each) in {dt:.1f} s, "
-                                         f"float64 NumPy oracle on the host"}
-    print(json.dumps(res), flush=True)
+    return start.elapsed_time(stop), t_plan, max(1, steps // L)
 
 
-OTHER = {"swa_tiny": 1, "hca_decode": 3, "csa_mtp": 4}
+def kernel_name(plan):
+    if plan.head_group == 64:
+        return "pf_kernel (whole-token)"
+    if plan.head_group > 0:
+        return f"dk_kernel (head-split, groups of {plan.head_group} heads over whole key lists)"
+    return f"attn_kernel<0> (split attention, {plan.splits} key splits)" + (" + combine_kernel" if plan.splits > 1
+                                                                           else "")
 
 
-def other(args, m, make_config, torch, np):
-    """Forward time of another configuration (inputs resident, one KV pool,
-    eager launches timed with HIP events on the kernels' stream), effective
-    KV bytes = unique (row) keys of each batch x 516 B."""
+ROTATED = {"csa_decode": 2, "hca_decode": 3, "csa_mtp": 4, "swa_tiny": 1}
+CONFIG_TEXT = {
+    2: dict(q_tokens_per_batch=1, ori_len=8192, band=128, cmp_ratio=4, topk=512),
+    3: dict(q_tokens_per_batch=1, ori_len="U[32768, 65536]", band=128, cmp_ratio=128, topk=0),
+    4: dict(q_tokens_per_batch=2, ori_len="U[65536, 131072]", band=128, cmp_ratio=4, topk=512),
+    1: dict(q_tokens_per_batch=4, ori_len="300 / 200", band=128, cmp_ratio=1, topk=0),
+}
+
+
+def rotated(args, m, make_config, torch, np):
+    """A decode-shaped workload as consecutive model layers would run it:
+    `layers` copies of the KV pools, each layer with its own q, q descales
+    and (CSA) top-k index rows, drawn by the config's recipe, and its own
+    output; block tables, lengths and sinks are shared, as the layers of
+    one sequence share them.  Step k runs layer k % layers, so each step's
+    KV rows, queries and indices come from HBM and not from the 256 MB
+    Infinity Cache."""
+    from workloads import redraw_query_side
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    k = OTHER[args.workload]
-    print(f"[bench] building inputs: {args.workload}", file=sys.stderr, flush=True)
-    inp = make_config(k, device=dev)
+    k = ROTATED[args.workload]
+    kw = {"batch": args.batch} if k in (2, 3, 4) and args.batch else {}
+    print(f"[bench] building inputs: {args.workload} {kw}", file=sys.stderr, flush=True)
+    inp = make_config(k, device=dev, **kw)
     T1 = inp.t1
     if not args.no_parity:
         from oracle import oracle_forward
@@ -291,49 +283,71 @@ def other(args, m, make_config, torch, np):
         torch.cuda.synchronize()
         compare(o.float().cpu().numpy(), ref.out, toks, name="bench precheck", verbose=False)
         print("[bench] parity precheck ok", file=sys.stderr, flush=True)
-    keys, counts = m.debug_resolve(inp, 1024)
-    torch.cuda.synchronize()
-    keys, counts = keys.cpu().numpy(), counts.cpu().numpy()
-    pairs = int(counts.sum())
-    rows = set()
-    for t in range(T1):
-        n_o, n_c = counts[t]
-        rows.update(("o", int(x)) for x in keys[t, :n_o])
-        rows.update(("c", int(x)) for x in keys[t, n_o:n_o + n_c])
-    kv_bytes = len(rows) * 516
+    pairs, uniq = unique_rows(m, inp, np, torch)
+    kv_bytes = uniq * (512 + 4)
+    out_bytes = T1 * 64 * 512 * 2
+    other_bytes = T1 * 64 * (512 + 4) + out_bytes + 4 * inp.topk * T1
+    pool = sum(x.numel() * x.element_size() for x in (inp.ori_kv, inp.ori_kv_descale, inp.cmp_kv, inp.cmp_kv_descale)
+               if x is not None)
+    L = max(2, min(args.layers, int(args.copy_budget_gb * 1e9 // pool)))
+    layers = [inp]
+    for l in range(1, L):
+        c = redraw_query_side(inp, k, l)
+        c.ori_kv, c.ori_kv_descale = inp.ori_kv.clone(), inp.ori_kv_descale.clone()
+        if inp.cmp_kv is not None:
+            c.cmp_kv, c.cmp_kv_descale = inp.cmp_kv.clone(), inp.cmp_kv_descale.clone()
+        layers.append(c)
+    print(f"[bench] {L} layers resident: KV pools {L * pool / 1e9:.1f} GB, {kv_bytes / 1e6:.2f} MB of KV rows "
+          f"touched per step", file=sys.stderr, flush=True)
     plan = m.Plan(inp)
-    out = torch.empty(inp.q.shape, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((T1, 64), dtype=torch.float32, device=dev) if getattr(inp, "return_lse", False) else None
-    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
-    tens = m.tensors_from(inp, out, lse, ws if plan.workspace_bytes else None)
-    stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
-    steps = max(1, min(args.steps, 200))
-    for _ in range(max(1, min(args.warmup, 20))):
-        m.csmla_forward(plan.problem, tens, plan.metadata, sp)
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        m.csmla_forward(plan.problem, tens, plan.metadata, sp)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / steps
-    gbs = kv_bytes / (ms / 1e3) / 1e9
-    kernel = ("pf_kernel (whole-token prefill)" if plan.head_group == 64
-              else f"dk_kernel (head groups of {plan.head_group})" if plan.head_group > 0
-              else f"attn_kernel (splits {plan.splits})" + (" + combine_kernel" if plan.splits > 1 else ""))
-    print(f"[bench] {args.workload} forward {ms * 1e3:.2f} us, {T1} query tokens, {pairs} pairs, "
-          f"{gbs:.1f} GB/s effective KV; {kernel}, grid {plan.grid}", file=sys.stderr, flush=True)
-    print(json.dumps({
-        "metric": f"{args.workload} query-tokens/s + effective KV HBM GB/s, 1 MI355X",
-        "value": round(T1 / (ms / 1e3), 1), "unit": "query-tokens/s", "n_gpus": 1, "steps": steps,
-        "ms_per_step": round(ms, 6), "higher_is_better": True, "data": f"synthetic, seeded (workloads.make_config({k}))",
-        "config": {"workload": args.workload, "t1": T1, "splits": plan.splits, "grid": plan.grid,
-                   "head_group": plan.head_group},
-        "pairs_per_step": pairs, "kv_bytes_per_step": kv_bytes,
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel}}), flush=True)
+    tens = []
+    for x in layers:
+        out = torch.empty(x.q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(x.q.shape[:2], dtype=torch.float32, device=dev) if x.return_lse else None
+        ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        tens.append((m.tensors_from(x, out, lse, ws if plan.workspace_bytes else None), out, x, lse, ws))
+    K, W = args.steps, args.warmup
+    total_ms, t_plan, passes = timed_graph_steps(m, torch, plan, tens, dev, K, W)
+    fwd_ms = total_ms / K
+    value = T1 * K / (total_ms / 1e3)
+    achieved = kv_bytes / (fwd_ms / 1e3) / 1e9
+    kern = kernel_name(plan)
+    print(f"[bench] {args.workload}: forward {fwd_ms * 1e3:.2f} us per step over {K} steps (graphs over {L} "
+          f"layers); {kern}, grid {plan.grid}; plan {1e6 * t_plan / passes:.0f} us host per pass",
+          file=sys.stderr, flush=True)
+    headline = args.workload == "csa_decode"
+    res = {
+        "metric": METRIC if headline else f"{args.workload} query-tokens/s + effective KV HBM GB/s, 1 MI355X",
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(fwd_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate)",
+        "data": f"synthetic, seeded (workloads.make_config({k}); layers 1.. redraw q and indices)",
+        "config": dict({"workload": args.workload, "batch": inp.batch, "n1": 64, "d": 512, "block_size": 128,
+                        "layers_rotated": L, "splits": plan.splits, "grid": plan.grid,
+                        "head_group": plan.head_group}, **CONFIG_TEXT[k]),
+        "effective_kv_gbs": round(achieved, 1),
+        "kv_bytes_per_step": kv_bytes,
+        "total_bytes_per_step": kv_bytes + other_bytes,
+        "pairs_per_step": pairs,
+        "forward_us": round(fwd_ms * 1e3, 3),
+        "plan_host_us": round(1e6 * t_plan / passes, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload), "kernel": kern},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle_forward
+        cpu = inp.to("cpu")
+        res["cpu_baseline"] = cpu_baseline(lambda t: oracle_forward(cpu, [t]), T1, args.cpu_seconds,
+                                           "query-tokens/s", f"{args.workload} query tokens")
+    print(json.dumps(res), flush=True)
 
 
 def prefill(args, m, make_config, torch, np):
@@ -401,6 +415,11 @@ def prefill(args, m, make_config, torch, np):
                                 if plan.head_group == 64 else
                                 "attn_kernel<1> (split attention, per-tile descales)")},
     }
+    if not args.no_cpu_baseline:
+        from oracle import oracle_forward
+        cpu = inp.to("cpu")
+        res["cpu_baseline"] = cpu_baseline(lambda t: oracle_forward(cpu, [t]), T1, args.cpu_seconds,
+                                           "query-tokens/s", "csa_prefill query tokens")
     print(json.dumps(res), flush=True)
 
 
@@ -500,23 +519,8 @@ def indexer(args, m, torch, np):
     }
     if not args.no_cpu_baseline:
         from oracle.indexer import oracle_indexer
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:
-            cores = len(os.sched_getaffinity(0))
-        order = np.random.default_rng(0).permutation(T1)
-        t0 = time.time()
-        done = 0
-        for t in order:
-            oracle_indexer(cpu, [int(t)])
-            done += 1
-            if time.time() - t0 > args.cpu_seconds:
-                break
-        dt = time.time() - t0
-        res["cpu_baseline"] = {"value": round(done / dt, 3), "unit": "query-rows/s",
-                               "cores": int(cores), "kind": "oracle",
-                               "sample": f"{done} random rows of {name} in {dt:.1f} s, NumPy oracle on the host"}
+        res["cpu_baseline"] = cpu_baseline(lambda t: oracle_indexer(cpu, [t]), T1, args.cpu_seconds,
+                                           "query-rows/s", f"{name} rows")
     print(json.dumps(res), flush=True)
 
 

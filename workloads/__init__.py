@@ -5,4 +5,4 @@ sparse index draws, random values and their fp8 e4m3 quantisation.  It holds
 none of the attention arithmetic, so both the CPU oracle (``oracle/``) and the
 HIP path can consume the same bytes without sharing any method code.
 """
-from .gen import Inputs, make_config, make_custom, CONFIG_NAMES, quantize_rows_e4m3  # noqa: F401
+from .gen import Inputs, make_config, make_custom, redraw_query_side, CONFIG_NAMES, quantize_rows_e4m3  # noqa: F401

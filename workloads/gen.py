@@ -298,12 +298,17 @@ def _swa_tiny(seed, device):
                        spare_blocks=3, return_lse=True, device=device, name="swa_tiny")
 
 
+def _csa_decode_indices(rng, batch, c, topk):
+    """One decode row per batch at position s2 - 1 sees every compressed token:
+    topk distinct ones drawn uniformly."""
+    return np.stack([_uniform_draw(rng, c, topk) for _ in range(batch)])
+
+
 def _csa_decode(seed, device, batch=32, s2=8192, topk=512, layout_q="BSND"):
     rng = np.random.default_rng(10_000 + seed)
     ratio = 4
     c = s2 // ratio
-    # single decode row sits at position s2-1: every compressed token is visible
-    idx = np.stack([_uniform_draw(rng, c, topk) for _ in range(batch)])
+    idx = _csa_decode_indices(rng, batch, c, topk)
     return make_custom(seed=seed, q_lens=[1] * batch, ori_lens=[s2] * batch, layout_q=layout_q,
                        cmp_lens=[c] * batch, cmp_ratio=ratio, residual=[0] * batch,
                        indices=idx, spare_blocks=8, device=device, name="csa_decode")
@@ -320,15 +325,11 @@ def _hca_decode(seed, device, batch=32, lo=32768, hi=65536):
                        table_cols=hi // 128, spare_blocks=8, device=device, name="hca_decode")
 
 
-def _csa_mtp(seed, device, batch=64, lo=65536, hi=131072, topk=512, recent=256):
-    rng = np.random.default_rng(10_000 + seed)
-    ratio = 4
-    s_q = 2
-    lens = rng.integers(lo, hi + 1, size=batch)
-    cmp = [int(x) // ratio for x in lens]
-    res = [int(x) % ratio for x in lens]
+def _csa_mtp_indices(rng, lens, s_q, ratio, topk, recent):
+    """Per query row: the `recent` most recent visible compressed tokens plus
+    uniform draws from the older ones, shuffled, -1 padded."""
     rows = []
-    for b in range(batch):
+    for b in range(len(lens)):
         L = int(lens[b])
         for i in range(s_q):
             # compressed tokens whose whole span lies at or before this row's position
@@ -341,8 +342,19 @@ def _csa_mtp(seed, device, batch=64, lo=65536, hi=131072, topk=512, recent=256):
             row = np.full(topk, -1, dtype=np.int32)
             row[:len(sel)] = sel
             rows.append(row)
+    return np.stack(rows)
+
+
+def _csa_mtp(seed, device, batch=64, lo=65536, hi=131072, topk=512, recent=256):
+    rng = np.random.default_rng(10_000 + seed)
+    ratio = 4
+    s_q = 2
+    lens = rng.integers(lo, hi + 1, size=batch)
+    cmp = [int(x) // ratio for x in lens]
+    res = [int(x) % ratio for x in lens]
+    rows = _csa_mtp_indices(rng, lens, s_q, ratio, topk, recent)
     return make_custom(seed=seed, q_lens=[s_q] * batch, ori_lens=[int(x) for x in lens], layout_q="BSND",
-                       cmp_lens=cmp, cmp_ratio=ratio, residual=res, indices=np.stack(rows),
+                       cmp_lens=cmp, cmp_ratio=ratio, residual=res, indices=rows,
                        table_cols=hi // 128, spare_blocks=8, device=device, name="csa_mtp_long")
 
 
@@ -359,6 +371,34 @@ def _csa_prefill(seed, device, batch=4, s=4096, topk=512):
     return make_custom(seed=seed, q_lens=[s] * batch, ori_lens=[s] * batch, layout_q="TND",
                        cmp_lens=[c] * batch, cmp_ratio=ratio, residual=[0] * batch, indices=rows,
                        kv_scale_mode=1, spare_blocks=4, return_lse=True, device=device, name="csa_prefill")
+
+
+def redraw_query_side(inp: Inputs, k: int, draw: int) -> Inputs:
+    """The same workload with a new draw of everything a model layer owns on
+    the query side: q and its descales, and (for the CSA configs) the top-k
+    index rows, by the config's own recipe.  The lengths, block tables,
+    sinks and the caches' bytes are shared (the caller replaces the caches
+    with copies of its own).  Tensors are made on inp's device."""
+    dev = inp.q.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7_000_003 * (draw + 1) + k)
+    qv = _randn(gen, tuple(inp.q.shape), dev)
+    q_codes, q_ds = quantize_rows_e4m3(qv)
+    out = replace(inp, q=q_codes.contiguous(), q_descale=q_ds.contiguous())
+    if inp.cmp_sparse_indices is None:
+        return out
+    rng = np.random.default_rng(20_000 + 1000 * k + draw)
+    topk = inp.topk
+    if k == 2:
+        c = int(inp.seqused_cmp_kv[0])
+        idx = _csa_decode_indices(rng, inp.batch, c, topk)
+    elif k == 4:
+        lens = inp.seqused_ori_kv.cpu().numpy()
+        idx = _csa_mtp_indices(rng, lens, inp.q_s, inp.cmp_ratio, topk, 256)
+    else:
+        raise ValueError(f"no query-side redraw recipe for config {k}")
+    out.cmp_sparse_indices = torch.as_tensor(idx.reshape(inp.t1, 1, topk), device=dev)
+    return out
 
 
 def make_config(k: int, seed: Optional[int] = None, device="cpu", **kw) -> Inputs:
