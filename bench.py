@@ -240,6 +240,8 @@ def timed_graph_steps(m, torch, plan, tens, dev, steps, warmup):
 
 
 def kernel_name(plan):
+    if plan.split_key:
+        return f"sk_kernel (split-key decode: 64 heads, {plan.splits} key splits per token, in-kernel merge)"
     if plan.head_group == 64:
         return "pf_kernel (whole-token)"
     if plan.head_group > 0:

@@ -274,6 +274,12 @@ class Plan:
         return int(self.metadata[7])
 
     @property
+    def split_key(self) -> bool:
+        """The split-key decode kernel (64 heads, <= 128 keys per unit, the
+        splits merged inside the kernel)."""
+        return bool(self.metadata[13])
+
+    @property
     def head_group(self) -> int:
         """Heads per work unit: 8 or 16 (head-split decode kernel), 64 (whole-token
         prefill kernel), or 0 (key-split kernel)."""

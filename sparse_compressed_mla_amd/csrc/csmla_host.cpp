@@ -16,6 +16,11 @@
 
 using namespace csmla;
 
+namespace {
+constexpr int64_t kSkKeys = 2 * kTileKeys;   // keys per split-key unit (two 64-key tiles)
+constexpr int64_t kSkMaxSplits = 16;
+}  // namespace
+
 static_assert(CSMLA_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "static scratch size");
 
 namespace {
@@ -159,11 +164,17 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of a split plan: bf16 partial outputs [units, 64, 512], then
 // (max, sum) [units, 64, 2] fp32.
+void csmla::workspace_offsets(int n_units, size_t* xcc, size_t* o, size_t* ml) {
+  *xcc = kWsSyncBytes;
+  *o = align256(*xcc + (size_t)n_units * sizeof(int32_t));
+  *ml = align256(*o + (size_t)n_units * kN1 * kD * 2);
+}
+
 size_t csmla::workspace_bytes_for(int n_units, int splits) {
   if (splits <= 1) return 0;
-  const size_t o = (size_t)n_units * kN1 * kD * 2;
-  const size_t ml = (size_t)n_units * kN1 * 2 * sizeof(float);
-  return align256(o) + ml;
+  size_t xcc, o, ml;
+  workspace_offsets(n_units, &xcc, &o, &ml);
+  return ml + (size_t)n_units * kN1 * 2 * sizeof(float);
 }
 
 extern "C" {
@@ -297,11 +308,28 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
     else if (pf_ok) hg = kN1;
   }
   if (T1 > 256 && pf_ok) hg = kN1;
+  // Split-key decode kernel: all 64 heads of a token over <= 128 keys per
+  // unit, the splits of a token merged inside the kernel.  It needs every
+  // unit resident at once (one work-group per CU: 8 S ceil(T1 / 8) <= 256)
+  // and top-k within the list buffer; S is as large as that allows.
+  const int64_t t_rounds = (T1 + 7) / 8;
+  const int64_t sk_min = std::max<int64_t>(1, (max_n + kSkKeys - 1) / kSkKeys);
+  const int64_t sk_max = std::min<int64_t>(kMaxGrid / (8 * t_rounds), kSkMaxSplits);
+  const bool sk_ok = pf_ok && T1 <= kSkMaxTokens && sk_min <= sk_max;
+  bool sk = false;
   if (const char* env = std::getenv("CSMLA_KERNEL")) {   // tuning / test override
     if (!std::strcmp(env, "split")) hg = 0;
     else if (!std::strcmp(env, "heads8") && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN) hg = 8;
     else if (!std::strcmp(env, "heads16") && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN) hg = 16;
     else if (!std::strcmp(env, "prefill") && pf_ok) hg = kN1;
+    else if (!std::strcmp(env, "splitkey") && sk_ok) { hg = 0; sk = true; }
+  }
+  if (sk) {
+    S = sk_max;
+    if (const char* env = std::getenv("CSMLA_SPLITS")) {
+      const int64_t f = std::atoll(env);
+      if (f >= 1) S = std::min(std::max(f, sk_min), sk_max);
+    }
   }
   if (hg > 0) S = 1;
   if (S > kMaxSplits) return fail(CSMLA_ERR_UNSUPPORTED, "a token needs %lld splits; at most %d are built", (long long)S, kMaxSplits);
@@ -309,7 +337,8 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   const int64_t n_units64 = (int64_t)T1 * per_token;
   if (n_units64 > (int64_t)1 << 30) return fail(CSMLA_ERR_UNSUPPORTED, "too many work units");
   const int n_units = (int)n_units64;
-  const int G = (int)std::min<int64_t>(n_units64, kMaxGrid);
+  // the split-key kernel's grid: 8 S ceil(T1 / 8) blocks, token t's splits on XCD t mod 8
+  const int G = sk ? (int)(8 * S * t_rounds) : (int)std::min<int64_t>(n_units64, kMaxGrid);
 
   // contiguous unit ranges per work-group, balanced by estimated keys
   std::vector<double> pre(n_units + 1, 0.0);
@@ -329,13 +358,15 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   std::vector<int32_t> starts(G + 1);
   starts[0] = 0;
   int u = 0;
-  for (int g = 1; g < G; ++g) {
+  for (int g = 1; g < G && !sk; ++g) {
     const double target = pre[n_units] * g / G;
     while (u < n_units && pre[u] < target) ++u;
     int lo = starts[g - 1] + 1, hi = n_units - (G - g);
     starts[g] = std::min(std::max(u, lo), hi);
     u = starts[g];
   }
+  if (sk)   // one unit per block; the block -> (token, split) map lives in the kernel
+    for (int g = 1; g < G; ++g) starts[g] = std::min(g, n_units);
   starts[G] = n_units;
 
   std::memset(md, 0, sizeof(int32_t) * CSMLA_METADATA_WORDS);
@@ -353,6 +384,7 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   md[MD_WS_HI] = (int32_t)(ws >> 31);
   md[MD_FLAGS] = S > 1 ? 1 : 0;
   md[MD_HEAD_GROUP] = hg;
+  md[MD_SPLIT_KEY] = sk ? 1 : 0;
   for (int g = 0; g <= G; ++g) md[MD_STARTS + g] = starts[g];
   if (ws_bytes) *ws_bytes = ws;
   g_last_error.clear();
@@ -410,13 +442,16 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
       return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was not written by csmla_plan of this version");
     if ((uint32_t)md[MD_PROBLEM_HASH] != problem_hash(p) || md[MD_T1] != p->t1)
       return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was planned for a different problem");
-    const int S = md[MD_SPLITS], U = md[MD_UNITS], G = md[MD_GRID], HG = md[MD_HEAD_GROUP];
+    const int S = md[MD_SPLITS], U = md[MD_UNITS], G = md[MD_GRID], HG = md[MD_HEAD_GROUP], SK = md[MD_SPLIT_KEY];
     const bool hg_ok = HG == 0 || ((HG == 8 || HG == 16) && S == 1 && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN) ||
                        (HG == kN1 && S == 1 && p->topk <= kListMax);
+    const bool sk_ok = SK == 0 || (SK == 1 && HG == 0 && S <= kSkMaxSplits && p->t1 <= kSkMaxTokens &&
+                                   p->topk <= kListMax && G == 8 * S * ((p->t1 + 7) / 8) && G <= kMaxGrid);
     const int per_token = HG > 0 ? kN1 / HG : S;
-    if (S < 1 || !hg_ok || U != p->t1 * per_token || G < 1 || G > kMaxGrid || G > U)
+    if (S < 1 || !hg_ok || !sk_ok || U != p->t1 * per_token || G < 1 || G > kMaxGrid || (!SK && G > U))
       return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata header is inconsistent");
     a.hg = HG;
+    a.sk = SK;
     for (int g = 0; g <= G; ++g) {
       const int s0 = md[MD_STARTS + g];
       if (s0 < 0 || s0 > U || (g > 0 && s0 < md[MD_STARTS + g - 1]) || (g == 0 && s0 != 0) || (g == G && s0 != U))
@@ -430,8 +465,12 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
         return fail(CSMLA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", ws, t->workspace ? t->workspace_bytes : (size_t)0);
       if ((reinterpret_cast<uintptr_t>(t->workspace) & 255) != 0)
         return fail(CSMLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-      a.ws_o = (uint16_t*)t->workspace;
-      a.ws_ml = (float*)((char*)t->workspace + align256((size_t)U * kN1 * kD * 2));
+      size_t o_xcc, o_o, o_ml;
+      workspace_offsets(U, &o_xcc, &o_o, &o_ml);
+      a.ws_sync = (int32_t*)t->workspace;
+      a.ws_xcc = (int32_t*)((char*)t->workspace + o_xcc);
+      a.ws_o = (uint16_t*)((char*)t->workspace + o_o);
+      a.ws_ml = (float*)((char*)t->workspace + o_ml);
     }
   }
   return CSMLA_OK;
@@ -475,7 +514,7 @@ csmla_status csmla_forward_noalloc(const csmla_problem* p, const csmla_tensors* 
                   need, kNoAllocScratchBytes);
     if (need > 0) {
       void* ptr = nullptr;
-      const int e = noalloc_scratch(&ptr);
+      const int e = noalloc_scratch(&ptr, stream);
       if (e != 0) return fail(CSMLA_ERR_HIP, "static scratch lookup failed (hipError %d)", e);
       ts.workspace = ptr;
       ts.workspace_bytes = kNoAllocScratchBytes;

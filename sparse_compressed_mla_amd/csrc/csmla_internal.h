@@ -19,8 +19,16 @@ constexpr int32_t kMagic = 0x4C4D5343;   // "CSML"
 enum {
   MD_MAGIC = 0, MD_VERSION = 1, MD_PROBLEM_HASH = 2, MD_LENGTHS_HASH = 3, MD_T1 = 4,
   MD_SPLITS = 5, MD_UNITS = 6, MD_GRID = 7, MD_LIST_MAX = 8, MD_WS_LO = 9, MD_WS_HI = 10,
-  MD_FLAGS = 11, MD_HEAD_GROUP = 12, MD_STARTS = kHeaderWords
+  MD_FLAGS = 11, MD_HEAD_GROUP = 12, MD_SPLIT_KEY = 13, MD_STARTS = kHeaderWords
 };
+
+// Workspace layout (every plan that needs one): a sync region of fixed size
+// first (the split-key decode kernel's per-token words; zero before the
+// workspace's first use, and every call leaves the arrival words zero, so one
+// buffer serves plans of any size), then per-unit XCD ids, the partial
+// outputs and their (max, sum).
+constexpr int kSkMaxTokens = 256;                          // tokens the split-key decode kernel takes
+constexpr size_t kWsSyncBytes = (size_t)kSkMaxTokens * 4 * 4;
 
 // Everything one kernel launch needs, passed by value in the kernarg segment:
 // the problem and tensors (KHdr), then the per-work-group unit ranges.
@@ -43,9 +51,11 @@ struct KHdr {
   const int32_t* res; const int32_t* topk_len; const float* sinks;
   uint16_t* out; float* lse;
   uint16_t* ws_o; float* ws_ml;
+  int32_t* ws_sync; int32_t* ws_xcc;
   // plan
   int32_t splits, n_units, grid;
   int32_t hg;                       // > 0: head-split kernel with groups of hg heads (8 or 16)
+  int32_t sk;                       // 1: split-key decode kernel (64 heads, <= 128 keys per unit, in-kernel merge)
 };
 
 struct KArgs : KHdr {
@@ -53,6 +63,8 @@ struct KArgs : KHdr {
 };
 
 size_t workspace_bytes_for(int n_units, int splits);
+// byte offsets of the workspace parts (xcc ids, partial outputs, (max, sum))
+void workspace_offsets(int n_units, size_t* xcc, size_t* o, size_t* ml);
 
 // Host helpers shared by the two halves of the library (csmla_host.cpp):
 // set the calling thread's last-error message and return `status`; clear it;
@@ -66,8 +78,9 @@ uint32_t hash_bytes(const void* data, size_t n, uint32_t seed = 2166136261u);
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 
 // Device address of that scratch on the current device (looked up once per
-// device, then cached); returns a hipError_t as int.
-int noalloc_scratch(void** ptr);
+// device, then cached; the first lookup also clears its sync words with a
+// fill kernel on `stream`); returns a hipError_t as int.
+int noalloc_scratch(void** ptr, void* stream);
 
 // launchers (csmla_kernels.hip); return a hipError_t as int
 int launch_forward(const KArgs& a, void* stream);

@@ -154,7 +154,7 @@ __device__ __forceinline__ KHdr hdr_view(HdrRegs r) {
   CSMLA_GLOBAL(cmp_kv); CSMLA_GLOBAL(cmp_ds); CSMLA_GLOBAL(idx); CSMLA_GLOBAL(ori_tab); CSMLA_GLOBAL(cmp_tab);
   CSMLA_GLOBAL(cu_q); CSMLA_GLOBAL(cu_ori); CSMLA_GLOBAL(cu_cmp); CSMLA_GLOBAL(su_q); CSMLA_GLOBAL(su_ori);
   CSMLA_GLOBAL(su_cmp); CSMLA_GLOBAL(res); CSMLA_GLOBAL(topk_len); CSMLA_GLOBAL(sinks); CSMLA_GLOBAL(out);
-  CSMLA_GLOBAL(lse); CSMLA_GLOBAL(ws_o); CSMLA_GLOBAL(ws_ml);
+  CSMLA_GLOBAL(lse); CSMLA_GLOBAL(ws_o); CSMLA_GLOBAL(ws_ml); CSMLA_GLOBAL(ws_sync); CSMLA_GLOBAL(ws_xcc);
 #undef CSMLA_GLOBAL
   return h;
 }
@@ -2013,14 +2013,16 @@ struct PfKey {
 };
 
 // It reads only the header fields it uses (no cache_sides, which pins all of
-// them in scalar registers): this runs in every step.
-__device__ __forceinline__ PfKey pf_resolve(const KHdr& a, const PfCursor& c, const int* list, bool live) {
+// them in scalar registers): this runs in every step.  Lane l resolves list
+// position key0 + l; positions at or past key_end are not keys (ok = false).
+__device__ __forceinline__ PfKey pf_resolve_keys(const KHdr& a, const PfCursor& c, const int* list, bool live,
+                                                 int key0, int key_end) {
   // Branch-free around the table load (a branch would make the compiler wait
   // for it at the join): without a paged key it reads the zero row.
   PfKey r;
-  const int n = c.n_o + c.n_c;
-  const int key = kTileKeys * c.tile + (opaque((int)threadIdx.x) & 63);
-  const bool any = live && n > 0;   // uniform
+  const int n = min(c.n_o + c.n_c, key_end);
+  const int key = key0 + (opaque((int)threadIdx.x) & 63);
+  const bool any = live && n > key0;   // uniform
   r.ok = live && key < n;
   bool is_cmp = false;
   int j = 0;
@@ -2046,6 +2048,11 @@ __device__ __forceinline__ PfKey pf_resolve(const KHdr& a, const PfCursor& c, co
   else if (a.layout_kv == 1) r.rc = (int64_t)(is_cmp ? c.k.cmp0 : c.k.kv0) + j;
   else r.rc = (int64_t)c.k.b * (is_cmp ? a.cmp_s : a.ori_s) + j;
   return r;
+}
+
+// The cursor's current tile of its token's list.
+__device__ __forceinline__ PfKey pf_resolve(const KHdr& a, const PfCursor& c, const int* list, bool live) {
+  return pf_resolve_keys(a, c, list, live, kTileKeys * c.tile, c.n_o + c.n_c);
 }
 
 // Move the cursor past its tile (every wave: entering a token compacts its
@@ -2543,6 +2550,402 @@ pf_kernel(const KArgs a) {
   pf_body<PER_TILE>((KArgPtr)__builtin_amdgcn_kernarg_segment_ptr(), smem, w);
 }
 
+// ---------------------------------------------------------------------------
+// split-key decode kernel: one work unit = (query token t, key split s), all
+// 64 heads of t against at most 128 consecutive keys of t's list (ori band
+// positions, then the compacted cmp entries).  QuantSparseFlashMla, 功能说明
+// (the formula and the SWA / CSA / HCA key sets); fused infer-attention page,
+// 输出说明 (the log-sum-exp that merges partial results).
+// ---------------------------------------------------------------------------
+//
+// For a decode batch the tokens are few (32 here) and their key lists short
+// (~640 keys), so each token's keys are split over S work-groups on one XCD
+// (block b runs on XCD b mod 8; the splits of token t take block ids that are
+// equal mod 8).  A work-group gathers its (at most two) 64-key tiles at once,
+// right after the key resolution, and computes them with the whole-token
+// kernel's step code (fp8 S^T with the D halves exchanged through LDS, f16
+// P V): no tile pipeline and no online reference, because all of the unit's
+// keys are in LDS together and the softmax reference is their exact maximum.
+//
+// Merge (S > 1): every unit writes its partial (bf16 O normalised by its own
+// row sum, and fp32 (max, sum) per head) to the workspace, then arrives at the
+// token's counter.  The last arriver starts a new generation of the token's
+// sync words; the other units wait for that (a bounded spin: after ~40 us a
+// unit leaves, and the work it would have done is claimed by the others) and
+// every unit present then claims groups of 8 heads and merges them (log-sum-
+// exp rule, sink added once), so the merge is spread over the token's
+// work-groups.  The exchange relies on the units of a token sharing one L2:
+// partial stores are complete (s_waitcnt) before the arrival atomic, the sync
+// words are only touched by L2 atomics or L1-bypassing loads, and merge reads
+// follow an L1 invalidate.  Each unit also records the XCD it ran on
+// (HW_REG_XCC_ID); a merge that finds a partial from another XCD writes NaN
+// instead of a result, so a broken placement cannot pass silently.
+// Sync words per token: [0] arrivals, [1] generation, [2] claims.  They must
+// be zero before a workspace's first use and every call leaves the arrivals
+// zero.
+
+constexpr int kSkMaxKeys = 2 * kTileKeys;    // keys per unit: two 64-key tiles in LDS at once
+constexpr int kSkHeadGroup = 8;              // heads per merge claim
+constexpr int kSkSpinTicks = 4000;           // s_memrealtime ticks (100 MHz): a waiting unit leaves after ~40 us
+constexpr int kSkMaxSplitsDev = 16;          // splits per token (the planner's bound)
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+struct LdsSK {
+  static constexpr int kTiles = 0;                          // 2 x 32 KiB fp8 tiles (whole-token kernel layout)
+  static constexpr int kXch = 2 * kTileBytes;               // f32 [2 tiles][8 waves][64 lanes][8]: S^T halves
+  static constexpr int kP = kXch + 2 * kPfThreads * 32;     // f16 P [2 tiles][64 heads][64 keys]
+  static constexpr int kSc = kP + 2 * 64 * 64 * 2;          // 2 scale sets (LdsPF layout)
+  static constexpr int kList = kSc + 2 * LdsPF::kScBytes;   // int [kListMax]: compacted cmp indices
+  static constexpr int kMax = kList + 4 * kListMax;         // f32 [8 waves][64]: maxima per head
+  static constexpr int kL = kMax + 4 * kPfThreads;          // f32 [8 waves][64]: row sums per head
+  static constexpr int kMisc = kL + 4 * kPfThreads;         // int [64]: compaction, broadcast words
+  static constexpr int kKaddr = kMisc + 4 * 64;             // u64 [2][64]: row addresses
+  static constexpr int kKds = kKaddr + 2 * 64 * 8;          // u64 [2][64]: descale addresses
+  static constexpr int kNvalid = kKds + 2 * 64 * 8;         // int [2]: keys of each tile
+  static constexpr int kBytes = kNvalid + 16;
+};
+static_assert(LdsSK::kBytes <= 160 * 1024, "LDS");
+
+// A read of a sync word where the atomics act (L2): an atomic add of zero
+// that returns the old value, waited for in the same asm.  (A load with the
+// workgroup-scope bit may be served by the CU's L1, which would keep
+// returning the value it cached first.)
+__device__ __forceinline__ int sk_poll(int* p) {
+  int v;
+  asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p), "v"(0) : "memory");
+  return v;
+}
+__device__ __forceinline__ int sk_atomic_add(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ int sk_atomic_xchg(int* p, int v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ int sk_xcc_id() {
+  int id;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(id));
+  return id & 0xf;
+}
+
+// The token's q fragments straight from global memory (the B operands of
+// S^T = K Q^T for heads [32 hb, +32), D half dh, in the order pf_op reads a
+// staged row: lane group g holds bytes 256 dh + 64 s4 + 32 g, +32).
+__device__ __forceinline__ void sk_q_frag(const uint8_t* q, int n1, int t, int hb, int dh, int lane, v8i (&qf)[4]) {
+  const uint8_t* row = q + ((size_t)t * n1 + 32 * hb + (lane & 31)) * kD + 256 * dh + 32 * (lane >> 5);
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const v4i lo = *(const v4i*)(row + 64 * s4);
+    const v4i hi = *(const v4i*)(row + 64 * s4 + 16);
+    qf[s4] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+// Merge heads [8 g, +8) of token t from its S partials (units t S .. t S + S - 1):
+// thread tid takes head 8 g + tid / 64 and columns 8 (tid % 64) .. +7.  Every
+// load of every split is issued before the first is used (splits past S
+// read split 0 again and weigh nothing).
+__device__ __forceinline__ void sk_merge(const KHdr& a, int t, int S, int grp, int my_xcc, const int* xcc) {
+  constexpr int SM = kSkMaxSplitsDev;
+  const int tid = opaque((int)threadIdx.x);
+  const int h = kSkHeadGroup * grp + (tid >> 6), col = 8 * (tid & 63);
+  const size_t u0 = (size_t)t * S;
+  const float sg = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+  v2f mlv[SM];
+  uint4 ov[SM];
+  int xv[SM];
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    const size_t u = u0 + (s < S ? s : 0);
+    mlv[s] = *(const v2f*)(a.ws_ml + (u * kN1 + h) * 2);
+    ov[s] = *(const uint4*)(a.ws_o + (u * kN1 + h) * kD + col);
+    xv[s] = xcc[u];
+  }
+  float M = sg;
+  bool padded = false, foreign = false;
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    if (s < S) {
+      M = fmaxf(M, mlv[s][0]);
+      padded |= mlv[s][1] < 0.f;
+      foreign |= xv[s] != my_xcc;
+    }
+  }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  float L = 0.f;
+  if (!padded && M != kNegInf) {
+    L = (sg == kNegInf) ? 0.f : exp2f(sg - M);
+#pragma unroll
+    for (int s = 0; s < SM; ++s) {
+      const float ms = mlv[s][0], ls = mlv[s][1];
+      const float wgt = (s >= S || ms == kNegInf) ? 0.f : ls * exp2f(ms - M);
+      const uint32_t xs[4] = {ov[s].x, ov[s].y, ov[s].z, ov[s].w};
+      L += wgt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += wgt * __uint_as_float(xs[e] << 16);
+        acc[2 * e + 1] += wgt * __uint_as_float(xs[e] & 0xffff0000u);
+      }
+    }
+  }
+  float inv = (L > 0.f) ? 1.0f / L : 0.f;
+  if (foreign) inv = __builtin_nanf("");
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  *(uint4*)(a.out + ((size_t)t * a.n1 + h) * kD + col) = make_uint4(o[0], o[1], o[2], o[3]);
+  if (a.lse && (tid & 63) == 0) {
+    float lse_v = (!padded && L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
+    if (foreign) lse_v = __builtin_nanf("");
+    a.lse[(size_t)t * a.n1 + h] = lse_v;
+  }
+}
+
+template <int PER_TILE>
+__device__ __forceinline__ void sk_body(KArgPtr ap, uint8_t* smem, int w) {
+  using L = LdsSK;
+  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5;
+  const int kb = w & 1, hb = (w >> 1) & 1, dh = w >> 2;
+  const HdrRegs hr = load_hdr_regs(ap);
+  const KHdr a = hdr_view(hr);
+  const int S = a.splits;
+  const int bid = blockIdx.x, xq = bid & 7, kq = bid >> 3;
+  const int t = xq + 8 * (kq / S), sp = kq - (kq / S) * S;
+  if (t >= a.t1) return;   // uniform: an idle block of the last XCD round
+  int* list = reinterpret_cast<int*>(smem + L::kList);
+  int* misc = reinterpret_cast<int*>(smem + L::kMisc);
+  float* maxb = reinterpret_cast<float*>(smem + L::kMax);
+  float* lbuf = reinterpret_cast<float*>(smem + L::kL);
+  uint64_t* kaddr = reinterpret_cast<uint64_t*>(smem + L::kKaddr);
+  uint64_t* kds = reinterpret_cast<uint64_t*>(smem + L::kKds);
+  int* nvalid = reinterpret_cast<int*>(smem + L::kNvalid);
+  int* sync = a.ws_sync;   // [kSkMaxTokens][4]
+  int* xcc = a.ws_xcc;     // [units]
+
+  // ---- every load of the prologue in flight together: lengths, index slots,
+  // q fragments and descale, the token's sync generation ----
+  const TokLens tl = token_lens(a, t);
+  const IdxPre<kPfThreads> ip = pf_idx_raw(a, t);
+  v8i qf[4];
+  sk_q_frag(a.q, a.n1, t, hb, dh, lane, qf);
+  const int hq = 32 * hb + (lane & 31);   // the lane's head in S^T and the softmax
+  const float qc = a.scale_log2 * pf_qds(a, t, hq);
+
+  PfCursor c;
+  c.u = t;
+  c.tile = 0;
+  c.k = token_ctx(a, t, tl);
+  c.n_o = c.k.hi - c.k.lo;
+  c.n_c = 0;
+  if (a.topk > 0) c.n_c = compact_indices<kPfThreads>(a, c.k, t, list, misc, 0, pf_idx_fix(a, ip));
+  else if (a.has_cmp) c.n_c = c.k.vis;
+  c.n_c = __builtin_amdgcn_readfirstlane(c.n_c);
+  const int n = c.n_o + c.n_c;
+  const int k0 = (int)(((int64_t)n * sp) / S), k1 = (int)(((int64_t)n * (sp + 1)) / S);
+  const int nk = k1 - k0;
+  const bool over = nk > kSkMaxKeys;          // the plan's key bound was exceeded: poison, never drop keys
+  const int ntiles = (nk > kTileKeys) ? 2 : 1;
+
+  // ---- key resolution (waves 0 and 1: one tile each), then both tiles'
+  // rows HBM -> LDS and their descales ----
+  if (w < ntiles) {
+    const PfKey k = pf_resolve_keys(a, c, list, c.k.valid != 0, k0 + kTileKeys * w, k1);
+    const PfSrc r = pf_src<PER_TILE>(a, k);
+    kaddr[64 * w + lane] = r.addr;
+    kds[64 * w + lane] = (uint64_t)(uintptr_t)r.ds;
+    const int nv = (int)__popcll(__ballot(r.ok));
+    if (lane == 0) nvalid[w] = nv;
+  }
+  lds_barrier();
+  float sd[2];
+  for (int x = 0; x < ntiles; ++x) {
+    pf_issue(smem + L::kTiles + x * kTileBytes, kaddr + 64 * x, w);
+    sd[x] = pf_load_scale<PER_TILE>(pf_scale_addr(kds + 64 * x));
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // rows, descales (and the prologue loads) landed
+  for (int x = 0; x < ntiles; ++x) pf_scales<PER_TILE>(smem + L::kSc + x * LdsPF::kScBytes, sd[x], nvalid[x]);
+  lds_barrier();
+
+  // ---- S^T per tile, the D halves exchanged through LDS ----
+  float E[2][8];
+  for (int x = 0; x < ntiles; ++x) {
+    const uint8_t* set = smem + L::kSc + x * LdsPF::kScBytes;
+    const v16f Sx = pf_qk<PER_TILE>(smem + L::kTiles + x * kTileBytes, qf,
+                                    reinterpret_cast<const float*>(set + LdsPF::kScKs), kb, dh, lane);
+    float* dst = reinterpret_cast<float*>(smem + L::kXch) + ((x * kPfWaves + w) * 64 + lane) * 8;
+    if (dh) {
+      *(v4f*)dst = v4f{Sx[0], Sx[1], Sx[2], Sx[3]};
+      *(v4f*)(dst + 4) = v4f{Sx[4], Sx[5], Sx[6], Sx[7]};
+    } else {
+      *(v4f*)dst = v4f{Sx[8], Sx[9], Sx[10], Sx[11]};
+      *(v4f*)(dst + 4) = v4f{Sx[12], Sx[13], Sx[14], Sx[15]};
+    }
+    // the wave keeps its own half of the 16 rows (dh 0: rows 0-7, dh 1: rows 8-15)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) E[x][i] = dh ? Sx[8 + i] : Sx[i];
+  }
+  lds_barrier();
+  float m = kNegInf;
+  for (int x = 0; x < ntiles; ++x) {
+    const uint8_t* set = smem + L::kSc + x * LdsPF::kScBytes;
+    const float* src = reinterpret_cast<const float*>(smem + L::kXch) + ((x * kPfWaves + (w ^ 4)) * 64 + lane) * 8;
+    const v4f x0 = *(const v4f*)src, x1 = *(const v4f*)(src + 4);
+    const int kt = 32 * kb + 16 * dh + 4 * g;
+    const float* lamp = reinterpret_cast<const float*>(set + LdsPF::kScLam) + kt;
+    const float* kdp = reinterpret_cast<const float*>(set + LdsPF::kScKd) + kt;
+    const v4f la0 = *(const v4f*)lamp, la1 = *(const v4f*)(lamp + 8);
+    v4f kd0 = v4f{1.f, 1.f, 1.f, 1.f}, kd1 = kd0;
+    if constexpr (!PER_TILE) {
+      kd0 = *(const v4f*)kdp;
+      kd1 = *(const v4f*)(kdp + 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s0 = E[x][i] + x0[i];
+      const float s1 = E[x][4 + i] + x1[i];
+      E[x][i] = s0 * (qc * kd0[i]) + la0[i];
+      E[x][4 + i] = s1 * (qc * kd1[i]) + la1[i];
+      m = fmaxf(m, fmaxf(E[x][i], E[x][4 + i]));
+    }
+  }
+  m = xor32_reduce(m, true);
+  maxb[w * 64 + lane] = m;
+  lds_barrier();
+  // the exact maximum of each head over the unit's keys (both head blocks:
+  // every wave's output columns cover all 64 heads)
+  float Mx[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    float mn = kNegInf;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) mn = fmaxf(mn, maxb[((y & 1) + 2 * x + 4 * (y >> 1)) * 64 + (lane & 31)]);
+    Mx[x] = mn;
+  }
+  // ---- P = 2^(E - M) (f16) and the row sums ----
+  float lt = 0.f;
+  for (int x = 0; x < ntiles; ++x) {
+    const uint8_t* set = smem + L::kSc + x * LdsPF::kScBytes;
+    const float* invp = reinterpret_cast<const float*>(set + LdsPF::kScInv) + 32 * kb + 16 * dh + 4 * g;
+    const v4f iv0 = *(const v4f*)invp, iv1 = *(const v4f*)(invp + 8);
+    const int pq = 2 * (2 * kb + dh) + g;
+    uint8_t* prow = smem + L::kP + x * 8192 + hq * 128 + 16 * (pq ^ (hq & 7));
+    lt += pf_probs(E[x], hb ? Mx[1] : Mx[0], iv0, iv1, prow);
+  }
+  lbuf[w * 64 + lane] = xor32_reduce(lt, false);
+  lds_barrier();
+  // ---- O^T = V'^T P^T ----
+  v16f acc[2][2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) acc[db][x] = v16f{};
+  for (int x = 0; x < ntiles; ++x) {
+    const uint8_t* set = smem + L::kSc + x * LdsPF::kScBytes;
+    pf_pv<PER_TILE>(smem + L::kTiles + x * kTileBytes, reinterpret_cast<const _Float16*>(set + LdsPF::kScVs),
+                    smem + L::kP + x * 8192, w, lane, acc);
+  }
+
+  // ---- epilogue: the final result (one split) or the unit's partial ----
+  const size_t unit = (size_t)t * S + sp;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int h = 32 * x + (lane & 31);
+    float Ls = 0.f;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) Ls += lbuf[((y & 1) + 2 * x + 4 * (y >> 1)) * 64 + (lane & 31)];
+    const float M = Mx[x];
+    float sc = 0.f;
+    uint16_t* orow;
+    if (S == 1) {
+      const float sg = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+      const float Mf = fmaxf(M, sg);
+      float lse_v = kNegInf;
+      if (c.k.valid && Mf != kNegInf) {
+        const float af = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - Mf);
+        const float Lf = af * Ls + ((sg == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sg - Mf));
+        sc = af * __builtin_amdgcn_rcpf(Lf);
+        lse_v = (Mf + __log2f(Lf)) * kLn2;
+      }
+      if (over) { sc = __builtin_nanf(""); lse_v = sc; }
+      if (a.lse && w == 0 && g == 0) a.lse[(size_t)t * a.n1 + h] = lse_v;
+      orow = a.out + ((size_t)t * a.n1 + h) * kD;
+    } else {
+      // partial: O / own row sum in bf16, (max, sum) in log2 units; a padded
+      // query row is marked by a negative sum
+      sc = (Ls > 0.f) ? __builtin_amdgcn_rcpf(Ls) : 0.f;
+      if (over) sc = __builtin_nanf("");
+      if (w == 0 && g == 0) {
+        float* ml = a.ws_ml + (unit * kN1 + h) * 2;
+        ml[0] = c.k.valid ? M : kNegInf;
+        ml[1] = c.k.valid ? Ls : -1.f;
+      }
+      orow = a.ws_o + (unit * kN1 + h) * kD;
+    }
+    // lanes l and l + 32 trade halves so each stores 16 contiguous bytes
+    // (columns 64 w + 32 db + 16 k2 + 8 g + [0, 8))
+    orow += 64 * w + 8 * g;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const v16f& o = acc[db][x];
+        const int q0 = 2 * k2, q1 = 2 * k2 + 1;
+        const uint2 A = pack_bf16x4(sc * o[4 * q0], sc * o[4 * q0 + 1], sc * o[4 * q0 + 2], sc * o[4 * q0 + 3]);
+        const uint2 B = pack_bf16x4(sc * o[4 * q1], sc * o[4 * q1 + 1], sc * o[4 * q1 + 2], sc * o[4 * q1 + 3]);
+        const auto sx = __builtin_amdgcn_permlane32_swap(A.x, B.x, false, false);
+        const auto sy = __builtin_amdgcn_permlane32_swap(A.y, B.y, false, false);
+        *(uint4*)(orow + 32 * db + 16 * k2) = make_uint4(sx[0], sy[0], sx[1], sy[1]);
+      }
+  }
+  if (S == 1) return;
+
+  // ---- merge: arrive, wait for the token's last arrival, claim head groups ----
+  const int my_xcc = sk_xcc_id();
+  if (threadIdx.x == 0) xcc[unit] = my_xcc;
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this thread's partial stores are in L2
+  __syncthreads();
+  int* sy = sync + 4 * t;
+  if (threadIdx.x == 0) {
+    int go = 1;
+    // the generation cannot move before this unit arrives
+    const int gen0 = sk_poll(sy + 1);
+    if (sk_atomic_add(sy, 1) == S - 1) {   // last arrival: a new generation, claims from 0
+      sk_atomic_xchg(sy, 0);
+      sk_atomic_xchg(sy + 2, 0);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      sk_atomic_add(sy + 1, 1);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    } else {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (sk_poll(sy + 1) == gen0) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)kSkSpinTicks) { go = 0; break; }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    misc[0] = go;
+  }
+  __syncthreads();
+  if (!misc[0]) return;   // uniform: the others merge every group
+  asm volatile("buffer_inv sc0" ::: "memory");   // partial reads come from L2, not from a stale L1 line
+  for (;;) {
+    __syncthreads();   // misc[1] is read by every thread before it is rewritten
+    if (threadIdx.x == 0) misc[1] = sk_atomic_add(sy + 2, 1);
+    __syncthreads();
+    const int grp = misc[1];
+    if (grp >= kN1 / kSkHeadGroup) break;
+    sk_merge(a, t, S, grp, my_xcc, xcc);
+  }
+}
+
+template <int PER_TILE>
+__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(kPfWaves / 4, kPfWaves / 4)))
+sk_kernel(const KArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LdsSK::kBytes];
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  sk_body<PER_TILE>((KArgPtr)__builtin_amdgcn_kernarg_segment_ptr(), smem, w);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -2586,7 +2989,11 @@ static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 constexpr int kMaxDevices = 64;
 
-int noalloc_scratch(void** ptr) {
+__global__ void zero_words_kernel(int32_t* p, int n) {
+  for (int i = (int)threadIdx.x; i < n; i += (int)blockDim.x) p[i] = 0;
+}
+
+int noalloc_scratch(void** ptr, void* stream) {
   static std::mutex mu;
   static void* addr[kMaxDevices] = {};
   int dev = -1;
@@ -2599,6 +3006,12 @@ int noalloc_scratch(void** ptr) {
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return (int)e;
     if (!p) return (int)hipErrorInvalidSymbol;
+    // the workspace's sync words start at zero (a fill kernel on the
+    // caller's stream, ahead of the first forward that uses them)
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, (int32_t*)p,
+                       (int)(kWsSyncBytes / 4));
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
     addr[dev] = p;
   }
   *ptr = addr[dev];
@@ -2607,6 +3020,13 @@ int noalloc_scratch(void** ptr) {
 
 int launch_forward(const KArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (a.sk) {
+    if (a.scale_mode == 1)
+      hipLaunchKernelGGL(sk_kernel<1>, dim3(a.grid), dim3(kPfThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(sk_kernel<0>, dim3(a.grid), dim3(kPfThreads), 0, st, a);
+    return (int)hipGetLastError();
+  }
   if (a.hg == kN1) {
     if (a.scale_mode == 1)
       hipLaunchKernelGGL(pf_kernel<1>, dim3(a.grid), dim3(kPfThreads), 0, st, a);

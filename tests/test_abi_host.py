@@ -142,7 +142,9 @@ def test_plan_invariants_and_determinism(monkeypatch):
     starts = md[16:16 + G + 1]
     assert starts[0] == 0 and starts[-1] == U and np.all(np.diff(starts) >= 1)
     a256 = lambda x: (x + 255) // 256 * 256
-    assert ws == (0 if S == 1 else a256(U * 64 * 512 * 2) + U * 64 * 8)
+    # workspace: 4 KiB of sync words, per-unit XCD ids, the partial outputs (bf16), their (max, sum)
+    o = a256(4096 + 4 * U)
+    assert ws == (0 if S == 1 else a256(o + U * 64 * 512 * 2) + U * 64 * 8)
     _, md2, ws2 = m.csmla_plan(p)
     assert np.array_equal(md, md2) and ws == ws2
     # a decode batch of 32 tokens is split so that the grid fills the chip
@@ -271,3 +273,26 @@ def test_noalloc_rejects_plans_beyond_the_static_scratch(monkeypatch):
     st = m.csmla_forward_noalloc(p, fake_tensors(0), md, raise_on_error=False)
     assert st == 3, (st, m.csmla_last_error())          # CSMLA_ERR_WORKSPACE
     assert "64" in m.csmla_last_error() or "67108864" in m.csmla_last_error()
+
+
+def test_plan_split_key_decode(monkeypatch):
+    """The split-key decode plan: token t's S splits on block ids equal mod 8
+    (grid 8 S ceil(T1 / 8) <= 256, one resident round), at most 128 keys per
+    unit, a workspace with the sync words, and forced S clamped to what fits."""
+    monkeypatch.setenv("CSMLA_KERNEL", "splitkey")
+    p = base_problem()                                  # 32 tokens, <= 128 band + 512 cmp keys
+    _, md, ws = m.csmla_plan(p)
+    S, U, G = md[5], md[6], md[7]
+    assert md[13] == 1 and md[12] == 0
+    assert S == 8 and U == 32 * 8 and G == 256 and ws > 4096
+    monkeypatch.setenv("CSMLA_SPLITS", "2")             # 640 keys need >= 5 splits of 128
+    _, md, _ = m.csmla_plan(p)
+    assert md[5] == 5 and md[7] == 8 * 5 * 4
+    monkeypatch.delenv("CSMLA_SPLITS")
+    _, md, _ = m.csmla_plan(base_problem(batch=20, t1=20))
+    assert md[13] == 1 and md[7] == 8 * md[5] * 3 and md[7] <= 256 and md[6] == 20 * md[5]
+    _, md, _ = m.csmla_plan(base_problem(batch=64, t1=64))   # 5 splits x 8 rounds > 256: not taken
+    assert md[13] == 0
+    bad = m.csmla_plan(p)[1].copy()
+    bad[7] = 128                                        # grid no longer 8 S ceil(T1 / 8)
+    assert m.csmla_forward(p, fake_tensors(ws), bad, raise_on_error=False) == MISMATCH

@@ -21,11 +21,12 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
-# Every test runs with the planner's own kernel choice ("auto": the head-split
-# kernel for small per-token batches, the whole-token prefill kernel for more
-# than 256 query tokens, the key-split kernel otherwise) and with each kernel
-# forced, so that every path meets the same bar on the same cases.
-KERNEL_MODES = ["auto", "split", "heads16", "prefill"]
+# Every test runs with the planner's own kernel choice ("auto") and with each
+# kernel forced (where the problem allows it), so that every path meets the
+# same bar on the same cases: the key-split kernel with its combine, the
+# head-split decode kernel, the whole-token prefill kernel and the split-key
+# decode kernel with its in-kernel merge.
+KERNEL_MODES = ["auto", "split", "heads16", "prefill", "splitkey"]
 
 
 @pytest.fixture(autouse=True, params=KERNEL_MODES)
@@ -62,7 +63,8 @@ def check(inp_cpu, tokens=None, name="", inp_gpu=None, splits=None, monkeypatch=
         plan = m.Plan(g)
     finally:
         os.environ.pop("CSMLA_SPLITS", None)
-    say(f"  plan splits={plan.splits} grid={plan.grid} head_group={plan.head_group}; launching")
+    say(f"  plan splits={plan.splits} grid={plan.grid} head_group={plan.head_group} "
+        f"split_key={plan.split_key}; launching")
     o, l = run_gpu(g, plan)
     stats = compare(o, ref.out, toks, l if inp_cpu.return_lse else None,
                     ref.lse if inp_cpu.return_lse else None, name=name)
@@ -102,8 +104,10 @@ def test_cfg1_swa_tiny():
     check_rows(inp, name="cfg1")
 
 
-def test_cfg2_csa_decode():
+def test_cfg2_csa_decode(kernel_mode):
     inp = make_config(2)
+    if kernel_mode == "splitkey":   # the forced mode really takes the split-key kernel here
+        assert m.Plan(inp.to(DEV)).split_key
     check(inp, name="cfg2 csa decode")
     check_rows(inp, name="cfg2")
 
