@@ -38,6 +38,11 @@ Readings of points the pages leave open:
   R8 no row visible: O = 0 and lse = sink (or -inf without sinks).
   R9 query rows at or past seqused_q inside a cu_seqlens_q span are padding:
      O = 0, lse = -inf.
+  R10 bf16 q with packed 640-byte KV rows (KvQuantSparseAttnSharedkv): q's
+     512 columns pair with the row's logical columns in storage order, the
+     64 rope columns first, then the 448 nope columns; the output keeps that
+     order.  There are no q or KV descales: the nope scales live in the row.
+  R11 bf16 q and bf16 KV (SparseCompressedFlashAttention): values as stored.
 """
 from __future__ import annotations
 
@@ -47,6 +52,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 from .fp8 import decode_e4m3
+from .formats import decode_bf16, decode_packed640
 
 TILE = 64
 KIND_ORI = 0
@@ -186,18 +192,37 @@ def token_rows(inp, t: int, tt=None) -> List[Tuple[int, int]]:
 # dequantisation and dense softmax attention
 # ---------------------------------------------------------------------------
 
-def _flat_cache(kv, ds, per_tile: bool):
+def _bits16(x) -> np.ndarray:
+    """Bit patterns of a 16-bit (bf16) tensor as uint16."""
+    import torch
+    return x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _flat_cache(kv, ds, per_tile, fmt: str = "fp8"):
+    """The cache as rows: fp8 codes with descales, bf16 bit patterns, or
+    packed 640-byte rows (no descales for the last two)."""
+    if fmt == "bf16":
+        bits = _bits16(kv)
+        return bits.reshape(-1, bits.shape[-1]), None, "bf16"
     d = kv.shape[-1]
     codes = _np(kv).reshape(-1, d)
+    if fmt == "packed640":
+        return codes, None, "packed640"
     dsn = _np(ds)
     return codes, dsn.reshape(codes.shape[0], -1) if per_tile else dsn.reshape(-1), per_tile
 
 
-def dequant_rows(codes: np.ndarray, ds: np.ndarray, per_tile: bool, rows: Sequence[int]) -> np.ndarray:
-    """Rows of an fp8 cache as float64 values: code * descale, with one
+def dequant_rows(codes: np.ndarray, ds: np.ndarray, per_tile, rows: Sequence[int]) -> np.ndarray:
+    """Rows of a cache as float64 values.  fp8: code * descale, with one
     descale per row or one per 64-wide tile of D (KvQuantSparseAttnSharedkv,
-    参数说明: kv_quant_mode / tile_size)."""
+    参数说明: kv_quant_mode / tile_size); bf16: the stored values
+    (SparseCompressedFlashAttention); packed640: rope then scaled nope
+    (KvQuantSparseAttnSharedkv, 约束说明: the 640-wide row)."""
     rows = np.asarray(rows, dtype=np.int64)
+    if per_tile == "bf16":
+        return decode_bf16(codes[rows]).reshape(len(rows), -1)
+    if per_tile == "packed640":
+        return decode_packed640(codes[rows]).reshape(len(rows), -1)
     vals = decode_e4m3(codes[rows])
     if per_tile:
         return vals * np.repeat(ds[rows].astype(np.float64), TILE, axis=-1)
@@ -257,13 +282,15 @@ def oracle_forward(inp, tokens: Optional[Sequence[int]] = None) -> OracleResult:
     T1, n1, d = inp.t1, inp.n1, inp.d
     tt = token_table(inp)
     toks = list(range(T1)) if tokens is None else [int(t) for t in tokens]
-    q = _np(inp.q).reshape(T1, n1, d)
-    qds = _np(inp.q_descale).astype(np.float64)
+    q_bf16 = getattr(inp, "q_format", "fp8") == "bf16"
+    fmt = getattr(inp, "kv_format", "fp8")
+    q = (_bits16(inp.q) if q_bf16 else _np(inp.q)).reshape(T1, n1, d)
+    qds = None if q_bf16 else _np(inp.q_descale).astype(np.float64)
     sinks = None if inp.sinks is None else _np(inp.sinks).astype(np.float64)
     per_tile = inp.kv_scale_mode == 1
-    ori_codes, ori_ds, ori_tile = _flat_cache(inp.ori_kv, inp.ori_kv_descale, per_tile)
+    ori_codes, ori_ds, ori_tile = _flat_cache(inp.ori_kv, inp.ori_kv_descale, per_tile, fmt)
     if inp.cmp_kv is not None:
-        cmp_codes, cmp_ds, cmp_tile = _flat_cache(inp.cmp_kv, inp.cmp_kv_descale, per_tile)
+        cmp_codes, cmp_ds, cmp_tile = _flat_cache(inp.cmp_kv, inp.cmp_kv_descale, per_tile, fmt)
     out = np.full((T1, n1, d), np.nan)
     lse = np.full((T1, n1), np.nan)
     lse_ns = np.full((T1, n1), np.nan)
@@ -277,8 +304,11 @@ def oracle_forward(inp, tokens: Optional[Sequence[int]] = None) -> OracleResult:
             lse[t] = -np.inf
             lse_ns[t] = -np.inf
             continue
-        qs = qds[t] if qds.ndim == 2 else np.full(n1, qds[t])
-        Q = decode_e4m3(q[t]) * qs[:, None]
+        if q_bf16:
+            Q = decode_bf16(q[t])
+        else:
+            qs = qds[t] if qds.ndim == 2 else np.full(n1, qds[t])
+            Q = decode_e4m3(q[t]) * qs[:, None]
         ori_r = [r for k, r in rows if k == KIND_ORI]
         cmp_r = [r for k, r in rows if k == KIND_CMP]
         parts = [dequant_rows(ori_codes, ori_ds, ori_tile, ori_r)]
@@ -299,6 +329,12 @@ def work_counts(inp, rows: Dict[int, List[Tuple[int, int]]]) -> Dict[str, float]
     for t, v in rows.items():
         per_batch.setdefault(tt[t][0], set()).update(v)
     uniq = sum(len(s) for s in per_batch.values())
-    scale_bytes = 4 * (inp.d // TILE) if inp.kv_scale_mode == 1 else 4
-    return dict(pairs=pairs, unique_rows=uniq, kv_bytes=uniq * (inp.d + scale_bytes),
+    fmt = getattr(inp, "kv_format", "fp8")
+    if fmt == "bf16":
+        row_bytes = 2 * inp.d
+    elif fmt == "packed640":
+        row_bytes = 640
+    else:
+        row_bytes = inp.d + (4 * (inp.d // TILE) if inp.kv_scale_mode == 1 else 4)
+    return dict(pairs=pairs, unique_rows=uniq, kv_bytes=uniq * row_bytes,
                 flops=4.0 * inp.n1 * inp.d * pairs)

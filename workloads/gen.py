@@ -39,8 +39,10 @@ CONFIG_NAMES = {
 class Inputs:
     """Every input of one call, in the layouts the pages give.
 
-    q                 uint8  [T1, N1, D]   (TND, or BSND flattened as t = b*Q_S + s)
-    q_descale         f32    [T1, N1]
+    q                 uint8  [T1, N1, D]   (TND, or BSND flattened as t = b*Q_S + s); bf16 with q_format "bf16"
+    q_descale         f32    [T1, N1]      (None with bf16 q)
+    kv_format "bf16": ori_kv / cmp_kv are bf16 [..., D]; "packed640": uint8 [..., 640] rows
+    (bf16 rope 64 | e4m3 nope 448 | 7 e8m0 scales | pad); descales None for both
     ori_kv            uint8  [blocks, block_size, 1, D] (PA_BBND) | [T_kv, 1, D] (TND) | [B, S2, 1, D] (BSND)
     ori_kv_descale    f32    same leading dims as ori_kv without (1, D); a trailing [D/64] for per-tile scales
     cmp_kv, cmp_kv_descale   as above, or None (SWA)
@@ -75,6 +77,8 @@ class Inputs:
     ori_win_left: int = 127
     ori_win_right: int = 0
     kv_scale_mode: int = 0          # 0: one descale per KV row; 1: one per 64-wide D tile
+    q_format: str = "fp8"           # "fp8" (e4m3 codes + q_descale) or "bf16" (q_descale None)
+    kv_format: str = "fp8"          # "fp8" (codes + descales), "bf16" or "packed640" (descales None)
     return_lse: bool = False
     name: str = ""
     extra: dict = field(default_factory=dict)
@@ -129,13 +133,60 @@ def quantize_rows_e4m3(x: torch.Tensor, tile: Optional[int] = None):
     return codes.contiguous(), ds.squeeze(-1).contiguous()
 
 
+PACKED_ROW = 640
+ROPE = 64
+BF16_NAN = 0x7FC0
+
+
+def pack_rows_640(x: torch.Tensor) -> torch.Tensor:
+    """Rows of 512 float32 values as 640-byte packed rows: the first 64 values
+    as bf16 (round to nearest even), the other 448 as e4m3 codes with one
+    e8m0 scale per 64-wide tile, E = ceil(log2(amax / 448)) + 127 (so every
+    value / 2^(E - 127) lies within e4m3's range; E = 127 for an all-zero
+    tile), then 57 zero pad bytes."""
+    n = x.shape[0]
+    out = torch.zeros((n, PACKED_ROW), dtype=torch.uint8, device=x.device)
+    out[:, :2 * ROPE] = x[:, :ROPE].to(torch.bfloat16).contiguous().view(torch.uint8).reshape(n, 2 * ROPE)
+    nope = x[:, ROPE:].float().unflatten(-1, (7, 64))
+    amax = nope.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.ceil(torch.log2(amax / E4M3_MAX)), torch.zeros_like(amax))
+    e = e.clamp(-127, 127)
+    codes = (nope / torch.pow(2.0, e)[..., None]).to(torch.float8_e4m3fn).view(torch.uint8).flatten(-2)
+    out[:, 2 * ROPE:2 * ROPE + 448] = codes
+    out[:, 2 * ROPE + 448:2 * ROPE + 455] = (e + 127).to(torch.uint8)
+    return out
+
+
+def _poison_rows(n: int, d: int, kv_format: str, device) -> torch.Tensor:
+    """Rows that decode to NaN in every format (unused cache slots)."""
+    if kv_format == "bf16":
+        return torch.full((n, d), BF16_NAN, dtype=torch.int16, device=device).view(torch.bfloat16)
+    if kv_format == "packed640":
+        r = torch.full((n, PACKED_ROW), NAN_CODE, dtype=torch.uint8, device=device)
+        r[:, 0:2 * ROPE:2] = 0xC0
+        r[:, 1:2 * ROPE:2] = 0x7F
+        r[:, 2 * ROPE + 448:2 * ROPE + 455] = 0xFF
+        r[:, 2 * ROPE + 455:] = 0
+        return r
+    return torch.full((n, d), NAN_CODE, dtype=torch.uint8, device=device)
+
+
+def _encode_rows(vals: torch.Tensor, kv_format: str, per_tile: bool):
+    """(rows in the cache's storage type, descales or None)."""
+    if kv_format == "bf16":
+        return vals.to(torch.bfloat16), None
+    if kv_format == "packed640":
+        return pack_rows_640(vals), None
+    return quantize_rows_e4m3(vals, TILE if per_tile else None)
+
+
 def _randn(gen: torch.Generator, shape, device) -> torch.Tensor:
     return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
 
 
 def _paged_cache(np_rng, gen, lengths: Sequence[int], block_size: int, d: int,
-                 per_tile: bool, spare_blocks: int, table_cols: Optional[int], device):
-    """Build a paged cache [blocks, block_size, 1, d] holding N(0,1) rows for
+                 per_tile: bool, spare_blocks: int, table_cols: Optional[int], device, kv_format: str = "fp8"):
+    """Build a paged cache [blocks, block_size, 1, row] holding N(0,1) rows for
     positions [0, len_b) of each batch, with a random permutation of physical
     block ids.  Unused table slots point at a NaN-poisoned spare block."""
     nblk = [(int(s) + block_size - 1) // block_size for s in lengths]
@@ -147,9 +198,13 @@ def _paged_cache(np_rng, gen, lengths: Sequence[int], block_size: int, d: int,
     assert cols >= max(nblk + [0])
     spare_id = int(perm[used])
     table = np.full((len(lengths), cols), spare_id, dtype=np.int32)
-    pool = torch.full((total, block_size, 1, d), NAN_CODE, dtype=torch.uint8, device=device)
-    ds_shape = (total, block_size, d // TILE) if per_tile else (total, block_size)
-    pool_ds = torch.full(ds_shape, float("nan"), dtype=torch.float32, device=device)
+    poison = _poison_rows(total * block_size, d, kv_format, device)
+    width = poison.shape[-1]
+    pool = poison.view(total, block_size, 1, width)
+    pool_ds = None
+    if kv_format == "fp8":
+        ds_shape = (total, block_size, d // TILE) if per_tile else (total, block_size)
+        pool_ds = torch.full(ds_shape, float("nan"), dtype=torch.float32, device=device)
     off = 0
     for b, s in enumerate(lengths):
         ids = perm[off:off + nblk[b]]
@@ -158,33 +213,40 @@ def _paged_cache(np_rng, gen, lengths: Sequence[int], block_size: int, d: int,
         if s == 0:
             continue
         vals = _randn(gen, (int(s), d), device)
-        codes, ds = quantize_rows_e4m3(vals, TILE if per_tile else None)
+        rows, ds = _encode_rows(vals, kv_format, per_tile)
         pad = nblk[b] * block_size - int(s)
         ids_t = torch.as_tensor(ids, device=device)
         if pad:
-            codes = torch.cat([codes, torch.full((pad, d), NAN_CODE, dtype=torch.uint8, device=device)])
-            ds = torch.cat([ds, torch.full((pad,) + tuple(ds.shape[1:]), float("nan"), device=device)])
-        pool[ids_t] = codes.view(nblk[b], block_size, 1, d)
-        pool_ds[ids_t] = ds.view((nblk[b], block_size) + tuple(ds.shape[1:]))
+            rows = torch.cat([rows, _poison_rows(pad, d, kv_format, device)])
+            if ds is not None:
+                ds = torch.cat([ds, torch.full((pad,) + tuple(ds.shape[1:]), float("nan"), device=device)])
+        pool[ids_t] = rows.view(nblk[b], block_size, 1, width)
+        if ds is not None:
+            pool_ds[ids_t] = ds.view((nblk[b], block_size) + tuple(ds.shape[1:]))
     return pool, pool_ds, torch.as_tensor(table, device=device)
 
 
-def _contig_cache(gen, lengths, d, per_tile, device, bsnd_len: Optional[int]):
-    """TND ([sum len, 1, d]) or BSND ([B, S2max, 1, d]) contiguous cache."""
+def _contig_cache(gen, lengths, d, per_tile, device, bsnd_len: Optional[int], kv_format: str = "fp8"):
+    """TND ([sum len, 1, row]) or BSND ([B, S2max, 1, row]) contiguous cache."""
     if bsnd_len is None:
         total = int(sum(lengths))
         vals = _randn(gen, (max(total, 1), d), device)[:total]
-        codes, ds = quantize_rows_e4m3(vals, TILE if per_tile else None)
-        return codes.view(total, 1, d), ds
+        rows, ds = _encode_rows(vals, kv_format, per_tile)
+        return rows.view(total, 1, rows.shape[-1]), ds
     B = len(lengths)
-    codes = torch.full((B, bsnd_len, 1, d), NAN_CODE, dtype=torch.uint8, device=device)
-    ds_shape = (B, bsnd_len, d // TILE) if per_tile else (B, bsnd_len)
-    dsall = torch.full(ds_shape, float("nan"), dtype=torch.float32, device=device)
+    poison = _poison_rows(B * bsnd_len, d, kv_format, device)
+    width = poison.shape[-1]
+    codes = poison.view(B, bsnd_len, 1, width)
+    dsall = None
+    if kv_format == "fp8":
+        ds_shape = (B, bsnd_len, d // TILE) if per_tile else (B, bsnd_len)
+        dsall = torch.full(ds_shape, float("nan"), dtype=torch.float32, device=device)
     for b, s in enumerate(lengths):
         if s:
-            c, ds = quantize_rows_e4m3(_randn(gen, (int(s), d), device), TILE if per_tile else None)
+            c, ds = _encode_rows(_randn(gen, (int(s), d), device), kv_format, per_tile)
             codes[b, :s, 0] = c
-            dsall[b, :s] = ds
+            if ds is not None:
+                dsall[b, :s] = ds
     return codes, dsall
 
 
@@ -208,7 +270,8 @@ def make_custom(*, seed: int, q_lens: Sequence[int], ori_lens: Sequence[int],
                 return_lse: bool = False, device="cpu",
                 n1: int = N1_DEFAULT, d: int = D_DEFAULT,
                 pass_seqused_cmp: bool = True, pass_residual: bool = True,
-                q_descale_per_head: bool = True, name: str = "custom") -> Inputs:
+                q_descale_per_head: bool = True, q_format: str = "fp8", kv_format: str = "fp8",
+                name: str = "custom") -> Inputs:
     """General builder: explicit per-batch lengths, modes and (optional) index array.
 
     q_lens: per-batch query rows (TND span, or Q_S for every batch in BSND).
@@ -227,7 +290,9 @@ def make_custom(*, seed: int, q_lens: Sequence[int], ori_lens: Sequence[int],
     T1 = int(sum(q_lens))
     qv = _randn(gen, (T1, n1, d), device)
     q_codes, q_ds = quantize_rows_e4m3(qv)
-    if not q_descale_per_head:
+    if q_format == "bf16":
+        q_codes, q_ds = qv.to(torch.bfloat16), None
+    elif not q_descale_per_head:
         # one descale per token: re-quantise each token with its global amax
         amax = qv.abs().amax(dim=(1, 2))
         ds = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
@@ -236,23 +301,25 @@ def make_custom(*, seed: int, q_lens: Sequence[int], ori_lens: Sequence[int],
 
     sinks = _randn(gen, (n1,), device) if with_sinks else None
     out = dict(layout_q=layout_q, layout_kv=layout_kv, batch=B, q_s=q_s, sinks=sinks,
-               q=q_codes.contiguous(), q_descale=q_ds.contiguous(),
+               q=q_codes.contiguous(), q_descale=None if q_ds is None else q_ds.contiguous(),
                softmax_scale=float(softmax_scale), cmp_ratio=int(cmp_ratio),
                ori_mask_mode=ori_mask_mode, cmp_mask_mode=cmp_mask_mode,
                ori_win_left=win_left, ori_win_right=win_right,
-               kv_scale_mode=kv_scale_mode, return_lse=return_lse, name=name)
+               kv_scale_mode=kv_scale_mode, q_format=q_format, kv_format=kv_format,
+               return_lse=return_lse, name=name)
     if layout_q == "TND":
         out["cu_seqlens_q"] = _cu(q_lens).to(device)
     if seqused_q is not None:
         out["seqused_q"] = torch.as_tensor(np.asarray(seqused_q, dtype=np.int32), device=device)
 
     if layout_kv == "PA_BBND":
-        kv, kds, tab = _paged_cache(np_rng, gen, ori_lens, block_size, d, per_tile, spare_blocks, table_cols, device)
+        kv, kds, tab = _paged_cache(np_rng, gen, ori_lens, block_size, d, per_tile, spare_blocks, table_cols, device,
+                                    kv_format)
         out.update(ori_kv=kv, ori_kv_descale=kds, ori_block_table=tab)
         out["seqused_ori_kv"] = torch.as_tensor(np.asarray(ori_lens, dtype=np.int32), device=device)
     else:
         bs_len = max(ori_lens) if layout_kv == "BSND" else None
-        kv, kds = _contig_cache(gen, ori_lens, d, per_tile, device, bs_len)
+        kv, kds = _contig_cache(gen, ori_lens, d, per_tile, device, bs_len, kv_format)
         out.update(ori_kv=kv, ori_kv_descale=kds)
         if layout_kv == "TND":
             out["cu_seqlens_ori_kv"] = _cu(ori_lens).to(device)
@@ -262,11 +329,12 @@ def make_custom(*, seed: int, q_lens: Sequence[int], ori_lens: Sequence[int],
     if cmp_lens is not None:
         cbs = cmp_block_size or block_size
         if layout_kv == "PA_BBND":
-            ckv, cds, ctab = _paged_cache(np_rng, gen, cmp_lens, cbs, d, per_tile, spare_blocks, None, device)
+            ckv, cds, ctab = _paged_cache(np_rng, gen, cmp_lens, cbs, d, per_tile, spare_blocks, None, device,
+                                          kv_format)
             out.update(cmp_kv=ckv, cmp_kv_descale=cds, cmp_block_table=ctab)
         else:
             bs_len = max(max(cmp_lens), 1) if layout_kv == "BSND" else None
-            ckv, cds = _contig_cache(gen, cmp_lens, d, per_tile, device, bs_len)
+            ckv, cds = _contig_cache(gen, cmp_lens, d, per_tile, device, bs_len, kv_format)
             out.update(cmp_kv=ckv, cmp_kv_descale=cds)
             if layout_kv == "TND":
                 out["cu_seqlens_cmp_kv"] = _cu(cmp_lens).to(device)
