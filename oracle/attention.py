@@ -220,9 +220,9 @@ def dequant_rows(codes: np.ndarray, ds: np.ndarray, per_tile, rows: Sequence[int
     (KvQuantSparseAttnSharedkv, 约束说明: the 640-wide row)."""
     rows = np.asarray(rows, dtype=np.int64)
     if per_tile == "bf16":
-        return decode_bf16(codes[rows]).reshape(len(rows), -1)
+        return decode_bf16(codes[rows])
     if per_tile == "packed640":
-        return decode_packed640(codes[rows]).reshape(len(rows), -1)
+        return decode_packed640(codes[rows])
     vals = decode_e4m3(codes[rows])
     if per_tile:
         return vals * np.repeat(ds[rows].astype(np.float64), TILE, axis=-1)

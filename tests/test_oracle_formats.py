@@ -171,7 +171,8 @@ def _brute(inp, ori, cmp, res):
             for j in range(s2):
                 dk = j - (s2 - 1)
                 keys.append(K_o[j]); ok.append(0 <= dq - dk <= inp.ori_win_left)
-            for c in [int(x) for x in inp.cmp_sparse_indices[t, 0]]:
+            cand = range(C) if inp.cmp_sparse_indices is None else [int(x) for x in inp.cmp_sparse_indices[t, 0]]
+            for c in cand:
                 keys.append(K_c[c] if 0 <= c < C else torch.zeros(512, dtype=torch.float64))
                 ok.append(0 <= c < C and (c * r + r - 1) - (L - 1) <= dq)
             Q = inp.q[t].to(torch.float64)
@@ -215,3 +216,16 @@ def test_bf16_oracle_vs_sdpa_float64():
     ref = torch.nn.functional.scaled_dot_product_attention(
         Q.transpose(0, 1)[None], K[None, None], K[None, None], scale=0.05)[0].transpose(0, 1)
     _assert_close(res.out, ref.numpy(), 1e-12)
+
+
+@pytest.mark.parametrize("kv_format", ["bf16", "packed640"])
+def test_variant_empty_rows(kv_format):
+    """Rows that see no key (more query rows than kv tokens): O = 0 and lse =
+    the sink (QuantSparseFlashMla readings R8), in both formats."""
+    inp = make_custom(seed=209, q_lens=[9, 4], ori_lens=[5, 300], cmp_lens=[1, 75], cmp_ratio=4, residual=[1, 0],
+                      indices=None, n1=4, block_size=16, q_format="bf16", kv_format=kv_format, return_lse=True)
+    res = oracle_forward(inp)
+    assert np.all(res.out[0] == 0) and np.array_equal(res.lse[0], inp.sinks.double().numpy())
+    out, lse = _brute(inp, [5, 300], [1, 75], [1, 0])
+    _assert_close(res.out, out.numpy())
+    _assert_close(res.lse, lse.numpy())
