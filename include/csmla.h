@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSMLA_ABI_VERSION 1
+#define CSMLA_ABI_VERSION 2
 /* Size of the split plan (QuantSparseFlashMla, 约束说明: metadata shape [1024]). */
 #define CSMLA_METADATA_WORDS 1024
 
@@ -64,6 +64,22 @@ enum { CSMLA_MASK_NONE = 0, CSMLA_MASK_RIGHT_DOWN_CAUSAL = 3, CSMLA_MASK_BAND = 
  * per-token) or one per 64-wide slice of D (KvQuantSparseAttnSharedkv,
  * kv_quant_mode 1 per-tile with tile_size 64, here with fp32 scales). */
 enum { CSMLA_KV_SCALE_PER_TOKEN = 0, CSMLA_KV_SCALE_PER_TILE64 = 1 };
+/* q_dtype: fp8 e4m3 codes with fp32 q_descale (QuantSparseFlashMla), or bf16
+ * without a descale (KvQuantSparseAttnSharedkv and SparseCompressedFlashAttention,
+ * 参数说明: q BFLOAT16). */
+enum { CSMLA_Q_FP8 = 0, CSMLA_Q_BF16 = 1 };
+/* kv_dtype: rows of ori_kv / cmp_kv.
+ *   CSMLA_KV_FP8        d fp8 e4m3 codes per row, fp32 descales beside (kv_scale_mode)
+ *   CSMLA_KV_BF16       d bf16 values per row, no descales
+ *                       (SparseCompressedFlashAttention, 参数说明: ori_kv / cmp_kv bfloat16)
+ *   CSMLA_KV_PACKED640  640 bytes per row: 64 bf16 rope values, 448 e4m3 nope codes,
+ *                       7 e8m0 scales (one per 64 nope columns: value = code * 2^(E - 127),
+ *                       E = 255 is NaN), 57 pad bytes; the row's 512 logical columns are
+ *                       rope then nope (KvQuantSparseAttnSharedkv, 约束说明: D 640;
+ *                       参数说明: kv_quant_mode 1, tile_size 64, rope_head_dim 64)
+ * bf16 and packed rows need q_dtype CSMLA_Q_BF16 (the pages pair them with bf16 q);
+ * q's 512 columns pair with the logical columns in that order. */
+enum { CSMLA_KV_FP8 = 0, CSMLA_KV_BF16 = 1, CSMLA_KV_PACKED640 = 2 };
 
 /* Shapes and attributes; host values.  Field order is part of the ABI. */
 typedef struct {
@@ -97,6 +113,8 @@ typedef struct {
   int32_t q_descale_per_head; /* 1: q_descale [t1, n1]; 0: q_descale [t1] */
   int32_t topk_value_mode;    /* only 0: an index is a token position within its batch */
   int32_t return_softmax_lse; /* 1: write softmax_lse */
+  int32_t q_dtype;            /* CSMLA_Q_FP8 or CSMLA_Q_BF16 */
+  int32_t kv_dtype;           /* CSMLA_KV_FP8, CSMLA_KV_BF16 or CSMLA_KV_PACKED640 */
 } csmla_problem;
 
 /* Host copies of the length tensors, used by csmla_plan to balance work.
@@ -113,12 +131,14 @@ typedef struct {
 } csmla_host_lengths;
 
 /* Device pointers; contiguous row-major tensors in the pages' layouts.
- *   q                 fp8 e4m3 bytes [t1, n1, d]   (BSND [B, Q_S, n1, d] is the same memory)
- *   q_descale         f32 [t1, n1] or [t1]
+ *   q                 fp8 e4m3 bytes [t1, n1, d] (bf16 [t1, n1, d] with CSMLA_Q_BF16)
+ *                     (BSND [B, Q_S, n1, d] is the same memory)
+ *   q_descale         f32 [t1, n1] or [t1]; unused (may be NULL) with CSMLA_Q_BF16
  *   ori_kv / cmp_kv   fp8 e4m3 bytes: PA [blocks, block_size, 1, d]; TND [rows, 1, d];
  *                     BSND [B, S, 1, d]
  *   *_kv_descale      f32 per-token: PA [blocks, block_size], TND [rows], BSND [B, S];
- *                     per-tile64: the same with a trailing [d/64]
+ *                     per-tile64: the same with a trailing [d/64]; unused (may be NULL) with
+ *                     bf16 or packed rows (rows of 2 d or 640 bytes instead of d)
  *   cmp_sparse_indices int32 [t1, 1, topk]  (BSND [B, Q_S, 1, topk])
  *   *_block_table     int32 [B, *_table_cols] (PA)
  *   cu_seqlens_*      int32 [B+1]; seqused_*, cmp_residual_kv int32 [B];

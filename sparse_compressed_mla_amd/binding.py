@@ -32,7 +32,11 @@ class CsmlaProblem(ctypes.Structure):
         "ori_block_size", "cmp_block_size", "ori_num_blocks", "cmp_num_blocks",
         "ori_table_cols", "cmp_table_cols", "has_cmp", "topk")] + [("softmax_scale", ctypes.c_float)] + [
         (n, _i32) for n in ("cmp_ratio", "ori_mask_mode", "cmp_mask_mode", "ori_win_left", "ori_win_right",
-                            "kv_scale_mode", "q_descale_per_head", "topk_value_mode", "return_softmax_lse")]
+                            "kv_scale_mode", "q_descale_per_head", "topk_value_mode", "return_softmax_lse",
+                            "q_dtype", "kv_dtype")]
+
+Q_DTYPES = {"fp8": 0, "bf16": 1}
+KV_DTYPES = {"fp8": 0, "bf16": 1, "packed640": 2}
 
 
 class CsmlaHostLengths(ctypes.Structure):
@@ -215,7 +219,9 @@ def problem_from(inp) -> CsmlaProblem:
     p.ori_win_left = int(inp.ori_win_left) if inp.ori_mask_mode == 4 else -1
     p.ori_win_right = int(inp.ori_win_right) if inp.ori_mask_mode == 4 else -1
     p.kv_scale_mode = int(inp.kv_scale_mode)
-    p.q_descale_per_head = 1 if inp.q_descale.dim() == 2 else 0
+    p.q_descale_per_head = 1 if (inp.q_descale is not None and inp.q_descale.dim() == 2) else 0
+    p.q_dtype = Q_DTYPES[getattr(inp, "q_format", "fp8")]
+    p.kv_dtype = KV_DTYPES[getattr(inp, "kv_format", "fp8")]
     p.topk_value_mode = 0
     p.return_softmax_lse = 1 if inp.return_lse else 0
     return p

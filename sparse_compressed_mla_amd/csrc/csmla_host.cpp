@@ -246,6 +246,17 @@ csmla_status csmla_validate(const csmla_problem* p) {
     return fail(CSMLA_ERR_INVALID_ARG, "kv_scale_mode must be 0 or 1");
   if (p->topk_value_mode != 0) return fail(CSMLA_ERR_UNSUPPORTED, "only topk_value_mode 0 is built");
   if (!(std::isfinite(p->softmax_scale))) return fail(CSMLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (p->q_dtype != CSMLA_Q_FP8 && p->q_dtype != CSMLA_Q_BF16) return fail(CSMLA_ERR_INVALID_ARG, "q_dtype must be 0 or 1");
+  if (p->kv_dtype != CSMLA_KV_FP8 && p->kv_dtype != CSMLA_KV_BF16 && p->kv_dtype != CSMLA_KV_PACKED640)
+    return fail(CSMLA_ERR_INVALID_ARG, "kv_dtype must be 0, 1 or 2");
+  if (p->kv_dtype != CSMLA_KV_FP8 && p->q_dtype != CSMLA_Q_BF16)
+    return fail(CSMLA_ERR_INVALID_ARG, "bf16 and packed KV rows go with bf16 q");
+  if (p->q_dtype == CSMLA_Q_BF16 && p->kv_dtype == CSMLA_KV_FP8)
+    return fail(CSMLA_ERR_UNSUPPORTED, "bf16 q with fp8 KV and fp32 descales is not built");
+  if (p->kv_dtype != CSMLA_KV_FP8 && p->kv_scale_mode != CSMLA_KV_SCALE_PER_TOKEN)
+    return fail(CSMLA_ERR_INVALID_ARG, "kv_scale_mode applies to fp8 KV only (leave it 0)");
+  if (p->kv_dtype != CSMLA_KV_FP8 && p->topk > kListMax)
+    return fail(CSMLA_ERR_UNSUPPORTED, "bf16 / packed KV: at most %d index slots per row are built", kListMax);
   g_last_error.clear();
   return CSMLA_OK;
 }
@@ -300,9 +311,11 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   // and per-tile descales keep the key split up to 256 tokens.
   // Prefill-sized batches (more tokens than CUs) with at most kListMax index
   // slots per token: whole tokens per unit, no splits.
-  const bool pf_ok = p->topk <= kListMax;
+  const bool pf_ok = p->topk <= kListMax && p->kv_dtype == CSMLA_KV_FP8;
+  const bool bf = p->kv_dtype != CSMLA_KV_FP8;   // the bf16-q kernel: key splits of <= kBkMaxUnitKeys keys
+  if (bf) S = std::max<int64_t>(S, (max_n + kBkMaxUnitKeys - 1) / kBkMaxUnitKeys);
   int hg = 0;
-  if (p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN && avg <= 8192) {
+  if (!bf && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN && avg <= 8192) {
     if (T1 * (kN1 / 8) <= kMaxGrid) hg = 8;
     else if (T1 <= 128 || (T1 <= 256 && !pf_ok)) hg = 16;
     else if (pf_ok) hg = kN1;
@@ -315,7 +328,7 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   const int64_t t_rounds = (T1 + 7) / 8;
   const int64_t sk_min = std::max<int64_t>(1, (max_n + kSkKeys - 1) / kSkKeys);
   const int64_t sk_max = std::min<int64_t>(kMaxGrid / (8 * t_rounds), kSkMaxSplits);
-  const bool sk_ok = pf_ok && T1 <= kSkMaxTokens && sk_min <= sk_max;
+  const bool sk_ok = pf_ok && T1 <= kSkMaxTokens && sk_min <= sk_max;   // (pf_ok: fp8 KV)
   bool sk = false;
   if (const char* env = std::getenv("CSMLA_KERNEL")) {   // tuning / test override
     if (!std::strcmp(env, "split")) hg = 0;
@@ -330,6 +343,11 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
       const int64_t f = std::atoll(env);
       if (f >= 1) S = std::min(std::max(f, sk_min), sk_max);
     }
+  }
+  if (bf) {   // every override keeps the bf16-q kernel (only CSMLA_SPLITS applies)
+    hg = 0;
+    sk = false;
+    S = std::max<int64_t>(S, (max_n + kBkMaxUnitKeys - 1) / kBkMaxUnitKeys);
   }
   if (hg > 0) S = 1;
   if (S > kMaxSplits) return fail(CSMLA_ERR_UNSUPPORTED, "a token needs %lld splits; at most %d are built", (long long)S, kMaxSplits);
@@ -396,10 +414,12 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
   csmla_status st = csmla_validate(p);
   if (st != CSMLA_OK) return st;
   if (!t) return fail(CSMLA_ERR_INVALID_ARG, "tensors is NULL");
-  if (!t->q || !t->q_descale) return fail(CSMLA_ERR_INVALID_ARG, "q and q_descale are required");
-  if (!t->ori_kv || !t->ori_kv_descale) return fail(CSMLA_ERR_INVALID_ARG, "ori_kv and ori_kv_descale are required");
-  if (p->has_cmp && (!t->cmp_kv || !t->cmp_kv_descale))
-    return fail(CSMLA_ERR_INVALID_ARG, "has_cmp needs cmp_kv and cmp_kv_descale");
+  const bool fp8q = p->q_dtype == CSMLA_Q_FP8, fp8kv = p->kv_dtype == CSMLA_KV_FP8;
+  if (!t->q || (fp8q && !t->q_descale)) return fail(CSMLA_ERR_INVALID_ARG, "q (and with fp8 q, q_descale) required");
+  if (!t->ori_kv || (fp8kv && !t->ori_kv_descale))
+    return fail(CSMLA_ERR_INVALID_ARG, "ori_kv (and with fp8 KV, ori_kv_descale) required");
+  if (p->has_cmp && (!t->cmp_kv || (fp8kv && !t->cmp_kv_descale)))
+    return fail(CSMLA_ERR_INVALID_ARG, "has_cmp needs cmp_kv (and with fp8 KV, cmp_kv_descale)");
   if (p->topk > 0 && !t->cmp_sparse_indices) return fail(CSMLA_ERR_INVALID_ARG, "topk > 0 needs cmp_sparse_indices");
   if (p->layout_q == CSMLA_LAYOUT_TND && !t->cu_seqlens_q) return fail(CSMLA_ERR_INVALID_ARG, "TND q needs cu_seqlens_q");
   if (p->layout_kv == CSMLA_LAYOUT_PA_BBND) {
@@ -425,6 +445,7 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
   a.win_right = p->ori_mask_mode == CSMLA_MASK_BAND ? p->ori_win_right : -1;
   a.scale_mode = p->kv_scale_mode; a.q_ds_per_head = p->q_descale_per_head; a.ret_lse = p->return_softmax_lse;
   a.n1 = p->n1;
+  a.kv_fmt = p->kv_dtype;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   a.q = (const uint8_t*)t->q; a.q_ds = t->q_descale;
   a.ori_kv = (const uint8_t*)t->ori_kv; a.ori_ds = t->ori_kv_descale;
@@ -485,10 +506,10 @@ csmla_status csmla_forward(const csmla_problem* p, const csmla_tensors* t, const
   // pointers at the half's first head and the token stride of n1 heads.
   for (int h0 = 0; h0 < p->n1; h0 += kN1) {
     KArgs ah = a;
-    ah.q = a.q + (size_t)h0 * kD;
+    ah.q = a.q + (size_t)h0 * kD * (p->q_dtype == CSMLA_Q_BF16 ? 2 : 1);
     ah.out = a.out + (size_t)h0 * kD;
     if (a.lse) ah.lse = a.lse + h0;
-    if (a.q_ds_per_head) ah.q_ds = a.q_ds + h0;
+    if (a.q_ds && a.q_ds_per_head) ah.q_ds = a.q_ds + h0;
     if (a.sinks) ah.sinks = a.sinks + h0;
     const int e = launch_forward(ah, stream);
     if (e != 0) return fail(CSMLA_ERR_HIP, "kernel launch failed (hipError %d)", e);

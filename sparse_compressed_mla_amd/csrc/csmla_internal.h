@@ -28,6 +28,7 @@ enum {
 // buffer serves plans of any size), then per-unit XCD ids, the partial
 // outputs and their (max, sum).
 constexpr int kSkMaxTokens = 256;                          // tokens the split-key decode kernel takes
+constexpr int kBkMaxUnitKeys = 1024;                       // keys per unit of the bf16-q kernel
 constexpr size_t kWsSyncBytes = (size_t)kSkMaxTokens * 4 * 4;
 
 // Everything one kernel launch needs, passed by value in the kernarg segment:
@@ -56,6 +57,7 @@ struct KHdr {
   int32_t splits, n_units, grid;
   int32_t hg;                       // > 0: head-split kernel with groups of hg heads (8 or 16)
   int32_t sk;                       // 1: split-key decode kernel (64 heads, <= 128 keys per unit, in-kernel merge)
+  int32_t kv_fmt;                   // 0: fp8 rows + descales; 1: bf16 rows; 2: packed 640-byte rows (bf16 q for 1, 2)
 };
 
 struct KArgs : KHdr {

@@ -78,7 +78,7 @@ typedef const __attribute__((address_space(4))) KArgs* KArgPtr;
 
 // Source of the rows of key slots past the end of a chunk: the gather always
 // issues the same number of loads per wave, so that the pipeline can count them.
-__device__ __attribute__((aligned(4096))) uint8_t g_zero_row[kD];
+__device__ __attribute__((aligned(4096))) uint8_t g_zero_row[2 * kD];   // covers a bf16 row too
 
 // Work-group barrier that orders LDS only: outstanding global loads (the
 // next tiles' gathers, stores of a finished unit) stay in flight across it.
@@ -2946,6 +2946,349 @@ sk_kernel(const KArgs a) {
   sk_body<PER_TILE>((KArgPtr)__builtin_amdgcn_kernarg_segment_ptr(), smem, w);
 }
 
+// ---------------------------------------------------------------------------
+// bf16-q kernel: bf16 q against bf16 KV rows (SparseCompressedFlashAttention,
+// 函数原型 / 参数说明: q, ori_kv, cmp_kv bfloat16, D = 512) or against packed
+// 640-byte rows (KvQuantSparseAttnSharedkv, 约束说明: bf16 rope 64, e4m3 nope
+// 448, seven e8m0 scales, pad; 参数说明: q bfloat16, tile_size 64).  One work
+// unit = (query token, key split), all 64 heads; the split partials go to the
+// split-KV combine, as with the key-split fp8 kernel.
+// ---------------------------------------------------------------------------
+//
+// 4 waves.  Per 32-key tile: every thread loads a block of 8 keys x 8 columns
+// (bf16 rows: 16 bytes per key; packed rows: the rope bytes, or 8 nope codes
+// and their tile's scale byte), turns it into bf16 (nope: e4m3 x 2^(E - 127),
+// exact) and writes it twice to LDS: as K [key][d] rows and, transposed in
+// registers, as V^T [d][key] rows.  The next tile's loads are in flight while
+// the current tile is computed.
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16: wave w scores the 32 keys against
+//                 heads [32 (w & 1), +32) over D half w >> 1 (q in VGPRs); the
+//                 half-1 partial is added through LDS
+//   softmax       online, in log2 units, per head (the D-half-0 waves)
+//   O^T += V^T P^T  same MFMA: wave w owns output columns [128 w, +128) of all
+//                 64 heads; P in bf16
+// LDS rows are XOR-swizzled by 16-byte chunk so that 16 lanes reading the
+// same chunk of 16 rows hit different banks.
+
+constexpr int kBkKeys = 32;          // keys per tile
+constexpr int kBkMaxKeys = 1024;     // keys per unit, resolved at once
+constexpr int kBkThreads = 256;
+
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+
+struct LdsBK {
+  static constexpr int kK = 0;                               // bf16 [32 keys][512]: 1 KiB rows, chunk ^ (key & 15)
+  static constexpr int kVT = kK + kBkKeys * 2 * kD;          // bf16 [512 d][32 keys]: 64-byte rows, chunk ^ ((d >> 2) & 3)
+  static constexpr int kP = kVT + kD * kBkKeys * 2;          // bf16 [64 heads][32 keys]: chunk ^ ((h >> 2) & 3)
+  static constexpr int kX = kP + kN1 * kBkKeys * 2;          // f32 [2 head blocks][64 lanes][16]: D-half-1 partials
+  static constexpr int kAddr = kX + 2 * 64 * 16 * 4;         // u64 [kBkMaxKeys]: the unit's row addresses
+  static constexpr int kList = kAddr + 8 * kBkMaxKeys;       // int [kListMax]: compacted cmp indices
+  static constexpr int kAlpha = kList + 4 * kListMax;        // f32 [64]: this tile's rescale per head
+  static constexpr int kM = kAlpha + 4 * kN1;                // f32 [64]: final maximum per head
+  static constexpr int kL = kM + 4 * kN1;                    // f32 [64]: final row sum per head
+  static constexpr int kMisc = kL + 4 * kN1;                 // int [64]: compaction
+  static constexpr int kBytes = kMisc + 4 * 64;
+};
+static_assert(LdsBK::kBytes <= 160 * 1024, "LDS");
+
+__device__ __forceinline__ v16f mma_bf16(bf8_t a, bf8_t b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The tile's raw bytes of one thread: keys 8 kq + j (j < 8) of the tile,
+// columns 8 dq .. 8 dq + 7.
+struct BkRaw {
+  v4i x[8];     // bf16 / rope: 8 bf16; nope: x[j].xy = 8 e4m3 codes
+  int sc[8];    // nope: the dword holding the column tile's e8m0 scale
+};
+
+template <int FMT>
+__device__ __forceinline__ BkRaw bk_load(const uint64_t* kaddr, int tile, int tid) {
+  const int kq = tid >> 6, dq = tid & 63;
+  BkRaw r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint8_t* row = gptr(reinterpret_cast<const uint8_t*>(kaddr[kBkKeys * tile + 8 * kq + j]));
+    if (FMT == 1 || dq < 8) {
+      r.x[j] = *(const v4i*)(row + 16 * dq);
+      r.sc[j] = 0;
+    } else {
+      const int nb = 8 * dq - 64;                       // nope column of the block's first value
+      const v2i c = *(const v2i*)(row + 128 + nb);
+      r.x[j] = v4i{c[0], c[1], 0, 0};
+      r.sc[j] = *(const int*)(row + 576 + 4 * ((nb >> 6) >> 2));
+    }
+  }
+  return r;
+}
+
+// bf16 of 8 e4m3 codes times 2^(E - 127) (E = 255: NaN), exact.
+__device__ __forceinline__ v4i bk_nope8(v4i x, int scw, int tile) {
+  const uint32_t e = ((uint32_t)scw >> (8 * (tile & 3))) & 0xffu;
+  const float sc = (e == 255u) ? __builtin_nanf("") : ((e == 0u) ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23));
+  const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(x[0], false);
+  const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(x[0], true);
+  const auto f45 = __builtin_amdgcn_cvt_pk_f32_fp8(x[1], false);
+  const auto f67 = __builtin_amdgcn_cvt_pk_f32_fp8(x[1], true);
+  return v4i{(int)pack_bf16x2(f01[0] * sc, f01[1] * sc), (int)pack_bf16x2(f23[0] * sc, f23[1] * sc),
+             (int)pack_bf16x2(f45[0] * sc, f45[1] * sc), (int)pack_bf16x2(f67[0] * sc, f67[1] * sc)};
+}
+
+// The block as bf16 into the K rows and, transposed, into the V^T rows.
+template <int FMT>
+__device__ __forceinline__ void bk_store(const BkRaw& r, uint8_t* smem, int tid) {
+  const int kq = tid >> 6, dq = tid & 63;
+  v4i v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (FMT == 2 && dq >= 8) ? bk_nope8(r.x[j], r.sc[j], (8 * dq - 64) >> 6) : r.x[j];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int key = 8 * kq + j;
+    *(v4i*)(smem + LdsBK::kK + key * 2 * kD + 16 * (dq ^ (key & 15))) = v[j];
+  }
+  // V^T row d = 8 dq + i holds keys 8 kq .. +7: the 16-bit element i of each
+  // key's block (low halves for even i, high halves for odd i)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+    v4i o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      o[p] = (int)__builtin_amdgcn_perm((uint32_t)v[2 * p + 1][i >> 1], (uint32_t)v[2 * p][i >> 1], sel);
+    const int d = 8 * dq + i;
+    *(v4i*)(smem + LdsBK::kVT + d * 64 + 16 * (kq ^ ((d >> 2) & 3))) = o;
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void bk_body(KArgPtr ap, uint8_t* smem, int w) {
+  using L = LdsBK;
+  constexpr int ROW = (FMT == 1) ? 2 * kD : 640;   // bytes per cache row
+  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5;
+  const int hb = w & 1, dh = w >> 1;
+  const HdrRegs hr = load_hdr_regs(ap);
+  const KHdr a0 = hdr_view(hr);
+  const int G = a0.grid, bid = blockIdx.x;
+  const int lw = (G % 8 == 0) ? ((bid & 7) * (G >> 3) + (bid >> 3)) : bid;  // one XCD per contiguous range
+  int u_begin = lw, u_end = lw + 1;
+  if (a0.n_units != G) {
+    u_begin = ap->starts[lw];
+    u_end = ap->starts[lw + 1];
+  }
+  int* list = reinterpret_cast<int*>(smem + L::kList);
+  int* misc = reinterpret_cast<int*>(smem + L::kMisc);
+  uint64_t* kaddr = reinterpret_cast<uint64_t*>(smem + L::kAddr);
+  float* alpha_s = reinterpret_cast<float*>(smem + L::kAlpha);
+  float* m_s = reinterpret_cast<float*>(smem + L::kM);
+  float* l_s = reinterpret_cast<float*>(smem + L::kL);
+  float* xch = reinterpret_cast<float*>(smem + L::kX) + (hb * 64 + lane) * 16;
+
+  for (int u = u_begin; u < u_end; ++u) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the previous unit's stores settle here
+    const KHdr a = hdr_view(hr);
+    const int tid = opaque((int)threadIdx.x);
+    const int S = a.splits;
+    const int t = (S == 1) ? u : u / S, sp = u - t * S;
+    const int hq = 32 * hb + (lane & 31);   // the lane's head in S^T and the softmax
+    // prologue loads: lengths, index slots, the q fragments (B operands of
+    // S^T: head hq, columns 256 dh + 16 ks + 8 g .. +7)
+    const TokLens tl = token_lens(a, t);
+    const IdxPre<kBkThreads> ip = load_indices<kBkThreads>(a, t, 0);
+    bf8_t qf[16];
+    {
+      const uint8_t* qrow = a.q + (((size_t)t * a.n1 + hq) * kD + 256 * dh + 8 * g) * 2;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf8_t, *(const v4i*)(qrow + 32 * ks));
+    }
+    const Tok k = token_ctx(a, t, tl);
+    if (!k.valid) {   // padded query row: O = 0, lse = -inf
+      if (S == 1) {
+        for (int x = tid; x < kN1 * kD / 8; x += kBkThreads)
+          *(v4i*)(a.out + ((size_t)t * a.n1 + x / (kD / 8)) * kD + 8 * (x % (kD / 8))) = v4i{0, 0, 0, 0};
+        if (a.lse && tid < kN1) a.lse[(size_t)t * a.n1 + tid] = kNegInf;
+      } else if (tid < kN1) {
+        a.ws_ml[((size_t)u * kN1 + tid) * 2] = kNegInf;
+        a.ws_ml[((size_t)u * kN1 + tid) * 2 + 1] = -1.0f;   // marks a padded row for the combine
+      }
+      continue;
+    }
+    const int n_o = k.hi - k.lo;
+    int n_c = 0;
+    if (a.topk > 0) n_c = compact_indices<kBkThreads>(a, k, t, list, misc, 0, ip);
+    else if (a.has_cmp) n_c = k.vis;
+    const int64_t n = (int64_t)n_o + n_c;
+    const int kb = (int)(n * sp / S), ke = (int)(n * (sp + 1) / S);
+    const bool over = ke - kb > kBkMaxKeys;    // the plan's key bound was exceeded: poison, never drop keys
+    const int nk = min(ke - kb, kBkMaxKeys);
+    const int tiles = (nk + kBkKeys - 1) / kBkKeys;
+
+    // ---- the unit's row addresses (the split kernels' resolution functions);
+    // slots past the unit's end read the zero row ----
+    {
+      const Sides sd = cache_sides(a);
+      for (int i = tid; i < tiles * kBkKeys; i += kBkThreads) {
+        const bool ok = i < nk;
+        bool is_cmp;
+        const int j = key_pos(a, k, n_o, kb + (ok ? i : 0), list, 0, is_cmp);
+        BlockPos bp{0, 0};
+        if (a.layout_kv == 2) bp = block_pos(sd, is_cmp, j);
+        const int blk = (a.layout_kv == 2) ? block_of(sd, k, is_cmp, bp.q) : 0;
+        const int64_t row = row_of(a, sd, k, is_cmp, j, blk, bp.r);
+        const uint8_t* src = (is_cmp ? sd.c.kv : sd.o.kv) + row * ROW;
+        kaddr[i] = (uint64_t)(uintptr_t)(ok ? src : g_zero_row);
+      }
+    }
+    lds_barrier();
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) acc[db][x] = v16f{};
+    float mrun = kNegInf, lrun = 0.f;   // the D-half-0 waves: head hq
+    BkRaw raw;
+    if (tiles > 0) raw = bk_load<FMT>(kaddr, 0, tid);
+    for (int it = 0; it < tiles; ++it) {
+      bk_store<FMT>(raw, smem, tid);
+      if (it + 1 < tiles) raw = bk_load<FMT>(kaddr, it + 1, tid);   // in flight during this tile
+      lds_barrier();
+      // ---- S^T: keys x heads [32 hb, +32), D half dh ----
+      v16f Sx = v16f{};
+      {
+        const int key = lane & 31;
+        const uint8_t* krow = smem + L::kK + key * 2 * kD;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          const int c = 32 * dh + 2 * ks + g;
+          const bf8_t av = __builtin_bit_cast(bf8_t, *(const v4i*)(krow + 16 * (c ^ (key & 15))));
+          Sx = mma_bf16(av, qf[ks], Sx);
+        }
+      }
+      if (dh) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) *(v4f*)(xch + 4 * q4) = v4f{Sx[4 * q4], Sx[4 * q4 + 1], Sx[4 * q4 + 2], Sx[4 * q4 + 3]};
+      }
+      lds_barrier();
+      if (dh == 0) {
+        const int nv = min(kBkKeys, nk - kBkKeys * it);
+        float E[16];
+        float mx = kNegInf;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const v4f o = *(const v4f*)(xch + 4 * q4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = 8 * q4 + 4 * g + r;
+            E[4 * q4 + r] = (key < nv) ? (Sx[4 * q4 + r] + o[r]) * a.scale_log2 : kNegInf;
+            mx = fmaxf(mx, E[4 * q4 + r]);
+          }
+        }
+        mx = xor32_reduce(mx, true);
+        const float mnew = fmaxf(mrun, mx);
+        const float al = (mrun == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
+        const float mz = (mnew == kNegInf) ? 0.f : mnew;
+        float ps = 0.f;
+        uint8_t* prow = smem + L::kP + hq * 64;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float p[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(E[4 * q4 + r] - mz);
+            ps += p[r];
+          }
+          *(uint2*)(prow + 16 * (q4 ^ ((hq >> 2) & 3)) + 8 * g) = pack_bf16x4(p[0], p[1], p[2], p[3]);
+        }
+        ps = xor32_reduce(ps, false);
+        lrun = al * lrun + ps;
+        mrun = mnew;
+        if (g == 0) alpha_s[hq] = al;
+      }
+      lds_barrier();
+      // ---- O^T += V^T P^T: columns [128 w, +128), all 64 heads ----
+      {
+        float al[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) al[x] = alpha_s[32 * x + (lane & 31)];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int x = 0; x < 2; ++x) acc[db][x] *= al[x];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int c = 2 * ks + g;
+          bf8_t pb[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int h = 32 * x + (lane & 31);
+            pb[x] = __builtin_bit_cast(bf8_t, *(const v4i*)(smem + L::kP + h * 64 + 16 * (c ^ ((h >> 2) & 3))));
+          }
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const int d = 128 * w + 32 * db + (lane & 31);
+            const bf8_t va = __builtin_bit_cast(bf8_t, *(const v4i*)(smem + L::kVT + d * 64 + 16 * (c ^ ((d >> 2) & 3))));
+#pragma unroll
+            for (int x = 0; x < 2; ++x) acc[db][x] = mma_bf16(va, pb[x], acc[db][x]);
+          }
+        }
+      }
+      lds_barrier();   // K, V^T and P are read before the next tile overwrites them
+    }
+
+    // ---- epilogue: the final result (one split) or the unit's partial ----
+    if (dh == 0 && g == 0) {
+      m_s[hq] = mrun;
+      l_s[hq] = lrun;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int h = 32 * x + (lane & 31);
+      const float M = m_s[h], Ls = l_s[h];
+      float sc;
+      uint16_t* orow;
+      if (S == 1) {
+        const float sg = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+        const float Mf = fmaxf(M, sg);
+        float lse_v = kNegInf;
+        sc = 0.f;
+        if (Mf != kNegInf) {
+          const float af = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - Mf);
+          const float Lf = af * Ls + ((sg == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sg - Mf));
+          sc = af / Lf;
+          lse_v = (Mf + __log2f(Lf)) * kLn2;
+        }
+        if (over) { sc = __builtin_nanf(""); lse_v = sc; }
+        if (a.lse && w == 0 && g == 0) a.lse[(size_t)t * a.n1 + h] = lse_v;
+        orow = a.out + ((size_t)t * a.n1 + h) * kD;
+      } else {
+        sc = (Ls > 0.f) ? 1.0f / Ls : 0.f;
+        if (over) sc = __builtin_nanf("");
+        if (w == 0 && g == 0) {
+          a.ws_ml[((size_t)u * kN1 + h) * 2] = M;
+          a.ws_ml[((size_t)u * kN1 + h) * 2 + 1] = Ls;
+        }
+        orow = a.ws_o + ((size_t)u * kN1 + h) * kD;
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const v16f& o = acc[db][x];
+          *(uint2*)(orow + 128 * w + 32 * db + 8 * q4 + 4 * g) =
+              pack_bf16x4(sc * o[4 * q4], sc * o[4 * q4 + 1], sc * o[4 * q4 + 2], sc * o[4 * q4 + 3]);
+        }
+    }
+  }
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(kBkThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) bk_kernel(const KArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LdsBK::kBytes];
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  bk_body<FMT>((KArgPtr)__builtin_amdgcn_kernarg_segment_ptr(), smem, w);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -3018,8 +3361,34 @@ int noalloc_scratch(void** ptr, void* stream) {
   return 0;
 }
 
+// Blocks of the split-KV combine (XCD-local token ranges when the grid is a
+// multiple of 8).
+static int combine_blocks(const KArgs& a) {
+  int blocks = a.t1 * 8;
+  if (a.grid % 8 == 0) {
+    int most = 0;
+    for (int x = 0; x < 8; ++x) {
+      int t0, t1;
+      xcd_tokens(a, x, t0, t1);
+      most = std::max(most, t1 - t0);
+    }
+    blocks = 8 * 8 * most;
+  }
+  return blocks;
+}
+
 int launch_forward(const KArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (a.kv_fmt != 0) {
+    if (a.kv_fmt == 1)
+      hipLaunchKernelGGL(bk_kernel<1>, dim3(a.grid), dim3(kBkThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(bk_kernel<2>, dim3(a.grid), dim3(kBkThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits == 1) return (int)e;
+    hipLaunchKernelGGL(combine_kernel, dim3(combine_blocks(a)), dim3(256), 0, st, a);
+    return (int)hipGetLastError();
+  }
   if (a.sk) {
     if (a.scale_mode == 1)
       hipLaunchKernelGGL(sk_kernel<1>, dim3(a.grid), dim3(kPfThreads), 0, st, a);
@@ -3045,16 +3414,7 @@ int launch_forward(const KArgs& a, void* stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   if (a.splits > 1) {
-    int blocks = a.t1 * 8;
-    if (a.grid % 8 == 0) {
-      int most = 0;
-      for (int x = 0; x < 8; ++x) {
-        int t0, t1;
-        xcd_tokens(a, x, t0, t1);
-        most = std::max(most, t1 - t0);
-      }
-      blocks = 8 * 8 * most;
-    }
+    const int blocks = combine_blocks(a);
     if (blocks > 0) hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, st, a);
     e = hipGetLastError();
   }

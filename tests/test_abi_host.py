@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert m.csmla_abi_version() == 1
+    assert m.csmla_abi_version() == 2
     assert m.csmla_metadata_words() == 1024
     for s in range(6):
         assert m.csmla_status_string(s)
@@ -86,6 +86,15 @@ def base_problem(**kw):
     (dict(kv_scale_mode=2), INVALID),
     (dict(topk_value_mode=1), UNSUPPORTED),
     (dict(softmax_scale=float("inf")), INVALID),
+    (dict(q_dtype=1, kv_dtype=1), OK),          # bf16 q and KV (SparseCompressedFlashAttention)
+    (dict(q_dtype=1, kv_dtype=2), OK),          # bf16 q, packed 640-byte rows (KvQuantSparseAttnSharedkv)
+    (dict(q_dtype=0, kv_dtype=1), INVALID),     # bf16 / packed rows pair with bf16 q
+    (dict(q_dtype=0, kv_dtype=2), INVALID),
+    (dict(q_dtype=1, kv_dtype=0), UNSUPPORTED), # bf16 q with fp8 rows and fp32 descales: not built
+    (dict(q_dtype=2), INVALID),
+    (dict(q_dtype=1, kv_dtype=3), INVALID),
+    (dict(q_dtype=1, kv_dtype=2, kv_scale_mode=1), INVALID),   # scales live in the packed row
+    (dict(q_dtype=1, kv_dtype=1, topk=2048), UNSUPPORTED),     # the bf16-q kernel keeps <= 1024 slots
 ])
 def test_validation_matrix(kw, status):
     assert m.csmla_validate(base_problem(**kw)) == status, m.csmla_last_error()
@@ -136,7 +145,7 @@ def test_plan_invariants_and_determinism(monkeypatch):
     monkeypatch.setenv("CSMLA_KERNEL", "split")
     p = base_problem()
     _, md, ws = m.csmla_plan(p)
-    assert md[0] == 0x4C4D5343 and md[1] == 1
+    assert md[0] == 0x4C4D5343 and md[1] == 2
     S, U, G = md[5], md[6], md[7]
     assert U == 32 * S and 1 <= G <= 256 and G <= U
     starts = md[16:16 + G + 1]
@@ -296,3 +305,20 @@ def test_plan_split_key_decode(monkeypatch):
     bad = m.csmla_plan(p)[1].copy()
     bad[7] = 128                                        # grid no longer 8 S ceil(T1 / 8)
     assert m.csmla_forward(p, fake_tensors(ws), bad, raise_on_error=False) == MISMATCH
+
+
+def test_plan_bf16_q_kernels(monkeypatch):
+    """bf16 q with bf16 or packed rows: key splits (the bf16-q kernel and the
+    combine) whatever kernel override is set, at most 1024 keys per unit."""
+    for env in (None, "heads8", "prefill", "splitkey"):
+        if env is None:
+            monkeypatch.delenv("CSMLA_KERNEL", raising=False)
+        else:
+            monkeypatch.setenv("CSMLA_KERNEL", env)
+        for kv in (1, 2):
+            _, md, ws = m.csmla_plan(base_problem(q_dtype=1, kv_dtype=kv))
+            assert md[12] == 0 and md[13] == 0 and md[5] >= 1
+            _, md, _ = m.csmla_plan(base_problem(q_dtype=1, kv_dtype=kv, batch=1, t1=1, ori_mask_mode=0,
+                                                 ori_win_left=-1, ori_win_right=-1, topk=0,
+                                                 ori_table_cols=40, cmp_table_cols=10))
+            assert md[5] >= 3                       # up to 5120 + 1280 keys: >= 7 units of <= 1024 ... per token
