@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0   # dense fp8 MFMA, MI355X
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
+# bytes of one KV row the method reads: fp8 codes + a 4-byte descale; a bf16
+# row; a packed row's rope, nope and scale bytes (its 57 pad bytes are not read)
+ROW_BYTES = {"fp8": 512 + 4, "bf16": 1024, "packed640": 128 + 448 + 7}
 METRIC = "CSA decode query-tokens/s + effective KV HBM GB/s (% roofline), 1 MI355X"
 
 
@@ -69,6 +73,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of each oracle timing sample (one thread, then all threads)")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--kv-format", choices=["fp8", "bf16", "packed640"], default="fp8",
+                    help="KV rows of the attention workloads: fp8 with descales (q fp8), or bf16 / packed "
+                         "640-byte rows (q bf16)")
     ap.add_argument("--workload", choices=["csa_decode", "csa_prefill", "swa_tiny", "hca_decode", "csa_mtp",
                                            "idx_csa_decode", "idx_csa_mtp_long", "idx_csa_prefill"],
                     default="csa_decode",
@@ -239,7 +246,10 @@ def timed_graph_steps(m, torch, plan, tens, dev, steps, warmup):
     return start.elapsed_time(stop), t_plan, max(1, steps // L)
 
 
-def kernel_name(plan):
+def kernel_name(plan, fmt="fp8"):
+    if fmt != "fp8":
+        return f"bk_kernel<{fmt}> (bf16 q, {plan.splits} key splits)" + (" + combine_kernel" if plan.splits > 1
+                                                                          else "")
     if plan.split_key:
         return f"sk_kernel (split-key decode: 64 heads, {plan.splits} key splits per token, in-kernel merge)"
     if plan.head_group == 64:
@@ -272,6 +282,9 @@ def rotated(args, m, make_config, torch, np):
     torch.cuda.set_device(dev)
     k = ROTATED[args.workload]
     kw = {"batch": args.batch} if k in (2, 3, 4) and args.batch else {}
+    fmt = args.kv_format
+    if fmt != "fp8":
+        kw.update(q_format="bf16", kv_format=fmt)
     print(f"[bench] building inputs: {args.workload} {kw}", file=sys.stderr, flush=True)
     inp = make_config(k, device=dev, **kw)
     T1 = inp.t1
@@ -286,18 +299,20 @@ def rotated(args, m, make_config, torch, np):
         compare(o.float().cpu().numpy(), ref.out, toks, name="bench precheck", verbose=False)
         print("[bench] parity precheck ok", file=sys.stderr, flush=True)
     pairs, uniq = unique_rows(m, inp, np, torch)
-    kv_bytes = uniq * (512 + 4)
+    kv_bytes = uniq * ROW_BYTES[fmt]
     out_bytes = T1 * 64 * 512 * 2
-    other_bytes = T1 * 64 * (512 + 4) + out_bytes + 4 * inp.topk * T1
+    q_bytes = T1 * 64 * (512 + 4) if fmt == "fp8" else T1 * 64 * 512 * 2
+    other_bytes = q_bytes + out_bytes + 4 * inp.topk * T1
     pool = sum(x.numel() * x.element_size() for x in (inp.ori_kv, inp.ori_kv_descale, inp.cmp_kv, inp.cmp_kv_descale)
                if x is not None)
     L = max(2, min(args.layers, int(args.copy_budget_gb * 1e9 // pool)))
     layers = [inp]
     for l in range(1, L):
         c = redraw_query_side(inp, k, l)
-        c.ori_kv, c.ori_kv_descale = inp.ori_kv.clone(), inp.ori_kv_descale.clone()
+        cl = lambda x: None if x is None else x.clone()
+        c.ori_kv, c.ori_kv_descale = cl(inp.ori_kv), cl(inp.ori_kv_descale)
         if inp.cmp_kv is not None:
-            c.cmp_kv, c.cmp_kv_descale = inp.cmp_kv.clone(), inp.cmp_kv_descale.clone()
+            c.cmp_kv, c.cmp_kv_descale = cl(inp.cmp_kv), cl(inp.cmp_kv_descale)
         layers.append(c)
     print(f"[bench] {L} layers resident: KV pools {L * pool / 1e9:.1f} GB, {kv_bytes / 1e6:.2f} MB of KV rows "
           f"touched per step", file=sys.stderr, flush=True)
@@ -313,13 +328,14 @@ def rotated(args, m, make_config, torch, np):
     fwd_ms = total_ms / K
     value = T1 * K / (total_ms / 1e3)
     achieved = kv_bytes / (fwd_ms / 1e3) / 1e9
-    kern = kernel_name(plan)
+    kern = kernel_name(plan, fmt)
     print(f"[bench] {args.workload}: forward {fwd_ms * 1e3:.2f} us per step over {K} steps (graphs over {L} "
           f"layers); {kern}, grid {plan.grid}; plan {1e6 * t_plan / passes:.0f} us host per pass",
           file=sys.stderr, flush=True)
-    headline = args.workload == "csa_decode"
+    headline = args.workload == "csa_decode" and fmt == "fp8"
+    wname = args.workload if fmt == "fp8" else f"{args.workload}_{fmt}"
     res = {
-        "metric": METRIC if headline else f"{args.workload} query-tokens/s + effective KV HBM GB/s, 1 MI355X",
+        "metric": METRIC if headline else f"{wname} query-tokens/s + effective KV HBM GB/s, 1 MI355X",
         "value": round(value, 1),
         "unit": "query-tokens/s",
         "n_gpus": 1,
@@ -329,9 +345,12 @@ def rotated(args, m, make_config, torch, np):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 (fp32 accumulate)",
+        "dtype": "fp8e4m3 (fp32 accumulate)" if fmt == "fp8" else
+                 ("bf16 q and KV (fp32 accumulate)" if fmt == "bf16" else
+                  "bf16 q, packed rows: bf16 rope + e4m3 nope x e8m0 scales, as bf16 (fp32 accumulate)"),
         "data": f"synthetic, seeded (workloads.make_config({k}); layers 1.. redraw q and indices)",
-        "config": dict({"workload": args.workload, "batch": inp.batch, "n1": 64, "d": 512, "block_size": 128,
+        "config": dict({"workload": wname, "batch": inp.batch, "n1": 64, "d": 512, "block_size": 128,
+                        "kv_format": fmt,
                         "layers_rotated": L, "splits": plan.splits, "grid": plan.grid,
                         "head_group": plan.head_group}, **CONFIG_TEXT[k]),
         "effective_kv_gbs": round(achieved, 1),
@@ -342,13 +361,13 @@ def rotated(args, m, make_config, torch, np):
         "plan_host_us": round(1e6 * t_plan / passes, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload), "kernel": kern},
+                     "traffic": measured_traffic(wname), "kernel": kern},
     }
     if not args.no_cpu_baseline:
         from oracle import oracle_forward
         cpu = inp.to("cpu")
         res["cpu_baseline"] = cpu_baseline(lambda t: oracle_forward(cpu, [t]), T1, args.cpu_seconds,
-                                           "query-tokens/s", f"{args.workload} query tokens")
+                                           "query-tokens/s", f"{wname} query tokens")
     print(json.dumps(res), flush=True)
 
 
@@ -360,8 +379,10 @@ def prefill(args, m, make_config, torch, np):
     token of the batch, so no layer rotation: the bound is the matrix cores."""
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print("[bench] building inputs: csa_prefill", file=sys.stderr, flush=True)
-    inp = make_config(5, device=dev)
+    fmt = args.kv_format
+    kw = {} if fmt == "fp8" else dict(q_format="bf16", kv_format=fmt)
+    print(f"[bench] building inputs: csa_prefill {kw}", file=sys.stderr, flush=True)
+    inp = make_config(5, device=dev, **kw)
     T1 = inp.t1
     if not args.no_parity:
         from oracle import oracle_forward
@@ -397,23 +418,27 @@ def prefill(args, m, make_config, torch, np):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
     tflops = flops / (ms / 1e3) / 1e12
+    peak = FP8_PEAK_TFLOPS if fmt == "fp8" else BF16_PEAK_TFLOPS
     print(f"[bench] prefill forward {ms * 1e3:.1f} us, {pairs} pairs, {tflops:.1f} TFLOP/s; "
           f"splits {plan.splits} grid {plan.grid} head_group {plan.head_group}", file=sys.stderr, flush=True)
     res = {
-        "metric": "CSA prefill query-tokens/s + fp8 MFMA TFLOP/s (% dense peak), 1 MI355X",
+        "metric": ("CSA prefill query-tokens/s + fp8 MFMA TFLOP/s (% dense peak), 1 MI355X" if fmt == "fp8" else
+                   f"CSA prefill ({fmt} KV, bf16 q) query-tokens/s + bf16 MFMA TFLOP/s (% dense peak), 1 MI355X"),
         "value": round(T1 / (ms / 1e3), 1), "unit": "query-tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warm, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8e4m3 S^T, f16 P V (fp32 accumulate)" if plan.head_group == 64
-                  else "fp8e4m3 (fp32 accumulate)"),
+        "dtype": ("fp8e4m3 S^T, f16 P V (fp32 accumulate)" if plan.head_group == 64 and fmt == "fp8"
+                  else "fp8e4m3 (fp32 accumulate)" if fmt == "fp8" else "bf16 (fp32 accumulate)"),
         "data": "synthetic, seeded (workloads.make_config(5))",
-        "config": {"workload": "csa_prefill", "batch": 4, "q_tokens_per_batch": 4096, "n1": 64, "d": 512,
-                   "band": 128, "cmp_ratio": 4, "topk": 512, "kv_scale": "per-tile-64", "lse": True,
+        "config": {"workload": "csa_prefill" if fmt == "fp8" else f"csa_prefill_{fmt}", "batch": 4,
+                   "q_tokens_per_batch": 4096, "n1": 64, "d": 512, "band": 128, "cmp_ratio": 4, "topk": 512,
+                   "kv_scale": "per-tile-64" if fmt == "fp8" else fmt, "lse": True,
                    "splits": plan.splits, "grid": plan.grid},
         "pairs_per_step": pairs,
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": ("pf_kernel<1> (whole-token prefill: fp8 S^T, f16 P V, per-tile descales)"
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "kernel": (kernel_name(plan, fmt) if fmt != "fp8" else
+                                "pf_kernel<1> (whole-token prefill: fp8 S^T, f16 P V, per-tile descales)"
                                 if plan.head_group == 64 else
                                 "attn_kernel<1> (split attention, per-tile descales)")},
     }

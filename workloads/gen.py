@@ -361,9 +361,15 @@ def _uniform_draw(rng, hi: int, k: int) -> np.ndarray:
     return rng.choice(hi, size=k, replace=False).astype(np.int32)
 
 
-def _swa_tiny(seed, device):
+def _fmt(kw):
+    """The q / KV format keywords of a config (fp8 by default); the per-tile
+    descale mode applies to fp8 rows only."""
+    return dict(q_format=kw.get("q_format", "fp8"), kv_format=kw.get("kv_format", "fp8"))
+
+
+def _swa_tiny(seed, device, **fmt):
     return make_custom(seed=seed, q_lens=[4, 4], ori_lens=[300, 200], layout_q="TND",
-                       spare_blocks=3, return_lse=True, device=device, name="swa_tiny")
+                       spare_blocks=3, return_lse=True, device=device, name="swa_tiny", **_fmt(fmt))
 
 
 def _csa_decode_indices(rng, batch, c, topk):
@@ -372,17 +378,17 @@ def _csa_decode_indices(rng, batch, c, topk):
     return np.stack([_uniform_draw(rng, c, topk) for _ in range(batch)])
 
 
-def _csa_decode(seed, device, batch=32, s2=8192, topk=512, layout_q="BSND"):
+def _csa_decode(seed, device, batch=32, s2=8192, topk=512, layout_q="BSND", **fmt):
     rng = np.random.default_rng(10_000 + seed)
     ratio = 4
     c = s2 // ratio
     idx = _csa_decode_indices(rng, batch, c, topk)
     return make_custom(seed=seed, q_lens=[1] * batch, ori_lens=[s2] * batch, layout_q=layout_q,
                        cmp_lens=[c] * batch, cmp_ratio=ratio, residual=[0] * batch,
-                       indices=idx, spare_blocks=8, device=device, name="csa_decode")
+                       indices=idx, spare_blocks=8, device=device, name="csa_decode", **_fmt(fmt))
 
 
-def _hca_decode(seed, device, batch=32, lo=32768, hi=65536):
+def _hca_decode(seed, device, batch=32, lo=32768, hi=65536, **fmt):
     rng = np.random.default_rng(10_000 + seed)
     ratio = 128
     lens = rng.integers(lo, hi + 1, size=batch)
@@ -390,7 +396,7 @@ def _hca_decode(seed, device, batch=32, lo=32768, hi=65536):
     res = [int(x) % ratio for x in lens]
     return make_custom(seed=seed, q_lens=[1] * batch, ori_lens=[int(x) for x in lens], layout_q="BSND",
                        cmp_lens=cmp, cmp_ratio=ratio, residual=res, indices=None,
-                       table_cols=hi // 128, spare_blocks=8, device=device, name="hca_decode")
+                       table_cols=hi // 128, spare_blocks=8, device=device, name="hca_decode", **_fmt(fmt))
 
 
 def _csa_mtp_indices(rng, lens, s_q, ratio, topk, recent):
@@ -413,7 +419,7 @@ def _csa_mtp_indices(rng, lens, s_q, ratio, topk, recent):
     return np.stack(rows)
 
 
-def _csa_mtp(seed, device, batch=64, lo=65536, hi=131072, topk=512, recent=256):
+def _csa_mtp(seed, device, batch=64, lo=65536, hi=131072, topk=512, recent=256, **fmt):
     rng = np.random.default_rng(10_000 + seed)
     ratio = 4
     s_q = 2
@@ -423,10 +429,10 @@ def _csa_mtp(seed, device, batch=64, lo=65536, hi=131072, topk=512, recent=256):
     rows = _csa_mtp_indices(rng, lens, s_q, ratio, topk, recent)
     return make_custom(seed=seed, q_lens=[s_q] * batch, ori_lens=[int(x) for x in lens], layout_q="BSND",
                        cmp_lens=cmp, cmp_ratio=ratio, residual=res, indices=rows,
-                       table_cols=hi // 128, spare_blocks=8, device=device, name="csa_mtp_long")
+                       table_cols=hi // 128, spare_blocks=8, device=device, name="csa_mtp_long", **_fmt(fmt))
 
 
-def _csa_prefill(seed, device, batch=4, s=4096, topk=512):
+def _csa_prefill(seed, device, batch=4, s=4096, topk=512, **fmt):
     rng = np.random.default_rng(10_000 + seed)
     ratio = 4
     c = s // ratio
@@ -438,7 +444,8 @@ def _csa_prefill(seed, device, batch=4, s=4096, topk=512):
             rows[b * s + p, :k] = _uniform_draw(rng, vis, k)
     return make_custom(seed=seed, q_lens=[s] * batch, ori_lens=[s] * batch, layout_q="TND",
                        cmp_lens=[c] * batch, cmp_ratio=ratio, residual=[0] * batch, indices=rows,
-                       kv_scale_mode=1, spare_blocks=4, return_lse=True, device=device, name="csa_prefill")
+                       kv_scale_mode=1 if _fmt(fmt)["kv_format"] == "fp8" else 0, spare_blocks=4,
+                       return_lse=True, device=device, name="csa_prefill", **_fmt(fmt))
 
 
 def redraw_query_side(inp: Inputs, k: int, draw: int) -> Inputs:
@@ -451,8 +458,11 @@ def redraw_query_side(inp: Inputs, k: int, draw: int) -> Inputs:
     gen = torch.Generator(device=dev)
     gen.manual_seed(7_000_003 * (draw + 1) + k)
     qv = _randn(gen, tuple(inp.q.shape), dev)
-    q_codes, q_ds = quantize_rows_e4m3(qv)
-    out = replace(inp, q=q_codes.contiguous(), q_descale=q_ds.contiguous())
+    if inp.q_format == "bf16":
+        out = replace(inp, q=qv.to(torch.bfloat16).contiguous(), q_descale=None)
+    else:
+        q_codes, q_ds = quantize_rows_e4m3(qv)
+        out = replace(inp, q=q_codes.contiguous(), q_descale=q_ds.contiguous())
     if inp.cmp_sparse_indices is None:
         return out
     rng = np.random.default_rng(20_000 + 1000 * k + draw)
