@@ -43,6 +43,12 @@ Readings of points the pages leave open:
      64 rope columns first, then the 448 nope columns; the output keeps that
      order.  There are no q or KV descales: the nope scales live in the row.
   R11 bf16 q and bf16 KV (SparseCompressedFlashAttention): values as stored.
+  R12 ori_sparse_indices (QuantSparseFlashMla, 参数说明: indices into ori_kv,
+     -1 invalid; ori_topk_length: the slots in effect): when given, the ori
+     part of K~ is the listed logical positions in slot order (duplicates
+     kept, -1 and out-of-range entries skipped) that the ori mask and window
+     also admit, the same rule as for the compressed side (R5); without them
+     it is the whole window.
 """
 from __future__ import annotations
 
@@ -170,7 +176,16 @@ def token_rows(inp, t: int, tt=None) -> List[Tuple[int, int]]:
     rows = []
     p = bl["s2"] - bl["s1"] + i
     lo, hi = ori_window(p, bl["s2"], inp.ori_mask_mode, inp.ori_win_left, inp.ori_win_right)
-    for j in range(lo, hi):
+    ori_idx = getattr(inp, "ori_sparse_indices", None)
+    if ori_idx is None:
+        ori_cand = range(lo, hi)
+    else:
+        slots = _np(ori_idx)[t, 0]
+        k1 = len(slots)
+        if getattr(inp, "ori_topk_length", None) is not None:
+            k1 = max(0, min(k1, int(_np(inp.ori_topk_length)[t])))
+        ori_cand = [int(x) for x in slots[:k1] if lo <= int(x) < hi]
+    for j in ori_cand:
         rows.append((KIND_ORI, _phys_row(inp, "ori", b, j, bl)))
     if inp.cmp_kv is not None:
         p_cmp = bl["L"] - bl["s1"] + i

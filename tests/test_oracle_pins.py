@@ -11,6 +11,7 @@
   order, block placement, split-merge algebra)
 """
 import json
+from dataclasses import replace
 import math
 import os
 
@@ -157,7 +158,14 @@ def _brute_force(inp, s2_of=None, c_of=None, r_of=None):
             Q = _dec_torch(inp.q[t]) * (qs[:, None] if qs.ndim == 1 else qs)
             keys, ok = [], []
             dq = i - (s1 - 1)          # offset of this row from the last query row
-            for j in range(s2):
+            ori_list = getattr(inp, "ori_sparse_indices", None)
+            if ori_list is None:
+                ori_cand = range(s2)
+            else:   # the listed slots, each one key (checked against the mask below)
+                ori_cand = [int(x) for x in ori_list[t, 0]]
+                if getattr(inp, "ori_topk_length", None) is not None:
+                    ori_cand = ori_cand[:max(0, int(inp.ori_topk_length[t]))]
+            for j in ori_cand:
                 dk = j - (s2 - 1)      # offset of kv token j from the last kv token
                 m = inp.ori_mask_mode
                 if m == 0:
@@ -167,7 +175,8 @@ def _brute_force(inp, s2_of=None, c_of=None, r_of=None):
                 else:
                     vis = (inp.ori_win_left < 0 or dq - dk <= inp.ori_win_left) and \
                           (inp.ori_win_right < 0 or dk - dq <= inp.ori_win_right)
-                keys.append(ori[j])
+                vis = vis and 0 <= j < s2
+                keys.append(ori[j] if 0 <= j < s2 else torch.zeros(d, dtype=torch.float64))
                 ok.append(vis)
             if inp.cmp_kv is not None:
                 def cvis(c):
@@ -568,3 +577,63 @@ def test_work_counts_cfg2_shape():
     wc = work_counts(inp, res.rows)
     assert wc["pairs"] == 2 * 640 and wc["unique_rows"] == 2 * 640
     assert wc["kv_bytes"] == 2 * 640 * 516
+
+
+# ---------------------------------------------------------------- ori_sparse_indices
+
+def _ori_idx_case(seed, k1=48, mode=4, wl=30, wr=5, with_len=True):
+    rng = np.random.default_rng(seed)
+    q_lens, ori = [3, 4], [260, 120]
+    cmp = [o // 4 for o in ori]
+    T1 = sum(q_lens)
+    oidx = rng.integers(-3, max(ori) + 4, size=(T1, k1))
+    oidx[rng.random(oidx.shape) < 0.15] = -1
+    oidx[0, 1:4] = oidx[0, 0]                     # duplicates are separate keys
+    cidx = rng.integers(-1, max(cmp) + 2, size=(T1, 16))
+    return make_custom(seed=seed, q_lens=q_lens, ori_lens=ori, cmp_lens=cmp, cmp_ratio=4,
+                       residual=[o % 4 for o in ori], indices=cidx, n1=4, d=128, block_size=16,
+                       ori_mask_mode=mode, win_left=wl, win_right=wr, ori_indices=oidx,
+                       ori_topk_length=rng.integers(0, k1 + 3, size=T1) if with_len else None, return_lse=True)
+
+
+@pytest.mark.parametrize("seed,kw", [
+    (91, dict()),
+    (92, dict(mode=3, wl=-1, wr=-1)),
+    (93, dict(mode=0, wl=-1, wr=-1, with_len=False)),
+    (94, dict(mode=4, wl=-1, wr=0, k1=300)),
+])
+def test_ori_indices_vs_brute_force(seed, kw):
+    """ori_sparse_indices (QuantSparseFlashMla, 参数说明; reading R12): the
+    listed positions in slot order that the ori mask admits, -1 and
+    out-of-range slots skipped, duplicates kept, the first ori_topk_length
+    slots only; the brute force checks each listed slot against the mask
+    cell by cell."""
+    inp = _ori_idx_case(seed, **kw)
+    res = oracle_forward(inp)
+    out, lse = _brute_force(inp)
+    _assert_close(res.out, out.numpy())
+    _assert_close(res.lse, lse.numpy())
+
+
+def test_ori_indices_listing_the_window_equals_no_indices():
+    """Listing exactly the window's positions (in order, then -1) reproduces
+    the window without indices; all -1 leaves only the compressed keys."""
+    inp = _ori_idx_case(95, with_len=False)
+    base = replace(inp, ori_sparse_indices=None, ori_topk_length=None)
+    want = oracle_forward(base)
+    tt = token_table(base)
+    rows = []
+    for t, (b, i) in enumerate(tt):
+        bl = batch_lengths(base, b)
+        lo, hi = ori_window(bl["s2"] - bl["s1"] + i, bl["s2"], base.ori_mask_mode, base.ori_win_left,
+                            base.ori_win_right)
+        r = np.full(80, -1)
+        r[:hi - lo] = np.arange(lo, hi)
+        rows.append(r)
+    listed = replace(base, ori_sparse_indices=torch.as_tensor(np.stack(rows)[:, None, :].astype(np.int32)))
+    got = oracle_forward(listed)
+    _assert_close(got.out, want.out, 0.0)
+    _assert_close(got.lse, want.lse, 0.0)
+    none = replace(base, ori_sparse_indices=torch.full((base.t1, 1, 8), -1, dtype=torch.int32))
+    r0 = oracle_forward(none)
+    assert all(all(k == 1 for k, _ in r0.rows[t]) for t in range(base.t1))

@@ -59,6 +59,8 @@ class Inputs:
     cmp_kv: Optional[torch.Tensor] = None
     cmp_kv_descale: Optional[torch.Tensor] = None
     cmp_sparse_indices: Optional[torch.Tensor] = None
+    ori_sparse_indices: Optional[torch.Tensor] = None   # int32 [T1, 1, K1]: listed ori positions (-1 invalid)
+    ori_topk_length: Optional[torch.Tensor] = None      # int32 [T1]
     ori_block_table: Optional[torch.Tensor] = None
     cmp_block_table: Optional[torch.Tensor] = None
     cu_seqlens_q: Optional[torch.Tensor] = None
@@ -271,6 +273,7 @@ def make_custom(*, seed: int, q_lens: Sequence[int], ori_lens: Sequence[int],
                 n1: int = N1_DEFAULT, d: int = D_DEFAULT,
                 pass_seqused_cmp: bool = True, pass_residual: bool = True,
                 q_descale_per_head: bool = True, q_format: str = "fp8", kv_format: str = "fp8",
+                ori_indices: Optional[np.ndarray] = None, ori_topk_length: Optional[Sequence[int]] = None,
                 name: str = "custom") -> Inputs:
     """General builder: explicit per-batch lengths, modes and (optional) index array.
 
@@ -311,6 +314,11 @@ def make_custom(*, seed: int, q_lens: Sequence[int], ori_lens: Sequence[int],
         out["cu_seqlens_q"] = _cu(q_lens).to(device)
     if seqused_q is not None:
         out["seqused_q"] = torch.as_tensor(np.asarray(seqused_q, dtype=np.int32), device=device)
+    if ori_indices is not None:
+        out["ori_sparse_indices"] = torch.as_tensor(np.asarray(ori_indices, dtype=np.int32).reshape(T1, 1, -1),
+                                                    device=device)
+    if ori_topk_length is not None:
+        out["ori_topk_length"] = torch.as_tensor(np.asarray(ori_topk_length, dtype=np.int32), device=device)
 
     if layout_kv == "PA_BBND":
         kv, kds, tab = _paged_cache(np_rng, gen, ori_lens, block_size, d, per_tile, spare_blocks, table_cols, device,
