@@ -115,6 +115,12 @@ typedef struct {
   int32_t return_softmax_lse; /* 1: write softmax_lse */
   int32_t q_dtype;            /* CSMLA_Q_FP8 or CSMLA_Q_BF16 */
   int32_t kv_dtype;           /* CSMLA_KV_FP8, CSMLA_KV_BF16 or CSMLA_KV_PACKED640 */
+  int32_t ori_topk;           /* K1 = slots per row of ori_sparse_indices; 0: no ori indices (the
+                                 whole window).  With them the ori keys are the listed positions
+                                 in slot order that the ori mask and window admit (-1 and
+                                 out-of-range slots skipped, duplicates kept); ori_topk + topk
+                                 <= 1024 (QuantSparseFlashMla, 参数说明: ori_sparse_indices,
+                                 ori_topk_length) */
 } csmla_problem;
 
 /* Host copies of the length tensors, used by csmla_plan to balance work.
@@ -128,6 +134,7 @@ typedef struct {
   const int32_t* cu_seqlens_cmp_kv; /* [B+1] (TND kv) */
   const int32_t* cmp_residual_kv;   /* [B] */
   const int32_t* cmp_topk_length;   /* [t1] */
+  const int32_t* ori_topk_length;   /* [t1] */
 } csmla_host_lengths;
 
 /* Device pointers; contiguous row-major tensors in the pages' layouts.
@@ -143,6 +150,8 @@ typedef struct {
  *   *_block_table     int32 [B, *_table_cols] (PA)
  *   cu_seqlens_*      int32 [B+1]; seqused_*, cmp_residual_kv int32 [B];
  *   cmp_topk_length   int32 [t1]
+ *   ori_sparse_indices int32 [t1, 1, ori_topk] (listed logical ori positions; -1 invalid)
+ *   ori_topk_length   int32 [t1] (slots in effect per row; NULL: all ori_topk)
  *   sinks             f32 [n1] (NULL: no sink)
  *   attn_out          bf16 [t1, n1, d]
  *   softmax_lse       f32 [t1, n1] (TND [1, t1, n1]; BSND [B, 1, Q_S, n1])
@@ -173,6 +182,8 @@ typedef struct {
   float*         softmax_lse;
   void*          workspace;
   size_t         workspace_bytes;
+  const int32_t* ori_sparse_indices;
+  const int32_t* ori_topk_length;
 } csmla_tensors;
 
 /* ABI version of the loaded library (CSMLA_ABI_VERSION). */

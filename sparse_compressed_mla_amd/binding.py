@@ -33,7 +33,7 @@ class CsmlaProblem(ctypes.Structure):
         "ori_table_cols", "cmp_table_cols", "has_cmp", "topk")] + [("softmax_scale", ctypes.c_float)] + [
         (n, _i32) for n in ("cmp_ratio", "ori_mask_mode", "cmp_mask_mode", "ori_win_left", "ori_win_right",
                             "kv_scale_mode", "q_descale_per_head", "topk_value_mode", "return_softmax_lse",
-                            "q_dtype", "kv_dtype")]
+                            "q_dtype", "kv_dtype", "ori_topk")]
 
 Q_DTYPES = {"fp8": 0, "bf16": 1}
 KV_DTYPES = {"fp8": 0, "bf16": 1, "packed640": 2}
@@ -42,7 +42,7 @@ KV_DTYPES = {"fp8": 0, "bf16": 1, "packed640": 2}
 class CsmlaHostLengths(ctypes.Structure):
     _fields_ = [(n, _p) for n in (
         "cu_seqlens_q", "seqused_q", "seqused_ori_kv", "cu_seqlens_ori_kv", "seqused_cmp_kv",
-        "cu_seqlens_cmp_kv", "cmp_residual_kv", "cmp_topk_length")]
+        "cu_seqlens_cmp_kv", "cmp_residual_kv", "cmp_topk_length", "ori_topk_length")]
 
 
 TENSOR_FIELDS = ("q", "q_descale", "ori_kv", "ori_kv_descale", "cmp_kv", "cmp_kv_descale", "cmp_sparse_indices",
@@ -51,8 +51,12 @@ TENSOR_FIELDS = ("q", "q_descale", "ori_kv", "ori_kv_descale", "cmp_kv", "cmp_kv
                  "attn_out", "softmax_lse", "workspace")
 
 
+TENSOR_FIELDS_TAIL = ("ori_sparse_indices", "ori_topk_length")
+
+
 class CsmlaTensors(ctypes.Structure):
-    _fields_ = [(n, _p) for n in TENSOR_FIELDS] + [("workspace_bytes", ctypes.c_size_t)]
+    _fields_ = ([(n, _p) for n in TENSOR_FIELDS] + [("workspace_bytes", ctypes.c_size_t)]
+                + [(n, _p) for n in TENSOR_FIELDS_TAIL])
 
 
 class CsmlaError(RuntimeError):
@@ -222,13 +226,15 @@ def problem_from(inp) -> CsmlaProblem:
     p.q_descale_per_head = 1 if (inp.q_descale is not None and inp.q_descale.dim() == 2) else 0
     p.q_dtype = Q_DTYPES[getattr(inp, "q_format", "fp8")]
     p.kv_dtype = KV_DTYPES[getattr(inp, "kv_format", "fp8")]
+    oi = getattr(inp, "ori_sparse_indices", None)
+    p.ori_topk = 0 if oi is None else int(oi.shape[-1])
     p.topk_value_mode = 0
     p.return_softmax_lse = 1 if inp.return_lse else 0
     return p
 
 
 _LEN_NAMES = ("cu_seqlens_q", "seqused_q", "seqused_ori_kv", "cu_seqlens_ori_kv", "seqused_cmp_kv",
-              "cu_seqlens_cmp_kv", "cmp_residual_kv", "cmp_topk_length")
+              "cu_seqlens_cmp_kv", "cmp_residual_kv", "cmp_topk_length", "ori_topk_length")
 
 
 def host_lengths_from(inp):
@@ -248,7 +254,7 @@ def host_lengths_from(inp):
 def tensors_from(inp, out, lse, workspace=None) -> CsmlaTensors:
     """Device pointers of the inputs (attributes of `inp`) and the outputs."""
     t = CsmlaTensors()
-    for n in TENSOR_FIELDS:
+    for n in TENSOR_FIELDS + TENSOR_FIELDS_TAIL:
         if n in ("attn_out", "softmax_lse", "workspace"):
             continue
         v = getattr(inp, n, None)

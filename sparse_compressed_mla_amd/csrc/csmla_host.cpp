@@ -101,6 +101,12 @@ std::vector<TokCost> token_costs(const csmla_problem* p, const csmla_host_length
           hi = std::max(hi, lo);
         }
         tc.n_o = hi - lo;
+        if (p->ori_topk > 0) {   // listed ori positions: at most the slots in effect
+          int64_t k = p->ori_topk;
+          const int64_t t = q0 + i;
+          if (h.ori_topk_length && t < p->t1) k = std::max<int64_t>(0, std::min<int64_t>(k, h.ori_topk_length[t]));
+          tc.n_o = tc.n_o > 0 ? k : 0;   // duplicates may list a window position more than once
+        }
         if (p->has_cmp) {
           int64_t vis = c;
           if (p->cmp_mask_mode == CSMLA_MASK_RIGHT_DOWN_CAUSAL)
@@ -138,6 +144,7 @@ uint32_t lengths_hash(const csmla_problem* p, const csmla_host_lengths* hl) {
   mix(hl->cu_seqlens_cmp_kv, B + 1, 6);
   mix(hl->cmp_residual_kv, B, 7);
   mix(hl->cmp_topk_length, p->t1, 8);
+  mix(hl->ori_topk_length, p->t1, 9);
   return h & 0x7fffffffu;
 }
 
@@ -257,6 +264,9 @@ csmla_status csmla_validate(const csmla_problem* p) {
     return fail(CSMLA_ERR_INVALID_ARG, "kv_scale_mode applies to fp8 KV only (leave it 0)");
   if (p->kv_dtype != CSMLA_KV_FP8 && p->topk > kListMax)
     return fail(CSMLA_ERR_UNSUPPORTED, "bf16 / packed KV: at most %d index slots per row are built", kListMax);
+  if (p->ori_topk < 0) return fail(CSMLA_ERR_INVALID_ARG, "ori_topk must be >= 0");
+  if (p->ori_topk > 0 && (int64_t)p->ori_topk + p->topk > kListMax)
+    return fail(CSMLA_ERR_UNSUPPORTED, "ori_topk + topk must be <= %d (one index list per row)", kListMax);
   g_last_error.clear();
   return CSMLA_OK;
 }
@@ -344,6 +354,10 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
       if (f >= 1) S = std::min(std::max(f, sk_min), sk_max);
     }
   }
+  if (p->ori_topk > 0) {   // listed ori keys: the key-split kernels (fp8 or bf16-q) only
+    hg = 0;
+    sk = false;
+  }
   if (bf) {   // every override keeps the bf16-q kernel (only CSMLA_SPLITS applies)
     hg = 0;
     sk = false;
@@ -421,6 +435,8 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
   if (p->has_cmp && (!t->cmp_kv || (fp8kv && !t->cmp_kv_descale)))
     return fail(CSMLA_ERR_INVALID_ARG, "has_cmp needs cmp_kv (and with fp8 KV, cmp_kv_descale)");
   if (p->topk > 0 && !t->cmp_sparse_indices) return fail(CSMLA_ERR_INVALID_ARG, "topk > 0 needs cmp_sparse_indices");
+  if (p->ori_topk > 0 && !t->ori_sparse_indices)
+    return fail(CSMLA_ERR_INVALID_ARG, "ori_topk > 0 needs ori_sparse_indices");
   if (p->layout_q == CSMLA_LAYOUT_TND && !t->cu_seqlens_q) return fail(CSMLA_ERR_INVALID_ARG, "TND q needs cu_seqlens_q");
   if (p->layout_kv == CSMLA_LAYOUT_PA_BBND) {
     if (!t->seqused_ori_kv || !t->ori_block_table)
@@ -446,6 +462,9 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
   a.scale_mode = p->kv_scale_mode; a.q_ds_per_head = p->q_descale_per_head; a.ret_lse = p->return_softmax_lse;
   a.n1 = p->n1;
   a.kv_fmt = p->kv_dtype;
+  a.ori_topk = p->ori_topk;
+  a.ori_idx = p->ori_topk > 0 ? t->ori_sparse_indices : nullptr;
+  a.ori_tkl = p->ori_topk > 0 ? t->ori_topk_length : nullptr;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   a.q = (const uint8_t*)t->q; a.q_ds = t->q_descale;
   a.ori_kv = (const uint8_t*)t->ori_kv; a.ori_ds = t->ori_kv_descale;
@@ -464,9 +483,11 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
     if ((uint32_t)md[MD_PROBLEM_HASH] != problem_hash(p) || md[MD_T1] != p->t1)
       return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was planned for a different problem");
     const int S = md[MD_SPLITS], U = md[MD_UNITS], G = md[MD_GRID], HG = md[MD_HEAD_GROUP], SK = md[MD_SPLIT_KEY];
-    const bool hg_ok = HG == 0 || ((HG == 8 || HG == 16) && S == 1 && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN) ||
-                       (HG == kN1 && S == 1 && p->topk <= kListMax);
-    const bool sk_ok = SK == 0 || (SK == 1 && HG == 0 && S <= kSkMaxSplits && p->t1 <= kSkMaxTokens &&
+    const bool hg_ok = HG == 0 || (p->ori_topk == 0 && p->kv_dtype == CSMLA_KV_FP8 &&
+                                   (((HG == 8 || HG == 16) && S == 1 && p->kv_scale_mode == CSMLA_KV_SCALE_PER_TOKEN) ||
+                                    (HG == kN1 && S == 1 && p->topk <= kListMax)));
+    const bool sk_ok = SK == 0 || (SK == 1 && HG == 0 && p->ori_topk == 0 && p->kv_dtype == CSMLA_KV_FP8 &&
+                                   S <= kSkMaxSplits && p->t1 <= kSkMaxTokens &&
                                    p->topk <= kListMax && G == 8 * S * ((p->t1 + 7) / 8) && G <= kMaxGrid);
     const int per_token = HG > 0 ? kN1 / HG : S;
     if (S < 1 || !hg_ok || !sk_ok || U != p->t1 * per_token || G < 1 || G > kMaxGrid || (!SK && G > U))
@@ -550,6 +571,8 @@ static csmla_status debug_resolve(const csmla_problem* p, const csmla_tensors* t
   csmla_status st = build_args(p, t, nullptr, a, false);
   if (st != CSMLA_OK) return st;
   if (!keys || !counts || max_keys < 0) return fail(CSMLA_ERR_INVALID_ARG, "keys/counts buffers are required");
+  if (whole_token && p->ori_topk > 0)
+    return fail(CSMLA_ERR_UNSUPPORTED, "the whole-token kernel takes no ori_sparse_indices");
   if (whole_token && p->topk > kListMax)
     return fail(CSMLA_ERR_UNSUPPORTED, "the whole-token kernel keeps at most %d index slots (topk %d)", kListMax,
                 p->topk);

@@ -58,6 +58,8 @@ struct KHdr {
   int32_t hg;                       // > 0: head-split kernel with groups of hg heads (8 or 16)
   int32_t sk;                       // 1: split-key decode kernel (64 heads, <= 128 keys per unit, in-kernel merge)
   int32_t kv_fmt;                   // 0: fp8 rows + descales; 1: bf16 rows; 2: packed 640-byte rows (bf16 q for 1, 2)
+  int32_t ori_topk;                 // > 0: the ori keys are listed in ori_idx [t1][ori_topk]
+  const int32_t* ori_idx; const int32_t* ori_tkl;
 };
 
 struct KArgs : KHdr {

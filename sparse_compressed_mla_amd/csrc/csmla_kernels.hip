@@ -155,6 +155,7 @@ __device__ __forceinline__ KHdr hdr_view(HdrRegs r) {
   CSMLA_GLOBAL(cu_q); CSMLA_GLOBAL(cu_ori); CSMLA_GLOBAL(cu_cmp); CSMLA_GLOBAL(su_q); CSMLA_GLOBAL(su_ori);
   CSMLA_GLOBAL(su_cmp); CSMLA_GLOBAL(res); CSMLA_GLOBAL(topk_len); CSMLA_GLOBAL(sinks); CSMLA_GLOBAL(out);
   CSMLA_GLOBAL(lse); CSMLA_GLOBAL(ws_o); CSMLA_GLOBAL(ws_ml); CSMLA_GLOBAL(ws_sync); CSMLA_GLOBAL(ws_xcc);
+  CSMLA_GLOBAL(ori_idx); CSMLA_GLOBAL(ori_tkl);
 #undef CSMLA_GLOBAL
   return h;
 }
@@ -208,6 +209,7 @@ struct Tok {
   int vis;         // visible compressed tokens: [0, vis)
   int kv0, cmp0;   // row offsets of a TND cache
   int k_eff;       // index slots read
+  int ko_eff;      // ori index slots read (listed ori keys)
 };
 
 // A token's lengths: one load per array, all issued before the first is
@@ -226,7 +228,7 @@ __device__ __forceinline__ int ld_len(const int32_t* p, int i, int zero) {
 
 struct TokLens {
   int b, q0, span;
-  int su_q, su_ori, cu_o0, cu_o1, su_cmp, cu_c0, cu_c1, res, tkl;
+  int su_q, su_ori, cu_o0, cu_o1, su_cmp, cu_c0, cu_c1, res, tkl, otkl;
 };
 
 __device__ __forceinline__ TokLens token_lens(const KHdr& a, int t) {
@@ -249,7 +251,7 @@ __device__ __forceinline__ TokLens token_lens(const KHdr& a, int t) {
   l.cu_o0 = ld_len(a.cu_ori, b, z); l.cu_o1 = ld_len(a.cu_ori, b + 1, z);
   l.su_cmp = ld_len(a.su_cmp, b, z);
   l.cu_c0 = ld_len(a.cu_cmp, b, z); l.cu_c1 = ld_len(a.cu_cmp, b + 1, z);
-  l.res = ld_len(a.res, b, z); l.tkl = ld_len(a.topk_len, t, z);
+  l.res = ld_len(a.res, b, z); l.tkl = ld_len(a.topk_len, t, z); l.otkl = ld_len(a.ori_tkl, t, z);
   return l;
 }
 
@@ -295,7 +297,10 @@ __device__ __forceinline__ Tok token_ctx(const KHdr& a, int t, const TokLens& l)
   int ke = a.topk;
   if (a.topk_len) ke = max(0, min(ke, v_tkl));
   k.k_eff = ke;
-  if (!k.valid) { k.lo = k.hi = 0; k.vis = 0; k.k_eff = 0; }
+  int ko = a.ori_topk;
+  if (a.ori_tkl) ko = max(0, min(ko, __builtin_amdgcn_readfirstlane(l.otkl)));
+  k.ko_eff = ko;
+  if (!k.valid) { k.lo = k.hi = 0; k.vis = 0; k.k_eff = 0; k.ko_eff = 0; }
   return k;
 }
 
@@ -374,6 +379,40 @@ __device__ __forceinline__ int compact_indices(const KHdr& a, const Tok& k, int 
   return compact_indices<NT>(a, k, t, list, wtot, w_lo, load_indices<NT>(a, t, 0));
 }
 
+// The listed ori positions of token t (ori_sparse_indices, slot order) that
+// lie in the token's window [lo, hi), compacted into list[0, n) the same way
+// (n <= kListMax: the plan bounds ori_topk + topk by it).  Returns n.
+// Whole-work-group call; ends with a barrier.
+template <int NT>
+__device__ __forceinline__ int compact_ori(const KHdr& a, const Tok& k, int t, int* list, int* wtot) {
+  constexpr int NW = NT / 64;
+  const int tid = opaque((int)threadIdx.x);
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int* row = a.ori_idx + (size_t)t * a.ori_topk;
+  int base = 0, parity = 0;
+  for (int s0 = 0; s0 < k.ko_eff; s0 += NT) {
+    const int slot = s0 + tid;
+    const int v = (slot < k.ko_eff) ? row[slot] : -1;
+    const bool ok = (slot < k.ko_eff) && (v >= k.lo) && (v < k.hi);
+    const uint64_t bal = __ballot(ok);
+    const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+    int* wt = wtot + NW * parity;
+    parity ^= 1;
+    if (lane == 0) wt[w] = __popcll(bal);
+    lds_barrier();
+    int off = 0;
+    for (int j = 0; j < w; ++j) off += wt[j];
+    int tot = 0;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) tot += wt[j];
+    const int pos = base + off + pre;
+    if (ok && pos < kListMax) list[pos] = v;
+    base += tot;
+  }
+  lds_barrier();
+  return base;
+}
+
 // ---------------------------------------------------------------------------
 // key resolution: list position -> cache row (QuantSparseFlashMla, 参数说明:
 // the block tables, the band window, cmp_sparse_indices with -1 skipped)
@@ -381,11 +420,14 @@ __device__ __forceinline__ int compact_indices(const KHdr& a, const Tok& k, int 
 
 // Logical token position of key `key` of the token's list (ori band first,
 // then cmp entries) and whether it lives in cmp_kv.
+// With listed ori keys (ori_topk > 0) the list holds the ori positions first,
+// then the compressed entries.
 __device__ __forceinline__ int key_pos(const KHdr& a, const Tok& k, int n_o, int key, const int* list, int w_lo,
                                        bool& is_cmp) {
   is_cmp = key >= n_o;
-  if (!is_cmp) return k.lo + key;
-  return (a.topk > 0) ? list[key - n_o - w_lo] : key - n_o;
+  const bool listed = a.ori_topk > 0;
+  if (!is_cmp) return listed ? list[key] : k.lo + key;
+  return (a.topk > 0) ? list[(listed ? key : key - n_o) - w_lo] : key - n_o;
 }
 
 // The two caches' attributes as uniform registers.  A per-key choice
@@ -1168,10 +1210,10 @@ __device__ __forceinline__ void attn_body(KArgPtr ap, uint8_t* smem, int w) {
       continue;
     }
 
-    us.n_o = us.k.hi - us.k.lo;
+    us.n_o = (a.ori_topk > 0) ? compact_ori<kThreads>(a, us.k, t, list, misc) : us.k.hi - us.k.lo;
     us.n_c = 0;
     us.w_lo = 0;
-    if (a.topk > 0) us.n_c = compact_indices<kThreads>(a, us.k, t, list, misc, 0, ip);
+    if (a.topk > 0) us.n_c = compact_indices<kThreads>(a, us.k, t, list + (a.ori_topk > 0 ? us.n_o : 0), misc, 0, ip);
     else if (a.has_cmp) us.n_c = us.k.vis;
     const int64_t n = (int64_t)us.n_o + us.n_c;
     us.kb = (int)(n * s / a.splits);
@@ -1837,9 +1879,9 @@ __global__ void __launch_bounds__(kThreads) debug_resolve_kernel(const KArgs a, 
   const int t = blockIdx.x;
   const Sides sd = cache_sides(a);
   const Tok k = token_ctx(a, t);
-  const int n_o = k.hi - k.lo;
+  const int n_o = (a.ori_topk > 0) ? compact_ori<kThreads>(a, k, t, list, wtot) : k.hi - k.lo;
   int n_c = 0;
-  if (a.topk > 0) n_c = compact_indices<kThreads>(a, k, t, list, wtot, 0);
+  if (a.topk > 0) n_c = compact_indices<kThreads>(a, k, t, list + (a.ori_topk > 0 ? n_o : 0), wtot, 0);
   else if (a.has_cmp) n_c = k.vis;
   if (threadIdx.x == 0) { counts[2 * t] = n_o; counts[2 * t + 1] = n_c; }
   const int n = min(n_o + n_c, max_keys);
@@ -3112,9 +3154,9 @@ __device__ __forceinline__ void bk_body(KArgPtr ap, uint8_t* smem, int w) {
       }
       continue;
     }
-    const int n_o = k.hi - k.lo;
+    const int n_o = (a.ori_topk > 0) ? compact_ori<kBkThreads>(a, k, t, list, misc) : k.hi - k.lo;
     int n_c = 0;
-    if (a.topk > 0) n_c = compact_indices<kBkThreads>(a, k, t, list, misc, 0, ip);
+    if (a.topk > 0) n_c = compact_indices<kBkThreads>(a, k, t, list + (a.ori_topk > 0 ? n_o : 0), misc, 0, ip);
     else if (a.has_cmp) n_c = k.vis;
     const int64_t n = (int64_t)n_o + n_c;
     const int kb = (int)(n * sp / S), ke = (int)(n * (sp + 1) / S);

@@ -95,6 +95,10 @@ def base_problem(**kw):
     (dict(q_dtype=1, kv_dtype=3), INVALID),
     (dict(q_dtype=1, kv_dtype=2, kv_scale_mode=1), INVALID),   # scales live in the packed row
     (dict(q_dtype=1, kv_dtype=1, topk=2048), UNSUPPORTED),     # the bf16-q kernel keeps <= 1024 slots
+    (dict(ori_topk=200), OK),                   # listed ori keys (QuantSparseFlashMla: ori_sparse_indices)
+    (dict(ori_topk=513), UNSUPPORTED),          # ori_topk + topk <= 1024 (one index list per row)
+    (dict(ori_topk=-1), INVALID),
+    (dict(ori_topk=100, q_dtype=1, kv_dtype=2), OK),
 ])
 def test_validation_matrix(kw, status):
     assert m.csmla_validate(base_problem(**kw)) == status, m.csmla_last_error()
@@ -322,3 +326,19 @@ def test_plan_bf16_q_kernels(monkeypatch):
                                                  ori_win_left=-1, ori_win_right=-1, topk=0,
                                                  ori_table_cols=40, cmp_table_cols=10))
             assert md[5] >= 3                       # up to 5120 + 1280 keys: >= 7 units of <= 1024 ... per token
+
+
+def test_plan_listed_ori_keys_take_the_key_split(monkeypatch):
+    """Listed ori keys run on the key-split kernels whatever the override."""
+    for env in (None, "heads8", "prefill", "splitkey"):
+        if env is None:
+            monkeypatch.delenv("CSMLA_KERNEL", raising=False)
+        else:
+            monkeypatch.setenv("CSMLA_KERNEL", env)
+        _, md, _ = m.csmla_plan(base_problem(ori_topk=64))
+        assert md[12] == 0 and md[13] == 0
+    monkeypatch.delenv("CSMLA_KERNEL", raising=False)
+    p = base_problem(ori_topk=64)
+    _, md, ws = m.csmla_plan(p)
+    bad = md.copy(); bad[12] = 8; bad[6] = 32 * 8; bad[5] = 1   # a head-split header for this problem
+    assert m.csmla_forward(p, fake_tensors(ws), bad, raise_on_error=False) == MISMATCH

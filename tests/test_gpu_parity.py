@@ -81,7 +81,8 @@ def check_rows(inp_cpu, tokens=None, name="", inp_gpu=None):
     want = {t: token_rows(inp_cpu, t, tt) for t in toks}
     max_keys = max([len(v) for v in want.values()] + [1])
     g = inp_gpu if inp_gpu is not None else inp_cpu.to(DEV)
-    for whole in ((False, True) if inp_cpu.topk <= 1024 else (False,)):
+    both = inp_cpu.topk <= 1024 and getattr(inp_cpu, "ori_sparse_indices", None) is None
+    for whole in ((False, True) if both else (False,)):
         say(f"rows {name}: max_keys={max_keys} whole_token={whole}")
         keys, counts = m.debug_resolve(g, max_keys, whole_token=whole)
         torch.cuda.synchronize()
