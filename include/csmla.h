@@ -212,9 +212,20 @@ csmla_status csmla_validate(const csmla_problem* problem);
  *   metadata         host int32[metadata_words], metadata_words >= 1024; written
  *   workspace_bytes  host; written: device scratch csmla_forward needs (may be 0)
  * The plan depends on the problem fields and on the host lengths given;
- * csmla_forward rejects a plan made for a different problem. */
+ * csmla_forward rejects a plan made for a different problem, and
+ * csmla_plan_check also one made for other host lengths. */
 csmla_status csmla_plan(const csmla_problem* problem, const csmla_host_lengths* lengths,
                         int32_t* metadata, size_t metadata_words, size_t* workspace_bytes);
+
+/* Whether `metadata` is csmla_plan's output for this problem and these host
+ * lengths (the plan records hashes of both; QuantSparseFlashMla, 功能说明:
+ * the metadata is made for the main op's inputs).  Host only.  Returns
+ * CSMLA_OK or CSMLA_ERR_METADATA_MISMATCH.  csmla_forward checks the problem
+ * hash itself but, having no host lengths, cannot see a plan made for other
+ * lengths: a caller that keeps a plan across steps whose lengths may change
+ * calls this first (or plans again). */
+csmla_status csmla_plan_check(const csmla_problem* problem, const csmla_host_lengths* lengths,
+                              const int32_t* metadata);
 
 /* The attention forward (QuantSparseFlashMla, 参数说明 inputs and outputs).
  *   metadata   host int32[1024] from csmla_plan for this problem (required)

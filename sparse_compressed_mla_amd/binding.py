@@ -14,7 +14,9 @@ from typing import Optional, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcsmla.so")
+# CSMLA_LIB points the binding at another build of the same ABI (the host-only
+# sanitizer build the host ABI tests use); by default the in-tree HIP library.
+LIB_PATH = os.environ.get("CSMLA_LIB") or os.path.join(_HERE, "libcsmla.so")
 
 CSMLA_METADATA_WORDS = 1024
 LAYOUTS = {"BSND": 0, "TND": 1, "PA_BBND": 2}
@@ -86,6 +88,9 @@ def load(path: str = LIB_PATH):
     lib.csmla_plan.restype = ctypes.c_int
     lib.csmla_plan.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaHostLengths),
                                ctypes.POINTER(_i32), ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
+    lib.csmla_plan_check.restype = ctypes.c_int
+    lib.csmla_plan_check.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaHostLengths),
+                                     ctypes.POINTER(_i32)]
     for fn in (lib.csmla_forward, lib.csmla_forward_noalloc):
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.POINTER(CsmlaProblem), ctypes.POINTER(CsmlaTensors), ctypes.POINTER(_i32), _p]
@@ -145,6 +150,14 @@ def csmla_forward(problem: CsmlaProblem, tensors: CsmlaTensors, metadata: np.nda
     if raise_on_error:
         _check(st, "csmla_forward")
     return st
+
+
+def csmla_plan_check(problem: CsmlaProblem, lengths: Optional[CsmlaHostLengths], metadata: np.ndarray) -> int:
+    """CSMLA_OK (0) if `metadata` was planned for this problem and these host
+    lengths, else CSMLA_ERR_METADATA_MISMATCH (4) or a validation status."""
+    md = np.ascontiguousarray(metadata, dtype=np.int32)
+    return load().csmla_plan_check(ctypes.byref(problem), ctypes.byref(lengths) if lengths is not None else None,
+                                   md.ctypes.data_as(ctypes.POINTER(_i32)))
 
 
 def csmla_forward_noalloc(problem: CsmlaProblem, tensors: CsmlaTensors, metadata: np.ndarray, stream: int = 0,
@@ -300,8 +313,13 @@ class Plan:
 
 def forward(inp, out=None, lse=None, workspace=None, plan: Optional[Plan] = None, stream=None):
     """Run the attention on inputs already on the GPU.  Allocates the outputs
-    (and the workspace) with torch when they are not given.  Returns (out, lse)."""
+    (and the workspace) with torch when they are not given.  A plan passed in
+    is checked against the inputs' host lengths (csmla_plan_check).  Returns
+    (out, lse)."""
     import torch
+    if plan is not None:
+        hl, keep = host_lengths_from(inp)
+        _check(csmla_plan_check(plan.problem, hl, plan.metadata), "csmla_plan_check")
     plan = plan or Plan(inp)
     dev = inp.q.device
     if out is None:

@@ -539,6 +539,20 @@ csmla_status csmla_forward(const csmla_problem* p, const csmla_tensors* t, const
   return CSMLA_OK;
 }
 
+csmla_status csmla_plan_check(const csmla_problem* p, const csmla_host_lengths* hl, const int32_t* md) {
+  csmla_status st = csmla_validate(p);
+  if (st != CSMLA_OK) return st;
+  if (!md) return fail(CSMLA_ERR_INVALID_ARG, "metadata is NULL");
+  if (md[MD_MAGIC] != kMagic || md[MD_VERSION] != CSMLA_ABI_VERSION)
+    return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was not written by csmla_plan of this version");
+  if ((uint32_t)md[MD_PROBLEM_HASH] != problem_hash(p) || md[MD_T1] != p->t1)
+    return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was planned for a different problem");
+  if ((uint32_t)md[MD_LENGTHS_HASH] != lengths_hash(p, hl))
+    return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata was planned for other host lengths");
+  g_last_error.clear();
+  return CSMLA_OK;
+}
+
 csmla_status csmla_forward_noalloc(const csmla_problem* p, const csmla_tensors* t, const int32_t* md, void* stream) {
   if (!t) return fail(CSMLA_ERR_INVALID_ARG, "tensors is NULL");
   csmla_tensors ts = *t;

@@ -15,10 +15,11 @@
 // With scale_q, scale_k >= 0, W * ReLU(scale_q * scale_k * x) equals
 // scale_k * (W * scale_q) * ReLU(x), so the key scale multiplies the sum once.
 //
-// idx_topk_kernel — one work-group per query row: four rounds of 8-bit radix
-// selection over order-preserving integer keys of the float32 scores (an LDS
-// histogram per round and a suffix scan to find the digit of the topk-th
-// largest), then one pass in index order that writes every score above the
+// idx_topk_kernel — one work-group per query row: up to three rounds of radix
+// selection (11, 11 and 10 bits) over order-preserving integer keys of the
+// float32 scores (an LDS histogram per round and a suffix scan to find the
+// digit of the topk-th largest; it stops as soon as the chosen bin is taken
+// whole), then one pass in index order that writes every score above the
 // threshold and the lowest-positioned ties, so the output comes out in
 // ascending position order.
 #include <hip/hip_runtime.h>

@@ -342,3 +342,22 @@ def test_plan_listed_ori_keys_take_the_key_split(monkeypatch):
     _, md, ws = m.csmla_plan(p)
     bad = md.copy(); bad[12] = 8; bad[6] = 32 * 8; bad[5] = 1   # a head-split header for this problem
     assert m.csmla_forward(p, fake_tensors(ws), bad, raise_on_error=False) == MISMATCH
+
+
+def test_plan_check_sees_other_lengths():
+    """csmla_plan_check: the plan's own problem and lengths pass; other host
+    lengths, another problem, or a foreign buffer do not (csmla_forward cannot
+    see lengths, so this is the check for a reused plan)."""
+    p = base_problem()
+    su = np.full(32, 8192, dtype=np.int32)
+    hl = m.CsmlaHostLengths()
+    hl.seqused_ori_kv = su.ctypes.data
+    _, md, _ = m.csmla_plan(p, hl)
+    assert m.csmla_plan_check(p, hl, md) == OK
+    su2 = su.copy(); su2[3] = 4000
+    hl2 = m.CsmlaHostLengths()
+    hl2.seqused_ori_kv = su2.ctypes.data
+    assert m.csmla_plan_check(p, hl2, md) == MISMATCH
+    assert m.csmla_plan_check(p, None, md) == MISMATCH
+    assert m.csmla_plan_check(base_problem(topk=256), hl, md) == MISMATCH
+    assert m.csmla_plan_check(p, hl, np.zeros(1024, dtype=np.int32)) == MISMATCH
