@@ -254,6 +254,9 @@ def kernel_name(plan, fmt="fp8"):
         return f"sk_kernel (split-key decode: 64 heads, {plan.splits} key splits per token, in-kernel merge)"
     if plan.head_group == 64:
         return "pf_kernel (whole-token)"
+    if plan.head_group > 0 and plan.dk_parts > 1:
+        return (f"dk_kernel (head-split, groups of {plan.head_group} heads, keys in {plan.dk_parts} parts "
+                "merged in-kernel)")
     if plan.head_group > 0:
         return f"dk_kernel (head-split, groups of {plan.head_group} heads over whole key lists)"
     return f"attn_kernel<0> (split attention, {plan.splits} key splits)" + (" + combine_kernel" if plan.splits > 1

@@ -156,8 +156,12 @@ typedef struct {
  *   attn_out          bf16 [t1, n1, d]
  *   softmax_lse       f32 [t1, n1] (TND [1, t1, n1]; BSND [B, 1, Q_S, n1])
  *   workspace         device scratch of the size csmla_plan reports (may be NULL if 0),
- *                     256-byte aligned; with splits it holds the partial outputs and
- *                     their (max, sum).  Calls that overlap in time must not share it.
+ *                     256-byte aligned and zero-filled before its first use: its first
+ *                     8.25 MiB hold sync words and the exchange slots of in-kernel
+ *                     merges, which every call leaves ready for the next (so one buffer
+ *                     serves any sequence of plans); after them, with splits, the
+ *                     partial outputs and their (max, sum).  Calls that overlap in time
+ *                     must not share it.
  * Descales must be finite and >= 0 (a zero descale is treated as 2^-126). */
 typedef struct {
   const void*    q;

@@ -310,6 +310,12 @@ class Plan:
         prefill kernel), or 0 (key-split kernel)."""
         return int(self.metadata[12])
 
+    @property
+    def dk_parts(self) -> int:
+        """Key parts per (token, head group) of the head-split kernel (1: none);
+        the last part of a group merges the others' partials inside the kernel."""
+        return int(self.metadata[14])
+
 
 def forward(inp, out=None, lse=None, workspace=None, plan: Optional[Plan] = None, stream=None):
     """Run the attention on inputs already on the GPU.  Allocates the outputs

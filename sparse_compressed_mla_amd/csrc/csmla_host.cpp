@@ -168,16 +168,18 @@ void csmla::clear_last_error() { g_last_error.clear(); }
 uint32_t csmla::hash_bytes(const void* data, size_t n, uint32_t seed) { return fnv1a(data, n, seed); }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Workspace of a split plan: bf16 partial outputs [units, 64, 512], then
 // (max, sum) [units, 64, 2] fp32.
 void csmla::workspace_offsets(int n_units, size_t* xcc, size_t* o, size_t* ml) {
-  *xcc = kWsSyncBytes;
+  *xcc = kWsFixedBytes;
   *o = align256(*xcc + (size_t)n_units * sizeof(int32_t));
   *ml = align256(*o + (size_t)n_units * kN1 * kD * 2);
 }
 
-size_t csmla::workspace_bytes_for(int n_units, int splits) {
+size_t csmla::workspace_bytes_for(int n_units, int splits, int dk_parts) {
+  if (dk_parts > 1) return kWsFixedBytes;
   if (splits <= 1) return 0;
   size_t xcc, o, ml;
   workspace_offsets(n_units, &xcc, &o, &ml);
@@ -364,13 +366,37 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
     S = std::max<int64_t>(S, (max_n + kBkMaxUnitKeys - 1) / kBkMaxUnitKeys);
   }
   if (hg > 0) S = 1;
+  // Key parts of the head-split kernel: each (token, head group) split into
+  // P parts of whole 128-key tiles on one XCD, the last merging the others'
+  // partials.  Every unit needs a work-group of its own (the grid rounded up
+  // to whole XCD rounds of groups, at most one work-group per CU), and a
+  // part gets at least one tile.  Two parts by default where they fit (8-head
+  // groups up to 16 tokens): measured on MI355X with 640 keys per token, 4 and
+  // 8 tokens run 15.1 and 15.3 us in two parts against 16.2 and 16.1 us whole,
+  // 16 tokens 16.3 against 16.4 us; at 32 tokens (16-head groups in two parts)
+  // nothing is gained, and four parts lose (the merger reads each writer's
+  // partial in a round trip of its own).  CSMLA_DK_PARTS overrides the count.
+  int parts = 1;
+  if (hg == 8 || hg == 16) {
+    int64_t want = hg == 8 ? 2 : 1;
+    if (const char* env = std::getenv("CSMLA_DK_PARTS")) want = std::atoll(env);
+    const int64_t tiles = std::max<int64_t>(1, (max_n + kDkTileKeys - 1) / kDkTileKeys);
+    const int64_t groups = (int64_t)T1 * (kN1 / hg);
+    while (parts * 2 <= want && parts * 2 <= kDkMaxParts && parts * 2 <= tiles &&
+           round_up(groups * parts * 2, 8 * parts * 2) <= kMaxGrid)
+      parts *= 2;
+  }
+  int dk_test = 0;
+  if (parts > 1)
+    if (const char* env = std::getenv("CSMLA_DK_TEST")) dk_test = std::atoi(env);
   if (S > kMaxSplits) return fail(CSMLA_ERR_UNSUPPORTED, "a token needs %lld splits; at most %d are built", (long long)S, kMaxSplits);
-  const int64_t per_token = hg > 0 ? kN1 / hg : S;   // units per query token
+  const int64_t per_token = hg > 0 ? (kN1 / hg) * parts : S;   // units per query token
   const int64_t n_units64 = (int64_t)T1 * per_token;
   if (n_units64 > (int64_t)1 << 30) return fail(CSMLA_ERR_UNSUPPORTED, "too many work units");
   const int n_units = (int)n_units64;
   // the split-key kernel's grid: 8 S ceil(T1 / 8) blocks, token t's splits on XCD t mod 8
-  const int G = sk ? (int)(8 * S * t_rounds) : (int)std::min<int64_t>(n_units64, kMaxGrid);
+  const int G = sk ? (int)(8 * S * t_rounds)
+                   : parts > 1 ? (int)round_up(n_units64, 8 * parts) : (int)std::min<int64_t>(n_units64, kMaxGrid);
 
   // contiguous unit ranges per work-group, balanced by estimated keys
   std::vector<double> pre(n_units + 1, 0.0);
@@ -390,14 +416,14 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   std::vector<int32_t> starts(G + 1);
   starts[0] = 0;
   int u = 0;
-  for (int g = 1; g < G && !sk; ++g) {
+  for (int g = 1; g < G && !sk && parts == 1; ++g) {
     const double target = pre[n_units] * g / G;
     while (u < n_units && pre[u] < target) ++u;
     int lo = starts[g - 1] + 1, hi = n_units - (G - g);
     starts[g] = std::min(std::max(u, lo), hi);
     u = starts[g];
   }
-  if (sk)   // one unit per block; the block -> (token, split) map lives in the kernel
+  if (sk || parts > 1)   // one unit per block; the block -> unit map lives in the kernel
     for (int g = 1; g < G; ++g) starts[g] = std::min(g, n_units);
   starts[G] = n_units;
 
@@ -411,12 +437,14 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   md[MD_UNITS] = n_units;
   md[MD_GRID] = G;
   md[MD_LIST_MAX] = kListMax;
-  const size_t ws = workspace_bytes_for(n_units, (int)S);
+  const size_t ws = workspace_bytes_for(n_units, (int)S, parts);
   md[MD_WS_LO] = (int32_t)(ws & 0x7fffffff);
   md[MD_WS_HI] = (int32_t)(ws >> 31);
   md[MD_FLAGS] = S > 1 ? 1 : 0;
   md[MD_HEAD_GROUP] = hg;
   md[MD_SPLIT_KEY] = sk ? 1 : 0;
+  md[MD_DK_PARTS] = parts;
+  md[MD_DK_TEST] = dk_test;
   for (int g = 0; g <= G; ++g) md[MD_STARTS + g] = starts[g];
   if (ws_bytes) *ws_bytes = ws;
   g_last_error.clear();
@@ -452,6 +480,7 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
     return fail(CSMLA_ERR_INVALID_ARG, "return_softmax_lse needs softmax_lse");
 
   std::memset(&a, 0, sizeof(a));
+  a.dk_parts = 1;
   a.batch = p->batch; a.t1 = p->t1; a.q_s = p->q_s; a.layout_q = p->layout_q; a.layout_kv = p->layout_kv;
   a.ori_s = p->ori_s; a.cmp_s = p->cmp_s; a.ori_bs = p->ori_block_size; a.cmp_bs = p->cmp_block_size;
   a.ori_cols = p->ori_table_cols; a.cmp_cols = p->cmp_table_cols;
@@ -489,11 +518,18 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
     const bool sk_ok = SK == 0 || (SK == 1 && HG == 0 && p->ori_topk == 0 && p->kv_dtype == CSMLA_KV_FP8 &&
                                    S <= kSkMaxSplits && p->t1 <= kSkMaxTokens &&
                                    p->topk <= kListMax && G == 8 * S * ((p->t1 + 7) / 8) && G <= kMaxGrid);
-    const int per_token = HG > 0 ? kN1 / HG : S;
-    if (S < 1 || !hg_ok || !sk_ok || U != p->t1 * per_token || G < 1 || G > kMaxGrid || (!SK && G > U))
+    const int PT = md[MD_DK_PARTS], DT = md[MD_DK_TEST];
+    const bool parts_ok = PT == 1 || ((PT == 2 || PT == 4 || PT == 8) && (HG == 8 || HG == 16) &&
+                                      G == (int)round_up(U, 8 * PT) && (DT >= 0 && DT <= 2));
+    const int per_token = HG > 0 ? (kN1 / HG) * PT : S;
+    if (S < 1 || !hg_ok || !sk_ok || !parts_ok || U != p->t1 * per_token || G < 1 || G > kMaxGrid ||
+        (!SK && PT == 1 && G > U))
       return fail(CSMLA_ERR_METADATA_MISMATCH, "metadata header is inconsistent");
     a.hg = HG;
     a.sk = SK;
+    a.dk_parts = PT;
+    a.dk_test = DT;
+    a.dk_ticks = DT ? 0 : kDkWaitTicks;
     for (int g = 0; g <= G; ++g) {
       const int s0 = md[MD_STARTS + g];
       if (s0 < 0 || s0 > U || (g > 0 && s0 < md[MD_STARTS + g - 1]) || (g == 0 && s0 != 0) || (g == G && s0 != U))
@@ -501,7 +537,7 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
       a.starts[g] = s0;
     }
     a.splits = S; a.n_units = U; a.grid = G;
-    const size_t ws = workspace_bytes_for(U, S);
+    const size_t ws = workspace_bytes_for(U, S, PT);
     if (ws > 0) {
       if (!t->workspace || t->workspace_bytes < ws)
         return fail(CSMLA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu", ws, t->workspace ? t->workspace_bytes : (size_t)0);
@@ -513,6 +549,7 @@ static csmla_status build_args(const csmla_problem* p, const csmla_tensors* t, c
       a.ws_xcc = (int32_t*)((char*)t->workspace + o_xcc);
       a.ws_o = (uint16_t*)((char*)t->workspace + o_o);
       a.ws_ml = (float*)((char*)t->workspace + o_ml);
+      a.ws_xch = (uint8_t*)t->workspace + kWsSyncBytes;
     }
   }
   return CSMLA_OK;
@@ -562,7 +599,7 @@ csmla_status csmla_forward_noalloc(const csmla_problem* p, const csmla_tensors* 
   // HIP call (a plan that is not csmla_plan's is rejected by csmla_forward)
   if (md && md[MD_MAGIC] == kMagic && md[MD_VERSION] == CSMLA_ABI_VERSION && md[MD_UNITS] >= 0 &&
       md[MD_SPLITS] >= 1) {
-    const size_t need = workspace_bytes_for(md[MD_UNITS], md[MD_SPLITS]);
+    const size_t need = workspace_bytes_for(md[MD_UNITS], md[MD_SPLITS], md[MD_DK_PARTS]);
     if (need > kNoAllocScratchBytes)
       return fail(CSMLA_ERR_WORKSPACE,
                   "the plan needs %zu bytes of workspace; csmla_forward_noalloc holds %zu (use csmla_forward with "

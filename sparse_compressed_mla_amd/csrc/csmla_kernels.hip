@@ -155,7 +155,7 @@ __device__ __forceinline__ KHdr hdr_view(HdrRegs r) {
   CSMLA_GLOBAL(cu_q); CSMLA_GLOBAL(cu_ori); CSMLA_GLOBAL(cu_cmp); CSMLA_GLOBAL(su_q); CSMLA_GLOBAL(su_ori);
   CSMLA_GLOBAL(su_cmp); CSMLA_GLOBAL(res); CSMLA_GLOBAL(topk_len); CSMLA_GLOBAL(sinks); CSMLA_GLOBAL(out);
   CSMLA_GLOBAL(lse); CSMLA_GLOBAL(ws_o); CSMLA_GLOBAL(ws_ml); CSMLA_GLOBAL(ws_sync); CSMLA_GLOBAL(ws_xcc);
-  CSMLA_GLOBAL(ori_idx); CSMLA_GLOBAL(ori_tkl);
+  CSMLA_GLOBAL(ori_idx); CSMLA_GLOBAL(ori_tkl); CSMLA_GLOBAL(ws_xch);
 #undef CSMLA_GLOBAL
   return h;
 }
@@ -1289,14 +1289,38 @@ attn_kernel(const KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// words shared by the work-groups of one XCD (workspace sync and exchange
+// words).  Global atomics act in the L2, which the CUs of an XCD share.
+// ---------------------------------------------------------------------------
+
+// A read of a sync word where the atomics act (L2): an atomic add of zero
+// that returns the old value, waited for in the same asm.  (A load with the
+// workgroup-scope bit may be served by the CU's L1, which would keep
+// returning the value it cached first.)
+__device__ __forceinline__ int ws_poll(int* p) {
+  int v;
+  asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p), "v"(0) : "memory");
+  return v;
+}
+__device__ __forceinline__ int ws_atomic_add(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ int ws_atomic_xchg(int* p, int v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// ---------------------------------------------------------------------------
 // head-split kernel (decode): one work unit = (query token, group of HG = 8
-// or 16 heads) over the token's whole key list, so no split partials exist.
+// or 16 heads, key part), over the part's share of the token's key list.
 // ---------------------------------------------------------------------------
 //
 // For a decode batch the tokens are few, and splitting each token's keys
 // over work-groups (the kernel above) leaves 64-head partial outputs that a
 // second pass must merge.  Here the work-groups of one token divide its heads
 // instead and read the same rows, which the XCD's L2 serves after the first.
+// With P > 1 key parts, each (token, head group) is also split into P parts
+// of whole 128-key tiles run by work-groups of one XCD; the last part merges
+// the others' 16-head partials (a 16 KiB exchange, described before dk_body).
 //
 // 8 waves (two per SIMD, so that one wave's MFMAs, LDS reads and gather
 // issues overlap the other's vector work; one wave alone issues at most one
@@ -1312,7 +1336,7 @@ attn_kernel(const KArgs a) {
 
 constexpr int kDkWaves = 8;
 constexpr int kDkThreads = 64 * kDkWaves;
-constexpr int kDkRows = 128;                          // keys per tile
+constexpr int kDkRows = kDkTileKeys;                  // keys per tile (128)
 constexpr int kDkTileBytes = kDkRows * kD;            // 64 KiB
 constexpr int kDkPxRow = 144;                         // bytes per head row of P (128 keys + pad)
 constexpr int kDkKB = kDkRows / 16 / kDkWaves;        // 16-key S^T blocks per wave
@@ -1377,10 +1401,12 @@ __device__ __forceinline__ void dk_src2(const uint64_t* kaddr, int tile, int w, 
 // M0 = the wave's row block of the half, plus the pair's offset added in
 // the same asm (per-instruction destinations would otherwise be formed once
 // for the whole kernel and held in spilled scalar registers).
+// (nt: the non-temporal policy; this kernel's gathers ran ~4% faster with it,
+// the whole-token kernel's, whose rows other tokens reuse, slower)
 __device__ __forceinline__ void dk_issue(const DkSrc& s, int mi, int half, uint8_t* tb, int w) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tb + (64 * half + 2 * kDkGI * w) * kD));
   const uint32_t off = (uint32_t)(2 * mi * kD);
-  asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(s.p[mi]),
+  asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(base), "v"(s.p[mi]),
                "s"(off) : "m0", "scc");
 }
 
@@ -1651,6 +1677,113 @@ __device__ __forceinline__ void dk_run(const KHdr& a, UnitState& us, int* list, 
   }
 }
 
+// ---- key parts: exchange of partial outputs between the parts of a group ----
+//
+// The parts of one (token, head group) run on one XCD (consecutive units of an
+// XCD's range).  Each writing part stores its partial output, normalised by
+// its own row sum, as 16-byte words {bf16 pair, tag, bf16 pair, tag} into its
+// unit's slot, plus the per-head (max, sum) words; every 8-byte half carries
+// the tag, so a reader that sees the tag in a half has that half's data (no
+// flag word and no wait for the stores to complete).  The tag is the slot's
+// epoch + 1; the merging part (the group's last) bumps the epoch after each
+// call, so stale words never match.  Presence word: a writer adds 1 when its
+// keys are known; a merger that has waited too long adds 2 and, if the writer
+// had not arrived, computes that part itself (the late writer then finds 2,
+// stores nothing and clears the word); a merger that finds the writer arrived
+// waits longer, then also computes the part itself.  So every wait is bounded
+// and the result never depends on a writer being scheduled; the words return
+// to zero by the end of every launch.
+
+constexpr uint64_t kDkWaitTicks2 = 20000;   // s_memrealtime ticks (100 MHz) a merger waits for an arrived writer
+
+__device__ __forceinline__ uint8_t* xch_slot(const KHdr& a, int unit) {
+  return a.ws_xch + (size_t)unit * kXchSlotBytes;
+}
+
+// Keys [lo(p), lo(p + 1)) of part p of P: whole 128-key tiles, the earlier
+// parts taking the larger shares.
+__device__ __forceinline__ int dk_part_lo(int p, int P, int nkeys) {
+  const int nt = (nkeys + kDkRows - 1) / kDkRows;
+  return min(nkeys, ((p * nt + P - 1) / P) * kDkRows);
+}
+
+// A writer's slot: its partial output O / l (bf16) and (max, sum) per head.
+__device__ __forceinline__ void dk_xch_write(uint8_t* slot, uint32_t tag, int w, int lane, const v4f (&o)[kDkDB],
+                                             float Mrun, float lh) {
+  const int j = lane & 15, g = lane >> 4;
+  const float inv = (lh > 0.f) ? 1.0f / lh : 0.f;
+#pragma unroll
+  for (int db = 0; db < kDkDB; ++db) {
+    const int quad = 4 * (kDkDB * w + db) + g;   // columns 4 quad .. +3
+    const v4i x{(int)pack_bf16x2(o[db][0] * inv, o[db][1] * inv), (int)tag,
+                (int)pack_bf16x2(o[db][2] * inv, o[db][3] * inv), (int)tag};
+    *(v4i*)(slot + kXchData + (size_t)(quad * 16 + j) * 16) = x;
+  }
+  if (w == 0 && g == 0)
+    *(v4i*)(slot + kXchMl + 16 * j) = v4i{__float_as_int(Mrun), (int)tag, __float_as_int(lh), (int)tag};
+}
+
+// Poll a writer's slot until every word the wave's lanes merge carries `tag`
+// (true) or `limit` ticks pass (false).  The words are read as agent-scope
+// atomic loads (8 bytes each, the granularity the tags cover), which the
+// CU's L1 does not serve, so every round reaches the L2 the writer's stores
+// went to.  (Measured on MI355X: plain loads after buffer_inv sc0 kept
+// returning the first line the L1 had cached; buffer_inv sc1 before plain
+// loads saw the words but cost ~5 us per round.)
+__device__ __forceinline__ v4i ld_v4i_agent(const uint8_t* p) {
+  uint64_t* q = (uint64_t*)(uintptr_t)p;
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v4i{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)(uint32_t)b, (int)(uint32_t)(b >> 32)};
+}
+
+__device__ __forceinline__ bool dk_xch_poll(const uint8_t* slot, uint32_t tag, int w, int lane, v4i (&d)[kDkDB],
+                                            v4i& ml, uint64_t limit) {
+  const int j = lane & 15, g = lane >> 4;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int db = 0; db < kDkDB; ++db) {
+      const int quad = 4 * (kDkDB * w + db) + g;
+      d[db] = ld_v4i_agent(slot + kXchData + (size_t)(quad * 16 + j) * 16);
+    }
+    ml = ld_v4i_agent(slot + kXchMl + 16 * j);
+#pragma unroll
+    for (int db = 0; db < kDkDB; ++db) ok = ok && (uint32_t)d[db][1] == tag && (uint32_t)d[db][3] == tag;
+    ok = ok && (uint32_t)ml[1] == tag && (uint32_t)ml[3] == tag;
+    if (__ballot(!ok) == 0) return true;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > limit) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// (M, L, acc) += a partial with maximum M2, row sum L2 and output x * xs
+// (x unnormalised with xs = 1, or normalised with xs = L2), all in the log2
+// domain of the scores.
+__device__ __forceinline__ void dk_acc_merge(float& M, float& L, v4f (&acc)[kDkDB], float M2, float L2,
+                                             const v4f (&x)[kDkDB], float xs) {
+  const float Mn = fmaxf(M, M2);
+  const float f1 = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+  const float f2 = (M2 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M2 - Mn);
+  const float fx = f2 * xs;
+#pragma unroll
+  for (int db = 0; db < kDkDB; ++db) acc[db] = acc[db] * f1 + x[db] * fx;
+  L = L * f1 + L2 * f2;
+  M = Mn;
+}
+
+// All waves' flags ANDed (every wave calls; two barriers).
+__device__ __forceinline__ bool wg_all(int* words, int w, bool v) {
+  if ((threadIdx.x & 63) == 0) words[w] = v ? 1 : 0;
+  lds_barrier();
+  int all = 1;
+#pragma unroll
+  for (int i = 0; i < kDkWaves; ++i) all &= words[i];
+  lds_barrier();
+  return all != 0;
+}
+
 __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
   using L = LdsDK;
   const int lane = (int)threadIdx.x & 63;
@@ -1661,9 +1794,12 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
   const int lw = (G % 8 == 0) ? ((bid & 7) * (G >> 3) + (bid >> 3)) : bid;  // one XCD per contiguous range
   // With as many units as work-groups the planner's ranges are [g, g + 1)
   // (any valid ranges cover each unit once, and units are independent): no
-  // load of the range table then.
+  // load of the range table then.  Key parts always take one unit per
+  // work-group (the grid rounded up to whole XCD rounds of groups).
   int u_begin = lw, u_end = lw + 1;
-  if (a0.n_units != G) {
+  if (a0.dk_parts > 1) {
+    if (lw >= a0.n_units) return;
+  } else if (a0.n_units != G) {
     u_begin = ap->starts[lw];
     u_end = ap->starts[lw + 1];
   }
@@ -1677,14 +1813,19 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     // across units with a wait placed after this unit's first loads.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     const KHdr a = hdr_view(hr);
+    const int P = a.dk_parts;                    // 1, 2, 4 or 8
+    const int part = u & (P - 1), ub = u - part;  // the group's first unit
+    const int ug = u >> (31 - __builtin_clz(P));
+    const bool writer = part < P - 1, merger = P > 1 && !writer;
     const int lg = (a.hg == 8) ? 3 : 4;          // head groups of 8 or 16
-    const int t = u >> (6 - lg), h0 = (u & ((kN1 >> lg) - 1)) << lg;
+    const int t = ug >> (6 - lg), h0 = (ug & ((kN1 >> lg) - 1)) << lg;
     const int j = opaque(lane) & 15, g = lane >> 4;
     const bool real = j < a.hg;                 // head column j holds a real head
     const int h = h0 + (real ? j : 0);
     // every load of the unit's prologue is issued before any is used: the
     // lengths, index slots, the q fragment (lane j+16g: q[t, h0+j, 128 k +
-    // 32 g .. +31] for K-step k; every wave holds all of it) and its descale
+    // 32 g .. +31] for K-step k; every wave holds all of it), its descale and
+    // the group's slot epochs (lane q: writer q's)
     const TokLens tl = token_lens(a, t);
     const IdxPre<L::kNT> ip = load_indices<L::kNT>(a, t, 0);
     // (columns j >= hg load head h0 and are zeroed: no branch around the loads)
@@ -1699,6 +1840,8 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
       }
     }
     const float qd_h = a.q_ds[a.q_ds_per_head ? (size_t)t * a.n1 + h : (size_t)t];
+    int ep = 0;
+    if (P > 1) ep = *(const int*)xch_slot(a, ub + min(opaque(lane), P - 2));
     UnitState us;
     us.t = t;
     us.k = token_ctx(a, t, tl);
@@ -1707,7 +1850,8 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qreg[k][e] = real ? qreg[k][e] : 0;
     const float qs = real ? a.scale_log2 * qd_h : 0.f;
-    if (!us.k.valid) {   // padded query row: O = 0, lse = -inf
+    if (!us.k.valid) {   // padded query row: O = 0, lse = -inf (written by the merging part)
+      if (writer && P > 1) continue;
       for (int x = opaque(lane); x < a.hg * 64; x += 64) {
         const int hr = h0 + x / 64, d = 8 * (x % 64);
         if (w == 0) *(v4i*)(a.out + ((size_t)t * a.n1 + hr) * kD + d) = v4i{0, 0, 0, 0};
@@ -1720,23 +1864,108 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     us.w_lo = 0;
     if (a.topk > 0) us.n_c = compact_indices<L::kNT>(a, us.k, t, list, misc, 0, ip);
     else if (a.has_cmp) us.n_c = us.k.vis;
-    us.kb = 0;
-    us.ke = us.n_o + us.n_c;
+    const int nkeys = us.n_o + us.n_c;
+    int run_lo = dk_part_lo(part, P, nkeys), run_hi = dk_part_lo(part + 1, P, nkeys);
+    // a writer with keys announces itself (the result is read at the end)
+    int pres_old = 0;
+    int* pres = reinterpret_cast<int*>(xch_slot(a, u) + 64);
+    if (P > 1 && writer && run_hi > run_lo && threadIdx.x == 0) {
+      if (a.dk_test == 1) {   // test hook: arrive only once the merger has given up (bounded)
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (!(ws_poll(pres) & 2) && __builtin_amdgcn_s_memrealtime() - t0 < 100000) __builtin_amdgcn_s_sleep(8);
+      }
+      pres_old = ws_atomic_add(pres, 1);
+    }
 
-    v4f oacc[kDkDB];
-    float Mrun = kNegInf, lsum = 0.f;
-    if (threadIdx.x < 2) misc[L::kFlag + threadIdx.x] = 0;   // seen at dk_run's first barrier
-    dk_run(a, us, list, misc, smem, o, w, lane, qreg, qs, oacc, Mrun, lsum);
+    // Own keys, then (a merger) the writers' partials; a writer part the
+    // merger had to take over is run here too, one range per pass.
+    float accM = kNegInf, accL = 0.f;
+    v4f acc[kDkDB];
+#pragma unroll
+    for (int db = 0; db < kDkDB; ++db) acc[db] = v4f{0.f, 0.f, 0.f, 0.f};
+    uint32_t todo = 0;
+    bool polled = false;
+    for (;;) {
+      us.kb = run_lo;
+      us.ke = run_hi;
+      v4f oacc[kDkDB];
+      float Mrun = kNegInf, lsum = 0.f;
+      if (threadIdx.x < 2) misc[L::kFlag + threadIdx.x] = 0;   // seen at dk_run's first barrier
+      dk_run(a, us, list, misc, smem, o, w, lane, qreg, qs, oacc, Mrun, lsum);
+      if (threadIdx.x == 0) misc[49] = pres_old;   // (after the run: its atomic is long back) seen after the reduction's barriers
+      const float lh = dk_heads_reduce(misc, w, lane, lsum, false);
+      if (P == 1) {
+        accM = Mrun;
+        accL = lh;
+#pragma unroll
+        for (int db = 0; db < kDkDB; ++db) acc[db] = oacc[db];
+        break;
+      }
+      if (writer) {
+        if (run_hi > run_lo) {
+          if (misc[49] & 2) {   // the merger took this part over
+            if (threadIdx.x == 0) ws_atomic_xchg(pres, 0);
+          } else {
+            dk_xch_write(xch_slot(a, u), (uint32_t)__builtin_amdgcn_readlane(ep, part) + 1u, w, lane, oacc, Mrun, lh);
+          }
+        }
+        break;
+      }
+      dk_acc_merge(accM, accL, acc, Mrun, lh, oacc, 1.f);
+      if (!polled) {
+        polled = true;
+        const uint64_t lim1 = (uint64_t)a.dk_ticks, lim2 = (a.dk_test == 2) ? 0 : kDkWaitTicks2;
+        for (int q = 0; q < P - 1; ++q) {
+          if (dk_part_lo(q + 1, P, nkeys) <= dk_part_lo(q, P, nkeys)) continue;   // no keys: nothing written
+          uint8_t* sq = xch_slot(a, ub + q);
+          int* wq = reinterpret_cast<int*>(sq + 64);
+          const uint32_t eq = (uint32_t)__builtin_amdgcn_readlane(ep, q);
+          v4i d[kDkDB], ml;
+          bool ok = wg_all(misc + 32, w, dk_xch_poll(sq, eq + 1u, w, lane, d, ml, lim1));
+          int old = 1;
+          if (!ok) {
+            if (threadIdx.x == 0) misc[48] = ws_atomic_add(wq, 2);
+            lds_barrier();
+            old = misc[48];
+            lds_barrier();
+            if (old & 1) ok = wg_all(misc + 32, w, dk_xch_poll(sq, eq + 1u, w, lane, d, ml, lim2));
+          }
+          if (ok) {
+            v4f x[kDkDB];
+#pragma unroll
+            for (int db = 0; db < kDkDB; ++db)
+              x[db] = v4f{__uint_as_float((uint32_t)d[db][0] << 16), __uint_as_float((uint32_t)d[db][0] & 0xffff0000u),
+                          __uint_as_float((uint32_t)d[db][2] << 16), __uint_as_float((uint32_t)d[db][2] & 0xffff0000u)};
+            const float Lq = __int_as_float(ml[2]);
+            dk_acc_merge(accM, accL, acc, __int_as_float(ml[0]), Lq, x, Lq);
+          } else {
+            todo |= 1u << q;
+          }
+          if (threadIdx.x == 0) {
+            if (old & 1) ws_atomic_xchg(wq, 0);   // (an absent writer clears the word when it comes)
+            *(int*)sq = (int)(eq + 1u);           // the slot's next epoch
+          }
+        }
+      }
+      if (!todo) break;
+      const int q = __builtin_ctz(todo);
+      todo &= todo - 1u;
+      run_lo = dk_part_lo(q, P, nkeys);
+      run_hi = dk_part_lo(q + 1, P, nkeys);
+    }
+    if (P > 1 && writer) {
+      if (u + 1 < u_end) lds_barrier();
+      continue;
+    }
 
     // ---------------- epilogue: normalise, add the sink, bf16 through LDS ----------------
     const KHdr& ae = a;
-    const float lh = dk_heads_reduce(misc, w, lane, lsum, false);
     const float sg = (ae.sinks && real) ? ae.sinks[h] * kLog2e : kNegInf;
-    const float Mf = fmaxf(Mrun, sg);
+    const float Mf = fmaxf(accM, sg);
     float lse_v = kNegInf, sc = 0.f;
     if (Mf != kNegInf) {
-      const float af = (Mrun == kNegInf) ? 0.f : exp2f(Mrun - Mf);
-      const float Lf = af * lh + ((sg == kNegInf) ? 0.f : exp2f(sg - Mf));
+      const float af = (accM == kNegInf) ? 0.f : exp2f(accM - Mf);
+      const float Lf = af * accL + ((sg == kNegInf) ? 0.f : exp2f(sg - Mf));
       sc = af / Lf;
       lse_v = (Mf + __log2f(Lf)) * kLn2;
     }
@@ -1746,7 +1975,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
 #pragma unroll
     for (int db = 0; db < kDkDB; ++db) {
       const int d = 16 * (kDkDB * w + db) + 4 * g;
-      *(uint2*)(smem + j * kRow + 2 * d) = pack_bf16x4(sc * oacc[db][0], sc * oacc[db][1], sc * oacc[db][2], sc * oacc[db][3]);
+      *(uint2*)(smem + j * kRow + 2 * d) = pack_bf16x4(sc * acc[db][0], sc * acc[db][1], sc * acc[db][2], sc * acc[db][3]);
     }
     lds_barrier();
     // wave w stores head rows w, w + waves, ...: a row is 1 KiB = 64 lanes x 16 bytes
@@ -2618,8 +2847,9 @@ pf_kernel(const KArgs a) {
 // exp rule, sink added once), so the merge is spread over the token's
 // work-groups.  The exchange relies on the units of a token sharing one L2:
 // partial stores are complete (s_waitcnt) before the arrival atomic, the sync
-// words are only touched by L2 atomics or L1-bypassing loads, and merge reads
-// follow an L1 invalidate.  Each unit also records the XCD it ran on
+// words are only touched by L2 atomics or L1-bypassing loads, and a merge
+// reads the other units' partial lines for the first time in the launch (so
+// its CU's L1 holds none of them).  Each unit also records the XCD it ran on
 // (HW_REG_XCC_ID); a merge that finds a partial from another XCD writes NaN
 // instead of a result, so a broken placement cannot pass silently.
 // Sync words per token: [0] arrivals, [1] generation, [2] claims.  They must
@@ -2648,21 +2878,6 @@ struct LdsSK {
 };
 static_assert(LdsSK::kBytes <= 160 * 1024, "LDS");
 
-// A read of a sync word where the atomics act (L2): an atomic add of zero
-// that returns the old value, waited for in the same asm.  (A load with the
-// workgroup-scope bit may be served by the CU's L1, which would keep
-// returning the value it cached first.)
-__device__ __forceinline__ int sk_poll(int* p) {
-  int v;
-  asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p), "v"(0) : "memory");
-  return v;
-}
-__device__ __forceinline__ int sk_atomic_add(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ int sk_atomic_xchg(int* p, int v) {
-  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
 __device__ __forceinline__ int sk_xcc_id() {
   int id;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(id));
@@ -2951,16 +3166,16 @@ __device__ __forceinline__ void sk_body(KArgPtr ap, uint8_t* smem, int w) {
   if (threadIdx.x == 0) {
     int go = 1;
     // the generation cannot move before this unit arrives
-    const int gen0 = sk_poll(sy + 1);
-    if (sk_atomic_add(sy, 1) == S - 1) {   // last arrival: a new generation, claims from 0
-      sk_atomic_xchg(sy, 0);
-      sk_atomic_xchg(sy + 2, 0);
+    const int gen0 = ws_poll(sy + 1);
+    if (ws_atomic_add(sy, 1) == S - 1) {   // last arrival: a new generation, claims from 0
+      ws_atomic_xchg(sy, 0);
+      ws_atomic_xchg(sy + 2, 0);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      sk_atomic_add(sy + 1, 1);
+      ws_atomic_add(sy + 1, 1);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     } else {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (sk_poll(sy + 1) == gen0) {
+      while (ws_poll(sy + 1) == gen0) {
         if (__builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)kSkSpinTicks) { go = 0; break; }
         __builtin_amdgcn_s_sleep(1);
       }
@@ -2969,10 +3184,10 @@ __device__ __forceinline__ void sk_body(KArgPtr ap, uint8_t* smem, int w) {
   }
   __syncthreads();
   if (!misc[0]) return;   // uniform: the others merge every group
-  asm volatile("buffer_inv sc0" ::: "memory");   // partial reads come from L2, not from a stale L1 line
+  asm volatile("buffer_inv sc0" ::: "memory");   // (the other units' partial lines are first read here: L1 holds none)
   for (;;) {
     __syncthreads();   // misc[1] is read by every thread before it is rewritten
-    if (threadIdx.x == 0) misc[1] = sk_atomic_add(sy + 2, 1);
+    if (threadIdx.x == 0) misc[1] = ws_atomic_add(sy + 2, 1);
     __syncthreads();
     const int grp = misc[1];
     if (grp >= kN1 / kSkHeadGroup) break;
@@ -3375,7 +3590,7 @@ static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 constexpr int kMaxDevices = 64;
 
 __global__ void zero_words_kernel(int32_t* p, int n) {
-  for (int i = (int)threadIdx.x; i < n; i += (int)blockDim.x) p[i] = 0;
+  for (int i = (int)(blockIdx.x * blockDim.x + threadIdx.x); i < n; i += (int)(gridDim.x * blockDim.x)) p[i] = 0;
 }
 
 int noalloc_scratch(void** ptr, void* stream) {
@@ -3391,10 +3606,10 @@ int noalloc_scratch(void** ptr, void* stream) {
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return (int)e;
     if (!p) return (int)hipErrorInvalidSymbol;
-    // the workspace's sync words start at zero (a fill kernel on the
-    // caller's stream, ahead of the first forward that uses them)
-    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, (int32_t*)p,
-                       (int)(kWsSyncBytes / 4));
+    // the workspace's sync words and exchange slots start at zero (a fill
+    // kernel on the caller's stream, ahead of the first forward that uses them)
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream, (int32_t*)p,
+                       (int)(kWsFixedBytes / 4));
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     addr[dev] = p;

@@ -15,6 +15,7 @@ from sparse_compressed_mla_amd.binding import CsmlaProblem, CsmlaHostLengths, Cs
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, MISMATCH = 0, 1, 2, 3, 4
+WS_FIXED = 4096 + 256 * 33792   # sync words + exchange slots, at the start of every workspace
 
 
 def declared_functions():
@@ -132,7 +133,50 @@ def test_plan_head_split_for_small_decode_batches(monkeypatch):
     assert md[12] == 0
     monkeypatch.setenv("CSMLA_KERNEL", "heads16")
     _, md, _ = m.csmla_plan(base_problem())
-    assert md[12] == 16 and md[6] == 32 * 4
+    assert md[12] == 16 and md[6] == 32 * 4 and md[14] == 1
+
+
+def test_plan_key_parts(monkeypatch):
+    """Up to 16 decode tokens: 8-head groups, each split into two key parts on
+    one XCD (the grid a whole number of XCD rounds of groups, one unit per
+    work-group, the fixed workspace of sync words and exchange slots);
+    CSMLA_DK_PARTS overrides the count within what fits 256 work-groups and
+    the key list's tiles."""
+    for k in ("CSMLA_KERNEL", "CSMLA_DK_PARTS", "CSMLA_DK_TEST"):
+        monkeypatch.delenv(k, raising=False)
+    _, md, ws = m.csmla_plan(base_problem())
+    assert md[12] == 8 and md[14] == 1 and ws == 0                 # 32 tokens: no parts
+    for b, grid in ((16, 256), (4, 64), (3, 48), (1, 16)):
+        _, md, ws = m.csmla_plan(base_problem(batch=b, t1=b))
+        assert md[12] == 8 and md[14] == 2 and md[6] == b * 16 and md[7] == grid and ws == WS_FIXED, (b, md[:16])
+        assert md[5] == 1 and md[15] == 0
+    monkeypatch.setenv("CSMLA_DK_PARTS", "8")
+    _, md, _ = m.csmla_plan(base_problem(batch=4, t1=4))
+    assert md[14] == 4 and md[6] == 4 * 8 * 4 and md[7] == 128     # 640 keys = 5 tiles: at most 4 parts
+    _, md, _ = m.csmla_plan(base_problem(batch=4, t1=4, topk=128))
+    assert md[14] == 2                                             # 256 keys: 2 tiles
+    monkeypatch.setenv("CSMLA_DK_PARTS", "1")
+    _, md, ws = m.csmla_plan(base_problem(batch=4, t1=4))
+    assert md[14] == 1 and md[6] == 32 and ws == 0
+    monkeypatch.setenv("CSMLA_DK_PARTS", "2")
+    monkeypatch.setenv("CSMLA_KERNEL", "heads16")
+    _, md, _ = m.csmla_plan(base_problem())
+    assert md[12] == 16 and md[14] == 2 and md[6] == 256 and md[7] == 256
+    monkeypatch.setenv("CSMLA_DK_TEST", "1")
+    _, md, _ = m.csmla_plan(base_problem())
+    assert md[15] == 1
+
+
+def test_forward_rejects_inconsistent_key_parts(monkeypatch):
+    for k in ("CSMLA_KERNEL", "CSMLA_DK_PARTS", "CSMLA_DK_TEST"):
+        monkeypatch.delenv(k, raising=False)
+    p = base_problem(batch=4, t1=4)
+    _, md, ws = m.csmla_plan(p)
+    assert md[14] == 2
+    for word, val in ((14, 3), (14, 4), (14, 1), (7, 48), (15, 3), (12, 64)):
+        bad = md.copy(); bad[word] = val
+        assert m.csmla_forward(p, fake_tensors(ws), bad, raise_on_error=False) == MISMATCH, (word, val)
+    assert m.csmla_forward(p, fake_tensors(ws - 256), md, raise_on_error=False) == WORKSPACE
 
 
 def test_forward_rejects_bad_head_group(monkeypatch):
@@ -155,8 +199,9 @@ def test_plan_invariants_and_determinism(monkeypatch):
     starts = md[16:16 + G + 1]
     assert starts[0] == 0 and starts[-1] == U and np.all(np.diff(starts) >= 1)
     a256 = lambda x: (x + 255) // 256 * 256
-    # workspace: 4 KiB of sync words, per-unit XCD ids, the partial outputs (bf16), their (max, sum)
-    o = a256(4096 + 4 * U)
+    # workspace: 4 KiB of sync words, 256 exchange slots of 33 KiB, per-unit XCD ids, the
+    # partial outputs (bf16), their (max, sum)
+    o = a256(WS_FIXED + 4 * U)
     assert ws == (0 if S == 1 else a256(o + U * 64 * 512 * 2) + U * 64 * 8)
     _, md2, ws2 = m.csmla_plan(p)
     assert np.array_equal(md, md2) and ws == ws2

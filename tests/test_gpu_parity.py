@@ -24,20 +24,26 @@ DEV = "cuda:0"
 # Every test runs with the planner's own kernel choice ("auto") and with each
 # kernel forced (where the problem allows it), so that every path meets the
 # same bar on the same cases: the key-split kernel with its combine, the
-# head-split decode kernel, the whole-token prefill kernel and the split-key
-# decode kernel with its in-kernel merge.
-KERNEL_MODES = ["auto", "split", "heads16", "prefill", "splitkey"]
+# head-split decode kernel (also with its keys split into parts that merge
+# inside the kernel, in groups of 16 and of 8 heads), the whole-token prefill
+# kernel and the split-key decode kernel with its in-kernel merge.
+KERNEL_MODES = ["auto", "split", "heads16", "parts16", "parts8", "prefill", "splitkey"]
+_MODE_ENV = {"parts16": ("heads16", "8"), "parts8": ("heads8", "8")}
 
 
 @pytest.fixture(autouse=True, params=KERNEL_MODES)
 def kernel_mode(request):
     mode = request.param
+    os.environ.pop("CSMLA_DK_PARTS", None)
     if mode == "auto":
         os.environ.pop("CSMLA_KERNEL", None)
+    elif mode in _MODE_ENV:
+        os.environ["CSMLA_KERNEL"], os.environ["CSMLA_DK_PARTS"] = _MODE_ENV[mode]
     else:
         os.environ["CSMLA_KERNEL"] = mode
     yield mode
     os.environ.pop("CSMLA_KERNEL", None)
+    os.environ.pop("CSMLA_DK_PARTS", None)
 
 
 def say(msg):
