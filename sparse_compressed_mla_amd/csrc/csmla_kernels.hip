@@ -1816,7 +1816,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     const int P = a.dk_parts;                    // 1, 2, 4 or 8
     const int part = u & (P - 1), ub = u - part;  // the group's first unit
     const int ug = u >> (31 - __builtin_clz(P));
-    const bool writer = part < P - 1, merger = P > 1 && !writer;
+    const bool writer = part < P - 1;
     const int lg = (a.hg == 8) ? 3 : 4;          // head groups of 8 or 16
     const int t = ug >> (6 - lg), h0 = (ug & ((kN1 >> lg) - 1)) << lg;
     const int j = opaque(lane) & 15, g = lane >> 4;
@@ -2550,7 +2550,7 @@ __device__ __forceinline__ float pf_probs(const float (&E)[8], float Mh, v4f iv0
 template <int PER_TILE>
 __device__ __forceinline__ void pf_body(KArgPtr ap, uint8_t* smem, int w) {
   using L = LdsPF;
-  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5;
+  const int lane = opaque((int)threadIdx.x & 63);
   const int kb = w & 1, hb = (w >> 1) & 1, dh = w >> 2;
   const HdrRegs hr = load_hdr_regs(ap);
   const KHdr a0 = hdr_view(hr);
