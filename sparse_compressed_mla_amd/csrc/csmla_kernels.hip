@@ -2037,56 +2037,55 @@ __global__ void __launch_bounds__(256) combine_kernel(const KArgs a) {
   const size_t ostride = (size_t)kN1 * kD;
   const uint16_t* op = a.ws_o + ((size_t)t * S * kN1 + h) * kD + col;
   const float sg = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
-  float M = sg;
+  // Eight splits at a time, every load of a group (the (m, l) pairs and the
+  // partial rows) issued together; the running maximum starts at the sink and
+  // the sums are rescaled when a later group raises it (one group, so one
+  // round trip, for up to eight splits).
+  float M = sg, L = 0.f;
   bool padded = false;
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float m8[8], l8[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      m8[j] = (s0 + j < S) ? ml[(size_t)(s0 + j) * kN1 * 2] : kNegInf;
-      l8[j] = (s0 + j < S) ? ml[(size_t)(s0 + j) * kN1 * 2 + 1] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      M = fmaxf(M, m8[j]);
-      padded |= l8[j] < 0.f;
-    }
-  }
   float acc[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-  float L = 0.f;
-  if (!padded && M != kNegInf) {
-    L = (sg == kNegInf) ? 0.f : exp2f(sg - M);
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      float wgt[8];
-      uint4 x0[8], x1[8];
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float m8[8], l8[8];
+    uint4 x0[8], x1[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool in = s0 + j < S;
-        const float Ms = in ? ml[(size_t)(s0 + j) * kN1 * 2] : kNegInf;
-        const float ls = in ? ml[(size_t)(s0 + j) * kN1 * 2 + 1] : 0.f;
-        wgt[j] = (Ms == kNegInf) ? 0.f : ls * exp2f(Ms - M);
-        if (in) {
-          const uint4* src = (const uint4*)(op + (size_t)(s0 + j) * ostride);
-          x0[j] = src[0];
-          x1[j] = src[1];
-        } else {
-          x0[j] = make_uint4(0, 0, 0, 0);
-          x1[j] = x0[j];
-        }
-      }
+    for (int j = 0; j < 8; ++j) {
+      const int sj = min(s0 + j, S - 1);   // past S: split S - 1 again, weighed zero
+      m8[j] = ml[(size_t)sj * kN1 * 2];
+      l8[j] = ml[(size_t)sj * kN1 * 2 + 1];
+      const uint4* src = (const uint4*)(op + (size_t)sj * ostride);
+      x0[j] = src[0];
+      x1[j] = src[1];
+    }
+    float Mn = M;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        L += wgt[j];
-        const uint32_t xs[8] = {x0[j].x, x0[j].y, x0[j].z, x0[j].w, x1[j].x, x1[j].y, x1[j].z, x1[j].w};
+    for (int j = 0; j < 8; ++j) {
+      const bool in = s0 + j < S;
+      Mn = in ? fmaxf(Mn, m8[j]) : Mn;
+      padded |= in && l8[j] < 0.f;
+    }
+    const float fa = (M == kNegInf) ? 0.f : exp2f(M - Mn);   // (the sink's own weight is added at the end)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          acc[2 * e] += wgt[j] * __uint_as_float(xs[e] << 16);
-          acc[2 * e + 1] += wgt[j] * __uint_as_float(xs[e] & 0xffff0000u);
-        }
+    for (int e = 0; e < 16; ++e) acc[e] *= fa;
+    L *= fa;
+    M = Mn;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float wgt = (s0 + j >= S || m8[j] == kNegInf) ? 0.f : l8[j] * exp2f(m8[j] - M);
+      L += wgt;
+      const uint32_t xs[8] = {x0[j].x, x0[j].y, x0[j].z, x0[j].w, x1[j].x, x1[j].y, x1[j].z, x1[j].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc[2 * e] += wgt * __uint_as_float(xs[e] << 16);
+        acc[2 * e + 1] += wgt * __uint_as_float(xs[e] & 0xffff0000u);
       }
     }
+  }
+  if (padded || M == kNegInf) {
+    L = 0.f;
+  } else if (sg != kNegInf) {
+    L += exp2f(sg - M);
   }
   const float inv = (L > 0.f) ? 1.0f / L : 0.f;
   uint32_t o[8];
