@@ -1401,23 +1401,31 @@ __device__ __forceinline__ void dk_src2(const uint64_t* kaddr, int tile, int w, 
 // M0 = the wave's row block of the half, plus the pair's offset added in
 // the same asm (per-instruction destinations would otherwise be formed once
 // for the whole kernel and held in spilled scalar registers).
-// (nt: the non-temporal policy; this kernel's gathers ran ~4% faster with it,
-// the whole-token kernel's, whose rows other tokens reuse, slower)
-__device__ __forceinline__ void dk_issue(const DkSrc& s, int mi, int half, uint8_t* tb, int w) {
+// nt (wave-uniform): the non-temporal policy, for work-groups that run one
+// unit.  The work-groups of a token then read its rows at about the same
+// time, and their gathers ran ~4% faster with it; a work-group that runs
+// several units of a token in turn re-reads the rows a unit's time later, and
+// such plans lost ~8% with it (so did the whole-token kernel, whose rows
+// later tokens reuse).
+__device__ __forceinline__ void dk_issue(const DkSrc& s, int mi, int half, uint8_t* tb, int w, bool nt) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tb + (64 * half + 2 * kDkGI * w) * kD));
   const uint32_t off = (uint32_t)(2 * mi * kD);
-  asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(base), "v"(s.p[mi]),
-               "s"(off) : "m0", "scc");
+  if (nt)
+    asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(base), "v"(s.p[mi]),
+                 "s"(off) : "m0", "scc");
+  else
+    asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(s.p[mi]),
+                 "s"(off) : "m0", "scc");
 }
 
 // The whole tile at once (both halves).
-__device__ __forceinline__ void dk_gather_tile(const uint64_t* kaddr, int tile, uint8_t* tb, int w) {
+__device__ __forceinline__ void dk_gather_tile(const uint64_t* kaddr, int tile, uint8_t* tb, int w, bool nt) {
   DkSrc s0, s1;
   dk_src2(kaddr, tile, w, s0, s1);
 #pragma unroll
-  for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s0, mi, 0, tb, w);
+  for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s0, mi, 0, tb, w, nt);
 #pragma unroll
-  for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s1, mi, 1, tb, w);
+  for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s1, mi, 1, tb, w, nt);
 }
 
 // The next tile's gather: src[h] holds half h's source addresses; half 0 is
@@ -1427,9 +1435,9 @@ struct DkFeed {
   DkSrc src[2];
   uint8_t* tb;
   int w;
-  bool on;
+  bool on, nt;
   __device__ __forceinline__ void operator()(int x) const {
-    if (on) dk_issue(src[x / kDkGI], x % kDkGI, x / kDkGI, tb, w);
+    if (on) dk_issue(src[x / kDkGI], x % kDkGI, x / kDkGI, tb, w, nt);
   }
 };
 
@@ -1603,7 +1611,7 @@ __device__ __forceinline__ float dk_heads_reduce(int* misc, int w, int lane, flo
 // and row sums, and rewrites the tile's P.  Flags start at zero.
 __device__ __forceinline__ void dk_run(const KHdr& a, UnitState& us, int* list, int* misc, uint8_t* smem,
                                        const DkOffsets& o, int w, int lane, const v8i (&qreg)[4], float qs,
-                                       v4f (&oacc)[kDkDB], float& Mrun, float& lsum) {
+                                       v4f (&oacc)[kDkDB], float& Mrun, float& lsum, bool nt) {
   using L = LdsDK;
   const int j = lane & 15, g = lane >> 4;
   int* flag = misc + L::kFlag;   // [2]: by tile parity
@@ -1619,13 +1627,14 @@ __device__ __forceinline__ void dk_run(const KHdr& a, UnitState& us, int* list, 
     {
       const ChunkScales<L> cs = resolve_rows<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
       lds_barrier();
-      dk_gather_tile(kaddr, 0, smem + L::kTiles, w);
+      dk_gather_tile(kaddr, 0, smem + L::kTiles, w, nt);
       resolve_scales<L>(cs, smem);
     }
     // source addresses of the next tile's gather, formed a step ahead (their
     // LDS round trip overlaps the end of the previous step)
     DkFeed feed;
     feed.w = w;
+    feed.nt = nt;
     if (tiles > 1) dk_src2(kaddr, 1, w, feed.src[0], feed.src[1]);
     gather_barrier(false);
     for (int i = 0; i < tiles; ++i, ++it) {
@@ -1645,7 +1654,7 @@ __device__ __forceinline__ void dk_run(const KHdr& a, UnitState& us, int* list, 
       }
       if (next) {   // half 1: in flight during the probabilities and P V
 #pragma unroll
-        for (int mi = 0; mi < kDkGI; ++mi) dk_issue(feed.src[1], mi, 1, feed.tb, w);
+        for (int mi = 0; mi < kDkGI; ++mi) dk_issue(feed.src[1], mi, 1, feed.tb, w, nt);
       }
       const float lprev = lsum;
       dk_probs(smem, i, w, j, g, Mrun, s, lsum);
@@ -1784,6 +1793,9 @@ __device__ __forceinline__ bool wg_all(int* words, int w, bool v) {
   return all != 0;
 }
 
+// NT: the gathers use the non-temporal policy (dk_issue); the host picks it
+// for plans whose work-groups run one unit each.
+template <int NT>
 __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
   using L = LdsDK;
   const int lane = (int)threadIdx.x & 63;
@@ -1803,6 +1815,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     u_begin = ap->starts[lw];
     u_end = ap->starts[lw + 1];
   }
+  const bool nt = NT != 0;
   int* list = reinterpret_cast<int*>(smem + L::kList);
   int* misc = reinterpret_cast<int*>(smem + L::kMisc);
   const DkOffsets o = dk_offsets(lane, w);
@@ -1891,7 +1904,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
       v4f oacc[kDkDB];
       float Mrun = kNegInf, lsum = 0.f;
       if (threadIdx.x < 2) misc[L::kFlag + threadIdx.x] = 0;   // seen at dk_run's first barrier
-      dk_run(a, us, list, misc, smem, o, w, lane, qreg, qs, oacc, Mrun, lsum);
+      dk_run(a, us, list, misc, smem, o, w, lane, qreg, qs, oacc, Mrun, lsum, nt);
       if (threadIdx.x == 0) misc[49] = pres_old;   // (after the run: its atomic is long back) seen after the reduction's barriers
       const float lh = dk_heads_reduce(misc, w, lane, lsum, false);
       if (P == 1) {
@@ -1987,11 +2000,12 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
   }
 }
 
+template <int NT>
 __global__ void __launch_bounds__(kDkThreads) __attribute__((amdgpu_waves_per_eu(kDkWaves / 4, kDkWaves / 4)))
 dk_kernel(const KArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LdsDK::kBytes];
   const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  dk_body((KArgPtr)__builtin_amdgcn_kernarg_segment_ptr(), smem, w);
+  dk_body<NT>((KArgPtr)__builtin_amdgcn_kernarg_segment_ptr(), smem, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -3660,7 +3674,10 @@ int launch_forward(const KArgs& a, void* stream) {
     return (int)hipGetLastError();
   }
   if (a.hg > 0) {
-    hipLaunchKernelGGL(dk_kernel, dim3(a.grid), dim3(kDkThreads), 0, st, a);
+    if (a.dk_parts > 1 || a.n_units <= a.grid)   // one unit per work-group
+      hipLaunchKernelGGL(dk_kernel<1>, dim3(a.grid), dim3(kDkThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(dk_kernel<0>, dim3(a.grid), dim3(kDkThreads), 0, st, a);
     return (int)hipGetLastError();
   }
   if (a.scale_mode == 1)
