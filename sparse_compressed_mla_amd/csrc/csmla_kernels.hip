@@ -1305,6 +1305,15 @@ __device__ __forceinline__ int ws_poll(int* p) {
 __device__ __forceinline__ int ws_atomic_add(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+// The same with the address in a register the compiler cannot see into: a
+// uniform-address add would be rewritten into one add per wave plus a scan of
+// the lanes, which reads the result at once (and so waits for every load
+// issued before it); this one is waited for only where its result is used.
+__device__ __forceinline__ int ws_atomic_add_late(int* p, int v) {
+  uint64_t q = (uint64_t)(uintptr_t)p;
+  asm volatile("" : "+v"(q));
+  return __hip_atomic_fetch_add(reinterpret_cast<int*>((uintptr_t)q), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 __device__ __forceinline__ int ws_atomic_xchg(int* p, int v) {
   return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -1426,6 +1435,38 @@ __device__ __forceinline__ void dk_gather_tile(const uint64_t* kaddr, int tile, 
   for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s0, mi, 0, tb, w, nt);
 #pragma unroll
   for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s1, mi, 1, tb, w, nt);
+}
+
+// Tile 0 of a unit whose keys start with a whole tile of band keys, in a
+// paged ori cache with blocks of >= 128 rows (the tile then spans at most two
+// blocks), gathered as soon as the token's lengths are known, before its
+// index slots are compacted.  The two block-table entries come through scalar
+// loads, so this waits neither for the index slots still in flight nor for
+// anything queued behind them on the vector memory counter; the row
+// addresses are formed in registers (no LDS round trip).
+__device__ __forceinline__ void dk_band_tile(const KHdr& a, const Tok& k, uint8_t* tb, int w, bool nt) {
+  const int bs = a.ori_bs, cols = a.ori_cols;
+  const int b0 = k.lo / bs, split = (b0 + 1) * bs;   // the second block starts at position split
+  const ConstI32 trow = (ConstI32)(a.ori_tab + (size_t)k.b * cols);
+  const int e0 = trow[b0], e1 = trow[min(b0 + 1, cols - 1)];
+  const uint8_t* kv = gptr(a.ori_kv);
+  const int lane = opaque((int)threadIdx.x & 63), g = lane >> 5, li = lane & 31;
+  constexpr int RW = 2 * kDkGI;
+  DkSrc s[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int mi = 0; mi < kDkGI; ++mi) {
+      const int r = RW * w + 2 * mi + g;
+      const int j = k.lo + 64 * half + r;
+      const bool second = j >= split;
+      const int64_t row = (int64_t)(second ? e1 : e0) * bs + (j - (second ? split : b0 * bs));
+      s[half].p[mi] = (uint64_t)(uintptr_t)(kv + row * kD) + 16u * (uint32_t)(li ^ swz(r));
+    }
+#pragma unroll
+  for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s[0], mi, 0, tb, w, nt);
+#pragma unroll
+  for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s[1], mi, 1, tb, w, nt);
 }
 
 // The next tile's gather: src[h] holds half h's source addresses; half 0 is
@@ -1610,8 +1651,8 @@ __device__ __forceinline__ float dk_heads_reduce(int* misc, int w, int lane, flo
 // then every wave takes the new per-head maximum, rescales its accumulators
 // and row sums, and rewrites the tile's P.  Flags start at zero.
 __device__ __forceinline__ void dk_run(const KHdr& a, UnitState& us, int* list, int* misc, uint8_t* smem,
-                                       const DkOffsets& o, int w, int lane, const v8i (&qreg)[4], float qs,
-                                       v4f (&oacc)[kDkDB], float& Mrun, float& lsum, bool nt) {
+                                       const DkOffsets& o, int w, int lane, const v8i (&qreg)[4], float qd,
+                                       v4f (&oacc)[kDkDB], float& Mrun, float& lsum, bool nt, bool band_pre) {
   using L = LdsDK;
   const int j = lane & 15, g = lane >> 4;
   int* flag = misc + L::kFlag;   // [2]: by tile parity
@@ -1627,7 +1668,7 @@ __device__ __forceinline__ void dk_run(const KHdr& a, UnitState& us, int* list, 
     {
       const ChunkScales<L> cs = resolve_rows<L>(a, us.k, us.n_o, list, us.w_lo, c0, c1, smem);
       lds_barrier();
-      dk_gather_tile(kaddr, 0, smem + L::kTiles, w, nt);
+      if (!(band_pre && c0 == us.kb)) dk_gather_tile(kaddr, 0, smem + L::kTiles, w, nt);   // (else in flight)
       resolve_scales<L>(cs, smem);
     }
     // source addresses of the next tile's gather, formed a step ahead (their
@@ -1637,6 +1678,10 @@ __device__ __forceinline__ void dk_run(const KHdr& a, UnitState& us, int* list, 
     feed.nt = nt;
     if (tiles > 1) dk_src2(kaddr, 1, w, feed.src[0], feed.src[1]);
     gather_barrier(false);
+    // (formed here, after the wait above, and kept here through an opaque
+    // copy: hoisted out of the chunk loop, its wait for the q descale would
+    // also wait for the band tile's gathers)
+    const float qs = a.scale_log2 * __int_as_float(opaque(__float_as_int(qd)));
     for (int i = 0; i < tiles; ++i, ++it) {
       uint8_t* tb = smem + L::kTiles + (i & 1) * kDkTileBytes;
       const bool next = __builtin_amdgcn_readfirstlane(i + 1 < tiles ? 1 : 0) != 0;
@@ -1841,10 +1886,11 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     // the group's slot epochs (lane q: writer q's)
     const TokLens tl = token_lens(a, t);
     const IdxPre<L::kNT> ip = load_indices<L::kNT>(a, t, 0);
-    // (columns j >= hg load head h0 and are zeroed: no branch around the loads)
+    // (columns j >= hg read the zero row: no branch around the loads, and no
+    // select on the loaded values, which would wait for them here)
     v8i qreg[4];
     {
-      const uint8_t* qrow = a.q + ((size_t)t * a.n1 + h) * kD + 32 * g;
+      const uint8_t* qrow = real ? a.q + ((size_t)t * a.n1 + h) * kD + 32 * g : g_zero_row + 32 * g;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const v4i x0 = *(const v4i*)(qrow + 128 * k);
@@ -1852,17 +1898,13 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
         qreg[k] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
     }
-    const float qd_h = a.q_ds[a.q_ds_per_head ? (size_t)t * a.n1 + h : (size_t)t];
+    const float qd_h = *(real ? a.q_ds + (a.q_ds_per_head ? (size_t)t * a.n1 + h : (size_t)t)
+                              : reinterpret_cast<const float*>(g_zero_row));
     int ep = 0;
     if (P > 1) ep = *(const int*)xch_slot(a, ub + min(opaque(lane), P - 2));
     UnitState us;
     us.t = t;
     us.k = token_ctx(a, t, tl);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qreg[k][e] = real ? qreg[k][e] : 0;
-    const float qs = real ? a.scale_log2 * qd_h : 0.f;
     if (!us.k.valid) {   // padded query row: O = 0, lse = -inf (written by the merging part)
       if (writer && P > 1) continue;
       for (int x = opaque(lane); x < a.hg * 64; x += 64) {
@@ -1875,6 +1917,11 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     us.n_o = us.k.hi - us.k.lo;
     us.n_c = 0;
     us.w_lo = 0;
+    // tile 0 in flight before the index slots are compacted (dk_band_tile);
+    // the first part's range starts at key 0
+    const bool band_pre = a.layout_kv == 2 && a.ori_topk == 0 && a.topk > 0 && part == 0 &&
+                          us.n_o >= kDkRows && a.ori_bs >= kDkRows;
+    if (band_pre) dk_band_tile(a, us.k, smem + L::kTiles, w, nt);
     if (a.topk > 0) us.n_c = compact_indices<L::kNT>(a, us.k, t, list, misc, 0, ip);
     else if (a.has_cmp) us.n_c = us.k.vis;
     const int nkeys = us.n_o + us.n_c;
@@ -1887,7 +1934,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         while (!(ws_poll(pres) & 2) && __builtin_amdgcn_s_memrealtime() - t0 < 100000) __builtin_amdgcn_s_sleep(8);
       }
-      pres_old = ws_atomic_add(pres, 1);
+      pres_old = ws_atomic_add_late(pres, 1);
     }
 
     // Own keys, then (a merger) the writers' partials; a writer part the
@@ -1904,7 +1951,7 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
       v4f oacc[kDkDB];
       float Mrun = kNegInf, lsum = 0.f;
       if (threadIdx.x < 2) misc[L::kFlag + threadIdx.x] = 0;   // seen at dk_run's first barrier
-      dk_run(a, us, list, misc, smem, o, w, lane, qreg, qs, oacc, Mrun, lsum, nt);
+      dk_run(a, us, list, misc, smem, o, w, lane, qreg, qd_h, oacc, Mrun, lsum, nt, band_pre && !polled);
       if (threadIdx.x == 0) misc[49] = pres_old;   // (after the run: its atomic is long back) seen after the reduction's barriers
       const float lh = dk_heads_reduce(misc, w, lane, lsum, false);
       if (P == 1) {
