@@ -3294,9 +3294,8 @@ constexpr int kBkThreads = 256;
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 
 struct LdsBK {
-  static constexpr int kK = 0;                               // bf16 [32 keys][512]: 1 KiB rows, chunk ^ (key & 15)
-  static constexpr int kVT = kK + kBkKeys * 2 * kD;          // bf16 [512 d][32 keys]: 64-byte rows, chunk ^ ((d >> 2) & 3)
-  static constexpr int kP = kVT + kD * kBkKeys * 2;          // bf16 [64 heads][32 keys]: chunk ^ ((h >> 2) & 3)
+  static constexpr int kK = 0;                               // bf16 [32 keys][512]: 1 KiB rows, chunk ^ bk_swz(key)
+  static constexpr int kP = kK + kBkKeys * 2 * kD;           // bf16 [64 heads][32 keys]: chunk ^ ((h >> 2) & 3)
   static constexpr int kX = kP + kN1 * kBkKeys * 2;          // f32 [2 head blocks][64 lanes][16]: D-half-1 partials
   static constexpr int kAddr = kX + 2 * 64 * 16 * 4;         // u64 [kBkMaxKeys]: the unit's row addresses
   static constexpr int kList = kAddr + 8 * kBkMaxKeys;       // int [kListMax]: compacted cmp indices
@@ -3310,6 +3309,36 @@ static_assert(LdsBK::kBytes <= 160 * 1024, "LDS");
 
 __device__ __forceinline__ v16f mma_bf16(bf8_t a, bf8_t b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte chunk c of key row `key` sits at chunk c ^ bk_swz(key).  Reads of
+// one chunk from 16 consecutive rows (S^T operands) and transpose reads of 4
+// consecutive rows x 2 chunks (P V operands) both reach 16 distinct chunks,
+// i.e. all 64 banks.
+__device__ __forceinline__ int bk_swz(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// V^T operand of O^T += V^T P^T (32 d x 16 keys, 8 keys per lane) straight
+// from the row-major K tile with two transpose reads: within each group of 16
+// lanes, lanes 4r..4r+3 address the 8-byte pieces of key row r (columns
+// dbase + 4 (j & 3) .. +3), and lane j receives column dbase + j of the four
+// rows.  Lane l: d = dblk + (l % 32), keys 16 ks + 8 (l / 32) .. +7.
+__device__ __forceinline__ bf8_t bk_vop(const uint8_t* kt, int dblk, int ks, int lane) {
+  const int gq = lane >> 4, j = lane & 15;
+  const int dbase = dblk + 16 * (gq & 1), e = dbase + 4 * (j & 3);
+  v4i out;
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int row = 16 * ks + 8 * (gq >> 1) + 4 * rd + (j >> 2);
+    const uint8_t* p = kt + row * 2 * kD + 16 * ((e >> 3) ^ bk_swz(row)) + 8 * ((e >> 2) & 1);
+    const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+    const v2i y = __builtin_bit_cast(v2i, x);
+    out[2 * rd] = y[0];
+    out[2 * rd + 1] = y[1];
+  }
+  return __builtin_bit_cast(bf8_t, out);
 }
 
 // The tile's raw bytes of one thread: keys 8 kq + j (j < 8) of the tile,
@@ -3351,29 +3380,15 @@ __device__ __forceinline__ v4i bk_nope8(v4i x, int scw, int tile) {
              (int)pack_bf16x2(f45[0] * sc, f45[1] * sc), (int)pack_bf16x2(f67[0] * sc, f67[1] * sc)};
 }
 
-// The block as bf16 into the K rows and, transposed, into the V^T rows.
+// The block as bf16 into the K rows (P V reads them transposed, bk_vop).
 template <int FMT>
 __device__ __forceinline__ void bk_store(const BkRaw& r, uint8_t* smem, int tid) {
   const int kq = tid >> 6, dq = tid & 63;
-  v4i v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (FMT == 2 && dq >= 8) ? bk_nope8(r.x[j], r.sc[j], (8 * dq - 64) >> 6) : r.x[j];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
+    const v4i v = (FMT == 2 && dq >= 8) ? bk_nope8(r.x[j], r.sc[j], (8 * dq - 64) >> 6) : r.x[j];
     const int key = 8 * kq + j;
-    *(v4i*)(smem + LdsBK::kK + key * 2 * kD + 16 * (dq ^ (key & 15))) = v[j];
-  }
-  // V^T row d = 8 dq + i holds keys 8 kq .. +7: the 16-bit element i of each
-  // key's block (low halves for even i, high halves for odd i)
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-    v4i o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      o[p] = (int)__builtin_amdgcn_perm((uint32_t)v[2 * p + 1][i >> 1], (uint32_t)v[2 * p][i >> 1], sel);
-    const int d = 8 * dq + i;
-    *(v4i*)(smem + LdsBK::kVT + d * 64 + 16 * (kq ^ ((d >> 2) & 3))) = o;
+    *(v4i*)(smem + LdsBK::kK + key * 2 * kD + 16 * (dq ^ bk_swz(key))) = v;
   }
 }
 
@@ -3477,7 +3492,7 @@ __device__ __forceinline__ void bk_body(KArgPtr ap, uint8_t* smem, int w) {
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
           const int c = 32 * dh + 2 * ks + g;
-          const bf8_t av = __builtin_bit_cast(bf8_t, *(const v4i*)(krow + 16 * (c ^ (key & 15))));
+          const bf8_t av = __builtin_bit_cast(bf8_t, *(const v4i*)(krow + 16 * (c ^ bk_swz(key))));
           Sx = mma_bf16(av, qf[ks], Sx);
         }
       }
@@ -3542,8 +3557,7 @@ __device__ __forceinline__ void bk_body(KArgPtr ap, uint8_t* smem, int w) {
           }
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
-            const int d = 128 * w + 32 * db + (lane & 31);
-            const bf8_t va = __builtin_bit_cast(bf8_t, *(const v4i*)(smem + L::kVT + d * 64 + 16 * (c ^ ((d >> 2) & 3))));
+            const bf8_t va = bk_vop(smem + L::kK, 128 * w + 32 * db, ks, lane);
 #pragma unroll
             for (int x = 0; x < 2; ++x) acc[db][x] = mma_bf16(va, pb[x], acc[db][x]);
           }
