@@ -3303,7 +3303,8 @@ struct LdsBK {
   static constexpr int kM = kAlpha + 4 * kN1;                // f32 [64]: final maximum per head
   static constexpr int kL = kM + 4 * kN1;                    // f32 [64]: final row sum per head
   static constexpr int kMisc = kL + 4 * kN1;                 // int [64]: compaction
-  static constexpr int kBytes = kMisc + 4 * 64;
+  static constexpr int kRaw = (kMisc + 4 * 64 + 1023) / 1024 * 1024;   // packed rows: the tile's raw 640-byte rows
+  static constexpr int kBytes = kRaw + kBkKeys * 640;
 };
 static_assert(LdsBK::kBytes <= 160 * 1024, "LDS");
 
@@ -3341,35 +3342,53 @@ __device__ __forceinline__ bf8_t bk_vop(const uint8_t* kt, int dblk, int ks, int
   return __builtin_bit_cast(bf8_t, out);
 }
 
-// The tile's raw bytes of one thread: keys 8 kq + j (j < 8) of the tile,
-// columns 8 dq .. 8 dq + 7.
+// bf16 rows: the tile's bytes of one thread, keys 8 kq + j (j < 8) of the
+// tile, columns 8 dq .. 8 dq + 7 (one 16-byte load per key).
 struct BkRaw {
-  v4i x[8];     // bf16 / rope: 8 bf16; nope: x[j].xy = 8 e4m3 codes
-  int sc[8];    // nope: the dword holding the column tile's e8m0 scale
+  v4i x[8];
 };
 
-template <int FMT>
 __device__ __forceinline__ BkRaw bk_load(const uint64_t* kaddr, int tile, int tid) {
   const int kq = tid >> 6, dq = tid & 63;
   BkRaw r;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint8_t* row = gptr(reinterpret_cast<const uint8_t*>(kaddr[kBkKeys * tile + 8 * kq + j]));
-    if (FMT == 1 || dq < 8) {
-      r.x[j] = *(const v4i*)(row + 16 * dq);
-      r.sc[j] = 0;
-    } else {
-      const int nb = 8 * dq - 64;                       // nope column of the block's first value
-      const v2i c = *(const v2i*)(row + 128 + nb);
-      r.x[j] = v4i{c[0], c[1], 0, 0};
-      r.sc[j] = *(const int*)(row + 576 + 4 * ((nb >> 6) >> 2));
-    }
+    r.x[j] = *(const v4i*)(row + 16 * dq);
   }
   return r;
 }
 
+// The block into the K rows (P V reads them transposed, bk_vop).
+__device__ __forceinline__ void bk_store(const BkRaw& r, uint8_t* smem, int tid) {
+  const int kq = tid >> 6, dq = tid & 63;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int key = 8 * kq + j;
+    *(v4i*)(smem + LdsBK::kK + key * 2 * kD + 16 * (dq ^ bk_swz(key))) = r.x[j];
+  }
+}
+
+// Packed rows: the tile's 32 raw 640-byte rows into LDS by LDS-DMA, 16 bytes
+// per lane (20 instructions of 1 KiB, 5 per wave: lane-chunk q = 64 i + lane
+// of the tile is chunk q % 40 of key q / 40, written at raw + 16 q).  Narrow
+// loads of the 8-byte code blocks and the scale words took 3 instructions per
+// key and wave, and the CU's address unit became the bound.
+__device__ __forceinline__ void bk_dma_packed(const uint64_t* kaddr, int tile, uint8_t* raw, int w) {
+  const int lane = opaque((int)threadIdx.x & 63);
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int q = 64 * (5 * w + i) + lane;
+    const int key = q / 40, c = q - 40 * key;
+    const uint64_t src = kaddr[kBkKeys * tile + key] + 16u * (uint32_t)c;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(raw + 1024 * (5 * w + i)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src)
+                 : "memory", "m0");
+  }
+}
+
 // bf16 of 8 e4m3 codes times 2^(E - 127) (E = 255: NaN), exact.
-__device__ __forceinline__ v4i bk_nope8(v4i x, int scw, int tile) {
+__device__ __forceinline__ v4i bk_nope8(v2i x, int scw, int tile) {
   const uint32_t e = ((uint32_t)scw >> (8 * (tile & 3))) & 0xffu;
   const float sc = (e == 255u) ? __builtin_nanf("") : ((e == 0u) ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23));
   const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(x[0], false);
@@ -3380,14 +3399,24 @@ __device__ __forceinline__ v4i bk_nope8(v4i x, int scw, int tile) {
              (int)pack_bf16x2(f45[0] * sc, f45[1] * sc), (int)pack_bf16x2(f67[0] * sc, f67[1] * sc)};
 }
 
-// The block as bf16 into the K rows (P V reads them transposed, bk_vop).
-template <int FMT>
-__device__ __forceinline__ void bk_store(const BkRaw& r, uint8_t* smem, int tid) {
+// The raw packed rows as bf16 into the K rows: thread (kq, dq) converts
+// columns 8 dq .. +7 of keys 8 kq + j (rope: the row's bf16 values; nope:
+// 8 codes and their tile's scale).
+__device__ __forceinline__ void bk_convert_packed(const uint8_t* raw, uint8_t* smem, int tid) {
   const int kq = tid >> 6, dq = tid & 63;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const v4i v = (FMT == 2 && dq >= 8) ? bk_nope8(r.x[j], r.sc[j], (8 * dq - 64) >> 6) : r.x[j];
     const int key = 8 * kq + j;
+    const uint8_t* row = raw + key * 640;
+    v4i v;
+    if (dq < 8) {
+      v = *(const v4i*)(row + 16 * dq);
+    } else {
+      const int nb = 8 * dq - 64;                       // nope column of the block's first value
+      const v2i c = *(const v2i*)(row + 128 + nb);
+      const int scw = *(const int*)(row + 576 + 4 * ((nb >> 6) >> 2));
+      v = bk_nope8(c, scw, nb >> 6);
+    }
     *(v4i*)(smem + LdsBK::kK + key * 2 * kD + 16 * (dq ^ bk_swz(key))) = v;
   }
 }
@@ -3478,12 +3507,26 @@ __device__ __forceinline__ void bk_body(KArgPtr ap, uint8_t* smem, int w) {
 #pragma unroll
       for (int x = 0; x < 2; ++x) acc[db][x] = v16f{};
     float mrun = kNegInf, lrun = 0.f;   // the D-half-0 waves: head hq
+    uint8_t* rawbuf = smem + L::kRaw;
     BkRaw raw;
-    if (tiles > 0) raw = bk_load<FMT>(kaddr, 0, tid);
+    if (FMT == 2) {
+      if (tiles > 0) {
+        bk_dma_packed(kaddr, 0, rawbuf, w);
+        gather_barrier(false);
+      }
+    } else if (tiles > 0) {
+      raw = bk_load(kaddr, 0, tid);
+    }
     for (int it = 0; it < tiles; ++it) {
-      bk_store<FMT>(raw, smem, tid);
-      if (it + 1 < tiles) raw = bk_load<FMT>(kaddr, it + 1, tid);   // in flight during this tile
-      lds_barrier();
+      if (FMT == 2) {
+        bk_convert_packed(rawbuf, smem, tid);
+        lds_barrier();   // the K rows are complete and the raw rows free
+        if (it + 1 < tiles) bk_dma_packed(kaddr, it + 1, rawbuf, w);   // in flight during this tile
+      } else {
+        bk_store(raw, smem, tid);
+        if (it + 1 < tiles) raw = bk_load(kaddr, it + 1, tid);   // in flight during this tile
+        lds_barrier();
+      }
       // ---- S^T: keys x heads [32 hb, +32), D half dh ----
       v16f Sx = v16f{};
       {
@@ -3563,7 +3606,10 @@ __device__ __forceinline__ void bk_body(KArgPtr ap, uint8_t* smem, int w) {
           }
         }
       }
-      lds_barrier();   // K, V^T and P are read before the next tile overwrites them
+      // K and P are read before the next tile overwrites them (packed rows:
+      // and the next tile's raw rows have landed)
+      if (FMT == 2) gather_barrier(false);
+      else lds_barrier();
     }
 
     // ---- epilogue: the final result (one split) or the unit's partial ----
