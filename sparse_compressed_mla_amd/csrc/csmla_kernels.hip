@@ -3289,6 +3289,7 @@ sk_kernel(const KArgs a) {
 
 constexpr int kBkKeys = 32;          // keys per tile
 constexpr int kBkMaxKeys = 1024;     // keys per unit, resolved at once
+constexpr float kBkRefSlack = 16.f;  // log2 units a tile maximum may pass the reference by
 constexpr int kBkThreads = 256;
 
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
@@ -3303,7 +3304,8 @@ struct LdsBK {
   static constexpr int kM = kAlpha + 4 * kN1;                // f32 [64]: final maximum per head
   static constexpr int kL = kM + 4 * kN1;                    // f32 [64]: final row sum per head
   static constexpr int kMisc = kL + 4 * kN1;                 // int [64]: compaction
-  static constexpr int kRaw = (kMisc + 4 * 64 + 1023) / 1024 * 1024;   // packed rows: the tile's raw 640-byte rows
+  static constexpr int kFlag = kMisc + 4 * 64;               // int [2]: a head block's reference moved this tile
+  static constexpr int kRaw = (kFlag + 8 + 1023) / 1024 * 1024;   // packed rows: the tile's raw 640-byte rows
   static constexpr int kBytes = kRaw + kBkKeys * 640;
 };
 static_assert(LdsBK::kBytes <= 160 * 1024, "LDS");
@@ -3442,6 +3444,7 @@ __device__ __forceinline__ void bk_body(KArgPtr ap, uint8_t* smem, int w) {
   float* alpha_s = reinterpret_cast<float*>(smem + L::kAlpha);
   float* m_s = reinterpret_cast<float*>(smem + L::kM);
   float* l_s = reinterpret_cast<float*>(smem + L::kL);
+  int* flag_s = reinterpret_cast<int*>(smem + L::kFlag);
   float* xch = reinterpret_cast<float*>(smem + L::kX) + (hb * 64 + lane) * 16;
 
   for (int u = u_begin; u < u_end; ++u) {
@@ -3559,8 +3562,13 @@ __device__ __forceinline__ void bk_body(KArgPtr ap, uint8_t* smem, int w) {
           }
         }
         mx = xor32_reduce(mx, true);
-        const float mnew = fmaxf(mrun, mx);
-        const float al = (mrun == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
+        // a head's reference moves only when the tile's maximum passes it
+        // by more than kBkRefSlack (P <= 2^kBkRefSlack is exact enough in
+        // bf16 and the sums have range to spare), so the accumulators are
+        // rescaled only on such tiles; the first finite maximum sets it
+        const bool move = mx > mrun + kBkRefSlack;
+        const float mnew = move ? mx : mrun;
+        const float al = (move && mrun != kNegInf) ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.f;
         const float mz = (mnew == kNegInf) ? 0.f : mnew;
         float ps = 0.f;
         uint8_t* prow = smem + L::kP + hq * 64;
@@ -3578,17 +3586,21 @@ __device__ __forceinline__ void bk_body(KArgPtr ap, uint8_t* smem, int w) {
         lrun = al * lrun + ps;
         mrun = mnew;
         if (g == 0) alpha_s[hq] = al;
+        const bool rescale = __ballot(al != 1.f) != 0;
+        if (lane == 0) flag_s[hb] = rescale ? 1 : 0;
       }
       lds_barrier();
       // ---- O^T += V^T P^T: columns [128 w, +128), all 64 heads ----
       {
-        float al[2];
+        if (__builtin_amdgcn_readfirstlane(flag_s[0] | flag_s[1])) {
+          float al[2];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) al[x] = alpha_s[32 * x + (lane & 31)];
+          for (int x = 0; x < 2; ++x) al[x] = alpha_s[32 * x + (lane & 31)];
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+          for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int x = 0; x < 2; ++x) acc[db][x] *= al[x];
+            for (int x = 0; x < 2; ++x) acc[db][x] *= al[x];
+        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int c = 2 * ks + g;

@@ -132,11 +132,14 @@ def test_block_sizes_and_128_heads(fmt):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("off", [-128, -127, 0])
-def test_dominant_band_key(fmt, off):
+@pytest.mark.parametrize("mixed", [False, True])
+def test_dominant_band_key(fmt, off, mixed):
     """Row 0 of a 2-row batch over 400 ori tokens sits at p = 398 (band
     [271, 398]); its query is a scaled copy of the key at p + off, which
     scores ~40 above the rest: the output follows that key's value row iff
-    the key is in the band."""
+    the key is in the band.  Mixed: only the even heads get that query, so
+    in the tile holding the key some heads' softmax maxima jump and the
+    others' do not."""
     inp = _mk(fmt, seed=216, q_lens=[2], ori_lens=[400], cmp_lens=[100], cmp_ratio=4, residual=[0],
               indices=None, return_lse=True)
     p = 398
@@ -150,9 +153,11 @@ def test_dominant_band_key(fmt, off):
         from oracle.formats import decode_packed640
         kvec = torch.from_numpy(decode_packed640(row.numpy()[None])[0])
     scale = 40.0 / (512 ** -0.5 * float((kvec ** 2).sum()))
-    inp.q[0] = (kvec * scale).to(torch.bfloat16)[None, :].expand(inp.n1, -1)
-    _, o, l, ref = check(inp, tokens=[0], name=f"{fmt} dominant band {off}")
+    heads = slice(0, inp.n1, 2) if mixed else slice(0, inp.n1)
+    dom = (kvec * scale).to(torch.bfloat16)[None, :]
+    inp.q[0, heads] = dom.expand(inp.q[0, heads].shape[0], -1)
+    _, o, l, ref = check(inp, tokens=[0], name=f"{fmt} dominant band {off}{' mixed' if mixed else ''}")
     visible = -127 <= off <= 0
     val = kvec.numpy()
-    assert (np.abs(ref.out[0] - val[None, :]).max() < 1e-2) == visible
-    assert (np.abs(o[0] - val[None, :]).max() < 0.05) == visible
+    assert (np.abs(ref.out[0][heads] - val[None, :]).max() < 1e-2) == visible
+    assert (np.abs(o[0][heads] - val[None, :]).max() < 0.05) == visible
