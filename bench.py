@@ -14,8 +14,12 @@ model layers would: --layers copies of the KV pools, each layer with its own
 q, q descales, top-k index rows and output (block tables, lengths and sinks
 shared); step k runs layer k % layers, so every step's rows come from HBM,
 not from the 256 MB Infinity Cache.  Exactly --steps forwards are timed
-after --warmup untimed ones (HIP graphs over the layers, HIP events on the
-stream the kernels run on).  The plan is made once per pass over the layers.
+after --warmup untimed ones, with HIP events on the stream the kernels run
+on: launched one after another behind a short spin kernel that keeps the
+GPU busy while the host submits them (--timing eager, the default), or as
+replays of HIP graphs over the layers (--timing graph).  Either way the
+graphs are captured and each replay is checked equal to the eager forwards.
+The plan is made once per pass over the layers.
 
 Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
@@ -69,6 +73,8 @@ def main():
     ap.add_argument("--copy-budget-gb", type=float, default=96.0,
                     help="device memory the KV pool copies may take (caps --layers for large caches)")
     ap.add_argument("--batch", type=int, default=0, help="batch of the decode workloads (0: the config's)")
+    ap.add_argument("--timing", choices=["eager", "graph"], default="eager",
+                    help="timed forwards as launches one after another, or as replays of captured graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of each oracle timing sample (one thread, then all threads)")
@@ -179,14 +185,29 @@ def unique_rows(m, inp, np, torch):
     return int(counts.sum()), sum(len(v) for v in per_batch.values())
 
 
-def timed_graph_steps(m, torch, plan, tens, dev, steps, warmup):
+def cover_submission(torch, stream):
+    """Queue a short spin kernel (well under a millisecond of GPU time) on
+    `stream` ahead of the start event, so that the host's submission of the
+    timed work (a graph launch takes some tens of microseconds) happens while
+    the GPU is still busy: the events then bracket the forwards running back
+    to back, as a model's layer loop runs them, and not the host's launch
+    latency.  Untimed."""
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(1_000_000)
+
+
+def timed_graph_steps(m, torch, plan, tens, dev, steps, warmup, timing="eager"):
     """Forward i of a pass uses layer i's tensors.  Graphs of forwards over
     the layers are captured once (a full pass, and the partial passes the
-    step counts need); every replay is checked equal to the eager forwards.
+    step counts need); each is replayed once and checked equal to the eager
+    forwards before the warm-up.
     Warm-up runs `warmup` untimed forwards on the last layers; the timed
     region runs exactly `steps` forwards from layer 0 on, with HIP events
-    on the stream the kernels run on.  The host planner runs once per full
-    pass (its host time is reported apart).  Returns (ms for the steps,
+    on the stream the kernels run on, as launches one after another
+    (timing "eager") or as graph replays ("graph": full passes, then the
+    partial one; each replay adds a fixed ~25 us on this stack, which a model
+    pays once per graph of all its layers).  The host planner runs once per
+    full pass (its host time is reported apart).  Returns (ms for the steps,
     host planner seconds, passes)."""
     L = len(tens)
     cap = torch.cuda.Stream(dev)
@@ -214,33 +235,51 @@ def timed_graph_steps(m, torch, plan, tens, dev, steps, warmup):
     full = capture(list(range(L)))
     part_k = capture(list(range(steps % L)))
     part_w = capture(list(range(L - warmup % L, L)) if warmup % L else [])
-    for g in (full,):
+    # every graph is replayed once here and checked (this first replay also
+    # uploads the graph, which otherwise costs ~30 us inside the first timed
+    # replay)
+    for g, layers in ((full, range(L)), (part_k, range(steps % L)), (part_w, range(L - warmup % L, L))):
+        if g is None:
+            continue
         for t in tens:
             t[1].zero_()
         torch.cuda.synchronize()
         with torch.cuda.stream(cap):
             g.replay()
         torch.cuda.synchronize()
-        for l, t in enumerate(tens):
-            assert torch.equal(t[1], eager[l]), f"graph replay differs from the eager forward (layer {l})"
+        for l in layers:
+            assert torch.equal(tens[l][1], eager[l]), f"graph replay differs from the eager forward (layer {l})"
     with torch.cuda.stream(cap):
-        if part_w is not None:
-            part_w.replay()
-        for _ in range(warmup // L):
-            full.replay()
+        if timing == "eager":
+            for i in range(warmup):
+                fwd((L - warmup % L + i) % L)
+        else:
+            if part_w is not None:
+                part_w.replay()
+            for _ in range(warmup // L):
+                full.replay()
     torch.cuda.synchronize()
     hl, keep = m.host_lengths_from(tens[0][2])
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_plan = 0.0
+    cover_submission(torch, cap)
     with torch.cuda.stream(cap):
         start.record(cap)
-        for _ in range(steps // L):
-            t0 = time.perf_counter()
-            m.csmla_plan(plan.problem, hl)
-            t_plan += time.perf_counter() - t0
-            full.replay()
-        if part_k is not None:
-            part_k.replay()
+        if timing == "eager":
+            for i in range(steps):
+                if i % L == L - 1:
+                    t0 = time.perf_counter()
+                    m.csmla_plan(plan.problem, hl)
+                    t_plan += time.perf_counter() - t0
+                fwd(i % L)
+        else:
+            for _ in range(steps // L):
+                t0 = time.perf_counter()
+                m.csmla_plan(plan.problem, hl)
+                t_plan += time.perf_counter() - t0
+                full.replay()
+            if part_k is not None:
+                part_k.replay()
         stop.record(cap)
     torch.cuda.synchronize()
     return start.elapsed_time(stop), t_plan, max(1, steps // L)
@@ -327,12 +366,12 @@ def rotated(args, m, make_config, torch, np):
         ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
         tens.append((m.tensors_from(x, out, lse, ws if plan.workspace_bytes else None), out, x, lse, ws))
     K, W = args.steps, args.warmup
-    total_ms, t_plan, passes = timed_graph_steps(m, torch, plan, tens, dev, K, W)
+    total_ms, t_plan, passes = timed_graph_steps(m, torch, plan, tens, dev, K, W, args.timing)
     fwd_ms = total_ms / K
     value = T1 * K / (total_ms / 1e3)
     achieved = kv_bytes / (fwd_ms / 1e3) / 1e9
     kern = kernel_name(plan, fmt)
-    print(f"[bench] {args.workload}: forward {fwd_ms * 1e3:.2f} us per step over {K} steps (graphs over {L} "
+    print(f"[bench] {args.workload}: forward {fwd_ms * 1e3:.2f} us per step over {K} steps ({args.timing}, {L} "
           f"layers); {kern}, grid {plan.grid}; plan {1e6 * t_plan / passes:.0f} us host per pass",
           file=sys.stderr, flush=True)
     headline = args.workload == "csa_decode" and fmt == "fp8"
@@ -354,7 +393,7 @@ def rotated(args, m, make_config, torch, np):
         "data": f"synthetic, seeded (workloads.make_config({k}); layers 1.. redraw q and indices)",
         "config": dict({"workload": wname, "batch": inp.batch, "n1": 64, "d": 512, "block_size": 128,
                         "kv_format": fmt,
-                        "layers_rotated": L, "splits": plan.splits, "grid": plan.grid,
+                        "layers_rotated": L, "timing": args.timing, "splits": plan.splits, "grid": plan.grid,
                         "head_group": plan.head_group}, **CONFIG_TEXT[k]),
         "effective_kv_gbs": round(achieved, 1),
         "kv_bytes_per_step": kv_bytes,
@@ -414,6 +453,7 @@ def prefill(args, m, make_config, torch, np):
         m.csmla_forward(plan.problem, tens, plan.metadata, sp)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cover_submission(torch, stream)
     start.record(stream)
     for _ in range(steps):
         m.csmla_forward(plan.problem, tens, plan.metadata, sp)
@@ -512,6 +552,7 @@ def indexer(args, m, torch, np):
         m.csmla_indexer_forward(plan.problem, tens[i % copies], plan.metadata, sp)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cover_submission(torch, stream)
     start.record(stream)
     for i in range(steps):
         m.csmla_indexer_forward(plan.problem, tens[i % copies], plan.metadata, sp)
