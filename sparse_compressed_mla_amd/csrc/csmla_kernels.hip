@@ -1388,6 +1388,13 @@ struct DkSrc {
   uint64_t p[kDkGI];
 };
 
+// The decode tiles' swizzle: source chunk c (16 bytes) of row r sits at chunk
+// c ^ dk_swz(r), a 4-bit value, so that 16 consecutive rows (the K operand
+// reads of a key block) and rows 8 m + [0, 8) with 32 + 8 m + [0, 8) (the
+// V^T transpose reads of two lane groups) each reach 16 distinct chunks of a
+// 256-byte window: every LDS bank once.  dk_swz(r + 64) == dk_swz(r).
+__device__ __forceinline__ int dk_swz(int r) { return (r & 15) ^ (((r >> 5) & 1) << 3); }
+
 // Both halves of a tile with one LDS round trip: every read of the
 // addresses is issued before the first is used.
 __device__ __forceinline__ void dk_src2(const uint64_t* kaddr, int tile, int w, DkSrc& s0, DkSrc& s1) {
@@ -1401,7 +1408,7 @@ __device__ __forceinline__ void dk_src2(const uint64_t* kaddr, int tile, int w, 
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int mi = 0; mi < kDkGI; ++mi) {
-    const uint32_t off = 16u * (uint32_t)(li ^ swz(RW * w + 2 * mi + g));   // swz(r + 64) == swz(r)
+    const uint32_t off = 16u * (uint32_t)(li ^ dk_swz(RW * w + 2 * mi + g));   // dk_swz(r + 64) == dk_swz(r)
     s0.p[mi] += off;
     s1.p[mi] += off;
   }
@@ -1461,7 +1468,7 @@ __device__ __forceinline__ void dk_band_tile(const KHdr& a, const Tok& k, uint8_
       const int j = k.lo + 64 * half + r;
       const bool second = j >= split;
       const int64_t row = (int64_t)(second ? e1 : e0) * bs + (j - (second ? split : b0 * bs));
-      s[half].p[mi] = (uint64_t)(uintptr_t)(kv + row * kD) + 16u * (uint32_t)(li ^ swz(r));
+      s[half].p[mi] = (uint64_t)(uintptr_t)(kv + row * kD) + 16u * (uint32_t)(li ^ dk_swz(r));
     }
 #pragma unroll
   for (int mi = 0; mi < kDkGI; ++mi) dk_issue(s[0], mi, 0, tb, w, nt);
@@ -1483,10 +1490,11 @@ struct DkFeed {
 };
 
 // Per-lane LDS offsets (tile buffer 0) of the wave's K and V^T operand reads.
-// In a tile row, source chunk c (16 bytes) sits at chunk c ^ swz(row).
+// In a tile row, source chunk c (16 bytes) sits at chunk c ^ dk_swz(row).
 struct DkOffsets {
-  int k[kDkKB][2];    // [key block b][16-byte half]: row 16 (KB w + b) + i, chunk (2 g + x) ^ swz, + 128 per K-step
-  int v[4][kDkDB];    // [m][d-block]: V^T transpose reads of keys 32 g + 8 m + .., columns 16 (DB w + db) + ..
+  int k[kDkKB][2][2];   // [key block b][K-step parity][16-byte half]: row 16 (KB w + b) + i, chunk
+                        // (8 k + 2 g + x) ^ dk_swz, + 256 per K-step pair
+  int v[4][kDkDB];      // [m][d-block]: V^T transpose reads of keys 32 g + 8 m + .., columns 16 (DB w + db) + ..
 };
 
 __device__ __forceinline__ DkOffsets dk_offsets(int lane, int w) {
@@ -1494,14 +1502,16 @@ __device__ __forceinline__ DkOffsets dk_offsets(int lane, int w) {
   const int i = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int b = 0; b < kDkKB; ++b) {
-    const int row = 16 * (kDkKB * w + b) + i, f = swz(row);
+    const int row = 16 * (kDkKB * w + b) + i, f = dk_swz(row);
 #pragma unroll
-    for (int x = 0; x < 2; ++x) o.k[b][x] = row * kD + 16 * ((2 * g + x) ^ f);
+    for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) o.k[b][kp][x] = row * kD + 16 * ((8 * kp + 2 * g + x) ^ f);
   }
   const int L = lane & 15;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const int row = 32 * g + 8 * m + (L >> 1), f = swz(row);
+    const int row = 32 * g + 8 * m + (L >> 1), f = dk_swz(row);
 #pragma unroll
     for (int db = 0; db < kDkDB; ++db) o.v[m][db] = row * kD + 16 * ((kDkDB * w + db) ^ f) + 8 * (L & 1);
   }
@@ -1511,8 +1521,8 @@ __device__ __forceinline__ DkOffsets dk_offsets(int lane, int w) {
 // S^T blocks (16 keys x 16 heads) of the wave's keys, full D; the next
 // K-step's operands are read while the current ones multiply.
 __device__ __forceinline__ v8i dk_kop(const uint8_t* tb, const DkOffsets& o, int b, int k) {
-  const v4i lo = *(const v4i*)(tb + o.k[b][0] + 128 * k);
-  const v4i hi = *(const v4i*)(tb + o.k[b][1] + 128 * k);
+  const v4i lo = *(const v4i*)(tb + o.k[b][k & 1][0] + 256 * (k >> 1));
+  const v4i hi = *(const v4i*)(tb + o.k[b][k & 1][1] + 256 * (k >> 1));
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
