@@ -2080,9 +2080,12 @@ dk_kernel(const KArgs a) {
 // ---------------------------------------------------------------------------
 
 // Tokens whose first split was computed by XCD x: [t0, t1).
+// With one unit per work-group the ranges are [g, g + 1) (no load of the
+// range table, whose read would precede the partials' loads).
 __host__ __device__ __forceinline__ void xcd_tokens(const KArgs& a, int x, int& t0, int& t1) {
   const int per = a.grid / 8;
-  const int u0 = a.starts[x * per], u1 = a.starts[(x + 1) * per];
+  const bool one = a.n_units == a.grid;
+  const int u0 = one ? x * per : a.starts[x * per], u1 = one ? (x + 1) * per : a.starts[(x + 1) * per];
   t0 = (u0 + a.splits - 1) / a.splits;
   t1 = (u1 + a.splits - 1) / a.splits;
 }
