@@ -3672,13 +3672,23 @@ __device__ __forceinline__ void bk_body(KArgPtr ap, uint8_t* smem, int w) {
         }
         orow = a.ws_o + ((size_t)u * kN1 + h) * kD;
       }
+      // lane (h, g) holds columns 8 q + 4 g + [0, 4) of each 32-column block;
+      // v_permlane32_swap trades the upper lanes' even-q half with the lower
+      // lanes' odd-q half of each q pair, so that each lane stores 16
+      // contiguous bytes (columns 16 k + 8 g + [0, 8)): half the store
+      // instructions of 8-byte pieces
+      uint16_t* ocol = orow + 128 * w + 8 * g;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
+        for (int k2 = 0; k2 < 2; ++k2) {
           const v16f& o = acc[db][x];
-          *(uint2*)(orow + 128 * w + 32 * db + 8 * q4 + 4 * g) =
-              pack_bf16x4(sc * o[4 * q4], sc * o[4 * q4 + 1], sc * o[4 * q4 + 2], sc * o[4 * q4 + 3]);
+          const int q0 = 2 * k2, q1 = 2 * k2 + 1;
+          const uint2 A = pack_bf16x4(sc * o[4 * q0], sc * o[4 * q0 + 1], sc * o[4 * q0 + 2], sc * o[4 * q0 + 3]);
+          const uint2 B = pack_bf16x4(sc * o[4 * q1], sc * o[4 * q1 + 1], sc * o[4 * q1 + 2], sc * o[4 * q1 + 3]);
+          const auto sx = __builtin_amdgcn_permlane32_swap(A.x, B.x, false, false);
+          const auto sy = __builtin_amdgcn_permlane32_swap(A.y, B.y, false, false);
+          *(uint4*)(ocol + 32 * db + 16 * k2) = make_uint4(sx[0], sy[0], sx[1], sy[1]);
         }
     }
   }
