@@ -3643,53 +3643,113 @@ __device__ __forceinline__ void bk_body(KArgPtr ap, uint8_t* smem, int w) {
       l_s[hq] = lrun;
     }
     lds_barrier();
+    if constexpr (FMT == 1) {
+      float scx[2];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int h = 32 * x + (lane & 31);
-      const float M = m_s[h], Ls = l_s[h];
-      float sc;
-      uint16_t* orow;
-      if (S == 1) {
-        const float sg = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
-        const float Mf = fmaxf(M, sg);
-        float lse_v = kNegInf;
-        sc = 0.f;
-        if (Mf != kNegInf) {
-          const float af = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - Mf);
-          const float Lf = af * Ls + ((sg == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sg - Mf));
-          sc = af / Lf;
-          lse_v = (Mf + __log2f(Lf)) * kLn2;
+      for (int x = 0; x < 2; ++x) {
+        const int h = 32 * x + (lane & 31);
+        const float M = m_s[h], Ls = l_s[h];
+        float sc;
+        if (S == 1) {
+          const float sg = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+          const float Mf = fmaxf(M, sg);
+          float lse_v = kNegInf;
+          sc = 0.f;
+          if (Mf != kNegInf) {
+            const float af = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - Mf);
+            const float Lf = af * Ls + ((sg == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sg - Mf));
+            sc = af / Lf;
+            lse_v = (Mf + __log2f(Lf)) * kLn2;
+          }
+          if (over) { sc = __builtin_nanf(""); lse_v = sc; }
+          if (a.lse && w == 0 && g == 0) a.lse[(size_t)t * a.n1 + h] = lse_v;
+        } else {
+          sc = (Ls > 0.f) ? 1.0f / Ls : 0.f;
+          if (over) sc = __builtin_nanf("");
+          if (w == 0 && g == 0) {
+            a.ws_ml[((size_t)u * kN1 + h) * 2] = M;
+            a.ws_ml[((size_t)u * kN1 + h) * 2 + 1] = Ls;
+          }
         }
-        if (over) { sc = __builtin_nanf(""); lse_v = sc; }
-        if (a.lse && w == 0 && g == 0) a.lse[(size_t)t * a.n1 + h] = lse_v;
-        orow = a.out + ((size_t)t * a.n1 + h) * kD;
-      } else {
-        sc = (Ls > 0.f) ? 1.0f / Ls : 0.f;
-        if (over) sc = __builtin_nanf("");
-        if (w == 0 && g == 0) {
-          a.ws_ml[((size_t)u * kN1 + h) * 2] = M;
-          a.ws_ml[((size_t)u * kN1 + h) * 2 + 1] = Ls;
-        }
-        orow = a.ws_o + ((size_t)u * kN1 + h) * kD;
+        scx[x] = sc;
       }
-      // lane (h, g) holds columns 8 q + 4 g + [0, 4) of each 32-column block;
-      // v_permlane32_swap trades the upper lanes' even-q half with the lower
-      // lanes' odd-q half of each q pair, so that each lane stores 16
-      // contiguous bytes (columns 16 k + 8 g + [0, 8)): half the store
-      // instructions of 8-byte pieces
-      uint16_t* ocol = orow + 128 * w + 8 * g;
+      // The output rows go through LDS, 32 heads at a time over the K tile and
+      // the P area (both free now), so that each store instruction writes one
+      // whole 1 KiB head row.  Lane (h, g) holds columns 8 q + 4 g + [0, 4) of
+      // each 32-column block.
+      constexpr int kRow = 2 * kD + 16;   // padded: the 8-byte writes of 32 rows reach distinct banks
+      static_assert(32 * kRow <= LdsBK::kX, "staging");
+      uint16_t* obase = (S == 1) ? a.out + (size_t)t * a.n1 * kD : a.ws_o + (size_t)u * kN1 * kD;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int x = 0; x < 2; ++x) {
+        uint8_t* srow = smem + (lane & 31) * kRow + 2 * (128 * w + 4 * g);
+        const float sc = scx[x];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const v16f& o = acc[db][x];
-          const int q0 = 2 * k2, q1 = 2 * k2 + 1;
-          const uint2 A = pack_bf16x4(sc * o[4 * q0], sc * o[4 * q0 + 1], sc * o[4 * q0 + 2], sc * o[4 * q0 + 3]);
-          const uint2 B = pack_bf16x4(sc * o[4 * q1], sc * o[4 * q1 + 1], sc * o[4 * q1 + 2], sc * o[4 * q1 + 3]);
-          const auto sx = __builtin_amdgcn_permlane32_swap(A.x, B.x, false, false);
-          const auto sy = __builtin_amdgcn_permlane32_swap(A.y, B.y, false, false);
-          *(uint4*)(ocol + 32 * db + 16 * k2) = make_uint4(sx[0], sy[0], sx[1], sy[1]);
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const v16f& o = acc[db][x];
+            *(uint2*)(srow + 2 * (32 * db + 8 * q4)) =
+                pack_bf16x4(sc * o[4 * q4], sc * o[4 * q4 + 1], sc * o[4 * q4 + 2], sc * o[4 * q4 + 3]);
+          }
+        lds_barrier();
+        for (int row = w; row < 32; row += kBkThreads / 64)
+          *(v4i*)(obase + (size_t)(32 * x + row) * kD + 8 * lane) = *(const v4i*)(smem + row * kRow + 16 * lane);
+        if (x == 0 || u + 1 < u_end) lds_barrier();   // the staged rows are read before they are overwritten
+      }
+    } else {
+      // (the packed-row instantiation keeps direct 16-byte stores: with the
+      // staged form, the compiler parked the per-lane address of the m_s /
+      // l_s reads in an AGPR through a copy inside a divergent block, so
+      // that every lane but 0 and 32 read head 0's values)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int h = 32 * x + (lane & 31);
+        const float M = m_s[h], Ls = l_s[h];
+        float sc;
+        uint16_t* orow;
+        if (S == 1) {
+          const float sg = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+          const float Mf = fmaxf(M, sg);
+          float lse_v = kNegInf;
+          sc = 0.f;
+          if (Mf != kNegInf) {
+            const float af = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - Mf);
+            const float Lf = af * Ls + ((sg == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sg - Mf));
+            sc = af / Lf;
+            lse_v = (Mf + __log2f(Lf)) * kLn2;
+          }
+          if (over) { sc = __builtin_nanf(""); lse_v = sc; }
+          if (a.lse && w == 0 && g == 0) a.lse[(size_t)t * a.n1 + h] = lse_v;
+          orow = a.out + ((size_t)t * a.n1 + h) * kD;
+        } else {
+          sc = (Ls > 0.f) ? 1.0f / Ls : 0.f;
+          if (over) sc = __builtin_nanf("");
+          if (w == 0 && g == 0) {
+            a.ws_ml[((size_t)u * kN1 + h) * 2] = M;
+            a.ws_ml[((size_t)u * kN1 + h) * 2 + 1] = Ls;
+          }
+          orow = a.ws_o + ((size_t)u * kN1 + h) * kD;
         }
+        // lane (h, g) holds columns 8 q + 4 g + [0, 4) of each 32-column block;
+        // v_permlane32_swap trades the upper lanes' even-q half with the lower
+        // lanes' odd-q half of each q pair, so that each lane stores 16
+        // contiguous bytes (columns 16 k + 8 g + [0, 8)): half the store
+        // instructions of 8-byte pieces
+        uint16_t* ocol = orow + 128 * w + 8 * g;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const v16f& o = acc[db][x];
+            const int q0 = 2 * k2, q1 = 2 * k2 + 1;
+            const uint2 A = pack_bf16x4(sc * o[4 * q0], sc * o[4 * q0 + 1], sc * o[4 * q0 + 2], sc * o[4 * q0 + 3]);
+            const uint2 B = pack_bf16x4(sc * o[4 * q1], sc * o[4 * q1 + 1], sc * o[4 * q1 + 2], sc * o[4 * q1 + 3]);
+            const auto sx = __builtin_amdgcn_permlane32_swap(A.x, B.x, false, false);
+            const auto sy = __builtin_amdgcn_permlane32_swap(A.y, B.y, false, false);
+            *(uint4*)(ocol + 32 * db + 16 * k2) = make_uint4(sx[0], sy[0], sx[1], sy[1]);
+          }
+      }
     }
   }
 }
