@@ -333,6 +333,17 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
     else if (pf_ok) hg = kN1;
   }
   if (T1 > 256 && pf_ok) hg = kN1;
+  // 12 to 24 tokens: 16-head groups in two key parts (below) instead of
+  // 8-head groups.  Measured on MI355X with 640 keys per token (two rounds,
+  // one box): 12 / 16 / 20 / 24 tokens 14.97 / 15.04 / 15.61 / 15.83 us
+  // against 15.10 / 15.62 / 16.14 / 16.08 us; equal at 28 tokens, slower at
+  // 4, 8 and 32 (14.61 / 14.51 / 16.62 against 14.37 / 14.44 / 16.40 us).  A
+  // kernel override (CSMLA_KERNEL) keeps its own choice.
+  bool h16_parts = false;
+  if (hg == 8 && T1 >= 12 && T1 <= 24 && !std::getenv("CSMLA_KERNEL")) {
+    hg = 16;
+    h16_parts = true;
+  }
   // Split-key decode kernel: all 64 heads of a token over <= 128 keys per
   // unit, the splits of a token merged inside the kernel.  It needs every
   // unit resident at once (one work-group per CU: 8 S ceil(T1 / 8) <= 256)
@@ -371,14 +382,14 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
   // partials.  Every unit needs a work-group of its own (the grid rounded up
   // to whole XCD rounds of groups, at most one work-group per CU), and a
   // part gets at least one tile.  Two parts by default where they fit (8-head
-  // groups up to 16 tokens): measured on MI355X with 640 keys per token, 4 and
-  // 8 tokens run 15.1 and 15.3 us in two parts against 16.2 and 16.1 us whole,
-  // 16 tokens 16.3 against 16.4 us; at 32 tokens (16-head groups in two parts)
-  // nothing is gained, and four parts lose (the merger reads each writer's
-  // partial in a round trip of its own).  CSMLA_DK_PARTS overrides the count.
+  // groups up to 16 tokens, and the 16-head groups chosen above): measured on
+  // MI355X with 640 keys per token, 4 and 8 tokens run 15.1 and 15.3 us in
+  // two parts against 16.2 and 16.1 us whole; four parts lose (the merger
+  // reads each writer's partial in a round trip of its own).  CSMLA_DK_PARTS
+  // overrides the count.
   int parts = 1;
   if (hg == 8 || hg == 16) {
-    int64_t want = hg == 8 ? 2 : 1;
+    int64_t want = (hg == 8 || h16_parts) ? 2 : 1;
     if (const char* env = std::getenv("CSMLA_DK_PARTS")) want = std::atoll(env);
     const int64_t tiles = std::max<int64_t>(1, (max_n + kDkTileKeys - 1) / kDkTileKeys);
     const int64_t groups = (int64_t)T1 * (kN1 / hg);

@@ -137,19 +137,24 @@ def test_plan_head_split_for_small_decode_batches(monkeypatch):
 
 
 def test_plan_key_parts(monkeypatch):
-    """Up to 16 decode tokens: 8-head groups, each split into two key parts on
+    """Up to 11 decode tokens: 8-head groups, each split into two key parts on
     one XCD (the grid a whole number of XCD rounds of groups, one unit per
-    work-group, the fixed workspace of sync words and exchange slots);
-    CSMLA_DK_PARTS overrides the count within what fits 256 work-groups and
-    the key list's tiles."""
+    work-group, the fixed workspace of sync words and exchange slots); 12 to
+    24 tokens: 16-head groups in two parts; CSMLA_DK_PARTS overrides the
+    count within what fits 256 work-groups and the key list's tiles."""
     for k in ("CSMLA_KERNEL", "CSMLA_DK_PARTS", "CSMLA_DK_TEST"):
         monkeypatch.delenv(k, raising=False)
     _, md, ws = m.csmla_plan(base_problem())
     assert md[12] == 8 and md[14] == 1 and ws == 0                 # 32 tokens: no parts
-    for b, grid in ((16, 256), (4, 64), (3, 48), (1, 16)):
+    for b, grid in ((11, 176), (8, 128), (4, 64), (3, 48), (1, 16)):
         _, md, ws = m.csmla_plan(base_problem(batch=b, t1=b))
         assert md[12] == 8 and md[14] == 2 and md[6] == b * 16 and md[7] == grid and ws == WS_FIXED, (b, md[:16])
         assert md[5] == 1 and md[15] == 0
+    for b, grid in ((12, 96), (16, 128), (24, 192)):
+        _, md, ws = m.csmla_plan(base_problem(batch=b, t1=b))
+        assert md[12] == 16 and md[14] == 2 and md[6] == b * 8 and md[7] == grid and ws == WS_FIXED, (b, md[:16])
+    _, md, ws = m.csmla_plan(base_problem(batch=25, t1=25))
+    assert md[12] == 8 and md[14] == 1 and ws == 0                 # 25 tokens: 8-head groups, whole
     monkeypatch.setenv("CSMLA_DK_PARTS", "8")
     _, md, _ = m.csmla_plan(base_problem(batch=4, t1=4))
     assert md[14] == 4 and md[6] == 4 * 8 * 4 and md[7] == 128     # 640 keys = 5 tiles: at most 4 parts
