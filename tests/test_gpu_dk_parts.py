@@ -126,3 +126,17 @@ def test_parts_lengths_leave_some_parts_empty():
     plan = plan_with(inp.to(DEV), "heads16", 8)
     assert plan.dk_parts == 4
     check_case("topk lengths", inp, plan, ws, ref, repeats=2)
+
+
+@pytest.mark.parametrize("batch", [12, 20])
+def test_default_plan_16_head_parts(batch, monkeypatch):
+    """12 to 24 decode tokens: the planner's own choice is 16-head groups in
+    two key parts (no override); parity on two calls of one workspace."""
+    for k in ("CSMLA_KERNEL", "CSMLA_DK_PARTS", "CSMLA_DK_TEST"):
+        monkeypatch.delenv(k, raising=False)
+    inp = make_config(2, batch=batch)
+    inp.return_lse = True
+    plan = m.Plan(inp.to(DEV))
+    assert plan.head_group == 16 and plan.dk_parts == 2, (plan.head_group, plan.dk_parts)
+    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=DEV)
+    check_case(f"default plan B={batch}", inp, plan, ws, oracle_forward(inp))
