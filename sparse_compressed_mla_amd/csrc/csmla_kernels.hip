@@ -1929,8 +1929,8 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
     us.w_lo = 0;
     // tile 0 in flight before the index slots are compacted (dk_band_tile);
     // the first part's range starts at key 0
-    const bool band_pre = a.layout_kv == 2 && a.ori_topk == 0 && a.topk > 0 && part == 0 &&
-                          us.n_o >= kDkRows && a.ori_bs >= kDkRows;
+    const bool band_pre = a.layout_kv == 2 && a.ori_topk == 0 && part == 0 && us.n_o >= kDkRows &&
+                          a.ori_bs >= kDkRows;
     if (band_pre) dk_band_tile(a, us.k, smem + L::kTiles, w, nt);
     if (a.topk > 0) us.n_c = compact_indices<L::kNT>(a, us.k, t, list, misc, 0, ip);
     else if (a.has_cmp) us.n_c = us.k.vis;
