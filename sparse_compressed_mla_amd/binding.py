@@ -142,11 +142,29 @@ def csmla_plan(problem: CsmlaProblem, lengths: Optional[CsmlaHostLengths] = None
     return st, md, int(ws.value)
 
 
+# (array, pointer) of the last metadata array passed in that needed no
+# conversion, one slot for the attention entry points and one for the
+# indexer's: numpy's ctypes pointer takes a few microseconds to form, as
+# much as the launch itself, so a caller that passes the same plan again
+# reuses it.  The pointer points into the caller's own buffer, so in-place
+# edits are seen; the reference held here keeps that buffer alive.
+_md_last = [(None, None), (None, None)]
+
+
+def _md_pointer(metadata, slot: int = 0):
+    last = _md_last[slot]
+    if metadata is last[0]:
+        return last[1]
+    md = np.ascontiguousarray(metadata, dtype=np.int32)
+    ptr = md.ctypes.data_as(ctypes.POINTER(_i32))
+    if md is metadata:
+        _md_last[slot] = (metadata, ptr)
+    return ptr
+
+
 def csmla_forward(problem: CsmlaProblem, tensors: CsmlaTensors, metadata: np.ndarray, stream: int = 0,
                   raise_on_error: bool = True) -> int:
-    md = np.ascontiguousarray(metadata, dtype=np.int32)
-    st = load().csmla_forward(ctypes.byref(problem), ctypes.byref(tensors),
-                              md.ctypes.data_as(ctypes.POINTER(_i32)), _p(stream))
+    st = load().csmla_forward(ctypes.byref(problem), ctypes.byref(tensors), _md_pointer(metadata), _p(stream))
     if raise_on_error:
         _check(st, "csmla_forward")
     return st
@@ -164,9 +182,8 @@ def csmla_forward_noalloc(problem: CsmlaProblem, tensors: CsmlaTensors, metadata
                           raise_on_error: bool = True) -> int:
     """csmla_forward with the split partials in the library's static device
     scratch (tensors.workspace is ignored); allocates nothing."""
-    md = np.ascontiguousarray(metadata, dtype=np.int32)
-    st = load().csmla_forward_noalloc(ctypes.byref(problem), ctypes.byref(tensors),
-                                      md.ctypes.data_as(ctypes.POINTER(_i32)), _p(stream))
+    st = load().csmla_forward_noalloc(ctypes.byref(problem), ctypes.byref(tensors), _md_pointer(metadata),
+                                      _p(stream))
     if raise_on_error:
         _check(st, "csmla_forward_noalloc")
     return st
@@ -423,9 +440,8 @@ def csmla_indexer_plan(problem: CsmlaIndexerProblem, lengths: Optional[CsmlaInde
 
 def csmla_indexer_forward(problem: CsmlaIndexerProblem, tensors: CsmlaIndexerTensors, metadata: np.ndarray,
                           stream: int = 0, raise_on_error: bool = True) -> int:
-    md = np.ascontiguousarray(metadata, dtype=np.int32)
     st = _load_indexer().csmla_indexer_forward(ctypes.byref(problem), ctypes.byref(tensors),
-                                               md.ctypes.data_as(ctypes.POINTER(_i32)), _p(stream))
+                                               _md_pointer(metadata, 1), _p(stream))
     if raise_on_error:
         _check(st, "csmla_indexer_forward")
     return st

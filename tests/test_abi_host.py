@@ -184,6 +184,31 @@ def test_forward_rejects_inconsistent_key_parts(monkeypatch):
     assert m.csmla_forward(p, fake_tensors(ws - 256), md, raise_on_error=False) == WORKSPACE
 
 
+def test_binding_metadata_pointer_follows_the_array(monkeypatch):
+    """The binding reuses the ctypes pointer of a metadata array passed again:
+    in-place edits of that array must still reach the C side, and a converted
+    copy (another dtype) must never be the one kept."""
+    from sparse_compressed_mla_amd import binding as bd
+    for k in ("CSMLA_KERNEL", "CSMLA_DK_PARTS", "CSMLA_DK_TEST"):
+        monkeypatch.delenv(k, raising=False)
+    p = base_problem(batch=4, t1=4)
+    _, md, ws = m.csmla_plan(p)
+    t = fake_tensors(ws)
+    ok = m.csmla_forward(p, t, md, raise_on_error=False)
+    assert ok not in (MISMATCH, INVALID, WORKSPACE)      # past every host check (no GPU here)
+    assert bd._md_pointer(md) is bd._md_pointer(md)
+    assert ctypes.addressof(bd._md_pointer(md).contents) == md.ctypes.data
+    md[14] = 3                                           # same object, edited in place
+    assert m.csmla_forward(p, t, md, raise_on_error=False) == MISMATCH
+    md[14] = 2
+    assert m.csmla_forward(p, t, md, raise_on_error=False) == ok
+    wide = md.astype(np.int64)
+    assert m.csmla_forward(p, t, wide, raise_on_error=False) == ok
+    assert bd._md_last[0][0] is md
+    wide[14] = 3
+    assert m.csmla_forward(p, t, wide, raise_on_error=False) == MISMATCH
+
+
 def test_forward_rejects_bad_head_group(monkeypatch):
     monkeypatch.delenv("CSMLA_KERNEL", raising=False)
     p = base_problem()
