@@ -2048,10 +2048,12 @@ __device__ __forceinline__ void dk_body(KArgPtr ap, uint8_t* smem, int w) {
       *(uint2*)(smem + j * kRow + 2 * d) = pack_bf16x4(sc * acc[db][0], sc * acc[db][1], sc * acc[db][2], sc * acc[db][3]);
     }
     lds_barrier();
-    // wave w stores head rows w, w + waves, ...: a row is 1 KiB = 64 lanes x 16 bytes
+    // wave w stores head rows w, w + waves, ...: a row is 1 KiB = 64 lanes x 16 bytes.
+    // Non-temporal: where a work-group runs several units, the rows then do
+    // not push the next unit's key rows out of L2.
     for (int row = w; row < ae.hg; row += kDkWaves) {
       const v4i x = *(const v4i*)(smem + row * kRow + 16 * lane);
-      *(v4i*)(ae.out + ((size_t)t * ae.n1 + h0 + row) * kD + 8 * lane) = x;
+      __builtin_nontemporal_store(x, (v4i*)(ae.out + ((size_t)t * ae.n1 + h0 + row) * kD + 8 * lane));
     }
     if (u + 1 < u_end) lds_barrier();   // the staging area is read before the next unit's gathers
   }
