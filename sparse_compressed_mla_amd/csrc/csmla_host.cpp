@@ -333,14 +333,20 @@ csmla_status csmla_plan(const csmla_problem* p, const csmla_host_lengths* hl, in
     else if (pf_ok) hg = kN1;
   }
   if (T1 > 256 && pf_ok) hg = kN1;
-  // 12 to 24 tokens: 16-head groups in two key parts (below) instead of
+  // 12 to 28 tokens: 16-head groups in two key parts (below) instead of
   // 8-head groups.  Measured on MI355X with 640 keys per token (two rounds,
   // one box): 12 / 16 / 20 / 24 tokens 14.97 / 15.04 / 15.61 / 15.83 us
   // against 15.10 / 15.62 / 16.14 / 16.08 us; equal at 28 tokens, slower at
-  // 4, 8 and 32 (14.61 / 14.51 / 16.62 against 14.37 / 14.44 / 16.40 us).  A
-  // kernel override (CSMLA_KERNEL) keeps its own choice.
+  // 4, 8 and 32 (14.61 / 14.51 / 16.62 against 14.37 / 14.44 / 16.40 us).
+  // With the output rows stored non-temporally the parted plan also wins
+  // from 25 to 28 tokens (four interleaved rounds, one box: 28 tokens 16.04
+  // against 16.40 us).  At 32 tokens it gains only 0.8% (16.25 against
+  // 16.38 us) while its exchange moves ~4 MB of tagged partials (22.8 MB
+  // per launch against 14.3 MB measured), so 8-head groups over whole key
+  // lists keep 29 to 32 tokens.  A kernel override (CSMLA_KERNEL) keeps its
+  // own choice.
   bool h16_parts = false;
-  if (hg == 8 && T1 >= 12 && T1 <= 24 && !std::getenv("CSMLA_KERNEL")) {
+  if (hg == 8 && T1 >= 12 && T1 <= 28 && !std::getenv("CSMLA_KERNEL")) {
     hg = 16;
     h16_parts = true;
   }

@@ -107,10 +107,14 @@ def test_validation_matrix(kw, status):
 
 def test_plan_head_split_for_small_decode_batches(monkeypatch):
     """A 32-token per-token-descale decode batch is planned as 8-head groups
-    over whole key lists: 256 units, one split, no workspace."""
-    monkeypatch.delenv("CSMLA_KERNEL", raising=False)
+    over whole key lists: 256 units, one split, no workspace; 33 tokens:
+    16-head groups over whole key lists."""
+    for k in ("CSMLA_KERNEL", "CSMLA_DK_PARTS", "CSMLA_DK_TEST"):
+        monkeypatch.delenv(k, raising=False)
     _, md, ws = m.csmla_plan(base_problem())
-    assert md[12] == 8 and md[5] == 1 and md[6] == 32 * 8 and md[7] == 256 and ws == 0
+    assert md[12] == 8 and md[14] == 1 and md[5] == 1 and md[6] == 32 * 8 and md[7] == 256 and ws == 0
+    _, md, ws = m.csmla_plan(base_problem(batch=33, t1=33))
+    assert md[12] == 16 and md[14] == 1 and md[6] == 33 * 4 and ws == 0
     _, md, _ = m.csmla_plan(base_problem(batch=48, t1=48))
     assert md[12] == 16 and md[6] == 48 * 4               # 8-head groups would need two rounds
     _, md, _ = m.csmla_plan(base_problem(batch=128, t1=128))
@@ -140,21 +144,20 @@ def test_plan_key_parts(monkeypatch):
     """Up to 11 decode tokens: 8-head groups, each split into two key parts on
     one XCD (the grid a whole number of XCD rounds of groups, one unit per
     work-group, the fixed workspace of sync words and exchange slots); 12 to
-    24 tokens: 16-head groups in two parts; CSMLA_DK_PARTS overrides the
+    28 tokens: 16-head groups in two parts; CSMLA_DK_PARTS overrides the
     count within what fits 256 work-groups and the key list's tiles."""
     for k in ("CSMLA_KERNEL", "CSMLA_DK_PARTS", "CSMLA_DK_TEST"):
         monkeypatch.delenv(k, raising=False)
-    _, md, ws = m.csmla_plan(base_problem())
-    assert md[12] == 8 and md[14] == 1 and ws == 0                 # 32 tokens: no parts
     for b, grid in ((11, 176), (8, 128), (4, 64), (3, 48), (1, 16)):
         _, md, ws = m.csmla_plan(base_problem(batch=b, t1=b))
         assert md[12] == 8 and md[14] == 2 and md[6] == b * 16 and md[7] == grid and ws == WS_FIXED, (b, md[:16])
         assert md[5] == 1 and md[15] == 0
-    for b, grid in ((12, 96), (16, 128), (24, 192)):
+    for b, grid in ((12, 96), (16, 128), (24, 192), (25, 208), (28, 224)):
         _, md, ws = m.csmla_plan(base_problem(batch=b, t1=b))
         assert md[12] == 16 and md[14] == 2 and md[6] == b * 8 and md[7] == grid and ws == WS_FIXED, (b, md[:16])
-    _, md, ws = m.csmla_plan(base_problem(batch=25, t1=25))
-    assert md[12] == 8 and md[14] == 1 and ws == 0                 # 25 tokens: 8-head groups, whole
+    for b in (29, 32):
+        _, md, ws = m.csmla_plan(base_problem(batch=b, t1=b))
+        assert md[12] == 8 and md[14] == 1 and md[6] == b * 8 and ws == 0, (b, md[:16])
     monkeypatch.setenv("CSMLA_DK_PARTS", "8")
     _, md, _ = m.csmla_plan(base_problem(batch=4, t1=4))
     assert md[14] == 4 and md[6] == 4 * 8 * 4 and md[7] == 128     # 640 keys = 5 tiles: at most 4 parts

@@ -128,9 +128,9 @@ def test_parts_lengths_leave_some_parts_empty():
     check_case("topk lengths", inp, plan, ws, ref, repeats=2)
 
 
-@pytest.mark.parametrize("batch", [12, 20])
+@pytest.mark.parametrize("batch", [12, 20, 28])
 def test_default_plan_16_head_parts(batch, monkeypatch):
-    """12 to 24 decode tokens: the planner's own choice is 16-head groups in
+    """12 to 28 decode tokens: the planner's own choice is 16-head groups in
     two key parts (no override); parity on two calls of one workspace."""
     for k in ("CSMLA_KERNEL", "CSMLA_DK_PARTS", "CSMLA_DK_TEST"):
         monkeypatch.delenv(k, raising=False)
