@@ -1646,7 +1646,9 @@ __device__ __forceinline__ float dk_heads_reduce(int* misc, int w, int lane, flo
   float x[kDkWaves];
 #pragma unroll
   for (int i = 0; i < kDkWaves; ++i) x[i] = red[16 * i + j];
-  lds_barrier();
+  // No barrier after the reads: every caller passes another barrier (the P
+  // barrier after the probabilities, the epilogue's staging barrier, or the
+  // next unit's resolution barrier) before any wave writes these words again.
 #pragma unroll
   for (int step = kDkWaves / 2; step >= 1; step /= 2)   // pairwise tree
 #pragma unroll
